@@ -1,0 +1,158 @@
+"""CPU oracle for the MSA forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library and its binding) never
+does.  The arithmetic lives in ``msa_oracle.c`` (plain C, fp64 accumulation,
+OpenMP over query rows); this module only compiles it with gcc and marshals
+numpy arrays into it.  See the header of ``msa_oracle.c`` for the passages each
+step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "msa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP).  Always recompiles."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-o", out, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load(path: str | None = None):
+    """Load the compiled oracle; compile it first only if nothing is built."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or _LIB
+    if not os.path.exists(p) or (path is None and os.path.getmtime(p) < os.path.getmtime(_SRC)):
+        build(out=p)
+    lib = ctypes.CDLL(p)
+    P = ctypes.c_void_p
+    i64, i32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+    lib.oracle_block_scores.argtypes = [P, P, i64, i32, i32, i32, P, i64, P]
+    lib.oracle_select.argtypes = [P, P, i64, i32, i64, i32, i32, P, P]
+    lib.oracle_attend.argtypes = [P, P, P, P, P, i64, i64, i32, i32, i32, i32, i32, f64, P]
+    lib.oracle_prefill_rows.argtypes = [P, P, P, P, P, i64, i32, i32, i32, i32, i32, i32, f64,
+                                        P, i64, P, P, P]
+    lib.oracle_decode.argtypes = [P, P, P, P, P, P, i64, i32, i32, i32, i32, i32, i32, f64,
+                                  P, i64, P, P, P]
+    for f in (lib.oracle_block_scores, lib.oracle_select, lib.oracle_attend,
+              lib.oracle_prefill_rows, lib.oracle_decode):
+        f.restype = None
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _u16(a) -> np.ndarray:
+    """bf16 data as a contiguous uint16 numpy array (torch bf16 tensors accepted)."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            return a.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    except ImportError:  # pragma: no cover - torch is always present in this image
+        pass
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        a = a.view(np.uint16)
+    return a
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _rows(rows, L):
+    if rows is None:
+        rows = np.arange(L, dtype=np.int64)
+    return np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+
+
+def block_scores(iq, ik, B, rows=None, lib=None):
+    """S[nrows, G, nb] fp32; entries outside the causal window are -inf."""
+    lib = lib or load()
+    iq, ik = _u16(iq), _u16(ik)
+    L, G, dI = iq.shape
+    rows = _rows(rows, L)
+    nb = (L + B - 1) // B
+    S = np.empty((len(rows), G, nb), np.float32)
+    lib.oracle_block_scores(_ptr(iq), _ptr(ik), L, G, dI, B, _ptr(rows), len(rows), _ptr(S))
+    return S
+
+
+def select(S, rows, B, k, lib=None):
+    """ids[nrows, G, k] (ascending, -1 padded) and gap[nrows, G] from block scores."""
+    lib = lib or load()
+    S = np.ascontiguousarray(S, dtype=np.float32)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    n, G, nb = S.shape
+    ids = np.empty((n, G, k), np.int32)
+    gap = np.empty((n, G), np.float32)
+    lib.oracle_select(_ptr(S), _ptr(rows), n, G, nb, B, k, _ptr(ids), _ptr(gap))
+    return ids, gap
+
+
+def attend(q, k, v, ids, B, scale, rows=None, lib=None):
+    """out[nrows, H, d] float64: exact softmax attention over the given blocks."""
+    lib = lib or load()
+    q, kk, vv = _u16(q), _u16(k), _u16(v)
+    L, H, d = q.shape
+    G = kk.shape[1]
+    rows = _rows(rows, L)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    kslots = ids.shape[2]
+    out = np.empty((len(rows), H, d), np.float64)
+    lib.oracle_attend(_ptr(q), _ptr(kk), _ptr(vv), _ptr(ids), _ptr(rows), len(rows), L, H, G, d,
+                      B, kslots, float(scale), _ptr(out))
+    return out
+
+
+def prefill(q, k, v, iq, ik, B, kslots, scale=None, rows=None, lib=None):
+    """Full MSA prefill for the listed rows: (ids, gap, out)."""
+    lib = lib or load()
+    q, kk, vv, iq, ik = _u16(q), _u16(k), _u16(v), _u16(iq), _u16(ik)
+    L, H, d = q.shape
+    G, dI = iq.shape[1], iq.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    rows = _rows(rows, L)
+    n = len(rows)
+    ids = np.empty((n, G, kslots), np.int32)
+    gap = np.empty((n, G), np.float32)
+    out = np.empty((n, H, d), np.float64)
+    lib.oracle_prefill_rows(_ptr(q), _ptr(kk), _ptr(vv), _ptr(iq), _ptr(ik), L, H, G, d, dI, B,
+                            kslots, float(scale), _ptr(rows), n, _ptr(ids), _ptr(gap), _ptr(out))
+    return ids, gap, out
+
+
+def decode(q, iq, k_cache, v_cache, ik_cache, seq_len, B, kslots, scale=None, seqs=None,
+           lib=None):
+    """MSA decode (query = last cached token of each sequence): (ids, gap, out)."""
+    lib = lib or load()
+    q, iq = _u16(q), _u16(iq)
+    kc, vc, ikc = _u16(k_cache), _u16(v_cache), _u16(ik_cache)
+    N, H, d = q.shape
+    G, dI = iq.shape[1], iq.shape[2]
+    Lmax = kc.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    seq_len = np.ascontiguousarray(np.asarray(seq_len, dtype=np.int64))
+    seqs = _rows(seqs, N)
+    n = len(seqs)
+    ids = np.empty((n, G, kslots), np.int32)
+    gap = np.empty((n, G), np.float32)
+    out = np.empty((n, H, d), np.float64)
+    lib.oracle_decode(_ptr(q), _ptr(iq), _ptr(kc), _ptr(vc), _ptr(ikc), _ptr(seq_len), Lmax, H,
+                      G, d, dI, B, kslots, float(scale), _ptr(seqs), n, _ptr(ids), _ptr(gap),
+                      _ptr(out))
+    return ids, gap, out

@@ -1,0 +1,405 @@
+"""Pins for the CPU oracle: each check ties the oracle to something other than
+itself -- a library routine in a special case the method reduces to, a
+mathematical property stated on the pages, a constructed case whose answer is
+fixed by construction, or brute force on tiny inputs.
+
+Pages: "MiniMax M3 算力省 20 倍" (mizuki-eaf.pages.dev) §二 Index/Main Branch,
+§三 item 4 (Local Block), §四 exp-free TopK; "MiniMax-M3上架DEVUP…" (163.com):
+MSA extends GQA, per-group selection, exact attention inside selected blocks.
+
+Every ``check_*`` takes the compiled oracle library, so the mutation test at
+the bottom can run the same battery against deliberately broken copies.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import _refs
+
+pytestmark = pytest.mark.filterwarnings("ignore::UserWarning")
+
+TIE = 1e-4
+
+
+def _inputs(L, H, G, d, dI, B, k, seed, plant="lit"):
+    s = synth.PrefillShape(L=L, H=H, G=G, d=d, dI=dI, B=B, k=k)
+    return s, synth.prefill_inputs(s, seed=seed, plant=plant)
+
+
+def _bf16(a) -> torch.Tensor:
+    return torch.as_tensor(np.asarray(a, np.float32)).to(torch.bfloat16)
+
+
+# --------------------------------------------------------------------------
+# 1. Special case k*B >= L: every causal block is selected, so MSA is exactly
+#    dense causal GQA ("MSA extends GQA", DEVUP) -> library SDPA, is_causal.
+# --------------------------------------------------------------------------
+def check_dense_equivalence(lib):
+    for (L, H, G, d, dI, B, k, seed) in [(96, 4, 2, 16, 8, 16, 6, 0), (130, 6, 3, 8, 8, 32, 5, 1)]:
+        s, x = _inputs(L, H, G, d, dI, B, k, seed)
+        scale = 1.0 / math.sqrt(d)
+        ids, gap, out = oracle.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], B, k, scale,
+                                       lib=lib)
+        for i in range(L):
+            bi = i // B
+            for g in range(G):
+                want = list(range(bi + 1)) + [-1] * (k - bi - 1)
+                assert ids[i, g].tolist() == want, (i, g, ids[i, g])
+        ref = _refs.sdpa_causal(x["q"], x["k"], x["v"], scale).numpy()
+        assert np.abs(out - ref).max() < 1e-9
+
+
+# --------------------------------------------------------------------------
+# 2. Special case k = 1: only the query's own block -> block-diagonal causal
+#    attention -> library SDPA with that mask.
+# --------------------------------------------------------------------------
+def check_local_only(lib):
+    L, H, G, d, dI, B = 100, 4, 2, 16, 8, 16
+    s, x = _inputs(L, H, G, d, dI, B, 1, 2)
+    scale = 0.3
+    ids, gap, out = oracle.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], B, 1, scale, lib=lib)
+    assert (ids[:, :, 0] == (np.arange(L) // B)[:, None]).all()
+    blk = torch.arange(L) // B
+    m = (blk[:, None] == blk[None, :]) & torch.tril(torch.ones(L, L, dtype=torch.bool))
+    ref = _refs.sdpa_masked(x["q"], x["k"], x["v"], m[None].expand(H, L, L), scale).numpy()
+    assert np.abs(out - ref).max() < 1e-9
+
+
+# --------------------------------------------------------------------------
+# 3. Main branch for an arbitrary selection equals library attention with
+#    the mask "block selected by the query's group, and t <= i".
+# --------------------------------------------------------------------------
+def check_masked_attention(lib):
+    for (L, H, G, d, dI, B, k, seed) in [(200, 8, 2, 16, 8, 16, 4, 3), (160, 6, 3, 24, 8, 32, 3, 4)]:
+        s, x = _inputs(L, H, G, d, dI, B, k, seed)
+        scale = 1.0 / math.sqrt(d)
+        ids, gap, out = oracle.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], B, k, scale,
+                                       lib=lib)
+        mask = _refs.mask_from_ids(ids, L, B, H, G)
+        ref = _refs.sdpa_masked(x["q"], x["k"], x["v"], mask, scale).numpy()
+        assert np.abs(out - ref).max() < 1e-9
+        # the same holds for ids that did not come from the index branch
+        rng = np.random.default_rng(seed)
+        ids2 = np.full_like(ids, -1)
+        for i in range(L):
+            bi = i // B
+            for g in range(G):
+                extra = rng.choice(bi, size=min(k - 1, bi), replace=False) if bi else []
+                ch = sorted(list(extra) + [bi])
+                ids2[i, g, :len(ch)] = ch
+        out2 = oracle.attend(x["q"], x["k"], x["v"], ids2, B, scale, lib=lib)
+        ref2 = _refs.sdpa_masked(x["q"], x["k"], x["v"],
+                                 _refs.mask_from_ids(ids2, L, B, H, G), scale).numpy()
+        assert np.abs(out2 - ref2).max() < 1e-9
+
+
+# --------------------------------------------------------------------------
+# 4. exp-free selection == selection after softmax (softmax keeps order;
+#    "MiniMax M3 算力省 20 倍" §四 exp-free TopK): softmax over the causal token
+#    scores, max-pool of probabilities, library top-k.
+# --------------------------------------------------------------------------
+def check_exp_free(lib):
+    for (L, G, dI, B, k, seed, plant) in [(384, 2, 16, 16, 5, 5, "lit"), (512, 3, 8, 32, 4, 6, "none"),
+                                          (256, 2, 32, 8, 6, 7, "hot")]:
+        s, x = _inputs(L, G, G, 8, dI, B, k, seed, plant)
+        S = oracle.block_scores(x["iq"], x["ik"], B, lib=lib)
+        ids, gap = oracle.select(S, np.arange(L), B, k, lib=lib)
+        ref = _refs.softmax_pool_topk(x["iq"], x["ik"], B, k)
+        ok = gap >= TIE
+        assert ok.mean() > 0.9
+        assert (ids[ok] == ref[ok]).all()
+
+
+# --------------------------------------------------------------------------
+# 5. Constructed cases: idx-K rows are multiples of basis vectors, so every
+#    token score, every block maximum and hence the selection are fixed by
+#    construction (no dot product is evaluated by the test).
+# --------------------------------------------------------------------------
+def _constructed(seed):
+    """G=3 groups, dI=4, B=8, L=96 (12 blocks), k=4.
+    ik[t] = w[t] * e_0 + z[t] * e_1.  Group 0 uses iq = e_0 (score w),
+    group 1 uses iq = -e_0 (score -w), group 2 uses iq = 2 e_1 (score 2 z)."""
+    rng = np.random.default_rng(seed)
+    L, G, dI, B, k = 96, 3, 4, 8, 4
+    nb = L // B
+    # block maxima: distinct integers; the max sits at a random position
+    peak_w = rng.permutation(nb) + 20          # max of w per block (group 0 ranks)
+    low_w = -(rng.permutation(nb) + 20)        # min of w per block (group 1 ranks -w)
+    peak_z = rng.permutation(nb) + 20
+    w = np.zeros(L)
+    z = np.zeros(L)
+    for b in range(nb):
+        vals = rng.integers(-8, 9, size=B).astype(float)   # filler strictly inside (-20, 20)
+        pw, pl = rng.choice(B, size=2, replace=False)
+        vals[pw] = peak_w[b]
+        vals[pl] = low_w[b]
+        w[b * B:(b + 1) * B] = vals
+        zv = rng.integers(-8, 9, size=B).astype(float)
+        zv[rng.integers(B)] = peak_z[b]
+        z[b * B:(b + 1) * B] = zv
+    ik = np.zeros((L, dI))
+    ik[:, 0] = w
+    ik[:, 1] = z
+    iq = np.zeros((L, G, dI))
+    iq[:, 0, 0] = 1.0
+    iq[:, 1, 0] = -1.0
+    iq[:, 2, 1] = 2.0
+    # expected: per group a rank value per block (larger = better), only blocks < b(i)
+    rank = np.stack([peak_w, -low_w, 2 * peak_z])          # [G, nb] block maxima by construction
+    return L, G, dI, B, k, ik, iq, rank, w, z
+
+
+def check_constructed(lib):
+    for seed in range(3):
+        L, G, dI, B, k, ik, iq, rank, w, z = _constructed(seed)
+        S = oracle.block_scores(_bf16(iq), _bf16(ik), B, lib=lib)
+        nb = L // B
+        for i in range(L):
+            bi = i // B
+            for g in range(G):
+                # competitors' block scores are the constructed maxima
+                assert np.array_equal(S[i, g, :bi], rank[g, :bi].astype(np.float32)), (i, g)
+                # the own block is scored over the causal window t <= i only
+                t = np.arange(bi * B, i + 1)
+                tok = [w[t], -w[t], 2 * z[t]][g]
+                assert S[i, g, bi] == np.float32(tok.max()), (i, g)
+                assert np.all(np.isneginf(S[i, g, bi + 1:]))
+        ids, gap = oracle.select(S, np.arange(L), B, k, lib=lib)
+        for i in range(L):
+            bi = i // B
+            for g in range(G):
+                order = np.argsort(-rank[g, :bi], kind="stable")[:k - 1]
+                want = sorted(list(order) + [bi])
+                want += [-1] * (k - len(want))
+                assert ids[i, g].tolist() == want, (seed, i, g, ids[i, g], want)
+
+
+def check_tie_break(lib):
+    """Equal block scores: the smaller block id wins (reading where the pages
+    are silent).  Every token score equals 1, so all blocks tie."""
+    L, G, dI, B, k = 64, 1, 2, 8, 3
+    ik = np.zeros((L, dI))
+    ik[:, 0] = 1.0
+    iq = np.zeros((L, G, dI))
+    iq[:, 0, 0] = 1.0
+    S = oracle.block_scores(_bf16(iq), _bf16(ik), B, lib=lib)
+    ids, gap = oracle.select(S, np.arange(L), B, k, lib=lib)
+    for i in range(L):
+        bi = i // B
+        want = sorted(set(list(range(min(k - 1, bi))) + [bi]))
+        assert ids[i, 0].tolist() == want + [-1] * (k - len(want))
+        if bi > k - 1:
+            assert gap[i, 0] == 0.0
+
+
+# --------------------------------------------------------------------------
+# 6. Brute force on tiny inputs: explicit token-score loops, pooled block
+#    scores, and the selection as the k-1-subset of competitors with the
+#    largest total score (equivalent to top-(k-1) when scores are distinct),
+#    then attention with explicit per-token weights.
+# --------------------------------------------------------------------------
+def _brute(q, kk, vv, iq, ik, B, k, scale):
+    q, kk, vv, iq, ik = (_refs.f64(a).numpy() for a in (q, kk, vv, iq, ik))
+    L, H, d = q.shape
+    G = kk.shape[1]
+    r = H // G
+    ids = np.full((L, G, k), -1, np.int32)
+    out = np.zeros((L, H, d))
+    for i in range(L):
+        bi = i // B
+        for g in range(G):
+            tok = {t: float(np.dot(iq[i, g], ik[t])) for t in range(i + 1)}
+            blk = {}
+            for t, sc in tok.items():
+                blk[t // B] = max(blk.get(t // B, -np.inf), sc)
+            comp = [b for b in range(bi)]
+            m = min(k - 1, len(comp))
+            best, best_sum = (), -np.inf
+            for sub in itertools.combinations(comp, m):
+                tot = sum(np.float32(blk[b]) for b in sub)
+                if tot > best_sum:
+                    best, best_sum = sub, tot
+            ch = sorted(list(best) + [bi])
+            ids[i, g, :len(ch)] = ch
+            toks = [t for t in range(i + 1) if t // B in ch]
+            for hh in range(g * r, (g + 1) * r):
+                z = np.array([scale * np.dot(q[i, hh], kk[t, g]) for t in toks])
+                p = np.exp(z - z.max())
+                p /= p.sum()
+                out[i, hh] = sum(p[u] * vv[t, g] for u, t in enumerate(toks))
+    return ids, out
+
+
+def check_brute_force(lib):
+    for (L, H, G, d, dI, B, k, seed) in [(40, 4, 2, 8, 4, 4, 3, 8), (48, 2, 1, 4, 4, 8, 2, 9),
+                                         (36, 6, 3, 4, 8, 4, 1, 10)]:
+        s, x = _inputs(L, H, G, d, dI, B, k, seed)
+        scale = 1.0 / math.sqrt(d)
+        ids, gap, out = oracle.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], B, k, scale,
+                                       lib=lib)
+        bids, bout = _brute(x["q"], x["k"], x["v"], x["iq"], x["ik"], B, k, scale)
+        ok = gap >= TIE
+        assert (ids[ok] == bids[ok]).all()
+        okrow = np.repeat(ok, H // G, axis=1)
+        assert np.abs(out - bout)[okrow].max() < 1e-9
+
+
+# --------------------------------------------------------------------------
+# 7. Invariants of every selection ("MiniMax M3 算力省 20 倍" §二, §三 item 4):
+#    own block present, ids unique/ascending/in range, count = min(k, b(i)+1).
+# --------------------------------------------------------------------------
+def assert_selection_invariants(ids: np.ndarray, rows: np.ndarray, B: int, k: int):
+    for r, i in enumerate(rows):
+        bi = int(i) // B
+        n = min(k, bi + 1)
+        for g in range(ids.shape[1]):
+            row = ids[r, g]
+            assert (row[n:] == -1).all(), (i, g, row)
+            v = row[:n]
+            assert (v >= 0).all() and (v <= bi).all(), (i, g, row)
+            assert (np.diff(v) > 0).all(), (i, g, row)
+            assert bi in v, (i, g, row)
+
+
+def check_invariants(lib):
+    for (L, G, dI, B, k, seed) in [(1000, 2, 16, 16, 5, 11), (777, 4, 8, 32, 3, 12)]:
+        s, x = _inputs(L, G, G, 8, dI, B, k, seed)
+        S = oracle.block_scores(x["iq"], x["ik"], B, lib=lib)
+        ids, gap = oracle.select(S, np.arange(L), B, k, lib=lib)
+        assert_selection_invariants(ids, np.arange(L), B, k)
+
+
+# --------------------------------------------------------------------------
+# 8. Property tests: scale invariance, within-block permutation, planted block.
+# --------------------------------------------------------------------------
+def check_properties(lib):
+    L, H, G, d, dI, B, k = 256, 4, 2, 16, 16, 16, 4
+    s, x = _inputs(L, H, G, d, dI, B, k, 13)
+    scale = 1.0 / math.sqrt(d)
+    ids, gap, out = oracle.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], B, k, scale, lib=lib)
+    # (a) doubling idx-Q (exact in bf16) changes no selection
+    ids2, gap2, _ = oracle.prefill(x["q"], x["k"], x["v"], x["iq"] * 2, x["ik"], B, k, scale,
+                                   lib=lib)
+    assert (ids2 == ids).all()
+    # (b) permuting the tokens inside block j leaves every later row unchanged
+    j = 5
+    perm = torch.randperm(B, generator=torch.Generator().manual_seed(0)) + j * B
+    y = {n: t.clone() for n, t in x.items() if isinstance(t, torch.Tensor)}
+    for n in ("k", "v", "ik"):
+        y[n][j * B:(j + 1) * B] = x[n][perm]
+    ids3, gap3, out3 = oracle.prefill(y["q"], y["k"], y["v"], y["iq"], y["ik"], B, k, scale,
+                                      lib=lib)
+    later = np.arange(L) >= (j + 1) * B
+    assert (ids3[later] == ids[later]).all()
+    assert np.abs(out3[later] - out[later]).max() < 1e-12
+    # (c) a planted block with a large score along each group's query direction
+    #     is selected by every row that can select it
+    j = 3
+    u = x["iq"].float().mean(0)                                   # [G, dI]
+    y = {n: t.clone() for n, t in x.items() if isinstance(t, torch.Tensor)}
+    y["iq"] = (x["iq"].float() + 3.0 * u.sign()[None]).to(torch.bfloat16)
+    y["ik"][j * B:(j + 1) * B] = (50.0 * u.sign().sum(0).sign())[None].to(torch.bfloat16)
+    ids4, _, _ = oracle.prefill(y["q"], y["k"], y["v"], y["iq"], y["ik"], B, k, scale, lib=lib)
+    rows = np.arange(L)[np.arange(L) // B > j]
+    assert all(j in ids4[i, g] for i in rows for g in range(G))
+
+
+# --------------------------------------------------------------------------
+# 9. Prefix consistency and decode == last prefill row.
+# --------------------------------------------------------------------------
+def check_prefix_and_decode(lib):
+    L, H, G, d, dI, B, k = 300, 4, 2, 16, 8, 16, 4
+    s, x = _inputs(L, H, G, d, dI, B, k, 14)
+    scale = 1.0 / math.sqrt(d)
+    ids, gap, out = oracle.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], B, k, scale, lib=lib)
+    Lp = 173
+    idsp, gapp, outp = oracle.prefill(x["q"][:Lp], x["k"][:Lp], x["v"][:Lp], x["iq"][:Lp],
+                                      x["ik"][:Lp], B, k, scale, lib=lib)
+    assert (idsp == ids[:Lp]).all()
+    assert np.array_equal(outp, out[:Lp])
+    # decode: sequence n holds the prefill tensors; its query is token seq_len-1
+    seq_len = np.array([300, 1, 16, 17, 255], np.int64)
+    N = len(seq_len)
+    qd = torch.stack([x["q"][sl - 1] for sl in seq_len])
+    iqd = torch.stack([x["iq"][sl - 1] for sl in seq_len])
+    kc = x["k"][None].expand(N, L, G, d).contiguous()
+    vc = x["v"][None].expand(N, L, G, d).contiguous()
+    ikc = x["ik"][None].expand(N, L, dI).contiguous()
+    idsd, gapd, outd = oracle.decode(qd, iqd, kc, vc, ikc, seq_len, B, k, scale, lib=lib)
+    for n, sl in enumerate(seq_len):
+        assert (idsd[n] == ids[sl - 1]).all()
+        assert np.array_equal(outd[n], out[sl - 1])
+
+
+PINS = [check_dense_equivalence, check_local_only, check_masked_attention, check_exp_free,
+        check_constructed, check_tie_break, check_brute_force, check_invariants,
+        check_properties, check_prefix_and_decode]
+
+
+@pytest.mark.parametrize("check", PINS, ids=[c.__name__ for c in PINS])
+def test_pin(check):
+    check(oracle.load())
+
+
+# --------------------------------------------------------------------------
+# 10. Mutation test: plausible mistakes planted in copies of the oracle source
+#     (on the CPU) must each fail at least one of the pins above.
+# --------------------------------------------------------------------------
+MUTANTS = {
+    "causal_window_excludes_self": ("if (t_end > i + 1) t_end = i + 1;", "if (t_end > i) t_end = i;"),
+    "pool_takes_first_token": ("if (s > best) best = s;", "if (t == b * B) best = s;"),
+    "pool_takes_min": ("double best = -INFINITY;", "double best = INFINITY;",
+                       "if (s > best) best = s;", "if (s < best) best = s;"),
+    "tie_break_larger_id": ("if (best < 0 || S[b] > S[best]) best = b;",
+                            "if (best < 0 || S[b] >= S[best]) best = b;"),
+    "select_smallest": ("if (best < 0 || S[b] > S[best]) best = b;",
+                        "if (best < 0 || S[b] < S[best]) best = b;"),
+    "local_not_forced": ("chosen[nchosen++] = (int32_t)bi;         /* local block takes one slot */",
+                         "if (bi < 0) chosen[nchosen++] = (int32_t)bi;"),
+    "attn_ignores_causal": ("if (t <= i) tok[n++] = t;", "tok[n++] = t;"),
+    "wrong_group_of_head": ("int g = h / r;", "int g = h % G;"),
+    "scale_dropped": ("z[u] = scale * s;", "z[u] = s;"),
+    "values_from_keys": ("const uint16_t *vt = vv + (tok[u] * G + g) * d;",
+                         "const uint16_t *vt = kk + (tok[u] * G + g) * d;"),
+    "index_key_row_stride": ("const uint16_t *kv = ik + t * dI;", "const uint16_t *kv = ik + t;"),
+    "index_group_ignored": ("const uint16_t *qv = iq_row + (int64_t)g * dI;",
+                            "const uint16_t *qv = iq_row;"),
+    "key_group_ignored": ("const uint16_t *kt = kk + (tok[u] * G + g) * d;",
+                          "const uint16_t *kt = kk + (tok[u] * G) * d;"),
+    "no_max_subtraction_sign": ("z[u] = exp(z[u] - m);", "z[u] = exp(m - z[u]);"),
+    "blocks_after_query_compete": ("int64_t ncand = bi;", "int64_t ncand = bi + 1;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = open(oracle._SRC).read()
+    rep = MUTANTS[name]
+    for a, b in zip(rep[0::2], rep[1::2]):
+        assert src.count(a) >= 1, f"mutation anchor not found: {a}"
+        src = src.replace(a, b)
+    path = tmp_path / f"{name}.c"
+    path.write_text(src)
+    so = tmp_path / f"{name}.so"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-o", str(so),
+                    str(path), "-lm"], check=True)
+    lib = oracle.load(str(so))
+    caught = []
+    for check in PINS:
+        try:
+            check(lib)
+        except AssertionError:
+            caught.append(check.__name__)
+        except Exception as e:  # a crash of the mutant also counts as caught
+            caught.append(f"{check.__name__}:{type(e).__name__}")
+    assert caught, f"mutant {name} passed every pin"
