@@ -1,0 +1,226 @@
+"""MiniMax Sparse Attention (MSA) forward pass on MI355X -- Python binding.
+
+A thin ctypes layer over ``libmsa.so`` (C ABI in ``include/msa.h``): it checks
+tensor dtypes/shapes/devices, allocates outputs and the workspace with torch,
+passes raw device pointers and torch's current HIP stream, and turns status
+codes into exceptions.  Every step of the computation runs in the library's
+HIP kernels; there is no fallback path.  If the library is not built, every call
+raises ``MSAError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["MSAError", "select_blocks", "sparse_attn", "prefill", "decode", "workspace_size",
+           "library_path", "load_library"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmsa.so")
+_lib = None
+
+MSA_OK = 0
+_STATUS = {0: "MSA_OK", 1: "MSA_ERR_INVALID_ARG", 2: "MSA_ERR_UNSUPPORTED",
+           3: "MSA_ERR_WORKSPACE_TOO_SMALL", 4: "MSA_ERR_HIP"}
+
+
+class MSAError(RuntimeError):
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmsa.so (built in-tree by ``build.py``); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise MSAError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                       "(or python block_sparse_long_idx_amd/build.py)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i32, i64, sz, f32 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
+                            ctypes.c_float)
+    lib.msa_status_string.argtypes = [i32]
+    lib.msa_status_string.restype = ctypes.c_char_p
+    lib.msa_select_blocks_workspace_size.argtypes = [i64, i32, i32, i32, i32]
+    lib.msa_select_blocks_workspace_size.restype = sz
+    lib.msa_select_blocks.argtypes = [P, P, i64, i32, i32, i32, i32, P, P, sz, P]
+    lib.msa_select_blocks.restype = i32
+    lib.msa_sparse_attn_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
+    lib.msa_sparse_attn_workspace_size.restype = sz
+    lib.msa_sparse_attn.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, i32, f32, P, P, sz, P]
+    lib.msa_sparse_attn.restype = i32
+    lib.msa_prefill_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32, i32]
+    lib.msa_prefill_workspace_size.restype = sz
+    lib.msa_prefill.argtypes = [P, P, P, P, P, i64, i32, i32, i32, i32, i32, i32, f32, P, P, P,
+                                sz, P]
+    lib.msa_prefill.restype = i32
+    lib.msa_decode_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32]
+    lib.msa_decode_workspace_size.restype = sz
+    lib.msa_decode.argtypes = [P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, i32, i32, f32, P,
+                               P, P, sz, P]
+    lib.msa_decode.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != MSA_OK:
+        raise MSAError(f"{what} failed: {_STATUS.get(status, status)}", status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, ndim, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise MSAError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise MSAError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise MSAError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise MSAError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise MSAError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise MSAError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    """uint8 device buffer whose data pointer is 256-byte aligned."""
+    buf = torch.empty(max(int(nbytes), 1) + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + max(int(nbytes), 1)]
+
+
+def _scale(scale, d):
+    return float(scale) if scale is not None else 1.0 / math.sqrt(d)
+
+
+def workspace_size(kind: str, **kw) -> int:
+    lib = load_library()
+    if kind == "select":
+        return lib.msa_select_blocks_workspace_size(kw["L"], kw["G"], kw["dI"], kw.get("B", 128),
+                                                    kw["k"])
+    if kind == "sparse_attn":
+        return lib.msa_sparse_attn_workspace_size(kw["L"], kw["H"], kw["G"], kw["d"],
+                                                  kw.get("B", 128), kw["k"])
+    if kind == "prefill":
+        return lib.msa_prefill_workspace_size(kw["L"], kw["H"], kw["G"], kw["d"], kw["dI"],
+                                              kw.get("B", 128), kw["k"])
+    if kind == "decode":
+        return lib.msa_decode_workspace_size(kw["N"], kw["Lmax"], kw["H"], kw["G"], kw["d"],
+                                             kw["dI"], kw.get("B", 128), kw["k"])
+    raise ValueError(kind)
+
+
+def select_blocks(idx_q, idx_k, k: int = 16, B: int = 128, out=None, workspace=None):
+    """Block ids [L, G, k] (int32, ascending, -1 padded) of the index branch."""
+    lib = load_library()
+    _need(idx_q, "idx_q", torch.bfloat16, 3)
+    _need(idx_k, "idx_k", torch.bfloat16, 2, idx_q.device)
+    L, G, dI = idx_q.shape
+    if idx_k.shape != (L, dI):
+        raise MSAError(f"idx_k must be [{L}, {dI}], got {tuple(idx_k.shape)}")
+    if out is None:
+        out = torch.empty((L, G, k), dtype=torch.int32, device=idx_q.device)
+    _need(out, "out", torch.int32, 3, idx_q.device)
+    nbytes = lib.msa_select_blocks_workspace_size(L, G, dI, B, k)
+    ws = workspace if workspace is not None else _workspace(nbytes, idx_q.device)
+    st = lib.msa_select_blocks(_ptr(idx_q), _ptr(idx_k), L, G, dI, B, k, _ptr(out), _ptr(ws),
+                               ws.numel(), _stream(idx_q.device))
+    _check(st, "msa_select_blocks")
+    return out
+
+
+def sparse_attn(q, k, v, block_ids, scale=None, B: int = 128, out=None, workspace=None):
+    """Exact softmax attention over the listed blocks: out [L, H, d] bf16."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(k, "k", torch.bfloat16, 3, dev)
+    _need(v, "v", torch.bfloat16, 3, dev)
+    _need(block_ids, "block_ids", torch.int32, 3, dev)
+    L, H, d = q.shape
+    G = k.shape[1]
+    kslots = block_ids.shape[2]
+    if k.shape != (L, G, d) or v.shape != (L, G, d) or block_ids.shape[:2] != (L, G):
+        raise MSAError("inconsistent shapes for q/k/v/block_ids")
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = lib.msa_sparse_attn_workspace_size(L, H, G, d, B, kslots)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    st = lib.msa_sparse_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(block_ids), L, H, G, d, B, kslots,
+                             _scale(scale, d), _ptr(out), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "msa_sparse_attn")
+    return out
+
+
+def prefill(q, k, v, idx_q, idx_k, kslots: int = 16, B: int = 128, scale=None,
+            return_ids: bool = False, out=None, ids_out=None, workspace=None):
+    """Whole MSA prefill: out [L, H, d] bf16 (and ids [L, G, k] if return_ids)."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    for name, t, nd in (("k", k, 3), ("v", v, 3), ("idx_q", idx_q, 3), ("idx_k", idx_k, 2)):
+        _need(t, name, torch.bfloat16, nd, dev)
+    L, H, d = q.shape
+    G, dI = idx_q.shape[1], idx_q.shape[2]
+    if (k.shape != (L, G, d) or v.shape != (L, G, d) or idx_q.shape[0] != L
+            or idx_k.shape != (L, dI)):
+        raise MSAError("inconsistent shapes for q/k/v/idx_q/idx_k")
+    if out is None:
+        out = torch.empty_like(q)
+    if return_ids and ids_out is None:
+        ids_out = torch.empty((L, G, kslots), dtype=torch.int32, device=dev)
+    nbytes = lib.msa_prefill_workspace_size(L, H, G, d, dI, B, kslots)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    st = lib.msa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(idx_q), _ptr(idx_k), L, H, G, d, dI, B,
+                         kslots, _scale(scale, d), _ptr(out), _ptr(ids_out), _ptr(ws), ws.numel(),
+                         _stream(dev))
+    _check(st, "msa_prefill")
+    return (out, ids_out) if return_ids else out
+
+
+def decode(q, idx_q, k_cache, v_cache, idx_k_cache, seq_len, kslots: int = 16, B: int = 128,
+           scale=None, return_ids: bool = False, out=None, ids_out=None, workspace=None):
+    """MSA decode of N sequences (query = last cached token): out [N, H, d] bf16."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(idx_q, "idx_q", torch.bfloat16, 3, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _need(idx_k_cache, "idx_k_cache", torch.bfloat16, 3, dev)
+    _need(seq_len, "seq_len", torch.int32, 1, dev)
+    N, H, d = q.shape
+    G, dI = idx_q.shape[1], idx_q.shape[2]
+    Lmax = k_cache.shape[1]
+    if (k_cache.shape != (N, Lmax, G, d) or v_cache.shape != (N, Lmax, G, d)
+            or idx_k_cache.shape != (N, Lmax, dI) or seq_len.shape != (N,)):
+        raise MSAError("inconsistent shapes for decode inputs")
+    if out is None:
+        out = torch.empty_like(q)
+    if return_ids and ids_out is None:
+        ids_out = torch.empty((N, G, kslots), dtype=torch.int32, device=dev)
+    nbytes = lib.msa_decode_workspace_size(N, Lmax, H, G, d, dI, B, kslots)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    st = lib.msa_decode(_ptr(q), _ptr(idx_q), _ptr(k_cache), _ptr(v_cache), _ptr(idx_k_cache),
+                        _ptr(seq_len), N, Lmax, H, G, d, dI, B, kslots, _scale(scale, d), _ptr(out),
+                        _ptr(ids_out), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "msa_decode")
+    return (out, ids_out) if return_ids else out

@@ -1,0 +1,266 @@
+// msa_api.hip -- the C ABI of libmsa.so (declared in include/msa.h): argument
+// validation, workspace carving and the launch sequence of each entry point.
+//
+// Prefill runs over query chunks of at most kChunkQ queries so that the
+// workspace stays bounded at any L (block scores and partials are per chunk);
+// every query's result is independent of the chunking.  Per chunk:
+//   K1 index score + block max-pool -> K2 exp-free top-k -> K3 schedule ->
+//   K4 KV-outer attention -> K5 combine.
+// Decode: K1d -> K2 -> K4d -> K5.
+// Nothing here allocates, frees or synchronises.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "msa.h"
+#include "msa_launch.h"
+
+namespace {
+
+using namespace msa;
+
+constexpr int64_t kChunkQ = 32768;     // queries per prefill chunk
+constexpr size_t kAlign = 256;
+
+// Workspace carving: with base == nullptr only the size is accumulated.
+struct Carver {
+    char *base;
+    size_t used = 0;
+    explicit Carver(void *b) : base(static_cast<char *>(b)) {}
+    template <typename T>
+    T *take(int64_t count) {
+        used = (used + kAlign - 1) / kAlign * kAlign;
+        T *p = base ? reinterpret_cast<T *>(base + used) : nullptr;
+        used += (size_t)std::max<int64_t>(count, 0) * sizeof(T);
+        return p;
+    }
+};
+
+struct AttnWs {
+    SchedBuffers sb;
+    uint16_t *po;
+    float *plse;
+};
+
+AttnWs carve_attn(Carver &c, int64_t C, int H, int G, int d, int k, int nb) {
+    AttnWs w;
+    const int64_t lists = (int64_t)G * nb;
+    w.sb.counts = c.take<int>(lists);
+    w.sb.offs = c.take<int>(lists + 1);
+    w.sb.toff = c.take<int>(lists + 1);
+    w.sb.cursor = c.take<int>(lists);
+    w.sb.total = c.take<int>(1);
+    w.sb.list = c.take<uint32_t>(C * G * k);
+    w.po = c.take<uint16_t>(C * H * k * d);
+    w.plse = c.take<float>(C * H * k);
+    return w;
+}
+
+int64_t chunk_of(int64_t L) { return std::min<int64_t>(round_up(std::max<int64_t>(L, 1), kBlock), kChunkQ); }
+int64_t nblocks(int64_t L) { return (L + kBlock - 1) / kBlock; }
+int nb_padded(int64_t L) { return (int)round_up(std::max<int64_t>(nblocks(L), 1), 8); }
+
+bool r_ok(int H, int G) {
+    if (G <= 0 || H % G) return false;
+    const int r = H / G;
+    return r == 1 || r == 2 || r == 4 || r == 8 || r == 16 || r == 32;
+}
+bool d_ok(int d) { return d == 64 || d == 128; }
+bool index_ok(int G, int dI) {
+    return (G == 1 || G == 2 || G == 4 || G == 8) && (dI == 32 || dI == 64 || dI == 128) &&
+           G * dI <= 512;
+}
+
+int check_ws(void *ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return MSA_OK;
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    return ws_bytes >= need ? MSA_OK : MSA_ERR_WORKSPACE_TOO_SMALL;
+}
+
+float default_scale(float scale, int d) { return scale > 0.0f ? scale : 1.0f / sqrtf((float)d); }
+
+#define MSA_TRY(expr)                                   \
+    do {                                                \
+        if ((expr) != hipSuccess) return MSA_ERR_HIP;   \
+    } while (0)
+
+// Shared by prefill and sparse_attn: K3 + K4 + K5 for queries [q0, qend).
+int attn_chunk(const uint16_t *q, const uint16_t *kx, const uint16_t *vx, const int32_t *ids_c,
+               int64_t L, int64_t q0, int64_t qend, int H, int G, int d, int k, float scale,
+               uint16_t *out, const AttnWs &w, hipStream_t s) {
+    const int64_t C = qend - q0;
+    const int nbc = (int)((qend - 1) / kBlock + 1);
+    MSA_TRY(launch_k3_schedule(ids_c, C, G, k, nbc, w.sb, s));
+    MSA_TRY(launch_k4_kv_outer(q, kx, vx, w.sb, nbc, L, q0, C, H, G, d, k, scale, w.po, w.plse, s));
+    MSA_TRY(launch_k5_combine(w.po, w.plse, ids_c, C, H, G, d, k, nbc, out + q0 * H * d, s));
+    return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *msa_status_string(int status) {
+    switch (status) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
+    case MSA_ERR_WORKSPACE_TOO_SMALL: return "MSA_ERR_WORKSPACE_TOO_SMALL";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP";
+    default: return "MSA_ERR_UNKNOWN";
+    }
+}
+
+// ------------------------------- select -----------------------------------
+size_t msa_select_blocks_workspace_size(int64_t L, int G, int dI, int B, int k) {
+    (void)dI; (void)B; (void)k;
+    if (L <= 0 || G <= 0) return 0;
+    Carver c(nullptr);
+    c.take<float>(chunk_of(L) * G * nb_padded(L));
+    return c.used;
+}
+
+int msa_select_blocks(const uint16_t *idx_q, const uint16_t *idx_k, int64_t L, int G, int dI,
+                      int B, int k, int32_t *block_ids, void *ws, size_t ws_bytes, void *stream) {
+    if (L < 0 || G <= 0 || dI <= 0 || B <= 0 || k < 1) return MSA_ERR_INVALID_ARG;
+    if (L == 0) return MSA_OK;
+    if (!idx_q || !idx_k || !block_ids) return MSA_ERR_INVALID_ARG;
+    if (B != kBlock || !index_ok(G, dI) || k > 32) return MSA_ERR_UNSUPPORTED;
+    const int st = check_ws(ws, ws_bytes, msa_select_blocks_workspace_size(L, G, dI, B, k));
+    if (st != MSA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Carver c(ws);
+    const int nbp = nb_padded(L);
+    float *S = c.take<float>(chunk_of(L) * G * nbp);
+    const int64_t C = chunk_of(L);
+    for (int64_t q0 = 0; q0 < L; q0 += C) {
+        const int64_t qend = std::min(L, q0 + C);
+        MSA_TRY(launch_k1_index_pool(idx_q, idx_k, S, L, q0, qend, G, dI, nbp, s));
+        MSA_TRY(launch_k2_select(S, nbp, (qend - q0) * G, G, k, q0, nullptr, 0,
+                                 block_ids + q0 * G * k, s));
+    }
+    return MSA_OK;
+}
+
+// ----------------------------- sparse attn --------------------------------
+size_t msa_sparse_attn_workspace_size(int64_t L, int H, int G, int d, int B, int kslots) {
+    (void)B;
+    if (L <= 0 || G <= 0 || H <= 0 || d <= 0 || kslots <= 0) return 0;
+    Carver c(nullptr);
+    carve_attn(c, chunk_of(L), H, G, d, kslots, (int)nblocks(L));
+    return c.used;
+}
+
+int msa_sparse_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    const int32_t *block_ids, int64_t L, int H, int G, int d, int B, int kslots,
+                    float scale, uint16_t *out, void *ws, size_t ws_bytes, void *stream) {
+    if (L < 0 || H <= 0 || G <= 0 || d <= 0 || B <= 0 || kslots < 1 || H % G)
+        return MSA_ERR_INVALID_ARG;
+    if (L == 0) return MSA_OK;
+    if (!q || !k || !v || !block_ids || !out) return MSA_ERR_INVALID_ARG;
+    if (B != kBlock || !d_ok(d) || !r_ok(H, G) || kslots > 32) return MSA_ERR_UNSUPPORTED;
+    const int st = check_ws(ws, ws_bytes, msa_sparse_attn_workspace_size(L, H, G, d, B, kslots));
+    if (st != MSA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    scale = default_scale(scale, d);
+    Carver c(ws);
+    const int64_t C = chunk_of(L);
+    const AttnWs w = carve_attn(c, C, H, G, d, kslots, (int)nblocks(L));
+    for (int64_t q0 = 0; q0 < L; q0 += C) {
+        const int64_t qend = std::min(L, q0 + C);
+        const int rc = attn_chunk(q, k, v, block_ids + q0 * G * kslots, L, q0, qend, H, G, d, kslots,
+                                  scale, out, w, s);
+        if (rc != MSA_OK) return rc;
+    }
+    return MSA_OK;
+}
+
+// -------------------------------- prefill ---------------------------------
+size_t msa_prefill_workspace_size(int64_t L, int H, int G, int d, int dI, int B, int k) {
+    (void)dI; (void)B;
+    if (L <= 0 || G <= 0 || H <= 0 || d <= 0 || k <= 0) return 0;
+    const int64_t C = chunk_of(L);
+    Carver c(nullptr);
+    c.take<float>(C * G * nb_padded(L));
+    c.take<int32_t>(C * G * k);
+    carve_attn(c, C, H, G, d, k, (int)nblocks(L));
+    return c.used;
+}
+
+int msa_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *idx_q,
+                const uint16_t *idx_k, int64_t L, int H, int G, int d, int dI, int B, int kslots,
+                float scale, uint16_t *out, int32_t *block_ids_out, void *ws, size_t ws_bytes,
+                void *stream) {
+    if (L < 0 || H <= 0 || G <= 0 || d <= 0 || dI <= 0 || B <= 0 || kslots < 1 || H % G)
+        return MSA_ERR_INVALID_ARG;
+    if (L == 0) return MSA_OK;
+    if (!q || !k || !v || !idx_q || !idx_k || !out) return MSA_ERR_INVALID_ARG;
+    if (B != kBlock || !d_ok(d) || !r_ok(H, G) || !index_ok(G, dI) || kslots > 32)
+        return MSA_ERR_UNSUPPORTED;
+    const int st = check_ws(ws, ws_bytes, msa_prefill_workspace_size(L, H, G, d, dI, B, kslots));
+    if (st != MSA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    scale = default_scale(scale, d);
+    const int64_t C = chunk_of(L);
+    const int nbp = nb_padded(L);
+    Carver c(ws);
+    float *S = c.take<float>(C * G * nbp);
+    int32_t *ids_ws = c.take<int32_t>(C * G * kslots);
+    const AttnWs w = carve_attn(c, C, H, G, d, kslots, (int)nblocks(L));
+    for (int64_t q0 = 0; q0 < L; q0 += C) {
+        const int64_t qend = std::min(L, q0 + C);
+        int32_t *ids_c = block_ids_out ? block_ids_out + q0 * G * kslots : ids_ws;
+        MSA_TRY(launch_k1_index_pool(idx_q, idx_k, S, L, q0, qend, G, dI, nbp, s));
+        MSA_TRY(launch_k2_select(S, nbp, (qend - q0) * G, G, kslots, q0, nullptr, 0, ids_c, s));
+        const int rc = attn_chunk(q, k, v, ids_c, L, q0, qend, H, G, d, kslots, scale, out, w, s);
+        if (rc != MSA_OK) return rc;
+    }
+    return MSA_OK;
+}
+
+// -------------------------------- decode ----------------------------------
+size_t msa_decode_workspace_size(int N, int64_t Lmax, int H, int G, int d, int dI, int B, int k) {
+    (void)dI; (void)B;
+    if (N <= 0 || Lmax <= 0 || G <= 0 || H <= 0 || d <= 0 || k <= 0) return 0;
+    Carver c(nullptr);
+    c.take<float>((int64_t)N * G * nb_padded(Lmax));
+    c.take<int32_t>((int64_t)N * G * k);
+    c.take<uint16_t>((int64_t)N * H * k * d);
+    c.take<float>((int64_t)N * H * k);
+    return c.used;
+}
+
+int msa_decode(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache,
+               const uint16_t *v_cache, const uint16_t *idx_k_cache, const int32_t *seq_len,
+               int N, int64_t Lmax, int H, int G, int d, int dI, int B, int kslots, float scale,
+               uint16_t *out, int32_t *block_ids_out, void *ws, size_t ws_bytes, void *stream) {
+    if (N < 0 || Lmax < 0 || H <= 0 || G <= 0 || d <= 0 || dI <= 0 || B <= 0 || kslots < 1 ||
+        H % G)
+        return MSA_ERR_INVALID_ARG;
+    if (N == 0) return MSA_OK;
+    if (Lmax == 0 || !q || !idx_q || !k_cache || !v_cache || !idx_k_cache || !seq_len || !out)
+        return MSA_ERR_INVALID_ARG;
+    if (B != kBlock || !d_ok(d) || !r_ok(H, G) || !index_ok(G, dI) || kslots > 32)
+        return MSA_ERR_UNSUPPORTED;
+    const int st = check_ws(ws, ws_bytes, msa_decode_workspace_size(N, Lmax, H, G, d, dI, B, kslots));
+    if (st != MSA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    scale = default_scale(scale, d);
+    const int nbp = nb_padded(Lmax);
+    Carver c(ws);
+    float *S = c.take<float>((int64_t)N * G * nbp);
+    int32_t *ids_ws = c.take<int32_t>((int64_t)N * G * kslots);
+    uint16_t *po = c.take<uint16_t>((int64_t)N * H * kslots * d);
+    float *plse = c.take<float>((int64_t)N * H * kslots);
+    int32_t *ids = block_ids_out ? block_ids_out : ids_ws;
+    MSA_TRY(launch_k1d_index_pool(idx_q, idx_k_cache, seq_len, S, N, Lmax, G, dI, nbp, s));
+    MSA_TRY(launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, seq_len, Lmax, ids, s));
+    MSA_TRY(launch_k4d_split(q, k_cache, v_cache, ids, seq_len, N, Lmax, H, G, d, kslots, scale, po,
+                             plse, s));
+    MSA_TRY(launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, s));
+    return MSA_OK;
+}
+
+}  // extern "C"

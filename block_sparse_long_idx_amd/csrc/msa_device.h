@@ -1,0 +1,136 @@
+// msa_device.h -- device helpers shared by the MSA kernels (gfx950, wave64).
+//
+// MFMA lane layouts used throughout (v_mfma_f32_32x32x16_bf16 and
+// v_mfma_f32_16x16x32_bf16; lane l, half hf = l / 32, quarter qt = l / 16):
+//   32x32x16:  A[m][k]: lane m + 32*hf holds k = 8*hf .. 8*hf+7 of row m
+//              B[k][n]: lane n + 32*hf holds k = 8*hf .. 8*hf+7 of column n
+//              D[m][n]: lane n + 32*((m/4)%2), register (m%4) + 4*(m/8)
+//   16x16x32:  A[m][k]: lane m + 16*qt holds k = 8*qt .. 8*qt+7
+//              B[k][n]: lane n + 16*qt holds k = 8*qt .. 8*qt+7
+//              D[m][n]: lane n + 16*(m/4), register m%4
+// Because A and B pair the same (lane half, element) to the same k, any
+// consistent relabelling of the contraction index is free; the kernels use that
+// to keep every operand load a single 16-byte contiguous read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "msa_launch.h"
+
+namespace msa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 with round-to-nearest-even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ u32x4 load16(const void *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ void store16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+__device__ __forceinline__ void store8(void *p, u32x2 v) { *reinterpret_cast<u32x2 *>(p) = v; }
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float xor_shfl(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+// Monotone map of a float to uint32 (larger float -> larger key).  -0 and +0
+// map to the same key after canonicalisation.
+__device__ __forceinline__ uint32_t float_order_key(float v) {
+    if (v == 0.0f) v = 0.0f;
+    uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// LDS tile of 128 rows x W bf16 (W = 8*CPR), 16-byte chunks XOR-swizzled by row so
+// that 16 consecutive rows read at one chunk position hit distinct banks.
+template <int CPR>
+__device__ __forceinline__ int swz(int row, int chunk) {
+    constexpr int kMask = (CPR < 16 ? CPR : 16) - 1;
+    return row * (CPR * 16) + ((chunk ^ (row & kMask)) << 4);
+}
+
+// Copy a 128-row tile of CPR 16-byte chunks per row from global rows at
+// `src + row*stride_bytes` (rows >= nrows are zero-filled) into swizzled LDS.
+// Called by all 256 threads of a work-group.
+template <int CPR>
+__device__ __forceinline__ void stage_rows(char *lds, const char *src, int64_t stride_bytes,
+                                           int nrows, int tid) {
+    constexpr int kRowsPerIter = 256 / CPR;
+    constexpr int kIters = kBlock / kRowsPerIter;
+    const int c = tid % CPR;
+    u32x4 regs[kIters];
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+        const int row = tid / CPR + it * kRowsPerIter;
+        regs[it] = (row < nrows) ? load16(src + row * stride_bytes + c * 16) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+        const int row = tid / CPR + it * kRowsPerIter;
+        store16(lds + swz<CPR>(row, c), regs[it]);
+    }
+}
+
+// Stage V (128 keys x D values, rows at `src + key*stride_bytes`) TRANSPOSED into
+// LDS as D rows of 128 keys (16 chunks of 8 keys, swizzled).  Keys >= nrows are 0.
+template <int D>
+__device__ __forceinline__ void stage_v_transposed(char *lds, const char *src,
+                                                   int64_t stride_bytes, int nrows, int tid) {
+    constexpr int CPR = D / 8;                   // 16-byte chunks of d per V row
+    constexpr int kQuadsPerIter = 256 / CPR;     // key quads covered per iteration
+    constexpr int kIters = (kBlock / 4) / kQuadsPerIter;
+    const int dc = tid % CPR;
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+        const int kq = tid / CPR + it * kQuadsPerIter;   // keys 4kq .. 4kq+3
+        u32x4 r[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int key = 4 * kq + kk;
+            r[kk] = (key < nrows) ? load16(src + key * stride_bytes + dc * 16) : u32x4{0, 0, 0, 0};
+        }
+        // element e of chunk dc is d = 8*dc + e; gather the 4 keys for each d
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int w = e >> 1, sh = (e & 1) * 16;
+            uint32_t v0 = (r[0][w] >> sh) & 0xFFFFu, v1 = (r[1][w] >> sh) & 0xFFFFu;
+            uint32_t v2 = (r[2][w] >> sh) & 0xFFFFu, v3 = (r[3][w] >> sh) & 0xFFFFu;
+            const int d = 8 * dc + e;
+            const int key0 = 4 * kq;
+            char *p = lds + swz<16>(d, key0 >> 3) + ((key0 >> 2) & 1) * 8;
+            store8(p, u32x2{v0 | (v1 << 16), v2 | (v3 << 16)});
+        }
+    }
+}
+
+}  // namespace msa

@@ -1,0 +1,262 @@
+// msa_index.hip -- index branch, scoring part: token index scores max-pooled
+// into block scores ("MiniMax M3 算力省 20 倍", §二 Index Branch: one index-query
+// head per GQA group, one index-key head shared by all groups, dot products
+// over the causal window, max-pooling into B = 128-token blocks).
+//
+// K1 (prefill) is a short-K GEMM with a max-pool epilogue, run on bf16 MFMA with
+// fp32 accumulation.  One work-group owns one query block (128 queries x G
+// groups = 128*G stacked index rows, which are contiguous in idx_q[L,G,dI]) and
+// a range of up to 32 key blocks strictly before the query block; the query's
+// own block is never scored because it is always selected.  Index rows stay in
+// registers for the whole range; each 128-key block of idx_k is staged once in
+// LDS (double-buffered) and multiplied as S^T = K * IQ^T so that a lane's
+// accumulators hold 16 keys of one index row: the 128-key max is an in-lane max
+// plus one exchange between the two half-waves.  Block maxima are buffered in
+// LDS and flushed as contiguous 32-byte row segments.  The L x L token score
+// matrix never exists in memory.
+//
+// K1d (decode) streams each sequence's idx_k cache once (the HBM-bound part of
+// decode): one wave per 128-key block, 16x16x32 MFMA with the G index heads as
+// the N dimension, operands loaded straight from global memory.
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+constexpr int kK1Flush = 8;   // key blocks buffered in LDS between flushes
+
+// Work items are ordered key-chunk-major: for key chunk c, query blocks
+// qb in [max(qb0, 32c+1), qb1) each score key blocks [32c, min(32c+32, qb)).
+__device__ __forceinline__ bool k1_item(int64_t item, int qb0, int qb1, int &qb, int &c) {
+    for (c = 0;; ++c) {
+        const int lo = max(qb0, c * kK1KeyChunk + 1);
+        if (lo >= qb1) return false;
+        const int64_t n = qb1 - lo;
+        if (item < n) {
+            qb = lo + (int)item;
+            return true;
+        }
+        item -= n;
+    }
+}
+
+int64_t k1_num_items(int qb0, int qb1) {
+    int64_t total = 0;
+    for (int c = 0;; ++c) {
+        const int lo = qb0 > c * kK1KeyChunk + 1 ? qb0 : c * kK1KeyChunk + 1;
+        if (lo >= qb1) break;
+        total += qb1 - lo;
+    }
+    return total;
+}
+
+template <int G, int DI>
+__global__ __launch_bounds__(256) void k1_index_pool(const uint16_t *__restrict__ iq,
+                                                     const uint16_t *__restrict__ ik,
+                                                     float *__restrict__ S, int64_t q0,
+                                                     int64_t qend, int nbp, int qb0, int qb1,
+                                                     int64_t n_items) {
+    constexpr int CPR = DI / 8;            // 16-byte chunks per index row
+    constexpr int KS = DI / 16;            // MFMA K-steps
+    constexpr int NCOL = kBlock * G;       // stacked index rows of the work-group
+    constexpr int TILE = kBlock * DI * 2;  // bytes of one staged key block
+    __shared__ __attribute__((aligned(16))) char lds_k[2][TILE];
+    __shared__ float lds_s[kK1Flush][NCOL];
+
+    // XCD-aware order: consecutive logical items (same key chunk) on one XCD.
+    const int64_t per = gridDim.x / 8;
+    const int64_t item = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    int qb, c;
+    if (item >= n_items || !k1_item(item, qb0, qb1, qb, c)) return;
+    const int j0 = c * kK1KeyChunk;
+    const int j1 = min(j0 + kK1KeyChunk, qb);
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int hf = lane >> 5, l32 = lane & 31;
+
+    // B operand: index rows of this wave, kept in registers.
+    bf16x8 bq[G][KS];
+    const int64_t row0 = (int64_t)qb * kBlock * G;   // flattened [L*G] row of column 0
+    const int64_t row_end = qend * G;
+#pragma unroll
+    for (int nt = 0; nt < G; ++nt) {
+        const int64_t row = row0 + wave * 32 * G + nt * 32 + l32;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            bq[nt][ks] = as_bf16x8(row < row_end ? load16(iq + row * DI + (2 * ks + hf) * 8)
+                                                 : u32x4{0, 0, 0, 0});
+    }
+
+    const char *ikb = reinterpret_cast<const char *>(ik);
+    const int64_t blk_bytes = (int64_t)kBlock * DI * 2;
+    stage_rows<CPR>(lds_k[0], ikb + j0 * blk_bytes, DI * 2, kBlock, tid);
+    __syncthreads();
+
+    constexpr int kRowsPerIter = 256 / CPR;
+    constexpr int kIters = kBlock / kRowsPerIter;
+    for (int j = j0; j < j1; ++j) {
+        const int buf = (j - j0) & 1;
+        // prefetch the next key block into registers
+        u32x4 pre[kIters];
+        const bool more = j + 1 < j1;
+        if (more) {
+            const char *src = ikb + (j + 1) * blk_bytes;
+#pragma unroll
+            for (int it = 0; it < kIters; ++it) {
+                const int row = tid / CPR + it * kRowsPerIter;
+                pre[it] = load16(src + row * (DI * 2) + (tid % CPR) * 16);
+            }
+        }
+        float mx[G];
+#pragma unroll
+        for (int nt = 0; nt < G; ++nt) mx[nt] = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x16 acc[G];
+#pragma unroll
+            for (int nt = 0; nt < G; ++nt) acc[nt] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = as_bf16x8(load16(lds_k[buf] + swz<CPR>(mt * 32 + l32, 2 * ks + hf)));
+#pragma unroll
+                for (int nt = 0; nt < G; ++nt) acc[nt] = mfma32(a, bq[nt][ks], acc[nt]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < G; ++nt) {
+                float m = acc[nt][0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[nt][r]);
+                mx[nt] = fmaxf(mx[nt], m);
+            }
+        }
+        const int slot = (j - j0) % kK1Flush;
+#pragma unroll
+        for (int nt = 0; nt < G; ++nt) {
+            const float m = fmaxf(mx[nt], xor_shfl(mx[nt], 32));
+            if (hf == 0) lds_s[slot][wave * 32 * G + nt * 32 + l32] = m;
+        }
+        if (more) {
+#pragma unroll
+            for (int it = 0; it < kIters; ++it) {
+                const int row = tid / CPR + it * kRowsPerIter;
+                store16(lds_k[buf ^ 1] + swz<CPR>(row, tid % CPR), pre[it]);
+            }
+        }
+        __syncthreads();
+        if (slot == kK1Flush - 1 || j == j1 - 1) {
+            const int nj = slot + 1;
+            const int jb = j - slot;
+            for (int col = tid; col < NCOL; col += 256) {
+                const int64_t row = row0 + col;
+                if (row >= row_end) continue;
+                float *dst = S + (row - q0 * G) * nbp + jb;
+                if (nj == kK1Flush) {
+                    store16(dst, u32x4{__float_as_uint(lds_s[0][col]), __float_as_uint(lds_s[1][col]),
+                                       __float_as_uint(lds_s[2][col]), __float_as_uint(lds_s[3][col])});
+                    store16(dst + 4, u32x4{__float_as_uint(lds_s[4][col]), __float_as_uint(lds_s[5][col]),
+                                           __float_as_uint(lds_s[6][col]), __float_as_uint(lds_s[7][col])});
+                } else {
+                    for (int jj = 0; jj < nj; ++jj) dst[jj] = lds_s[jj][col];
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+template <int G, int DI>
+static hipError_t k1_dispatch(const uint16_t *iq, const uint16_t *ik, float *S, int64_t q0,
+                              int64_t qend, int nbp, hipStream_t s) {
+    const int qb0 = (int)(q0 / kBlock);
+    const int qb1 = (int)((qend + kBlock - 1) / kBlock);
+    const int64_t n = k1_num_items(qb0, qb1);
+    if (n == 0) return hipSuccess;
+    const int64_t grid = round_up(n, 8);
+    hipLaunchKernelGGL((k1_index_pool<G, DI>), dim3((unsigned)grid), dim3(256), 0, s, iq, ik, S,
+                       q0, qend, nbp, qb0, qb1, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_k1_index_pool(const uint16_t *iq, const uint16_t *ik, float *S, int64_t L,
+                                int64_t q0, int64_t qend, int G, int dI, int nbp,
+                                hipStream_t s) {
+    (void)L;
+#define K1_CASE(g, di) \
+    if (G == g && dI == di) return k1_dispatch<g, di>(iq, ik, S, q0, qend, nbp, s);
+    K1_CASE(1, 32) K1_CASE(1, 64) K1_CASE(1, 128)
+    K1_CASE(2, 32) K1_CASE(2, 64) K1_CASE(2, 128)
+    K1_CASE(4, 32) K1_CASE(4, 64) K1_CASE(4, 128)
+    K1_CASE(8, 32) K1_CASE(8, 64)
+#undef K1_CASE
+    return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// K1d: one wave per (sequence, 128-key block).  grid = (ceil(nbmax/4), N).
+// ---------------------------------------------------------------------------
+template <int G, int DI>
+__global__ __launch_bounds__(256) void k1d_index_pool(const uint16_t *__restrict__ iq,
+                                                      const uint16_t *__restrict__ ikc,
+                                                      const int32_t *__restrict__ seq_len,
+                                                      float *__restrict__ S, int64_t Lmax,
+                                                      int nbp) {
+    constexpr int KS = DI / 32;
+    const int n = blockIdx.y;
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int b = blockIdx.x * 4 + wave;
+    const int sl = seq_len[n];
+    if (sl < 1 || sl > Lmax) return;
+    const int ncomp = (sl - 1) / kBlock;       // blocks before the query's own block
+    if (b >= ncomp) return;
+    const int l16 = lane & 15, qt = lane >> 4;
+
+    bf16x8 bq[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        bq[ks] = as_bf16x8(l16 < G ? load16(iq + ((int64_t)n * G + l16) * DI + 32 * ks + 8 * qt)
+                                   : u32x4{0, 0, 0, 0});
+    const uint16_t *base = ikc + ((int64_t)n * Lmax + (int64_t)b * kBlock) * DI;
+    u32x4 a[8][KS];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            a[mt][ks] = load16(base + (mt * 16 + l16) * DI + 32 * ks + 8 * qt);
+    float m = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+        f32x4 acc = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma16(as_bf16x8(a[mt][ks]), bq[ks], acc);
+        m = fmaxf(m, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+    }
+    m = fmaxf(m, xor_shfl(m, 16));
+    m = fmaxf(m, xor_shfl(m, 32));
+    if (lane < G) S[((int64_t)n * G + lane) * nbp + b] = m;
+}
+
+template <int G, int DI>
+static hipError_t k1d_dispatch(const uint16_t *iq, const uint16_t *ikc, const int32_t *seq_len,
+                               float *S, int N, int64_t Lmax, int nbp, hipStream_t s) {
+    const int64_t nbmax = (Lmax - 1) / kBlock;   // competitors of the longest sequence
+    if (nbmax <= 0 || N <= 0) return hipSuccess;
+    dim3 grid((unsigned)((nbmax + 3) / 4), (unsigned)N);
+    hipLaunchKernelGGL((k1d_index_pool<G, DI>), grid, dim3(256), 0, s, iq, ikc, seq_len, S, Lmax,
+                       nbp);
+    return hipGetLastError();
+}
+
+hipError_t launch_k1d_index_pool(const uint16_t *iq, const uint16_t *ikc, const int32_t *seq_len,
+                                 float *S, int N, int64_t Lmax, int G, int dI, int nbp,
+                                 hipStream_t s) {
+#define K1D_CASE(g, di) \
+    if (G == g && dI == di) return k1d_dispatch<g, di>(iq, ikc, seq_len, S, N, Lmax, nbp, s);
+    K1D_CASE(1, 32) K1D_CASE(1, 64) K1D_CASE(1, 128)
+    K1D_CASE(2, 32) K1D_CASE(2, 64) K1D_CASE(2, 128)
+    K1D_CASE(4, 32) K1D_CASE(4, 64) K1D_CASE(4, 128)
+    K1D_CASE(8, 32) K1D_CASE(8, 64)
+#undef K1D_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace msa

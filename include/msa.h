@@ -1,0 +1,140 @@
+/*
+ * msa.h -- C ABI of libmsa.so: the MiniMax Sparse Attention (MSA) forward pass
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Pages defining the operations (cited by title and section):
+ *   [M3-20x] "MiniMax M3 算力省 20 倍" (mizuki-eaf.pages.dev): §二 MSA -- Index
+ *            Branch (one index-query head per GQA group, one index-key head shared
+ *            by all groups, dot-product scores over the causal window, max-pooled
+ *            into blocks, top-k blocks chosen per group, the query's own block always
+ *            chosen) and Main Branch (standard softmax attention over the tokens of
+ *            the chosen blocks only; B = 128, k = 16, a 2048-token budget);
+ *            §三 item 4 (the local block keeps one of the slots);
+ *            §四 Kernel (exp-free top-k; KV-outer iteration that gathers the queries
+ *            of each KV block; pre-scheduled chunking of hot tiles; two-phase combine
+ *            without atomics).
+ *   [SERVE]  "MiniMax M3 的采用瓶颈，会卡在 serving 生态" (the-context.pages.dev):
+ *            §发生了什么 / §对建设者的影响 -- a block-selection step plus a dedicated
+ *            sparse kernel, a KV-block-major layout, index scoring, paged decode.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are DEVICE pointers owned by the caller, row-major, token-major.
+ *     bf16 values are passed as their uint16_t bit patterns.
+ *   - Shapes: L tokens, H query heads, G KV heads (= index groups; H % G == 0,
+ *     query head h belongs to group h / (H/G)), d head dim, dI index dim, B block
+ *     size, k slots per (query, group) INCLUDING the query's own block.
+ *   - Token i sees keys t <= i.  Block of token i: b(i) = i / B.
+ *   - scale: softmax scale applied to q.k; pass a value <= 0 for 1/sqrt(d).
+ *   - ws / ws_bytes: caller-owned device workspace of at least the size returned
+ *     by the matching *_workspace_size() call; 256-byte alignment required.
+ *     The library never allocates device memory and never synchronises; all work is
+ *     enqueued on `stream` (a hipStream_t passed as void*, NULL = default stream).
+ *   - Return value: an msa_status.  Every argument is validated BEFORE anything is
+ *     launched; on an error nothing is launched and no output is written.  Faults
+ *     inside kernels surface at the caller's next synchronisation of `stream`.
+ *   - Functions are stateless and thread-safe; calls on one stream are ordered.
+ *   - Supported on the GPU: B = 128; d in {64, 128}; dI in {32, 64, 128};
+ *     H/G in {1, 2, 4, 8, 16, 32}; G * dI <= 512; 1 <= k <= 32; any L >= 0.
+ *     Anything else returns MSA_ERR_UNSUPPORTED.
+ *   - Rows are independent: results do not depend on how the library splits the
+ *     queries into chunks, and repeated calls give bitwise-identical outputs.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MSA_API __attribute__((visibility("default")))
+#else
+#define MSA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum msa_status {
+    MSA_OK = 0,
+    MSA_ERR_INVALID_ARG = 1,          /* null pointer, negative size, H % G != 0, k < 1 */
+    MSA_ERR_UNSUPPORTED = 2,          /* shape outside the supported set above */
+    MSA_ERR_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes below the required size, or ws misaligned */
+    MSA_ERR_HIP = 4                   /* a HIP launch reported an error */
+} msa_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+MSA_API const char *msa_status_string(int status);
+
+/* ---------------------------------------------------------------------------
+ * Index branch [M3-20x §二 Index Branch; §三 item 4; §四 exp-free TopK].
+ * For every token i and group g: score every key t <= i as
+ * s = sum_c idx_q[i,g,c] * idx_k[t,c], max-pool the scores of each B-token block,
+ * and select the query's own block b(i) plus the k-1 blocks b < b(i) with the
+ * largest block scores (raw scores, no exp; equal scores -> smaller id first).
+ *   idx_q     [L, G, dI] bf16      index-query head of each group
+ *   idx_k     [L, dI]    bf16      index-key head shared by all groups
+ *   block_ids [L, G, k]  int32 OUT selected block ids, ascending, padded with -1
+ *                                  when b(i) + 1 < k (fewer blocks exist)
+ * ------------------------------------------------------------------------- */
+MSA_API size_t msa_select_blocks_workspace_size(int64_t L, int G, int dI, int B, int k);
+MSA_API int msa_select_blocks(const uint16_t *idx_q, const uint16_t *idx_k, int64_t L, int G, int dI,
+                      int B, int k, int32_t *block_ids, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Main branch [M3-20x §二 Main Branch; §四 KV-outer attention, hot-tile chunking,
+ * two-phase combine].  Exact softmax attention of each query head over the tokens
+ * t <= i of the blocks listed for its group (entries < 0 are ignored):
+ *   out[i,h] = sum_t softmax_t(scale * q[i,h].k[t,g]) v[t,g],  g = h / (H/G).
+ *   q         [L, H, d]  bf16
+ *   k, v      [L, G, d]  bf16
+ *   block_ids [L, G, kslots] int32  each valid id must lie in [0, b(i)] and be
+ *                                   unique within its row; the own block b(i) must
+ *                                   be present (it is what msa_select_blocks emits).
+ *                                   Rows violating this give unspecified values in
+ *                                   their own output rows only.
+ *   out       [L, H, d]  bf16 OUT
+ * ------------------------------------------------------------------------- */
+MSA_API size_t msa_sparse_attn_workspace_size(int64_t L, int H, int G, int d, int B, int kslots);
+MSA_API int msa_sparse_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    const int32_t *block_ids, int64_t L, int H, int G, int d, int B, int kslots,
+                    float scale, uint16_t *out, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Whole prefill: msa_select_blocks followed by msa_sparse_attn on the same rows.
+ * block_ids_out [L, G, k] may be NULL (the ids then live only in the workspace).
+ * ------------------------------------------------------------------------- */
+MSA_API size_t msa_prefill_workspace_size(int64_t L, int H, int G, int d, int dI, int B, int k);
+MSA_API int msa_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *idx_q,
+                const uint16_t *idx_k, int64_t L, int H, int G, int d, int dI, int B, int kslots,
+                float scale, uint16_t *out, int32_t *block_ids_out, void *ws, size_t ws_bytes,
+                void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode [M3-20x §二, §四 decode result; SERVE: paged MSA decode].  N independent
+ * sequences; sequence n holds seq_len[n] cached tokens and its query is the LAST
+ * cached token, position p = seq_len[n] - 1 (the new token is already inserted).
+ * The query scores every block of its own cache, selects as in the index branch,
+ * and attends over the selected blocks (split over the k slots, then combined).
+ *   q           [N, H, d]         bf16   query of each sequence
+ *   idx_q       [N, G, dI]        bf16
+ *   k_cache     [N, Lmax, G, d]   bf16   contiguous per-sequence caches
+ *   v_cache     [N, Lmax, G, d]   bf16
+ *   idx_k_cache [N, Lmax, dI]     bf16
+ *   seq_len     [N] int32 DEVICE  1 <= seq_len[n] <= Lmax.  A sequence outside that
+ *                                 range gets ids all -1 and a zero output row;
+ *                                 nothing outside its cache is read.
+ *   out         [N, H, d]         bf16 OUT
+ *   block_ids_out [N, G, k] int32 OUT, may be NULL
+ * ------------------------------------------------------------------------- */
+MSA_API size_t msa_decode_workspace_size(int N, int64_t Lmax, int H, int G, int d, int dI, int B, int k);
+MSA_API int msa_decode(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache,
+               const uint16_t *v_cache, const uint16_t *idx_k_cache, const int32_t *seq_len,
+               int N, int64_t Lmax, int H, int G, int d, int dI, int B, int kslots, float scale,
+               uint16_t *out, int32_t *block_ids_out, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

@@ -46,8 +46,10 @@ def load(path: str | None = None):
                                         P, i64, P, P, P]
     lib.oracle_decode.argtypes = [P, P, P, P, P, P, i64, i32, i32, i32, i32, i32, i32, f64,
                                   P, i64, P, P, P]
+    lib.oracle_decode_attend.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, i32, f64, P, i64,
+                                         P, P]
     for f in (lib.oracle_block_scores, lib.oracle_select, lib.oracle_attend,
-              lib.oracle_prefill_rows, lib.oracle_decode):
+              lib.oracle_prefill_rows, lib.oracle_decode, lib.oracle_decode_attend):
         f.restype = None
     if path is None:
         _lib = lib
@@ -156,3 +158,19 @@ def decode(q, iq, k_cache, v_cache, ik_cache, seq_len, B, kslots, scale=None, se
                       G, d, dI, B, kslots, float(scale), _ptr(seqs), n, _ptr(ids), _ptr(gap),
                       _ptr(out))
     return ids, gap, out
+
+
+def decode_attend(q, k_cache, v_cache, seq_len, ids, B, scale, seqs, lib=None):
+    """Decode main branch for the listed sequences with given ids [nseqs, G, k]."""
+    lib = lib or load()
+    q, kc, vc = _u16(q), _u16(k_cache), _u16(v_cache)
+    N, H, d = q.shape
+    Lmax, G = kc.shape[1], kc.shape[2]
+    seq_len = np.ascontiguousarray(np.asarray(seq_len, dtype=np.int64))
+    seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    out = np.empty((len(seqs), H, d), np.float64)
+    lib.oracle_decode_attend(_ptr(q), _ptr(kc), _ptr(vc), _ptr(seq_len), Lmax, H, G, d, B,
+                             ids.shape[2], float(scale), _ptr(seqs), len(seqs), _ptr(ids),
+                             _ptr(out))
+    return out

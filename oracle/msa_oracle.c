@@ -272,3 +272,18 @@ void oracle_decode(const uint16_t *q, const uint16_t *iq, const uint16_t *kc,
         free(S);
     }
 }
+
+/* Decode main branch only, for the listed sequences with the given ids[nseqs,G,k]. */
+void oracle_decode_attend(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
+                          const int64_t *seq_len, int64_t Lmax, int H, int G, int d, int B, int k,
+                          double scale, const int64_t *seqs, int64_t nseqs, const int32_t *ids,
+                          double *out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nseqs; ++r) {
+        int64_t n = seqs[r];
+        int64_t Ln = seq_len[n];
+        row_attend(q + n * H * d, kc + n * Lmax * G * d, vc + n * Lmax * G * d, ids + r * G * k,
+                   Ln - 1, Ln, H, G, d, B, k, scale, out + r * H * d);
+    }
+}

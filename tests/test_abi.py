@@ -1,0 +1,129 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports exactly the
+symbols include/msa.h declares, sizes its workspaces, and rejects bad arguments
+with the documented status codes before launching anything."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_long_idx_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"MSA_API\s+[\w\s\*]+?\b(msa_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(msa.library_path()):
+        pytest.skip("libmsa.so not built")
+    return msa.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for want in ("msa_select_blocks", "msa_sparse_attn", "msa_prefill", "msa_decode",
+                 "msa_select_blocks_workspace_size", "msa_sparse_attn_workspace_size",
+                 "msa_prefill_workspace_size", "msa_decode_workspace_size", "msa_status_string"):
+        assert want in names
+
+
+def test_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", msa.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    # nothing beyond the declared C ABI is exported as a function
+    assert {n for n in exported if n.startswith("msa")} == set(_declared())
+
+
+def test_status_strings(lib):
+    assert lib.msa_status_string(0) == b"MSA_OK"
+    assert lib.msa_status_string(3) == b"MSA_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.msa_status_string(99) == b"MSA_ERR_UNKNOWN"
+
+
+def test_workspace_sizes(lib):
+    assert lib.msa_select_blocks_workspace_size(0, 4, 128, 128, 16) == 0
+    s1 = lib.msa_select_blocks_workspace_size(4096, 2, 32, 128, 4)
+    assert s1 >= 4096 * 2 * 32 * 4
+    s2 = lib.msa_prefill_workspace_size(131072, 64, 4, 128, 128, 128, 16)
+    # bounded by the query chunk, not by L
+    s3 = lib.msa_prefill_workspace_size(1048576, 64, 4, 128, 128, 128, 16)
+    assert s2 > 0 and s3 < 4 * s2 + (1 << 34)
+    assert lib.msa_decode_workspace_size(64, 262144, 64, 4, 128, 128, 128, 16) > 0
+
+
+P = ctypes.c_void_p
+
+
+def _fake(n=1 << 20):
+    """A host address used only as a non-null token: every call below must fail
+    validation before it could be dereferenced."""
+    return P(0x1000)
+
+
+def test_invalid_and_unsupported_arguments(lib):
+    f = _fake()
+    ws = P(0x100000)   # 256-byte aligned token
+    big = ctypes.c_size_t(1 << 40)
+    s = None
+    # null pointers with L > 0
+    assert lib.msa_select_blocks(None, f, 256, 2, 32, 128, 4, f, ws, big, s) == INVALID
+    # k < 1, negative L
+    assert lib.msa_select_blocks(f, f, 256, 2, 32, 128, 0, f, ws, big, s) == INVALID
+    assert lib.msa_select_blocks(f, f, -1, 2, 32, 128, 4, f, ws, big, s) == INVALID
+    # unsupported: B != 128, dI, k > 32, G*dI > 512
+    assert lib.msa_select_blocks(f, f, 256, 2, 32, 64, 4, f, ws, big, s) == UNSUPPORTED
+    assert lib.msa_select_blocks(f, f, 256, 2, 48, 128, 4, f, ws, big, s) == UNSUPPORTED
+    assert lib.msa_select_blocks(f, f, 256, 2, 32, 128, 33, f, ws, big, s) == UNSUPPORTED
+    assert lib.msa_select_blocks(f, f, 256, 8, 128, 128, 4, f, ws, big, s) == UNSUPPORTED
+    # workspace too small / misaligned
+    assert lib.msa_select_blocks(f, f, 256, 2, 32, 128, 4, f, ws, ctypes.c_size_t(16), s) == WS_SMALL
+    assert lib.msa_select_blocks(f, f, 256, 2, 32, 128, 4, f, P(0x100010), big, s) == WS_SMALL
+    # sparse attention: H % G, d, r
+    assert lib.msa_sparse_attn(f, f, f, f, 256, 6, 4, 64, 128, 4, ctypes.c_float(0), f, ws, big,
+                               s) == INVALID
+    assert lib.msa_sparse_attn(f, f, f, f, 256, 8, 2, 96, 128, 4, ctypes.c_float(0), f, ws, big,
+                               s) == UNSUPPORTED
+    assert lib.msa_sparse_attn(f, f, f, f, 256, 128, 2, 64, 128, 4, ctypes.c_float(0), f, ws, big,
+                               s) == UNSUPPORTED
+    # prefill and decode null / size checks
+    assert lib.msa_prefill(f, f, f, f, None, 256, 8, 2, 64, 32, 128, 4, ctypes.c_float(0), f, None,
+                           ws, big, s) == INVALID
+    assert lib.msa_decode(f, f, f, f, f, None, 2, 1024, 8, 2, 64, 32, 128, 4, ctypes.c_float(0), f,
+                          None, ws, big, s) == INVALID
+    assert lib.msa_decode(f, f, f, f, f, f, 2, 1024, 8, 2, 64, 32, 128, 4, ctypes.c_float(0), f,
+                          None, ws, ctypes.c_size_t(8), s) == WS_SMALL
+
+
+def test_empty_inputs_are_no_ops(lib):
+    # L == 0 / N == 0: valid empty problems, nothing launched, null pointers allowed
+    assert lib.msa_select_blocks(None, None, 0, 2, 32, 128, 4, None, None, 0, None) == OK
+    assert lib.msa_sparse_attn(None, None, None, None, 0, 8, 2, 64, 128, 4, ctypes.c_float(0),
+                               None, None, 0, None) == OK
+    assert lib.msa_prefill(None, None, None, None, None, 0, 8, 2, 64, 32, 128, 4,
+                           ctypes.c_float(0), None, None, None, 0, None) == OK
+    assert lib.msa_decode(None, None, None, None, None, None, 0, 1024, 8, 2, 64, 32, 128, 4,
+                          ctypes.c_float(0), None, None, None, 0, None) == OK
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    if not os.path.exists(msa.library_path()):
+        pytest.skip("libmsa.so not built")
+    x = torch.zeros(4, 2, 32, dtype=torch.bfloat16)
+    with pytest.raises(msa.MSAError):
+        msa.select_blocks(x, torch.zeros(4, 32, dtype=torch.bfloat16), k=4)

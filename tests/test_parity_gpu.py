@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path (through the C ABI via the thin binding) against the
+CPU oracle on the same seeded inputs.  Block ids bit-exact outside near-ties
+(relative boundary gap < 1e-4); outputs within max-abs 2e-2 / mean-abs 2e-3."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import _parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(f"[parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_long_idx_amd as msa  # noqa: F401  (fails loudly if not built)
+    msa.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _msa():
+    import block_sparse_long_idx_amd as msa
+    return msa
+
+
+def _prefill_gpu(x, k, return_ids=True):
+    msa = _msa()
+    dev = {n: t.to(DEV) for n, t in x.items() if isinstance(t, torch.Tensor)}
+    out, ids = msa.prefill(dev["q"], dev["k"], dev["v"], dev["iq"], dev["ik"], kslots=k,
+                           return_ids=True)
+    torch.cuda.synchronize()
+    return out, ids
+
+
+def _full_check(shape, seed, plant="lit", rows=None, **kw):
+    _say(f"prefill L={shape.L} H={shape.H} G={shape.G} d={shape.d} dI={shape.dI} "
+         f"k={shape.k} seed={seed} plant={plant}")
+    x = synth.prefill_inputs(shape, seed=seed, plant=plant, **kw)
+    out, ids = _prefill_gpu(x, shape.k)
+    if rows is None:
+        rows = np.arange(shape.L)
+    scale = 1.0 / math.sqrt(shape.d)
+    st = _parity.prefill_rows_vs_oracle(x, rows, ids.cpu().numpy()[rows],
+                                        out.float().cpu().numpy()[rows], 128, shape.k, scale)
+    _say(f"  -> {st}")
+    assert st["id_mismatches"] == 0
+    assert st["max_abs"] < _parity.MAX_ABS and st["mean_abs"] < _parity.MEAN_ABS
+    return st, out, ids
+
+
+TINY = synth.WORKLOADS["tiny_prefill_L4096"].shape
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("plant", ["lit", "hot"])
+def test_tiny_prefill_full(seed, plant):
+    _full_check(TINY, seed, plant)
+
+
+def test_select_blocks_tiny():
+    msa = _msa()
+    x = synth.prefill_inputs(TINY, seed=3)
+    _say("select_blocks tiny")
+    ids = msa.select_blocks(x["iq"].to(DEV), x["ik"].to(DEV), k=TINY.k).cpu().numpy()
+    S = oracle.block_scores(x["iq"], x["ik"], 128)
+    rows = np.arange(TINY.L)
+    oids, gap = oracle.select(S, rows, 128, TINY.k)
+    _parity.check_selection_valid(ids, rows, TINY.k)
+    tie, nmis = _parity.compare_ids(ids, oids, gap)
+    assert nmis == 0
+
+
+def test_sparse_attn_with_oracle_ids():
+    """Main branch alone, fed the oracle's ids (decoupled from selection)."""
+    msa = _msa()
+    x = synth.prefill_inputs(TINY, seed=4)
+    scale = 1.0 / math.sqrt(TINY.d)
+    ids, gap, ref = oracle.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], 128, TINY.k, scale)
+    _say("sparse_attn with oracle ids")
+    out = msa.sparse_attn(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV),
+                          torch.from_numpy(ids).to(DEV)).float().cpu().numpy()
+    mx, mean = _parity.compare_out(out, ref)
+    _say(f"  -> max {mx:.3e} mean {mean:.3e}")
+    assert mx < _parity.MAX_ABS and mean < _parity.MEAN_ABS
+    # arbitrary valid ids (not from the index branch), including -1 padding
+    rng = np.random.default_rng(0)
+    ids2 = np.full_like(ids, -1)
+    for i in range(TINY.L):
+        bi = i // 128
+        for g in range(TINY.G):
+            m = int(rng.integers(0, min(TINY.k - 1, bi) + 1))
+            ch = sorted(list(rng.choice(bi, size=m, replace=False)) + [bi]) if bi else [0]
+            ids2[i, g, :len(ch)] = ch
+    ref2 = oracle.attend(x["q"], x["k"], x["v"], ids2, 128, scale)
+    out2 = msa.sparse_attn(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV),
+                           torch.from_numpy(ids2).to(DEV)).float().cpu().numpy()
+    mx, mean = _parity.compare_out(out2, ref2)
+    assert mx < _parity.MAX_ABS and mean < _parity.MEAN_ABS
+
+
+@pytest.mark.parametrize("L", [1, 127, 128, 129, 1000, 4097])
+def test_ragged_lengths(L):
+    shape = synth.PrefillShape(L=L, H=8, G=2, d=64, dI=32, B=128, k=4)
+    _full_check(shape, seed=5)
+
+
+@pytest.mark.parametrize("H,G,d,dI,k", [
+    (64, 4, 128, 128, 16),   # the pages' research-model shape
+    (16, 8, 64, 64, 3),
+    (32, 1, 128, 128, 5),    # 32 query heads per group
+    (4, 4, 64, 32, 1),       # one head per group; local block only
+    (8, 2, 128, 64, 32),     # k = 32 slots
+])
+def test_shape_grid(H, G, d, dI, k):
+    shape = synth.PrefillShape(L=2000, H=H, G=G, d=d, dI=dI, B=128, k=k)
+    _full_check(shape, seed=6)
+
+
+def test_determinism():
+    x = synth.prefill_inputs(TINY, seed=7)
+    _say("determinism")
+    o1, i1 = _prefill_gpu(x, TINY.k)
+    o2, i2 = _prefill_gpu(x, TINY.k)
+    assert torch.equal(i1, i2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def _sample_rows(L, n, seed):
+    rng = np.random.default_rng(seed)
+    head = np.arange(min(L, 256))
+    tail = np.arange(max(0, L - 128), L)
+    mid = rng.choice(L, size=min(n, L), replace=False)
+    return np.unique(np.concatenate([head, tail, mid]))
+
+
+def test_prefill_32k_sampled():
+    shape = synth.WORKLOADS["prefill_L32768"].shape
+    _full_check(shape, seed=0, rows=_sample_rows(shape.L, 512, 0))
+
+
+def test_hot_blocks_16k_sampled():
+    """Blocks 0-3 picked by (nearly) every query: long lists split over many tiles."""
+    shape = synth.PrefillShape(L=16384, H=64, G=4, d=128, dI=128, B=128, k=16)
+    st, out, ids = _full_check(shape, seed=1, plant="hot", rows=_sample_rows(shape.L, 512, 1),
+                               n_plant=0, c=3.0, hot_blocks=(0, 1, 2, 3))
+    idn = ids.cpu().numpy()
+    late = idn[1024:]
+    frac = np.mean([(late[:, :, :4] == np.arange(4)).all(-1).mean()])
+    _say(f"  hot-block selection fraction {frac:.4f}")
+    assert frac > 0.99
+
+
+def test_prefill_128k_sampled():
+    """The 128K workload in the launch configuration the benchmark times."""
+    wl = synth.WORKLOADS["prefill_L131072"]
+    shape = wl.shape
+    _say("prefill 128K: generate on GPU")
+    x = synth.prefill_inputs(shape, seed=0, plant=wl.plant, device=DEV)
+    msa = _msa()
+    out, ids = msa.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], kslots=shape.k,
+                           return_ids=True)
+    torch.cuda.synchronize()
+    rows = _sample_rows(shape.L, 192, 2)
+    _say(f"  oracle on {len(rows)} rows")
+    st = _parity.prefill_rows_vs_oracle(x, rows, ids[rows].cpu().numpy(),
+                                        out[rows].float().cpu().numpy(), 128, shape.k,
+                                        1.0 / math.sqrt(shape.d))
+    _say(f"  -> {st}")
+    assert st["id_mismatches"] == 0
+    assert st["max_abs"] < _parity.MAX_ABS and st["mean_abs"] < _parity.MEAN_ABS
+    # every row's selection is valid
+    _parity.check_selection_valid(ids.cpu().numpy(), np.arange(shape.L), shape.k)
+
+
+# ------------------------------- decode ------------------------------------
+def _decode_check(shape, seq_len, seed, seqs=None, device="cpu"):
+    msa = _msa()
+    _say(f"decode N={shape.N} Lmax={shape.Lc} seq_len[:8]={list(seq_len[:8])} seed={seed}")
+    x = synth.decode_inputs(shape, seed=seed, seq_len=np.clip(seq_len, 1, shape.Lc), device=device)
+    sl = torch.tensor(np.asarray(seq_len, np.int32), device=DEV)
+    d = {n: (t.to(DEV) if isinstance(t, torch.Tensor) else t) for n, t in x.items()}
+    out, ids = msa.decode(d["q"], d["iq"], d["k_cache"], d["v_cache"], d["ik_cache"], sl,
+                          kslots=shape.k, return_ids=True)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    ids = ids.cpu().numpy()
+    valid = (np.asarray(seq_len) >= 1) & (np.asarray(seq_len) <= shape.Lc)
+    if seqs is None:
+        seqs = np.nonzero(valid)[0]
+    scale = 1.0 / math.sqrt(shape.d)
+    oids, gap, oout = oracle.decode(x["q"], x["iq"], x["k_cache"], x["v_cache"], x["ik_cache"],
+                                    np.clip(seq_len, 1, shape.Lc), 128, shape.k, scale, seqs=seqs)
+    pos = np.asarray(seq_len)[seqs] - 1
+    _parity.check_selection_valid(ids[seqs], pos, shape.k)
+    tie, nmis = _parity.compare_ids(ids[seqs], oids, gap)
+    ref = oout.copy()
+    if tie.any():
+        tr = np.nonzero(tie.any(axis=1))[0]
+        ref[tr] = oracle.decode_attend(x["q"], x["k_cache"], x["v_cache"],
+                                       np.clip(seq_len, 1, shape.Lc), ids[seqs[tr]], 128, scale,
+                                       seqs[tr])
+    mx, mean = _parity.compare_out(out[seqs], ref)
+    _say(f"  -> near_ties {int(tie.sum())} mismatches {nmis} max {mx:.3e} mean {mean:.3e}")
+    assert nmis == 0
+    assert mx < _parity.MAX_ABS and mean < _parity.MEAN_ABS
+    for n in np.nonzero(~valid)[0]:
+        assert (ids[n] == -1).all() and (out[n] == 0).all()
+
+
+def test_decode_small_ragged():
+    shape = synth.DecodeShape(N=8, Lc=2000, H=64, G=4, d=128, dI=128, B=128, k=16)
+    seq_len = np.array([1, 127, 128, 129, 2000, 1500, 0, 2001])   # last two invalid
+    _decode_check(shape, seq_len, seed=0)
+
+
+def test_decode_tiny_dims():
+    shape = synth.DecodeShape(N=5, Lc=4096, H=8, G=2, d=64, dI=32, B=128, k=4)
+    _decode_check(shape, np.array([4096, 3000, 129, 640, 1]), seed=1)
+
+
+def test_decode_full_size_subset():
+    """64 sequences x 262144 cached tokens; oracle on 6 of them."""
+    wl = synth.WORKLOADS["decode_N64_L262144"]
+    shape = wl.shape
+    seq_len = np.full(shape.N, shape.Lc)
+    _decode_check(shape, seq_len, seed=0, seqs=np.array([0, 1, 17, 31, 48, 63]), device=DEV)
