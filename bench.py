@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA forward pass on one MI355X.
+
+One step = one full pass of the hot path over one batch of seeded synthetic
+input already resident in HBM: for prefill workloads a whole ``msa_prefill``
+(index score + block max-pool, exp-free top-k, scheduling, KV-outer attention,
+combine); for the decode workload one ``msa_decode`` over all sequences.
+
+Prints ONE JSON line with the throughput, the roofline position of the kernel
+that dominates the step (its per-launch duration measured in-process with HIP
+events recorded on the library's stream), and the CPU oracle timed on a bounded
+sample of the same workload as a reported baseline.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "MSA prefill tokens/s @128K & 1M (1 GPU, % MFMA peak); decode us/step @256K"
+PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12      # MI355X HBM3E
+B_BLOCK = 128
+
+
+# --------------------------------------------------------------------------
+# Algorithmic work model
+# --------------------------------------------------------------------------
+def paper_flop_ratio(H: int, G: int, d: int, dI: int, L: int, kB: int) -> float:
+    """Per-token attention FLOPs of dense causal GQA over MSA (index branch plus
+    main branch), averaged over a causal sequence of L tokens."""
+    dense = 4 * H * d * (L / 2)
+    msa = 4 * H * d * kB + 2 * G * dI * (L / 2)
+    return dense / msa
+
+
+def prefill_work(L, H, G, d, dI, k, B=B_BLOCK, list_counts=None):
+    """Algorithmic FLOPs and bytes of each prefill kernel over one whole step.
+
+    K1 scores every competitor key of every (query, group): 2*G*dI FLOP per
+    (query, key) pair with key block < b(i).  K4 attends, per (query, group),
+    the tokens of its selected blocks inside the causal window: 4*r*d FLOP per
+    attended (query, group, token) for the r heads of the group.
+    """
+    r = H // G
+    i = np.arange(L, dtype=np.int64)
+    bi = i // B
+    nsel = np.minimum(k, bi + 1)
+    pairs = float(np.sum(bi * B))                                     # scored (query, key)
+    attended = float(np.sum((nsel - 1) * B + (i - bi * B + 1)))       # per group
+    entries = float(np.sum(nsel)) * G                                 # (query, group, slot)
+    f_idx = 2.0 * G * dI * pairs
+    f_attn = 4.0 * r * d * G * attended
+    comp_rows = np.maximum(bi - 0, 0)
+    k2_bytes = 4.0 * G * float(np.sum(np.where(bi > k - 1, comp_rows, 0))) + 4.0 * L * G * k
+    items = float(np.sum(np.ceil(np.asarray(list_counts) / 64.0))) if list_counts is not None \
+        else entries / 64.0
+    k4_bytes = (entries * r * d * 2            # gathered q rows
+                + entries * r * (2 * d + 4)    # partial (o bf16, lse fp32) writes
+                + items * 2 * B * d * 2)       # K and V block staged per work item
+    k5_bytes = entries * r * (2 * d + 4) + L * H * d * 2 + 4.0 * L * G * k
+    k1_bytes = (L * G * dI * 2 + 4.0 * G * float(np.sum(bi)))   # idx_q once + block scores out
+    return {
+        "flops": {"k1_index_pool": f_idx, "k4_kv_outer": f_attn},
+        "bytes": {"k1_index_pool": k1_bytes, "k2_select": k2_bytes,
+                  "k3_schedule": 12.0 * L * G * k, "k4_kv_outer": k4_bytes,
+                  "k5_combine": k5_bytes},
+        "pairs": pairs, "attended_per_group": attended, "entries": entries,
+        "f_total": f_idx + f_attn,
+        "dense_gqa_flops": 4.0 * H * d * float(np.sum(i + 1)),
+    }
+
+
+def decode_work(N, Lc, H, G, d, dI, k, B=B_BLOCK):
+    p = Lc - 1
+    nb = p // B                                        # competitor blocks per sequence
+    nsel = min(k, nb + 1)
+    idx_bytes = N * nb * B * dI * 2.0                  # idx-K cache stream
+    kv_bytes = N * G * nsel * 2 * B * d * 2.0          # selected K and V blocks
+    small = N * (H * d * 2 * 2 + G * dI * 2) + N * G * (nb * 4 * 2 + k * 4)
+    part = N * H * nsel * (2 * d + 4) * 2.0
+    return {
+        "bytes": {"k1d_index_pool": idx_bytes + N * G * nb * 4.0,
+                  "k4d_split": kv_bytes + N * H * nsel * (d * 2 + 2 * d + 4),
+                  "k2_select": N * G * (nb * 4.0 + k * 4), "k5_combine": part / 2 + N * H * d * 2},
+        "total_bytes": idx_bytes + kv_bytes + small + part,
+        "flops": 2.0 * N * G * dI * nb * B + 4.0 * N * H * d * ((nsel - 1) * B + (p % B) + 1),
+    }
+
+
+# --------------------------------------------------------------------------
+def _sample_rows(L, n, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(L, size=min(n, L), replace=False))
+
+
+def cpu_baseline_prefill(x, shape, target_s=15.0):
+    """Time the oracle on a random sample of query rows of the same workload."""
+    import oracle
+    lib = oracle.load()
+    host = {n: x[n].cpu() for n in ("q", "k", "v", "iq", "ik")}
+    scale = 1.0 / math.sqrt(shape.d)
+    n = 16
+    total_rows, total_s = 0, 0.0
+    seed = 1
+    while total_s < target_s:
+        rows = _sample_rows(shape.L, n, seed)
+        t0 = time.perf_counter()
+        oracle.prefill(host["q"], host["k"], host["v"], host["iq"], host["ik"], B_BLOCK, shape.k,
+                       scale, rows=rows, lib=lib)
+        dt = time.perf_counter() - t0
+        total_rows += len(rows)
+        total_s += dt
+        seed += 1
+        if dt < target_s / 8:
+            n *= 2
+    return {"value": total_rows / total_s, "unit": "tokens/s",
+            "cores": oracle.num_threads(lib), "kind": "oracle",
+            "sample": f"{total_rows} query rows drawn uniformly from the L={shape.L} workload "
+                      f"(each row: index scores vs all causal keys, selection, attention over "
+                      f"its blocks), {total_s:.1f} s wall"}
+
+
+def cpu_baseline_decode(x, shape, target_s=15.0):
+    import oracle
+    lib = oracle.load()
+    t_copy = time.perf_counter()
+    n_seq = 1
+    host = None
+    total, total_s = 0, 0.0
+    while total_s < target_s and total < shape.N:
+        seqs = np.arange(total, min(shape.N, total + n_seq))
+        if host is None:
+            host = {n: x[n].cpu() for n in ("q", "iq")}
+        kc = x["k_cache"][seqs[0]:seqs[-1] + 1].cpu()
+        vc = x["v_cache"][seqs[0]:seqs[-1] + 1].cpu()
+        ikc = x["ik_cache"][seqs[0]:seqs[-1] + 1].cpu()
+        t0 = time.perf_counter()
+        oracle.decode(host["q"][seqs[0]:seqs[-1] + 1], host["iq"][seqs[0]:seqs[-1] + 1], kc, vc,
+                      ikc, np.asarray(x["seq_len"])[seqs], B_BLOCK, shape.k, lib=lib)
+        total_s += time.perf_counter() - t0
+        total += len(seqs)
+        n_seq = min(16, n_seq * 2)
+    us_per_step = total_s / total * shape.N * 1e6
+    del t_copy
+    return {"value": us_per_step, "unit": "us/step", "cores": oracle.num_threads(lib),
+            "kind": "oracle",
+            "sample": f"{total} of {shape.N} sequences ({total_s:.1f} s wall), scaled to all "
+                      f"{shape.N}"}
+
+
+def _load_traffic(kernel: str, workload: str):
+    """HBM traffic per launch from committed rocprofv3 counter summaries, if any
+    are recorded for this kernel, workload and the current kernel sources."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    src = os.path.join(here, "block_sparse_long_idx_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(src)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(src, f), "rb").read())
+    digest = h.hexdigest()[:16]
+    rec = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith("-"):
+            key, _, val = line.strip("- \n").partition(":")
+            rec[key.strip()] = val.strip()
+    if rec.get("sources_sha256_16") != digest:
+        return None
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_L131072")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_long_idx_amd as msa
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {wl.name}: generating inputs on {dev}", file=sys.stderr, flush=True)
+    s = wl.shape
+
+    if wl.kind == "prefill":
+        x = synth.prefill_inputs(s, seed=args.seed, plant=wl.plant, n_plant=wl.n_plant, c=wl.c,
+                                 hot_blocks=wl.hot_blocks, device=dev)
+        out = torch.empty_like(x["q"])
+        ids = torch.empty((s.L, s.G, s.k), dtype=torch.int32, device=dev)
+        ws = msa._workspace(msa.workspace_size("prefill", L=s.L, H=s.H, G=s.G, d=s.d, dI=s.dI,
+                                               k=s.k), dev)
+
+        def step():
+            msa.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], kslots=s.k, out=out,
+                        ids_out=ids, workspace=ws, return_ids=True)
+    else:
+        x = synth.decode_inputs(s, seed=args.seed, device=dev)
+        seq_len = torch.tensor(np.asarray(x["seq_len"], np.int32), device=dev)
+        out = torch.empty_like(x["q"])
+        ids = torch.empty((s.N, s.G, s.k), dtype=torch.int32, device=dev)
+        ws = msa._workspace(msa.workspace_size("decode", N=s.N, Lmax=s.Lc, H=s.H, G=s.G, d=s.d,
+                                               dI=s.dI, k=s.k), dev)
+
+        def step():
+            msa.decode(x["q"], x["iq"], x["k_cache"], x["v_cache"], x["ik_cache"], seq_len,
+                       kslots=s.k, out=out, ids_out=ids, workspace=ws, return_ids=True)
+
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps --------------------------------------
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # ---- per-kernel breakdown: the same K steps with stage events -----------
+    msa.timing_enable(64 * args.steps + 64)
+    for _ in range(args.steps):
+        step()
+    per_kernel = msa.timing_collect()
+    msa.timing_disable()
+    kernels = {name: {"launches_per_step": n / args.steps, "ms_per_step": tot / args.steps,
+                      "avg_launch_ms": tot / n} for name, (n, tot) in per_kernel.items()}
+    dominant = max(kernels, key=lambda k_: kernels[k_]["ms_per_step"])
+
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "ms_per_step": ms_per_step, "scaling": "weak", "vs_baseline": None,
+              "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, planted blocks)"}
+    if wl.kind == "prefill":
+        counts = None
+        idn = ids.cpu().numpy()
+        valid = idn >= 0
+        g_idx = np.broadcast_to(np.arange(s.G)[None, :, None], idn.shape)
+        counts = np.bincount((g_idx[valid] * ((s.L + 127) // 128) + idn[valid]).ravel(),
+                             minlength=s.G * ((s.L + 127) // 128))
+        work = prefill_work(s.L, s.H, s.G, s.d, s.dI, s.k, list_counts=counts)
+        result.update({"value": s.L / (ms_per_step / 1e3), "unit": "tokens/s",
+                       "higher_is_better": True})
+        result["config"] = {"workload": wl.name, "L": s.L, "H": s.H, "G": s.G, "d": s.d,
+                            "dI": s.dI, "B": s.B, "k": s.k, "planting": wl.plant,
+                            "query_chunk": 32768}
+        result["step_mfma_frac"] = work["f_total"] / (ms_per_step / 1e3) / PEAK_BF16_FLOPS
+        result["algorithmic_flops_per_step"] = work["f_total"]
+        result["dense_gqa_flops_per_step"] = work["dense_gqa_flops"]
+    else:
+        work = decode_work(s.N, s.Lc, s.H, s.G, s.d, s.dI, s.k)
+        result.update({"value": ms_per_step * 1e3, "unit": "us/step", "higher_is_better": False})
+        result["config"] = {"workload": wl.name, "N": s.N, "Lc": s.Lc, "H": s.H, "G": s.G,
+                            "d": s.d, "dI": s.dI, "B": s.B, "k": s.k}
+        result["step_hbm_frac"] = work["total_bytes"] / (ms_per_step / 1e3) / PEAK_HBM_BYTES
+
+    # ---- roofline of the dominant kernel -------------------------------------
+    kd = kernels[dominant]
+    n_launch = kd["launches_per_step"]
+    t_launch = kd["avg_launch_ms"] / 1e3
+    flops = work.get("flops", {})
+    if isinstance(flops, dict) and dominant in flops:
+        per_launch_flops = flops[dominant] / n_launch
+        per_launch_bytes = work["bytes"].get(dominant, 0.0) / n_launch
+        intensity = per_launch_flops / max(per_launch_bytes, 1.0)
+        if intensity >= PEAK_BF16_FLOPS / PEAK_HBM_BYTES or dominant == "k1_index_pool":
+            roof = {"bound": "mfma", "achieved": per_launch_flops / t_launch / 1e12,
+                    "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"}
+        else:
+            roof = {"bound": "hbm", "achieved": per_launch_bytes / t_launch / 1e9,
+                    "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s"}
+        roof["mfma_tflops"] = per_launch_flops / t_launch / 1e12
+        roof["mfma_frac"] = roof["mfma_tflops"] * 1e12 / PEAK_BF16_FLOPS
+    else:
+        per_launch_bytes = work["bytes"][dominant] / n_launch
+        roof = {"bound": "hbm", "achieved": per_launch_bytes / t_launch / 1e9,
+                "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = _load_traffic(dominant, wl.name)
+    roof["kernel"] = dominant
+    roof["launches_per_step"] = n_launch
+    roof["avg_launch_ms"] = kd["avg_launch_ms"]
+    result["roofline"] = roof
+    result["kernels"] = {k_: {"ms_per_step": round(v["ms_per_step"], 4),
+                              "launches_per_step": v["launches_per_step"]}
+                         for k_, v in kernels.items()}
+
+    # ---- CPU oracle baseline (rank 0, N=1) ------------------------------------
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        if wl.kind == "prefill":
+            result["cpu_baseline"] = cpu_baseline_prefill(x, s, args.cpu_seconds)
+        else:
+            result["cpu_baseline"] = cpu_baseline_decode(x, s, args.cpu_seconds)
+    result["wall_s_timed_region"] = wall_s
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -16,7 +16,7 @@ import os
 import torch
 
 __all__ = ["MSAError", "select_blocks", "sparse_attn", "prefill", "decode", "workspace_size",
-           "library_path", "load_library"]
+           "library_path", "load_library", "timing_enable", "timing_collect", "timing_disable"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libmsa.so")
@@ -31,6 +31,29 @@ class MSAError(RuntimeError):
     def __init__(self, msg, status=None):
         super().__init__(msg)
         self.status = status
+
+
+class _KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int),
+                ("total_ms", ctypes.c_double)]
+
+
+def timing_enable(max_launches: int = 4096):
+    """Start per-kernel HIP-event timing of every stage the library enqueues."""
+    _check(load_library().msa_timing_enable(max_launches), "msa_timing_enable")
+
+
+def timing_collect() -> dict:
+    """Wait for the recorded stages; {stage: (launches, total_ms)}; clears the record."""
+    lib = load_library()
+    buf = (_KernelTime * 16)()
+    n = ctypes.c_int(0)
+    _check(lib.msa_timing_collect(buf, 16, ctypes.byref(n)), "msa_timing_collect")
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(n.value)}
+
+
+def timing_disable():
+    load_library().msa_timing_disable()
 
 
 def library_path() -> str:
@@ -68,6 +91,12 @@ def load_library():
     lib.msa_decode.argtypes = [P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, i32, i32, f32, P,
                                P, P, sz, P]
     lib.msa_decode.restype = i32
+    lib.msa_timing_enable.argtypes = [i32]
+    lib.msa_timing_enable.restype = i32
+    lib.msa_timing_collect.argtypes = [ctypes.POINTER(_KernelTime), i32, ctypes.POINTER(i32)]
+    lib.msa_timing_collect.restype = i32
+    lib.msa_timing_disable.argtypes = []
+    lib.msa_timing_disable.restype = None
     _lib = lib
     return lib
 

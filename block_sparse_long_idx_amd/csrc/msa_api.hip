@@ -7,12 +7,16 @@
 //   K1 index score + block max-pool -> K2 exp-free top-k -> K3 schedule ->
 //   K4 KV-outer attention -> K5 combine.
 // Decode: K1d -> K2 -> K4d -> K5.
-// Nothing here allocates, frees or synchronises.
+// The compute entry points never allocate device memory, free or synchronise;
+// only the optional timing calls at the end create events and synchronise.
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include <stdio.h>
+
 #include <algorithm>
+#include <new>
 
 #include "msa.h"
 #include "msa_launch.h"
@@ -81,10 +85,41 @@ int check_ws(void *ws, size_t ws_bytes, size_t need) {
 
 float default_scale(float scale, int d) { return scale > 0.0f ? scale : 1.0f / sqrtf((float)d); }
 
+// ---- optional per-kernel timing (see msa_timing_enable in msa.h) ----------
+struct TimedLaunch {
+    int name;
+    hipEvent_t start, stop;
+};
+enum StageName { kK1, kK2, kK3, kK4, kK5, kK1d, kK4d, kNumStages };
+const char *const kStageNames[kNumStages] = {"k1_index_pool", "k2_select", "k3_schedule",
+                                             "k4_kv_outer", "k5_combine", "k1d_index_pool",
+                                             "k4d_split"};
+struct Timing {
+    bool on = false;
+    int cap = 0, used = 0;
+    TimedLaunch *rec = nullptr;
+};
+Timing g_timing;
+
+// Runs `launch` (returning hipError_t), bracketed by events when timing is on.
+template <typename F>
+hipError_t timed(int stage, hipStream_t s, F &&launch) {
+    if (!g_timing.on || g_timing.used >= g_timing.cap) return launch();
+    TimedLaunch &t = g_timing.rec[g_timing.used];
+    if (hipEventRecord(t.start, s) != hipSuccess) return hipErrorUnknown;
+    const hipError_t e = launch();
+    if (e != hipSuccess) return e;
+    if (hipEventRecord(t.stop, s) != hipSuccess) return hipErrorUnknown;
+    t.name = stage;
+    ++g_timing.used;
+    return hipSuccess;
+}
+
 #define MSA_TRY(expr)                                   \
     do {                                                \
         if ((expr) != hipSuccess) return MSA_ERR_HIP;   \
     } while (0)
+#define MSA_TIMED(stage, expr) MSA_TRY(timed(stage, s, [&]() { return (expr); }))
 
 // Shared by prefill and sparse_attn: K3 + K4 + K5 for queries [q0, qend).
 int attn_chunk(const uint16_t *q, const uint16_t *kx, const uint16_t *vx, const int32_t *ids_c,
@@ -92,9 +127,9 @@ int attn_chunk(const uint16_t *q, const uint16_t *kx, const uint16_t *vx, const 
                uint16_t *out, const AttnWs &w, hipStream_t s) {
     const int64_t C = qend - q0;
     const int nbc = (int)((qend - 1) / kBlock + 1);
-    MSA_TRY(launch_k3_schedule(ids_c, C, G, k, nbc, w.sb, s));
-    MSA_TRY(launch_k4_kv_outer(q, kx, vx, w.sb, nbc, L, q0, C, H, G, d, k, scale, w.po, w.plse, s));
-    MSA_TRY(launch_k5_combine(w.po, w.plse, ids_c, C, H, G, d, k, nbc, out + q0 * H * d, s));
+    MSA_TIMED(kK3, launch_k3_schedule(ids_c, C, G, k, nbc, w.sb, s));
+    MSA_TIMED(kK4, launch_k4_kv_outer(q, kx, vx, w.sb, nbc, L, q0, C, H, G, d, k, scale, w.po, w.plse, s));
+    MSA_TIMED(kK5, launch_k5_combine(w.po, w.plse, ids_c, C, H, G, d, k, nbc, out + q0 * H * d, s));
     return MSA_OK;
 }
 
@@ -137,9 +172,9 @@ int msa_select_blocks(const uint16_t *idx_q, const uint16_t *idx_k, int64_t L, i
     const int64_t C = chunk_of(L);
     for (int64_t q0 = 0; q0 < L; q0 += C) {
         const int64_t qend = std::min(L, q0 + C);
-        MSA_TRY(launch_k1_index_pool(idx_q, idx_k, S, L, q0, qend, G, dI, nbp, s));
-        MSA_TRY(launch_k2_select(S, nbp, (qend - q0) * G, G, k, q0, nullptr, 0,
-                                 block_ids + q0 * G * k, s));
+        MSA_TIMED(kK1, launch_k1_index_pool(idx_q, idx_k, S, L, q0, qend, G, dI, nbp, s));
+        MSA_TIMED(kK2, launch_k2_select(S, nbp, (qend - q0) * G, G, k, q0, nullptr, 0,
+                                        block_ids + q0 * G * k, s));
     }
     return MSA_OK;
 }
@@ -212,8 +247,8 @@ int msa_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
     for (int64_t q0 = 0; q0 < L; q0 += C) {
         const int64_t qend = std::min(L, q0 + C);
         int32_t *ids_c = block_ids_out ? block_ids_out + q0 * G * kslots : ids_ws;
-        MSA_TRY(launch_k1_index_pool(idx_q, idx_k, S, L, q0, qend, G, dI, nbp, s));
-        MSA_TRY(launch_k2_select(S, nbp, (qend - q0) * G, G, kslots, q0, nullptr, 0, ids_c, s));
+        MSA_TIMED(kK1, launch_k1_index_pool(idx_q, idx_k, S, L, q0, qend, G, dI, nbp, s));
+        MSA_TIMED(kK2, launch_k2_select(S, nbp, (qend - q0) * G, G, kslots, q0, nullptr, 0, ids_c, s));
         const int rc = attn_chunk(q, k, v, ids_c, L, q0, qend, H, G, d, kslots, scale, out, w, s);
         if (rc != MSA_OK) return rc;
     }
@@ -255,12 +290,67 @@ int msa_decode(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache
     uint16_t *po = c.take<uint16_t>((int64_t)N * H * kslots * d);
     float *plse = c.take<float>((int64_t)N * H * kslots);
     int32_t *ids = block_ids_out ? block_ids_out : ids_ws;
-    MSA_TRY(launch_k1d_index_pool(idx_q, idx_k_cache, seq_len, S, N, Lmax, G, dI, nbp, s));
-    MSA_TRY(launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, seq_len, Lmax, ids, s));
-    MSA_TRY(launch_k4d_split(q, k_cache, v_cache, ids, seq_len, N, Lmax, H, G, d, kslots, scale, po,
-                             plse, s));
-    MSA_TRY(launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, s));
+    MSA_TIMED(kK1d, launch_k1d_index_pool(idx_q, idx_k_cache, seq_len, S, N, Lmax, G, dI, nbp, s));
+    MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, seq_len, Lmax, ids, s));
+    MSA_TIMED(kK4d, launch_k4d_split(q, k_cache, v_cache, ids, seq_len, N, Lmax, H, G, d, kslots,
+                                     scale, po, plse, s));
+    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, s));
     return MSA_OK;
+}
+
+// ------------------------------ timing ------------------------------------
+int msa_timing_enable(int max_launches) {
+    if (max_launches <= 0) return MSA_ERR_INVALID_ARG;
+    msa_timing_disable();
+    g_timing.rec = new (std::nothrow) TimedLaunch[max_launches];
+    if (!g_timing.rec) return MSA_ERR_INVALID_ARG;
+    for (int i = 0; i < max_launches; ++i) {
+        if (hipEventCreate(&g_timing.rec[i].start) != hipSuccess ||
+            hipEventCreate(&g_timing.rec[i].stop) != hipSuccess) {
+            g_timing.cap = i;
+            msa_timing_disable();
+            return MSA_ERR_HIP;
+        }
+    }
+    g_timing.cap = max_launches;
+    g_timing.used = 0;
+    g_timing.on = true;
+    return MSA_OK;
+}
+
+int msa_timing_collect(msa_kernel_time *out, int max_entries, int *n_out) {
+    if (!out || !n_out || max_entries < kNumStages) return MSA_ERR_INVALID_ARG;
+    double total[kNumStages] = {};
+    int count[kNumStages] = {};
+    for (int i = 0; i < g_timing.used; ++i) {
+        const TimedLaunch &t = g_timing.rec[i];
+        float ms = 0.0f;
+        if (hipEventSynchronize(t.stop) != hipSuccess ||
+            hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess)
+            return MSA_ERR_HIP;
+        total[t.name] += ms;
+        ++count[t.name];
+    }
+    int n = 0;
+    for (int k = 0; k < kNumStages; ++k) {
+        if (!count[k]) continue;
+        snprintf(out[n].name, sizeof out[n].name, "%s", kStageNames[k]);
+        out[n].launches = count[k];
+        out[n].total_ms = total[k];
+        ++n;
+    }
+    *n_out = n;
+    g_timing.used = 0;
+    return MSA_OK;
+}
+
+void msa_timing_disable(void) {
+    for (int i = 0; i < g_timing.cap; ++i) {
+        (void)hipEventDestroy(g_timing.rec[i].start);
+        (void)hipEventDestroy(g_timing.rec[i].stop);
+    }
+    delete[] g_timing.rec;
+    g_timing = Timing{};
 }
 
 }  // extern "C"

@@ -32,7 +32,8 @@
  *   - Return value: an msa_status.  Every argument is validated BEFORE anything is
  *     launched; on an error nothing is launched and no output is written.  Faults
  *     inside kernels surface at the caller's next synchronisation of `stream`.
- *   - Functions are stateless and thread-safe; calls on one stream are ordered.
+ *   - The compute entry points are stateless and thread-safe; calls on one stream
+ *     are ordered.  (The optional timing facility at the end is process-wide.)
  *   - Supported on the GPU: B = 128; d in {64, 128}; dI in {32, 64, 128};
  *     H/G in {1, 2, 4, 8, 16, 32}; G * dI <= 512; 1 <= k <= 32; any L >= 0.
  *     Anything else returns MSA_ERR_UNSUPPORTED.
@@ -132,6 +133,29 @@ MSA_API int msa_decode(const uint16_t *q, const uint16_t *idx_q, const uint16_t 
                const uint16_t *v_cache, const uint16_t *idx_k_cache, const int32_t *seq_len,
                int N, int64_t Lmax, int H, int G, int d, int dI, int B, int kslots, float scale,
                uint16_t *out, int32_t *block_ids_out, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Optional per-kernel timing (measurement support, process-wide, not
+ * thread-safe).  While enabled, every kernel stage the entry points above enqueue
+ * is bracketed by a pair of hipEvents recorded on the caller's stream; stages are
+ * named "k1_index_pool", "k2_select", "k3_schedule" (its four small kernels as
+ * one), "k4_kv_outer", "k5_combine", "k1d_index_pool", "k4d_split".
+ *   msa_timing_enable(max_launches): start recording (events for up to
+ *       max_launches stages are created up front; further stages are not timed).
+ *   msa_timing_collect(out, max_entries, n_out): waits for the recorded events
+ *       (this call synchronises), sums the elapsed times per stage name into `out`
+ *       and clears the record; recording stays enabled.
+ *   msa_timing_disable(): stop recording and release the events.
+ * ------------------------------------------------------------------------- */
+typedef struct msa_kernel_time {
+    char name[32];
+    int launches;
+    double total_ms;
+} msa_kernel_time;
+
+MSA_API int msa_timing_enable(int max_launches);
+MSA_API int msa_timing_collect(msa_kernel_time *out, int max_entries, int *n_out);
+MSA_API void msa_timing_disable(void);
 
 #ifdef __cplusplus
 }

@@ -51,9 +51,15 @@ def load(path: str | None = None):
     for f in (lib.oracle_block_scores, lib.oracle_select, lib.oracle_attend,
               lib.oracle_prefill_rows, lib.oracle_decode, lib.oracle_decode_attend):
         f.restype = None
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = i32
     if path is None:
         _lib = lib
     return lib
+
+
+def num_threads(lib=None) -> int:
+    return int((lib or load()).oracle_num_threads())
 
 
 def _u16(a) -> np.ndarray:

@@ -48,6 +48,7 @@
  * Rows are processed in parallel with OpenMP; each row is independent.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -286,4 +287,10 @@ void oracle_decode_attend(const uint16_t *q, const uint16_t *kc, const uint16_t 
         row_attend(q + n * H * d, kc + n * Lmax * G * d, vc + n * Lmax * G * d, ids + r * G * k,
                    Ln - 1, Ln, H, G, d, B, k, scale, out + r * H * d);
     }
+}
+
+/* Threads an OpenMP parallel region of the oracle uses. */
+int oracle_num_threads(void)
+{
+    return omp_get_max_threads();
 }

@@ -17,8 +17,11 @@ Planting (so that selection is not tie-dominated, and to create hot blocks):
   mean this barely changes which blocks win; it is kept because it is the
   literal reading.
 * ``"hot"`` -- a seeded unit vector ``u_g`` per group is made the real idx-Q
-  mean (``iq[:,g,:] += 4 u_g``) and ``c * sqrt(dI) * u_g`` is added to the
+  mean (``iq[:,g,:] += 8 u_g``) and ``c * sqrt(dI) * u_g`` is added to the
   planted idx-K rows, so planted blocks are selected by (nearly) every query.
+  (The query's own N(0,1) part projected on the planted vector is shared by
+  every token of a planted block; a mean of 8 keeps that term at about a
+  quarter of the planted signal.)
   With ``hot_blocks=(0,1,2,3)`` every group's direction is added to those
   blocks: the long-context skewed workload.
 * ``"none"`` -- plain N(0,1).
@@ -34,6 +37,7 @@ import torch
 _CHUNK_ELEMS = 1 << 26  # elements drawn per generator chunk (256 MiB of fp32)
 
 T_Q, T_K, T_V, T_IQ, T_IK, T_PLANT = 1, 2, 3, 4, 5, 6
+HOT_MEAN = 8.0   # strength of the group mean direction in idx-Q for "hot" planting
 
 
 @dataclass(frozen=True)
@@ -150,7 +154,7 @@ def prefill_inputs(shape: PrefillShape, seed: int, plant: str = "lit", n_plant: 
     if plant == "hot":
         u = torch.tensor(_unit_vectors(s.G, s.dI, seed), dtype=torch.float32, device=device)
         iq32 = randn_fp32((s.L, s.G, s.dI), seed, T_IQ, device)
-        iq32 += 4.0 * u[None, :, :]
+        iq32 += HOT_MEAN * u[None, :, :]
         iq = iq32.to(torch.bfloat16)
         del iq32
         amp = c * math.sqrt(s.dI)

@@ -1,0 +1,43 @@
+"""Accounting pins (CPU): the FLOP model the benchmark reports against.
+
+"MiniMax M3 算力省 20 倍" §四 (and "MiniMax-M3上架DEVUP…") quote 28.4x fewer
+attention FLOPs per token at 1M context for the 109B research model (64 query
+heads, 4 KV heads, k*B = 2048).  Dense causal GQA spends 4*H*d*(L/2) per token on
+average; MSA spends 4*H*d*kB on the main branch plus 2*G*dI*(L/2) on index
+scores.  With dI = d the ratio is 28.44 for any d, which is the quoted figure.
+"""
+import numpy as np
+
+import bench
+
+
+def test_paper_ratio_28_4():
+    r = bench.paper_flop_ratio(H=64, G=4, d=128, dI=128, L=1 << 20, kB=2048)
+    assert round(r, 1) == 28.4
+    assert abs(r - 28.44) < 0.01
+    # independent of d when dI = d
+    assert abs(bench.paper_flop_ratio(64, 4, 64, 64, 1 << 20, 2048) - r) < 1e-9
+
+
+def test_prefill_work_matches_closed_forms():
+    L, H, G, d, dI, k = 131072, 64, 4, 128, 128, 16
+    w = bench.prefill_work(L, H, G, d, dI, k)
+    nb = L // 128
+    # competitor keys: sum over query blocks b of 128 queries x 128*b keys
+    assert w["pairs"] == 128 * 128 * nb * (nb - 1) / 2
+    assert abs(w["flops"]["k1_index_pool"] - 8.79e12) / 8.79e12 < 1e-3
+    # attended tokens per group: full budget minus the causal part of the own block
+    assert abs(w["flops"]["k4_kv_outer"] - 8.46e12) / 8.46e12 < 2e-2
+    dense = w["dense_gqa_flops"]
+    assert abs(dense - 4 * H * d * L * (L + 1) / 2) < 1
+    # at 1M the index branch dominates MSA's algorithmic FLOPs (~89%)
+    w1 = bench.prefill_work(1 << 20, H, G, d, dI, k)
+    frac = w1["flops"]["k1_index_pool"] / w1["f_total"]
+    assert 0.88 < frac < 0.90
+
+
+def test_decode_work():
+    w = bench.decode_work(64, 262144, 64, 4, 128, 128, 16)
+    # idx-K stream of all competitor blocks dominates: ~4 GiB of the ~4.57 GB step
+    assert 4.2e9 < w["bytes"]["k1d_index_pool"] < 4.4e9
+    assert 4.4e9 < w["total_bytes"] < 4.7e9
