@@ -28,6 +28,7 @@ METRIC = "MSA prefill tokens/s @128K & 1M (1 GPU, % MFMA peak); decode us/step @
 PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12      # MI355X HBM3E
 B_BLOCK = 128
+K4_QUERIES = 128             # (query, slot) entries per KV-outer work item
 
 
 # --------------------------------------------------------------------------
@@ -60,8 +61,8 @@ def prefill_work(L, H, G, d, dI, k, B=B_BLOCK, list_counts=None):
     f_attn = 4.0 * r * d * G * attended
     comp_rows = np.maximum(bi - 0, 0)
     k2_bytes = 4.0 * G * float(np.sum(np.where(bi > k - 1, comp_rows, 0))) + 4.0 * L * G * k
-    items = float(np.sum(np.ceil(np.asarray(list_counts) / 64.0))) if list_counts is not None \
-        else entries / 64.0
+    items = float(np.sum(np.ceil(np.asarray(list_counts) / K4_QUERIES))) \
+        if list_counts is not None else entries / K4_QUERIES
     k4_bytes = (entries * r * d * 2            # gathered q rows
                 + entries * r * (2 * d + 4)    # partial (o bf16, lse fp32) writes
                 + items * 2 * B * d * 2)       # K and V block staged per work item
@@ -156,6 +157,20 @@ def cpu_baseline_decode(x, shape, target_s=15.0):
                       f"{shape.N}"}
 
 
+def copy_calibration(gib: float):
+    """A plain copy of known size: each launch reads and writes exactly n bytes."""
+    import torch
+    n = int(gib * (1 << 30)) // 16 * 16
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 4}), flush=True)
+
+
 def _load_traffic(kernel: str, workload: str):
     """HBM traffic per launch from committed rocprofv3 counter summaries, if any
     are recorded for this kernel, workload and the current kernel sources."""
@@ -192,7 +207,13 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="only run a plain device-to-device copy of GIB GiB (4 times), the "
+                         "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the library has no multi-GPU path); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -275,7 +296,7 @@ def main():
                        "higher_is_better": True})
         result["config"] = {"workload": wl.name, "L": s.L, "H": s.H, "G": s.G, "d": s.d,
                             "dI": s.dI, "B": s.B, "k": s.k, "planting": wl.plant,
-                            "query_chunk": 32768}
+                            "query_chunk": min(-(-s.L // 128) * 128, 131072)}
         result["step_mfma_frac"] = work["f_total"] / (ms_per_step / 1e3) / PEAK_BF16_FLOPS
         result["algorithmic_flops_per_step"] = work["f_total"]
         result["dense_gqa_flops_per_step"] = work["dense_gqa_flops"]

@@ -1,9 +1,11 @@
 // msa_api.hip -- the C ABI of libmsa.so (declared in include/msa.h): argument
 // validation, workspace carving and the launch sequence of each entry point.
 //
-// Prefill runs over query chunks of at most kChunkQ queries so that the
-// workspace stays bounded at any L (block scores and partials are per chunk);
-// every query's result is independent of the chunking.  Per chunk:
+// Prefill runs over query chunks so that the workspace stays bounded at any L
+// (block scores and partials are per chunk): the preferred chunk is kChunkQ
+// queries; a caller that passes a smaller workspace gets the largest chunk
+// (a multiple of 128 queries) that fits.  Every query's result is independent of
+// the chunking.  Per chunk:
 //   K1 index score + block max-pool -> K2 exp-free top-k -> K3 schedule ->
 //   K4 KV-outer attention -> K5 combine.
 // Decode: K1d -> K2 -> K4d -> K5.
@@ -25,7 +27,7 @@ namespace {
 
 using namespace msa;
 
-constexpr int64_t kChunkQ = 32768;     // queries per prefill chunk
+constexpr int64_t kChunkQ = 131072;    // preferred queries per prefill chunk
 constexpr size_t kAlign = 256;
 
 // Workspace carving: with base == nullptr only the size is accumulated.
@@ -54,7 +56,7 @@ AttnWs carve_attn(Carver &c, int64_t C, int H, int G, int d, int k, int nb) {
     w.sb.counts = c.take<int>(lists);
     w.sb.offs = c.take<int>(lists + 1);
     w.sb.toff = c.take<int>(lists + 1);
-    w.sb.cursor = c.take<int>(lists);
+    w.sb.wcnt = c.take<int>((int64_t)k3_num_groups(C) * lists);
     w.sb.total = c.take<int>(1);
     w.sb.list = c.take<uint32_t>(C * G * k);
     w.po = c.take<uint16_t>(C * H * k * d);
@@ -66,12 +68,45 @@ int64_t chunk_of(int64_t L) { return std::min<int64_t>(round_up(std::max<int64_t
 int64_t nblocks(int64_t L) { return (L + kBlock - 1) / kBlock; }
 int nb_padded(int64_t L) { return (int)round_up(std::max<int64_t>(nblocks(L), 1), 8); }
 
+size_t select_bytes(int64_t C, int64_t L, int G) {
+    Carver c(nullptr);
+    c.take<float>(C * G * nb_padded(L));
+    return c.used;
+}
+size_t attn_bytes(int64_t C, int64_t L, int H, int G, int d, int k) {
+    Carver c(nullptr);
+    carve_attn(c, C, H, G, d, k, (int)nblocks(L));
+    return c.used;
+}
+size_t prefill_bytes(int64_t C, int64_t L, int H, int G, int d, int k) {
+    Carver c(nullptr);
+    c.take<float>(C * G * nb_padded(L));
+    c.take<int32_t>(C * G * k);
+    carve_attn(c, C, H, G, d, k, (int)nblocks(L));
+    return c.used;
+}
+
+// Largest chunk (preferred size, then halving in multiples of 128 queries) whose
+// workspace fits in ws_bytes; 0 when not even one 128-query chunk fits.
+template <typename SizeFn>
+int64_t fit_chunk(int64_t L, size_t ws_bytes, SizeFn size_of) {
+    int64_t C = chunk_of(L);
+    while (C > kBlock && size_of(C) > ws_bytes) C = round_up(C / 2, kBlock);
+    return size_of(C) <= ws_bytes ? C : 0;
+}
+
+int check_ptr(void *ws) {
+    return (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign)) ? MSA_ERR_WORKSPACE_TOO_SMALL : MSA_OK;
+}
+
 bool r_ok(int H, int G) {
     if (G <= 0 || H % G) return false;
     const int r = H / G;
     return r == 1 || r == 2 || r == 4 || r == 8 || r == 16 || r == 32;
 }
 bool d_ok(int d) { return d == 64 || d == 128; }
+// The scheduler keeps two LDS counters per block of a group: at most 8192 blocks.
+constexpr int64_t kMaxPrefillLen = 8192 * (int64_t)kBlock;
 bool index_ok(int G, int dI) {
     return (G == 1 || G == 2 || G == 4 || G == 8) && (dI == 32 || dI == 64 || dI == 128) &&
            G * dI <= 512;
@@ -152,9 +187,7 @@ const char *msa_status_string(int status) {
 size_t msa_select_blocks_workspace_size(int64_t L, int G, int dI, int B, int k) {
     (void)dI; (void)B; (void)k;
     if (L <= 0 || G <= 0) return 0;
-    Carver c(nullptr);
-    c.take<float>(chunk_of(L) * G * nb_padded(L));
-    return c.used;
+    return select_bytes(chunk_of(L), L, G);
 }
 
 int msa_select_blocks(const uint16_t *idx_q, const uint16_t *idx_k, int64_t L, int G, int dI,
@@ -163,13 +196,13 @@ int msa_select_blocks(const uint16_t *idx_q, const uint16_t *idx_k, int64_t L, i
     if (L == 0) return MSA_OK;
     if (!idx_q || !idx_k || !block_ids) return MSA_ERR_INVALID_ARG;
     if (B != kBlock || !index_ok(G, dI) || k > 32) return MSA_ERR_UNSUPPORTED;
-    const int st = check_ws(ws, ws_bytes, msa_select_blocks_workspace_size(L, G, dI, B, k));
-    if (st != MSA_OK) return st;
+    if (check_ptr(ws) != MSA_OK) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    const int64_t C = fit_chunk(L, ws_bytes, [&](int64_t c) { return select_bytes(c, L, G); });
+    if (C == 0) return MSA_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     Carver c(ws);
     const int nbp = nb_padded(L);
-    float *S = c.take<float>(chunk_of(L) * G * nbp);
-    const int64_t C = chunk_of(L);
+    float *S = c.take<float>(C * G * nbp);
     for (int64_t q0 = 0; q0 < L; q0 += C) {
         const int64_t qend = std::min(L, q0 + C);
         MSA_TIMED(kK1, launch_k1_index_pool(idx_q, idx_k, S, L, q0, qend, G, dI, nbp, s));
@@ -183,9 +216,7 @@ int msa_select_blocks(const uint16_t *idx_q, const uint16_t *idx_k, int64_t L, i
 size_t msa_sparse_attn_workspace_size(int64_t L, int H, int G, int d, int B, int kslots) {
     (void)B;
     if (L <= 0 || G <= 0 || H <= 0 || d <= 0 || kslots <= 0) return 0;
-    Carver c(nullptr);
-    carve_attn(c, chunk_of(L), H, G, d, kslots, (int)nblocks(L));
-    return c.used;
+    return attn_bytes(chunk_of(L), L, H, G, d, kslots);
 }
 
 int msa_sparse_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -195,13 +226,15 @@ int msa_sparse_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         return MSA_ERR_INVALID_ARG;
     if (L == 0) return MSA_OK;
     if (!q || !k || !v || !block_ids || !out) return MSA_ERR_INVALID_ARG;
-    if (B != kBlock || !d_ok(d) || !r_ok(H, G) || kslots > 32) return MSA_ERR_UNSUPPORTED;
-    const int st = check_ws(ws, ws_bytes, msa_sparse_attn_workspace_size(L, H, G, d, B, kslots));
-    if (st != MSA_OK) return st;
+    if (B != kBlock || !d_ok(d) || !r_ok(H, G) || kslots > 32 || L > kMaxPrefillLen)
+        return MSA_ERR_UNSUPPORTED;
+    if (check_ptr(ws) != MSA_OK) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    const int64_t C = fit_chunk(L, ws_bytes,
+                                [&](int64_t c) { return attn_bytes(c, L, H, G, d, kslots); });
+    if (C == 0) return MSA_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     scale = default_scale(scale, d);
     Carver c(ws);
-    const int64_t C = chunk_of(L);
     const AttnWs w = carve_attn(c, C, H, G, d, kslots, (int)nblocks(L));
     for (int64_t q0 = 0; q0 < L; q0 += C) {
         const int64_t qend = std::min(L, q0 + C);
@@ -216,12 +249,7 @@ int msa_sparse_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 size_t msa_prefill_workspace_size(int64_t L, int H, int G, int d, int dI, int B, int k) {
     (void)dI; (void)B;
     if (L <= 0 || G <= 0 || H <= 0 || d <= 0 || k <= 0) return 0;
-    const int64_t C = chunk_of(L);
-    Carver c(nullptr);
-    c.take<float>(C * G * nb_padded(L));
-    c.take<int32_t>(C * G * k);
-    carve_attn(c, C, H, G, d, k, (int)nblocks(L));
-    return c.used;
+    return prefill_bytes(chunk_of(L), L, H, G, d, k);
 }
 
 int msa_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *idx_q,
@@ -232,13 +260,15 @@ int msa_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
         return MSA_ERR_INVALID_ARG;
     if (L == 0) return MSA_OK;
     if (!q || !k || !v || !idx_q || !idx_k || !out) return MSA_ERR_INVALID_ARG;
-    if (B != kBlock || !d_ok(d) || !r_ok(H, G) || !index_ok(G, dI) || kslots > 32)
+    if (B != kBlock || !d_ok(d) || !r_ok(H, G) || !index_ok(G, dI) || kslots > 32 ||
+        L > kMaxPrefillLen)
         return MSA_ERR_UNSUPPORTED;
-    const int st = check_ws(ws, ws_bytes, msa_prefill_workspace_size(L, H, G, d, dI, B, kslots));
-    if (st != MSA_OK) return st;
+    if (check_ptr(ws) != MSA_OK) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    const int64_t C = fit_chunk(L, ws_bytes,
+                                [&](int64_t c) { return prefill_bytes(c, L, H, G, d, kslots); });
+    if (C == 0) return MSA_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     scale = default_scale(scale, d);
-    const int64_t C = chunk_of(L);
     const int nbp = nb_padded(L);
     Carver c(ws);
     float *S = c.take<float>(C * G * nbp);

@@ -6,7 +6,7 @@
 // "MiniMax-M3上架DEVUP…": no approximation inside a selected block).
 //
 // K4  (prefill, KV-outer): one work item = one (group g, KV block j) list slice of
-//     up to 64 (query, slot) entries.  K_j and V_j of KV head g are staged once in
+//     up to 128 (query, slot) entries.  K_j and V_j of KV head g are staged once in
 //     LDS (V transposed); every wave then takes 32 MFMA columns = 32/R queries x R
 //     heads of the group, gathers their q rows straight into MFMA registers,
 //     computes S^T = K Q^T, the block-local softmax (causal mask only in the query's
@@ -27,19 +27,28 @@
 
 namespace msa {
 
-// Key offset (within a 32-key M-tile) of A-operand row m.
-__device__ __forceinline__ int k_row_perm(int m) {
-    return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
+// A-operand row m of an S^T M-tile holds key pi(m) = m with bits 2 and 3 swapped:
+//   pi(m) = 16*(m>>4) + 8*((m>>2)&1) + 4*((m>>3)&1) + (m&3).
+// K tiles are staged with that permutation applied (stage_rows<.., true>), so the
+// MFMA operand reads are plain row reads.
+
+// Q operand of one lane's column: D/16 chunks of 8 values (K-step ks takes chunk 2ks+hf).
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8 (&qb)[D / 16], const uint16_t *qrow, bool active,
+                                       int hf) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+        qb[ks] = as_bf16x8(active ? load16(qrow + (2 * ks + hf) * 8) : u32x4{0, 0, 0, 0});
 }
 
 // One pass of 32 columns of a wave over a staged block.  Lane column = l % 32.
-//   qrow   : the column's q row (d values), read only when `active`
+//   qb     : the column's q row as the B operand (see load_q)
 //   qpos   : the column's token position (its causal limit in its own block)
 //   j      : the staged KV block
 //   orow / lse_dst : destination of the column's partial (written when active)
 template <int D>
 __device__ __forceinline__ void attend_pass(const char *lds_k, const char *lds_vt, int j,
-                                            const uint16_t *qrow, bool active, int64_t qpos,
+                                            const bf16x8 (&qb)[D / 16], bool active, int64_t qpos,
                                             uint16_t *orow, float *lse_dst, float scale_log2,
                                             int lane) {
     constexpr int KS = D / 16;   // K-steps of S^T over d
@@ -47,45 +56,47 @@ __device__ __forceinline__ void attend_pass(const char *lds_k, const char *lds_v
     constexpr int MD = D / 32;   // M-tiles of O^T over d
     const int hf = lane >> 5, l32 = lane & 31;
 
-    bf16x8 qb[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        qb[ks] = as_bf16x8(active ? load16(qrow + (2 * ks + hf) * 8) : u32x4{0, 0, 0, 0});
-
-    const int prow = k_row_perm(l32);
     f32x16 sc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         sc[mt] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 a = as_bf16x8(load16(lds_k + swz<CPR>(mt * 32 + prow, 2 * ks + hf)));
+            const bf16x8 a = as_bf16x8(load16(lds_k + swz<CPR>(mt * 32 + l32, 2 * ks + hf)));
             sc[mt] = mfma32(a, qb[ks], sc[mt]);
         }
+        // keep each M-tile's operand reads next to its MFMAs (bounds live registers)
+        __builtin_amdgcn_sched_barrier(0);
     }
-    // scale to the log2 domain; causal mask inside the query's own block
+    // causal mask inside the query's own block (skipped by waves holding no such
+    // query); register r of M-tile mt holds key 32mt + 16(ip/2) + 8hf + 4(ip%2) + jj
     const bool local = active && (qpos / kBlock == j);
-    const int lim = (int)(qpos - (int64_t)j * kBlock);
-    float mx = -INFINITY;
+    if (__ballot(local)) {
+        const int lim = local ? (int)(qpos - (int64_t)j * kBlock) - 8 * hf : kBlock;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int ip = r >> 2, jj = r & 3;
-            const int key = 32 * mt + 16 * (ip >> 1) + 8 * hf + 4 * (ip & 1) + jj;
-            float v = sc[mt][r] * scale_log2;
-            if (local && key > lim) v = -INFINITY;
-            sc[mt][r] = v;
-            mx = fmaxf(mx, v);
+            for (int r = 0; r < 16; ++r) {
+                const int ip = r >> 2, jj = r & 3;
+                const int key = 32 * mt + 16 * (ip >> 1) + 4 * (ip & 1) + jj;   // minus 8hf
+                if (key > lim) sc[mt][r] = -INFINITY;
+            }
         }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[mt][r]);
     mx = fmaxf(mx, xor_shfl(mx, 32));
+    // p = 2^((s - max) * scale * log2 e), one FMA + one exp per score
+    const float nmx = -mx * scale_log2;
     float sum = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(sc[mt][r] - mx);
+            const float p = __builtin_amdgcn_exp2f(fmaf(sc[mt][r], scale_log2, nmx));
             sc[mt][r] = p;
             sum += p;
         }
@@ -112,26 +123,37 @@ __device__ __forceinline__ void attend_pass(const char *lds_k, const char *lds_v
             const bf16x8 a = as_bf16x8(load16(lds_vt + swz<16>(md * 32 + l32, 2 * kt + hf)));
             o[md] = mfma32(a, pb[kt], o[md]);
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
-    if (!active) return;
+    // normalise, pack to bf16, and swap half-rows between the lane halves
+    // (v_permlane32_swap) so each lane stores 8 consecutive d values (16 bytes):
+    // before, lane half hf holds d = 16q + 4hf + {0..3} and 16q + 8 + 4hf + {0..3}
     const float inv = 1.0f / sum;
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
 #pragma unroll
-        for (int ip = 0; ip < 4; ++ip) {
-            const int d0 = 32 * md + 8 * ip + 4 * hf;
-            store8(orow + d0, u32x2{pack_bf16x2(o[md][4 * ip + 0] * inv, o[md][4 * ip + 1] * inv),
-                                    pack_bf16x2(o[md][4 * ip + 2] * inv, o[md][4 * ip + 3] * inv)});
+        for (int q2 = 0; q2 < 2; ++q2) {
+            const f32x16 &acc = o[md];
+            const int r0 = 8 * q2;          // registers of ip = 2q2 (r0..r0+3) and 2q2+1
+            uint32_t a0 = pack_bf16x2(acc[r0 + 0] * inv, acc[r0 + 1] * inv);
+            uint32_t a1 = pack_bf16x2(acc[r0 + 2] * inv, acc[r0 + 3] * inv);
+            uint32_t b0 = pack_bf16x2(acc[r0 + 4] * inv, acc[r0 + 5] * inv);
+            uint32_t b1 = pack_bf16x2(acc[r0 + 6] * inv, acc[r0 + 7] * inv);
+            const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+            // lower half now holds d = 16q2 + 0..7, upper half d = 16q2 + 8..15
+            if (active)
+                store16(orow + 32 * md + 16 * q2 + 8 * hf, u32x4{s0[0], s1[0], s0[1], s1[1]});
         }
     }
-    if (hf == 0) *lse_dst = mx + __log2f(sum);
+    if (active && hf == 0) *lse_dst = mx * scale_log2 + __log2f(sum);
 }
 
 // ---------------------------------------------------------------------------
 // K4: KV-outer sparse attention over the scheduled lists.
 // ---------------------------------------------------------------------------
 template <int D, int R>
-__global__ __launch_bounds__(256) void k4_kv_outer(
+__global__ __launch_bounds__(256, 2) void k4_kv_outer(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kx,
     const uint16_t *__restrict__ vx, const int *__restrict__ offs, const int *__restrict__ toff,
     const int *__restrict__ total, const uint32_t *__restrict__ list, int nlists, int nb,
@@ -139,6 +161,8 @@ __global__ __launch_bounds__(256) void k4_kv_outer(
     float *__restrict__ plse) {
     __shared__ __attribute__((aligned(16))) char lds_k[kBlock * D * 2];
     __shared__ __attribute__((aligned(16))) char lds_vt[D * kBlock * 2];
+    static_assert(kK4Queries <= 256, "one entry per thread is staged");
+    __shared__ uint32_t lds_e[kK4Queries];                   // the item's (query, slot) entries
     const int per = gridDim.x / 8;
     const int x = (blockIdx.x % 8) * per + blockIdx.x / 8;   // XCD-contiguous items
     if (x >= *total) return;
@@ -155,29 +179,60 @@ __global__ __launch_bounds__(256) void k4_kv_outer(
     const int cnt = min(kK4Queries, offs[li + 1] - begin);
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int hf = lane >> 5, l32 = lane & 31;
+    constexpr int QPW = 32 / R;   // queries per wave pass
+    const int a = l32 / R, h = l32 % R;
+    const int64_t hh = (int64_t)g * R + h;
+
+    // the first pass's q rows are requested before the K/V staging, the second's
+    // right after it; every pass then prefetches the pass two ahead (entries come
+    // from LDS, so those loads issue without waiting)
+    int base = wave * QPW;
+    bool act = base + a < cnt;
+    uint32_t entry = act ? list[begin + base + a] : 0u;
+    bf16x8 qb[D / 16];
+    load_q<D>(qb, q + ((q0 + (entry >> 5)) * H + hh) * D, act, hf);
+
+    if (tid < cnt) lds_e[tid] = list[begin + tid];
     const int64_t kv_row_bytes = (int64_t)G * D * 2;
     const char *ksrc = reinterpret_cast<const char *>(kx + ((int64_t)j * kBlock * G + g) * D);
     const char *vsrc = reinterpret_cast<const char *>(vx + ((int64_t)j * kBlock * G + g) * D);
     const int nrows = (int)min<int64_t>(kBlock, L - (int64_t)j * kBlock);
-    stage_rows<D / 8>(lds_k, ksrc, kv_row_bytes, nrows, tid);
+    stage_rows<D / 8, true>(lds_k, ksrc, kv_row_bytes, nrows, tid);
     stage_v_transposed<D>(lds_vt, vsrc, kv_row_bytes, nrows, tid);
     __syncthreads();
 
-    constexpr int QPW = 32 / R;   // queries per wave pass
-    const int l32 = lane & 31;
-    const int a = l32 / R, h = l32 % R;
-    for (int base = wave * QPW; base < cnt; base += 4 * QPW) {
-        const int e = base + a;
-        const bool active = e < cnt;
-        const uint32_t entry = active ? list[begin + e] : 0u;
+    constexpr int STEP = 4 * QPW;
+    int nbase = base + STEP;
+    bool nact = nbase + a < cnt;
+    uint32_t nentry = nact ? lds_e[nbase + a] : 0u;
+    bf16x8 qn[D / 16];
+    load_q<D>(qn, q + ((q0 + (nentry >> 5)) * H + hh) * D, nact, hf);
+
+    while (base < cnt) {
+        const int fbase = nbase + STEP;
+        const bool fact = fbase + a < cnt;
+        const uint32_t fentry = fact ? lds_e[fbase + a] : 0u;
+        bf16x8 qf[D / 16];
+        load_q<D>(qf, q + ((q0 + (fentry >> 5)) * H + hh) * D, fact, hf);
+
         const int64_t il = entry >> 5;
         const int s = entry & 31;
-        const int64_t i = q0 + il;
-        const int64_t hh = (int64_t)g * R + h;
-        const uint16_t *qrow = q + (i * H + hh) * D;
         const int64_t prow = (il * H + hh) * kslots + s;
-        attend_pass<D>(lds_k, lds_vt, j, qrow, active, i, po + prow * D, plse + prow, scale_log2,
+        const int64_t lrow = ((il * G + g) * kslots + s) * R + h;
+        attend_pass<D>(lds_k, lds_vt, j, qb, act, q0 + il, po + prow * D, plse + lrow, scale_log2,
                        lane);
+        base = nbase;
+        act = nact;
+        entry = nentry;
+        nbase = fbase;
+        nact = fact;
+        nentry = fentry;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            qb[ks] = qn[ks];
+            qn[ks] = qf[ks];
+        }
     }
 }
 
@@ -233,7 +288,8 @@ __global__ __launch_bounds__(256) void k4d_split(const uint16_t *__restrict__ q,
     const int64_t kv_row_bytes = (int64_t)G * D * 2;
     const int64_t row0 = (n * Lmax + (int64_t)j * kBlock) * G + g;
     const int nrows = (int)min<int64_t>(kBlock, Lmax - (int64_t)j * kBlock);
-    stage_rows<D / 8>(lds_k, reinterpret_cast<const char *>(kc + row0 * D), kv_row_bytes, nrows, tid);
+    stage_rows<D / 8, true>(lds_k, reinterpret_cast<const char *>(kc + row0 * D), kv_row_bytes,
+                            nrows, tid);
     stage_v_transposed<D>(lds_vt, reinterpret_cast<const char *>(vc + row0 * D), kv_row_bytes,
                           nrows, tid);
     __syncthreads();
@@ -242,8 +298,10 @@ __global__ __launch_bounds__(256) void k4d_split(const uint16_t *__restrict__ q,
     const bool active = l32 < R;
     const int64_t hh = (int64_t)g * R + (active ? l32 : 0);
     const int64_t prow = (n * H + hh) * kslots + s;
-    attend_pass<D>(lds_k, lds_vt, j, q + (n * H + hh) * D, active, p, po + prow * D, plse + prow,
-                   scale_log2, lane);
+    const int64_t lrow = ((n * G + g) * kslots + s) * R + (active ? l32 : 0);
+    bf16x8 qb[D / 16];
+    load_q<D>(qb, q + (n * H + hh) * D, active, lane >> 5);
+    attend_pass<D>(lds_k, lds_vt, j, qb, active, p, po + prow * D, plse + lrow, scale_log2, lane);
 }
 
 template <int D, int R>
@@ -273,10 +331,12 @@ hipError_t launch_k4d_split(const uint16_t *q, const uint16_t *kc, const uint16_
 }
 
 // ---------------------------------------------------------------------------
-// K5: combine.  D/8 threads per (query, head), 8 d values per thread.
-// Slots are valid when 0 <= id < nb_lim (the same rule K3 used to build lists).
+// K5: combine.  D/8 threads per (query, head), 8 d values per thread.  All KMAX
+// slot partials of a thread are requested at once (every slot location exists in
+// the workspace); slots are merged only when 0 <= id < nb_lim -- the rule K3 used
+// to build the lists -- so stale workspace contents never enter the result.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int KMAX>
 __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ po,
                                                   const float *__restrict__ plse,
                                                   const int32_t *__restrict__ ids, int64_t nq,
@@ -290,25 +350,57 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
     const int64_t i = ih / H;
     const int h = (int)(ih % H);
     const int g = h / (H / G);
+    const int R = H / G;
     const int32_t *idr = ids + (i * G + g) * kslots;
-    const float *lr = plse + ih * kslots;
-    float M = -INFINITY;
-    for (int s = 0; s < kslots; ++s) {
-        const int id = idr[s];
-        if (id >= 0 && id < nb_lim) M = fmaxf(M, lr[s]);
+    const float *lr = plse + (i * G + g) * kslots * R + (h - g * R);   // slot s at lr[s * R]
+    const uint16_t *pr = po + ih * kslots * D + sub * 8;
+    u32x4 v[KMAX];
+    float l[KMAX];
+    bool ok[KMAX];
+    if (kslots == KMAX) {
+        // full rows: ids as 16-byte vectors (rows are 16-byte aligned)
+#pragma unroll
+        for (int s4 = 0; s4 < KMAX / 4; ++s4) {
+            const u32x4 iv = load16(idr + 4 * s4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int id = (int)iv[e];
+                ok[4 * s4 + e] = id >= 0 && id < nb_lim;
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < KMAX; ++s) {
+            l[s] = lr[s * R];
+            v[s] = load16(pr + s * D);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < KMAX; ++s) {
+            if (s < kslots) {
+                const int id = idr[s];
+                ok[s] = id >= 0 && id < nb_lim;
+                l[s] = lr[s * R];
+                v[s] = load16(pr + s * D);
+            } else {
+                ok[s] = false;
+            }
+        }
     }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s)
+        if (ok[s]) M = fmaxf(M, l[s]);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float wsum = 0.0f;
-    for (int s = 0; s < kslots; ++s) {
-        const int id = idr[s];
-        if (id < 0 || id >= nb_lim) continue;
-        const float w = __builtin_amdgcn_exp2f(lr[s] - M);
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+        if (!ok[s]) continue;
+        const float w = __builtin_amdgcn_exp2f(l[s] - M);
         wsum += w;
-        const u32x4 v = load16(po + (ih * kslots + s) * D + sub * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            acc[2 * e] += w * bf16_to_f32(v[e] & 0xFFFFu);
-            acc[2 * e + 1] += w * bf16_to_f32(v[e] >> 16);
+            acc[2 * e] += w * bf16_to_f32(v[s][e] & 0xFFFFu);
+            acc[2 * e + 1] += w * bf16_to_f32(v[s][e] >> 16);
         }
     }
     const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
@@ -318,21 +410,30 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
     store16(out + ih * D + sub * 8, r);
 }
 
+template <int D>
+static hipError_t k5_dispatch(const uint16_t *po, const float *plse, const int32_t *ids,
+                              int64_t nq, int H, int G, int k, int nb_lim, uint16_t *out,
+                              hipStream_t s) {
+    constexpr int PPW = 256 / (D / 8);
+    const dim3 grid((unsigned)((nq * H + PPW - 1) / PPW));
+    if (k <= 4)
+        hipLaunchKernelGGL((k5_combine<D, 4>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out);
+    else if (k <= 8)
+        hipLaunchKernelGGL((k5_combine<D, 8>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out);
+    else if (k <= 16)
+        hipLaunchKernelGGL((k5_combine<D, 16>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out);
+    else
+        hipLaunchKernelGGL((k5_combine<D, 32>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_k5_combine(const uint16_t *po, const float *plse, const int32_t *ids, int64_t nq,
                              int H, int G, int d, int k, int nb_lim, uint16_t *out,
                              hipStream_t s) {
     if (nq <= 0) return hipSuccess;
-    const int64_t pairs = nq * H;
-    if (d == 64) {
-        hipLaunchKernelGGL((k5_combine<64>), dim3((unsigned)((pairs + 31) / 32)), dim3(256), 0, s,
-                           po, plse, ids, nq, H, G, k, nb_lim, out);
-    } else if (d == 128) {
-        hipLaunchKernelGGL((k5_combine<128>), dim3((unsigned)((pairs + 15) / 16)), dim3(256), 0, s,
-                           po, plse, ids, nq, H, G, k, nb_lim, out);
-    } else {
-        return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    if (d == 64) return k5_dispatch<64>(po, plse, ids, nq, H, G, k, nb_lim, out, s);
+    if (d == 128) return k5_dispatch<128>(po, plse, ids, nq, H, G, k, nb_lim, out, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace msa

@@ -33,15 +33,13 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-// fp32 -> bf16 with round-to-nearest-even (inputs are finite).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// Two fp32 -> two bf16 (round-to-nearest-even) in one v_cvt_pk_bf16_f32; `lo`
+// lands in the low half-word.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -82,7 +80,9 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 // Copy a 128-row tile of CPR 16-byte chunks per row from global rows at
 // `src + row*stride_bytes` (rows >= nrows are zero-filled) into swizzled LDS.
 // Called by all 256 threads of a work-group.
-template <int CPR>
+// With SwapBits23, source row t is stored at LDS row t with bits 2 and 3 swapped
+// (an involution), so that reading LDS row m yields source row pi(m).
+template <int CPR, bool SwapBits23 = false>
 __device__ __forceinline__ void stage_rows(char *lds, const char *src, int64_t stride_bytes,
                                            int nrows, int tid) {
     constexpr int kRowsPerIter = 256 / CPR;
@@ -97,7 +97,8 @@ __device__ __forceinline__ void stage_rows(char *lds, const char *src, int64_t s
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
         const int row = tid / CPR + it * kRowsPerIter;
-        store16(lds + swz<CPR>(row, c), regs[it]);
+        const int lrow = SwapBits23 ? ((row & ~12) | ((row & 4) << 1) | ((row & 8) >> 1)) : row;
+        store16(lds + swz<CPR>(lrow, c), regs[it]);
     }
 }
 

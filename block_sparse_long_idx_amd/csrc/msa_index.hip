@@ -4,8 +4,8 @@
 // over the causal window, max-pooling into B = 128-token blocks).
 //
 // K1 (prefill) is a short-K GEMM with a max-pool epilogue, run on bf16 MFMA with
-// fp32 accumulation.  One work-group owns one query block (128 queries x G
-// groups = 128*G stacked index rows, which are contiguous in idx_q[L,G,dI]) and
+// fp32 accumulation.  One work-group (up to 8 waves) owns one query block (128
+// queries x G groups = 128*G stacked index rows, contiguous in idx_q[L,G,dI]) and
 // a range of up to 32 key blocks strictly before the query block; the query's
 // own block is never scored because it is always selected.  Index rows stay in
 // registers for the whole range; each 128-key block of idx_k is staged once in
@@ -50,12 +50,20 @@ int64_t k1_num_items(int qb0, int qb1) {
     return total;
 }
 
+// Columns per wave: 32 * NT.  G = 1: 4 waves x 32;  G = 2: 8 x 32;  G = 4: 8 x 64;
+// G = 8: 16 x 64.
+template <int G> struct K1Tiling {
+    static constexpr int NT = G >= 4 ? 2 : 1;
+    static constexpr int WAVES = kBlock * G / (32 * NT);
+    static constexpr int THREADS = WAVES * kWave;
+};
+
 template <int G, int DI>
-__global__ __launch_bounds__(256) void k1_index_pool(const uint16_t *__restrict__ iq,
-                                                     const uint16_t *__restrict__ ik,
-                                                     float *__restrict__ S, int64_t q0,
-                                                     int64_t qend, int nbp, int qb0, int qb1,
-                                                     int64_t n_items) {
+__global__ __launch_bounds__(K1Tiling<G>::THREADS, 1) void k1_index_pool(
+    const uint16_t *__restrict__ iq, const uint16_t *__restrict__ ik, float *__restrict__ S,
+    int64_t q0, int64_t qend, int nbp, int qb0, int qb1, int64_t n_items) {
+    constexpr int NT = K1Tiling<G>::NT;
+    constexpr int NTHR = K1Tiling<G>::THREADS;
     constexpr int CPR = DI / 8;            // 16-byte chunks per index row
     constexpr int KS = DI / 16;            // MFMA K-steps
     constexpr int NCOL = kBlock * G;       // stacked index rows of the work-group
@@ -75,12 +83,12 @@ __global__ __launch_bounds__(256) void k1_index_pool(const uint16_t *__restrict_
     const int hf = lane >> 5, l32 = lane & 31;
 
     // B operand: index rows of this wave, kept in registers.
-    bf16x8 bq[G][KS];
+    bf16x8 bq[NT][KS];
     const int64_t row0 = (int64_t)qb * kBlock * G;   // flattened [L*G] row of column 0
     const int64_t row_end = qend * G;
 #pragma unroll
-    for (int nt = 0; nt < G; ++nt) {
-        const int64_t row = row0 + wave * 32 * G + nt * 32 + l32;
+    for (int nt = 0; nt < NT; ++nt) {
+        const int64_t row = row0 + wave * 32 * NT + nt * 32 + l32;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             bq[nt][ks] = as_bf16x8(row < row_end ? load16(iq + row * DI + (2 * ks + hf) * 8)
@@ -89,11 +97,20 @@ __global__ __launch_bounds__(256) void k1_index_pool(const uint16_t *__restrict_
 
     const char *ikb = reinterpret_cast<const char *>(ik);
     const int64_t blk_bytes = (int64_t)kBlock * DI * 2;
-    stage_rows<CPR>(lds_k[0], ikb + j0 * blk_bytes, DI * 2, kBlock, tid);
+    constexpr int kRowsPerIter = NTHR / CPR;   // may exceed 128 rows: extra threads idle
+    constexpr int kIters = (kBlock + kRowsPerIter - 1) / kRowsPerIter;
+    {
+        const char *src = ikb + j0 * blk_bytes;
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int row = tid / CPR + it * kRowsPerIter;
+            if (row < kBlock)
+                store16(lds_k[0] + swz<CPR>(row, tid % CPR),
+                        load16(src + row * (DI * 2) + (tid % CPR) * 16));
+        }
+    }
     __syncthreads();
 
-    constexpr int kRowsPerIter = 256 / CPR;
-    constexpr int kIters = kBlock / kRowsPerIter;
     for (int j = j0; j < j1; ++j) {
         const int buf = (j - j0) & 1;
         // prefetch the next key block into registers
@@ -104,25 +121,25 @@ __global__ __launch_bounds__(256) void k1_index_pool(const uint16_t *__restrict_
 #pragma unroll
             for (int it = 0; it < kIters; ++it) {
                 const int row = tid / CPR + it * kRowsPerIter;
-                pre[it] = load16(src + row * (DI * 2) + (tid % CPR) * 16);
+                if (row < kBlock) pre[it] = load16(src + row * (DI * 2) + (tid % CPR) * 16);
             }
         }
-        float mx[G];
+        float mx[NT];
 #pragma unroll
-        for (int nt = 0; nt < G; ++nt) mx[nt] = -INFINITY;
+        for (int nt = 0; nt < NT; ++nt) mx[nt] = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            f32x16 acc[G];
+            f32x16 acc[NT];
 #pragma unroll
-            for (int nt = 0; nt < G; ++nt) acc[nt] = f32x16{};
+            for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const bf16x8 a = as_bf16x8(load16(lds_k[buf] + swz<CPR>(mt * 32 + l32, 2 * ks + hf)));
 #pragma unroll
-                for (int nt = 0; nt < G; ++nt) acc[nt] = mfma32(a, bq[nt][ks], acc[nt]);
+                for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma32(a, bq[nt][ks], acc[nt]);
             }
 #pragma unroll
-            for (int nt = 0; nt < G; ++nt) {
+            for (int nt = 0; nt < NT; ++nt) {
                 float m = acc[nt][0];
 #pragma unroll
                 for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[nt][r]);
@@ -131,22 +148,22 @@ __global__ __launch_bounds__(256) void k1_index_pool(const uint16_t *__restrict_
         }
         const int slot = (j - j0) % kK1Flush;
 #pragma unroll
-        for (int nt = 0; nt < G; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
             const float m = fmaxf(mx[nt], xor_shfl(mx[nt], 32));
-            if (hf == 0) lds_s[slot][wave * 32 * G + nt * 32 + l32] = m;
+            if (hf == 0) lds_s[slot][wave * 32 * NT + nt * 32 + l32] = m;
         }
         if (more) {
 #pragma unroll
             for (int it = 0; it < kIters; ++it) {
                 const int row = tid / CPR + it * kRowsPerIter;
-                store16(lds_k[buf ^ 1] + swz<CPR>(row, tid % CPR), pre[it]);
+                if (row < kBlock) store16(lds_k[buf ^ 1] + swz<CPR>(row, tid % CPR), pre[it]);
             }
         }
         __syncthreads();
         if (slot == kK1Flush - 1 || j == j1 - 1) {
             const int nj = slot + 1;
             const int jb = j - slot;
-            for (int col = tid; col < NCOL; col += 256) {
+            for (int col = tid; col < NCOL; col += NTHR) {
                 const int64_t row = row0 + col;
                 if (row >= row_end) continue;
                 float *dst = S + (row - q0 * G) * nbp + jb;
@@ -172,8 +189,8 @@ static hipError_t k1_dispatch(const uint16_t *iq, const uint16_t *ik, float *S, 
     const int64_t n = k1_num_items(qb0, qb1);
     if (n == 0) return hipSuccess;
     const int64_t grid = round_up(n, 8);
-    hipLaunchKernelGGL((k1_index_pool<G, DI>), dim3((unsigned)grid), dim3(256), 0, s, iq, ik, S,
-                       q0, qend, nbp, qb0, qb1, n);
+    hipLaunchKernelGGL((k1_index_pool<G, DI>), dim3((unsigned)grid), dim3(K1Tiling<G>::THREADS), 0,
+                       s, iq, ik, S, q0, qend, nbp, qb0, qb1, n);
     return hipGetLastError();
 }
 

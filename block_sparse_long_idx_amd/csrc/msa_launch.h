@@ -11,7 +11,9 @@ constexpr int kBlock = 128;   // tokens per MSA block (B)
 // Key blocks scored by one K1 work-group item, and blocks buffered before a flush.
 constexpr int kK1KeyChunk = 32;
 // Queries per K4 work item (one staged K/V block serves up to this many queries).
-constexpr int kK4Queries = 64;
+constexpr int kK4Queries = 128;
+// Queries whose entries one K3 work-group sorts.
+constexpr int kK3Queries = 2048;
 
 // Round n up to a multiple of m.
 inline int64_t round_up(int64_t n, int64_t m) { return (n + m - 1) / m * m; }
@@ -39,16 +41,18 @@ struct SchedBuffers {
     int *counts;     // [nlists]
     int *offs;       // [nlists + 1]
     int *toff;       // [nlists + 1] prefix sum of ceil(count / kK4Queries)
-    int *cursor;     // [nlists]
+    int *wcnt;       // [G * k3_num_groups(C) * nb] per-work-group counts / prefixes
     int *total;      // [1] number of K4 work items
     uint32_t *list;  // [C * G * k] entries (i - q0) << 5 | slot
 };
 hipError_t launch_k3_schedule(const int32_t *ids, int64_t C, int G, int k, int nb,
                               const SchedBuffers &sb, hipStream_t s);
 int64_t k4_max_items(int64_t C, int G, int k, int nb);
+int k3_num_groups(int64_t C);
 
-// K4: KV-outer attention over the scheduled lists -> partials (o, lse) per
-// (query, head, slot).  po [C*H*k][d] bf16, plse [C*H*k] fp32.
+// K4: KV-outer attention over the scheduled lists -> partials per (query, head,
+// slot): po [(i*H + h)*k + slot][d] bf16 (normalised o), plse [((i*G + g)*k + slot)*R
+// + h % R] fp32 (log2-sum-exp of the scaled scores).
 hipError_t launch_k4_kv_outer(const uint16_t *q, const uint16_t *kx, const uint16_t *vx,
                               const SchedBuffers &sb, int nb, int64_t L, int64_t q0, int64_t C,
                               int H, int G, int d, int k, float scale, uint16_t *po, float *plse,

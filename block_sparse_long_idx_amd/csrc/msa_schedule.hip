@@ -4,17 +4,16 @@
 // query dimension so no single work-group owns a block picked by almost every query;
 // "MiniMax M3 的采用瓶颈…" §对建设者的影响: KV-block-major layout).
 //
-//   hist    count[g*nb + b]  += 1 for every valid (query, group, slot) entry
-//   scan    offs = exclusive prefix of counts; toff = exclusive prefix of the number
-//           of pre-sized tiles ceil(count / kK4Queries) per list; total tiles
-//   scatter list[offs[l] + rank] = (query - q0) << 5 | slot
-//
-// Threads walk the entries slot-major and query-fastest, so a wave holds 64
-// consecutive queries at one (group, slot).  Hot blocks (selected by nearly every
-// query) then sit in the same slot of all 64 lanes and are counted with one
-// atomic per wave (wave-aggregated leader atomics).  The order of entries inside a
-// list depends on atomic timing, but no result does: every entry's partial is
-// written to its own (query, head, slot) location.
+// A counting sort with no global atomics.  Work-group (w, g) owns the entries of
+// group g for kK3Queries consecutive queries of the chunk:
+//   count    per-work-group histogram over the group's blocks, in LDS
+//   colscan  per list: exclusive prefix of the work-group counts, list total
+//   scan     offs = exclusive prefix of the list totals; toff = exclusive prefix of
+//            the number of pre-sized tiles ceil(count / kK4Queries) per list
+//   scatter  list[offs[l] + prefix(w) + rank] = (query - q0) << 5 | slot
+// Hot blocks (picked by nearly every query) only cost LDS atomics.  The order of
+// entries inside one work-group's share of a list depends on LDS atomic timing, but
+// no result does: every entry's partial goes to its own (query, head, slot).
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -31,66 +30,81 @@ hipError_t launch_fill_i32(int *p, int64_t n, int value, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Adds 1 to ctr[key] for every lane with key >= 0 and returns each such lane's
-// previous-count rank.  Lanes sharing the first active lane's key use one atomic.
-__device__ __forceinline__ int aggregated_increment(int *ctr, int key) {
-    const int lane = lane_id();
-    const bool valid = key >= 0;
-    const uint64_t act = __ballot(valid);
-    if (act == 0) return 0;
-    const int first = __ffsll((unsigned long long)act) - 1;
-    const int lead = __shfl(key, first, kWave);
-    const bool same = valid && key == lead;
-    const uint64_t m = __ballot(same);
-    int base = 0;
-    if (lane == first) base = atomicAdd(&ctr[lead], (int)__popcll(m));
-    base = __shfl(base, first, kWave);
-    const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-    if (same) return base + rank;
-    if (valid) return atomicAdd(&ctr[key], 1);
-    return 0;
-}
-
-__device__ __forceinline__ int entry_key(const int32_t *ids, int64_t t, int64_t C, int G, int k,
-                                         int nb, int64_t &i, int &s) {
-    i = t % C;
-    const int64_t gs = t / C;
-    const int g = (int)(gs / k);
-    s = (int)(gs % k);
+// Entries of one work-group: queries [w*kK3Queries, (w+1)*kK3Queries) of the chunk,
+// group g, all k slots; entry e -> query w*kK3Queries + e / k, slot e % k.
+__device__ __forceinline__ int entry_block(const int32_t *ids, int64_t C, int G, int k, int nb,
+                                           int g, int64_t i, int s) {
+    if (i >= C) return -1;
     const int id = ids[(i * G + g) * k + s];
-    return (id >= 0 && id < nb) ? g * nb + id : -1;   // ids outside [0, nb) are ignored
+    return (id >= 0 && id < nb) ? id : -1;   // ids outside [0, nb) are ignored
 }
 
-__global__ __launch_bounds__(256) void k3_hist(const int32_t *__restrict__ ids, int64_t C, int G,
-                                               int k, int nb, int *__restrict__ counts) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    int key = -1;
-    if (t < C * G * k) {
-        int64_t i;
-        int s;
-        key = entry_key(ids, t, C, G, k, nb, i, s);
+// Count pass: per-work-group histogram in LDS, written (zeros included) to
+// wcnt[(g * nW + w) * nb + b].  No global atomics.
+__global__ __launch_bounds__(256) void k3_count(const int32_t *__restrict__ ids, int64_t C, int G,
+                                                int k, int nb, int *__restrict__ wcnt) {
+    extern __shared__ int lds_cnt[];
+    const int w = blockIdx.x, g = blockIdx.y, nW = gridDim.x;
+    for (int b = threadIdx.x; b < nb; b += 256) lds_cnt[b] = 0;
+    __syncthreads();
+    const int64_t i0 = (int64_t)w * kK3Queries;
+    for (int e = threadIdx.x; e < kK3Queries * k; e += 256) {
+        const int id = entry_block(ids, C, G, k, nb, g, i0 + e / k, e % k);
+        if (id >= 0) atomicAdd(&lds_cnt[id], 1);
     }
-    aggregated_increment(counts, key);
+    __syncthreads();
+    int *dst = wcnt + ((int64_t)g * nW + w) * nb;
+    for (int b = threadIdx.x; b < nb; b += 256) dst[b] = lds_cnt[b];
 }
 
+// Column pass: for every list (g, b), turn the work-group counts into exclusive
+// prefixes over w (in place) and store the list's total in counts[g * nb + b].
+__global__ __launch_bounds__(256) void k3_colscan(int *__restrict__ wcnt, int G, int nb, int nW,
+                                                  int *__restrict__ counts) {
+    const int64_t l = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (l >= (int64_t)G * nb) return;
+    const int g = (int)(l / nb), b = (int)(l % nb);
+    int run = 0;
+    for (int w = 0; w < nW; ++w) {
+        int *p = wcnt + ((int64_t)g * nW + w) * nb + b;
+        const int c = *p;
+        *p = run;
+        run += c;
+    }
+    counts[l] = run;
+}
+
+// Scatter pass: each work-group places its entries at
+// offs[list] + (entries of earlier work-groups) + (rank inside this work-group).
 __global__ __launch_bounds__(256) void k3_scatter(const int32_t *__restrict__ ids, int64_t C, int G,
                                                   int k, int nb, const int *__restrict__ offs,
-                                                  int *__restrict__ cursor,
+                                                  const int *__restrict__ wcnt,
                                                   uint32_t *__restrict__ list) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    int key = -1;
-    int64_t i = 0;
-    int s = 0;
-    if (t < C * G * k) key = entry_key(ids, t, C, G, k, nb, i, s);
-    const int rank = aggregated_increment(cursor, key);
-    if (key >= 0) list[offs[key] + rank] = ((uint32_t)i << 5) | (uint32_t)s;
+    extern __shared__ int lds[];
+    int *base = lds;          // [nb] first position of this work-group's entries per list
+    int *rank = lds + nb;     // [nb] entries placed so far per list
+    const int w = blockIdx.x, g = blockIdx.y, nW = gridDim.x;
+    const int *pre = wcnt + ((int64_t)g * nW + w) * nb;
+    for (int b = threadIdx.x; b < nb; b += 256) {
+        base[b] = offs[g * nb + b] + pre[b];
+        rank[b] = 0;
+    }
+    __syncthreads();
+    const int64_t i0 = (int64_t)w * kK3Queries;
+    for (int e = threadIdx.x; e < kK3Queries * k; e += 256) {
+        const int64_t i = i0 + e / k;
+        const int s = e % k;
+        const int id = entry_block(ids, C, G, k, nb, g, i, s);
+        if (id < 0) continue;
+        const int r = atomicAdd(&rank[id], 1);
+        list[base[id] + r] = ((uint32_t)i << 5) | (uint32_t)s;
+    }
 }
 
 // One work-group of 1024 threads scans all lists.
 __global__ __launch_bounds__(1024) void k3_scan(const int *__restrict__ counts, int nlists,
                                                 int *__restrict__ offs, int *__restrict__ toff,
-                                                int *__restrict__ cursor, int *__restrict__ total) {
+                                                int *__restrict__ total) {
     __shared__ int sc[1024], st[1024];
     const int tid = threadIdx.x;
     const int per = (nlists + 1023) / 1024;
@@ -117,7 +131,6 @@ __global__ __launch_bounds__(1024) void k3_scan(const int *__restrict__ counts, 
         const int c = counts[l];
         offs[l] = ec;
         toff[l] = et;
-        cursor[l] = 0;
         ec += c;
         et += (c + kK4Queries - 1) / kK4Queries;
     }
@@ -134,26 +147,25 @@ int64_t k4_max_items(int64_t C, int G, int k, int nb) {
     return (entries + kK4Queries - 1) / kK4Queries + (lists < entries ? lists : entries);
 }
 
+int k3_num_groups(int64_t C) { return (int)((C + kK3Queries - 1) / kK3Queries); }
+
 hipError_t launch_k3_schedule(const int32_t *ids, int64_t C, int G, int k, int nb,
                               const SchedBuffers &sb, hipStream_t s) {
     const int nlists = G * nb;
-    hipError_t e = launch_fill_i32(sb.counts, nlists, 0, s);
-    if (e != hipSuccess) return e;
-    const int64_t entries = C * G * k;
-    const unsigned grid = (unsigned)((entries + 255) / 256);
-    if (entries > 0) {
-        hipLaunchKernelGGL(k3_hist, dim3(grid), dim3(256), 0, s, ids, C, G, k, nb, sb.counts);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(k3_scan, dim3(1), dim3(1024), 0, s, sb.counts, nlists, sb.offs, sb.toff,
-                       sb.cursor, sb.total);
+    const int nW = k3_num_groups(C);
+    hipError_t e;
+    const dim3 grid((unsigned)nW, (unsigned)G);
+    hipLaunchKernelGGL(k3_count, grid, dim3(256), nb * sizeof(int), s, ids, C, G, k, nb, sb.wcnt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (entries > 0) {
-        hipLaunchKernelGGL(k3_scatter, dim3(grid), dim3(256), 0, s, ids, C, G, k, nb, sb.offs,
-                           sb.cursor, sb.list);
-        e = hipGetLastError();
-    }
-    return e;
+    hipLaunchKernelGGL(k3_colscan, dim3((unsigned)((nlists + 255) / 256)), dim3(256), 0, s,
+                       sb.wcnt, G, nb, nW, sb.counts);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k3_scan, dim3(1), dim3(1024), 0, s, sb.counts, nlists, sb.offs, sb.toff,
+                       sb.total);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k3_scatter, grid, dim3(256), 2 * nb * sizeof(int), s, ids, C, G, k, nb,
+                       sb.offs, sb.wcnt, sb.list);
+    return hipGetLastError();
 }
 
 }  // namespace msa

@@ -8,7 +8,8 @@
 // one 64-bit key (order-preserving float bits in the high word, inverted id in
 // the low word), so "larger score first, smaller id on ties" is plain unsigned
 // order and every key is distinct.
-//   1. each lane streams its strided share of the row and keeps its best key;
+//   1. each lane streams its strided share of the row and keeps its best key (the
+//      first 1024 scores of a row stay in registers for step 3);
 //   2. a bitonic sort of the 64 lane-best keys across the wave gives tau, the
 //      (k-1)-th largest lane best; every one of the true top k-1 keys is >= tau;
 //   3. a second pass compacts the keys >= tau into a per-wave LDS list (in the
@@ -95,9 +96,20 @@ __global__ __launch_bounds__(256) void k2_select(const float *__restrict__ S, in
     }
     const float *srow = S + row * nbp;
 
-    // 1. lane-best keys
+    // 1. lane-best keys; the first 1024 scores of the row stay in registers
+    constexpr int kCache = 16;
+    float cache[kCache];
     uint64_t best = 0;
-    for (int idx = lane; idx < n; idx += kWave) {
+#pragma unroll
+    for (int t = 0; t < kCache; ++t) {
+        const int idx = lane + kWave * t;
+        cache[t] = idx < n ? srow[idx] : 0.0f;
+        if (idx < n) {
+            const uint64_t key = make_key(cache[t], idx);
+            best = key > best ? key : best;
+        }
+    }
+    for (int idx = kCache * kWave + lane; idx < n; idx += kWave) {
         const uint64_t key = make_key(srow[idx], idx);
         best = key > best ? key : best;
     }
@@ -109,14 +121,9 @@ __global__ __launch_bounds__(256) void k2_select(const float *__restrict__ S, in
 
     // 3. compact keys >= tau
     int cnt = 0;
-    for (int base = 0; base < n; base += kWave) {
-        const int idx = base + lane;
-        uint64_t key = 0;
-        bool f = false;
-        if (idx < n) {
-            key = make_key(srow[idx], idx);
-            f = key >= tau;
-        }
+    auto consider = [&](bool inrow, float v, int idx) {
+        const uint64_t key = inrow ? make_key(v, idx) : 0;
+        const bool f = inrow && key >= tau;
         const uint64_t m = __ballot(f);
         if (f) {
             const int p = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
@@ -124,6 +131,16 @@ __global__ __launch_bounds__(256) void k2_select(const float *__restrict__ S, in
             if (p < 64) cand[wave][p] = key;
         }
         cnt += __popcll(m);
+    };
+#pragma unroll
+    for (int t = 0; t < kCache; ++t) {
+        if (t * kWave >= n) break;
+        const int idx = lane + kWave * t;
+        consider(idx < n, cache[t], idx);
+    }
+    for (int base = kCache * kWave; base < n; base += kWave) {
+        const int idx = base + lane;
+        consider(idx < n, idx < n ? srow[idx] : 0.0f, idx);
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");

@@ -25,8 +25,12 @@
  *     size, k slots per (query, group) INCLUDING the query's own block.
  *   - Token i sees keys t <= i.  Block of token i: b(i) = i / B.
  *   - scale: softmax scale applied to q.k; pass a value <= 0 for 1/sqrt(d).
- *   - ws / ws_bytes: caller-owned device workspace of at least the size returned
- *     by the matching *_workspace_size() call; 256-byte alignment required.
+ *   - ws / ws_bytes: caller-owned device workspace, 256-byte aligned.  The size
+ *     returned by the matching *_workspace_size() call is the preferred one (largest
+ *     query chunk).  msa_select_blocks, msa_sparse_attn and msa_prefill also accept
+ *     less: they then process the queries in smaller chunks (multiples of 128
+ *     queries) and fail with MSA_ERR_WORKSPACE_TOO_SMALL only when not even one
+ *     128-query chunk fits.  msa_decode needs its full workspace size.
  *     The library never allocates device memory and never synchronises; all work is
  *     enqueued on `stream` (a hipStream_t passed as void*, NULL = default stream).
  *   - Return value: an msa_status.  Every argument is validated BEFORE anything is
@@ -35,7 +39,9 @@
  *   - The compute entry points are stateless and thread-safe; calls on one stream
  *     are ordered.  (The optional timing facility at the end is process-wide.)
  *   - Supported on the GPU: B = 128; d in {64, 128}; dI in {32, 64, 128};
- *     H/G in {1, 2, 4, 8, 16, 32}; G * dI <= 512; 1 <= k <= 32; any L >= 0.
+ *     H/G in {1, 2, 4, 8, 16, 32}; G * dI <= 512; 1 <= k <= 32;
+ *     0 <= L <= 1048576 for msa_prefill / msa_sparse_attn (any L for
+ *     msa_select_blocks; any Lmax for msa_decode).
  *     Anything else returns MSA_ERR_UNSUPPORTED.
  *   - Rows are independent: results do not depend on how the library splits the
  *     queries into chunks, and repeated calls give bitwise-identical outputs.

@@ -240,3 +240,32 @@ def test_decode_full_size_subset():
     shape = wl.shape
     seq_len = np.full(shape.N, shape.Lc)
     _decode_check(shape, seq_len, seed=0, seqs=np.array([0, 1, 17, 31, 48, 63]), device=DEV)
+
+
+def test_chunked_workspace_invariance():
+    """A smaller workspace makes the library split the queries into several chunks;
+    every row's result must be bitwise the same as with one chunk."""
+    msa = _msa()
+    shape = synth.PrefillShape(L=5000, H=16, G=4, d=128, dI=128, B=128, k=8)
+    x = synth.prefill_inputs(shape, seed=8)
+    d = {n: t.to(DEV) for n, t in x.items() if isinstance(t, torch.Tensor)}
+    _say("chunked workspace invariance")
+    o1, i1 = msa.prefill(d["q"], d["k"], d["v"], d["iq"], d["ik"], kslots=shape.k, return_ids=True)
+    pref = msa.workspace_size("prefill", L=shape.L, H=shape.H, G=shape.G, d=shape.d, dI=shape.dI,
+                              k=shape.k)
+    for frac in (3, 9):
+        ws = msa._workspace(pref // frac, DEV)
+        o2, i2 = msa.prefill(d["q"], d["k"], d["v"], d["iq"], d["ik"], kslots=shape.k,
+                             return_ids=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(i1, i2)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    o3 = msa.sparse_attn(d["q"], d["k"], d["v"], i1,
+                         workspace=msa._workspace(msa.workspace_size(
+                             "sparse_attn", L=shape.L, H=shape.H, G=shape.G, d=shape.d,
+                             k=shape.k) // 4, DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+    with pytest.raises(msa.MSAError):
+        msa.prefill(d["q"], d["k"], d["v"], d["iq"], d["ik"], kslots=shape.k,
+                    workspace=msa._workspace(4096, DEV))
