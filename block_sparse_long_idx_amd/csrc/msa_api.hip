@@ -58,6 +58,7 @@ AttnWs carve_attn(Carver &c, int64_t C, int H, int G, int d, int k, int nb) {
     w.sb.toff = c.take<int>(lists + 1);
     w.sb.wcnt = c.take<int>((int64_t)k3_num_groups(C) * lists);
     w.sb.total = c.take<int>(1);
+    w.sb.items = c.take<int>(k4_max_items(C, G, k, nb));
     w.sb.list = c.take<uint32_t>(C * G * k);
     w.po = c.take<uint16_t>(C * H * k * d);
     w.plse = c.take<float>(C * H * k);

@@ -120,7 +120,7 @@ __device__ __forceinline__ void attend_pass(const char *lds_k, const char *lds_v
         o[md] = f32x16{};
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt) {
-            const bf16x8 a = as_bf16x8(load16(lds_vt + swz<16>(md * 32 + l32, 2 * kt + hf)));
+            const bf16x8 a = as_bf16x8(load16(lds_vt + swz_vt(md * 32 + l32, 2 * kt + hf)));
             o[md] = mfma32(a, pb[kt], o[md]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -156,9 +156,9 @@ template <int D, int R>
 __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kx,
     const uint16_t *__restrict__ vx, const int *__restrict__ offs, const int *__restrict__ toff,
-    const int *__restrict__ total, const uint32_t *__restrict__ list, int nlists, int nb,
-    int64_t L, int64_t q0, int H, int G, int kslots, float scale_log2, uint16_t *__restrict__ po,
-    float *__restrict__ plse) {
+    const int *__restrict__ total, const int *__restrict__ items,
+    const uint32_t *__restrict__ list, int nb, int64_t L, int64_t q0, int H, int G, int kslots,
+    float scale_log2, uint16_t *__restrict__ po, float *__restrict__ plse) {
     __shared__ __attribute__((aligned(16))) char lds_k[kBlock * D * 2];
     __shared__ __attribute__((aligned(16))) char lds_vt[D * kBlock * 2];
     static_assert(kK4Queries <= 256, "one entry per thread is staged");
@@ -166,13 +166,7 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     const int per = gridDim.x / 8;
     const int x = (blockIdx.x % 8) * per + blockIdx.x / 8;   // XCD-contiguous items
     if (x >= *total) return;
-    int lo = 0, hi = nlists;                                 // toff[lo] <= x < toff[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (toff[mid] <= x) lo = mid;
-        else hi = mid;
-    }
-    const int li = lo;
+    const int li = items[x];                                 // list of this tile
     const int g = li / nb, j = li % nb;
     const int t = x - toff[li];
     const int begin = offs[li] + t * kK4Queries;
@@ -244,7 +238,7 @@ static hipError_t k4_dispatch(const uint16_t *q, const uint16_t *kx, const uint1
     const int64_t grid = round_up(k4_max_items(C, G, k, nb), 8);
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((k4_kv_outer<D, R>), dim3((unsigned)grid), dim3(256), 0, s, q, kx, vx,
-                       sb.offs, sb.toff, sb.total, sb.list, G * nb, nb, L, q0, H, G, k,
+                       sb.offs, sb.toff, sb.total, sb.items, sb.list, nb, L, q0, H, G, k,
                        scale_log2, po, plse);
     return hipGetLastError();
 }

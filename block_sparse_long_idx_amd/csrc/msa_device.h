@@ -102,8 +102,42 @@ __device__ __forceinline__ void stage_rows(char *lds, const char *src, int64_t s
     }
 }
 
+typedef void __attribute__((address_space(3))) *lds_ptr_t;
+
+// Direct global -> LDS copy (global_load_lds_dwordx4, no registers) of a full
+// 128-row tile with CPR 16-byte chunks per row into the swz<CPR> layout.  One
+// instruction of a wave fills 1 KB of LDS, lane l the bytes [16 l, 16 l + 16), so
+// each lane fetches the global chunk that the swizzle places there.  NTHR threads
+// call it; the data is visible after an s_waitcnt on vmcnt and a barrier.
+template <int CPR, int NTHR>
+__device__ __forceinline__ void stage_rows_direct(char *lds, const char *src, int64_t stride_bytes,
+                                                  int tid) {
+    constexpr int kSegs = kBlock * CPR * 16 / 1024;
+    constexpr int kWaves = NTHR / kWave;
+    static_assert(kSegs % kWaves == 0, "tile must split evenly over the waves");
+    constexpr int kMask = (CPR < 16 ? CPR : 16) - 1;
+    const int lane = tid % kWave, wave = tid / kWave;
+#pragma unroll
+    for (int it = 0; it < kSegs / kWaves; ++it) {
+        const int seg = it * kWaves + wave;
+        const int pos = seg * 1024 + lane * 16;
+        const int row = pos / (CPR * 16);
+        const int chunk = ((pos / 16) % CPR) ^ (row & kMask);
+        __builtin_amdgcn_global_load_lds(src + row * stride_bytes + chunk * 16,
+                                         (lds_ptr_t)(lds + seg * 1024), 16, 0, 0);
+    }
+}
+
+// V^T tile: D rows (one per d) of 128 keys = 16 chunks of 8 keys.  The chunk is
+// XOR-swizzled with bits 0-3 and 4-6 of d: operand reads (32 consecutive d, one
+// chunk) and the transposing stores (d = 8*dc + e over 16 dc, one e) both spread
+// over distinct banks.
+__device__ __forceinline__ int swz_vt(int d, int chunk) {
+    return d * 256 + ((chunk ^ (d & 15) ^ ((d >> 4) & 7)) << 4);
+}
+
 // Stage V (128 keys x D values, rows at `src + key*stride_bytes`) TRANSPOSED into
-// LDS as D rows of 128 keys (16 chunks of 8 keys, swizzled).  Keys >= nrows are 0.
+// LDS as D rows of 128 keys (swz_vt layout).  Keys >= nrows are 0.
 template <int D>
 __device__ __forceinline__ void stage_v_transposed(char *lds, const char *src,
                                                    int64_t stride_bytes, int nrows, int tid) {
@@ -128,7 +162,7 @@ __device__ __forceinline__ void stage_v_transposed(char *lds, const char *src,
             uint32_t v2 = (r[2][w] >> sh) & 0xFFFFu, v3 = (r[3][w] >> sh) & 0xFFFFu;
             const int d = 8 * dc + e;
             const int key0 = 4 * kq;
-            char *p = lds + swz<16>(d, key0 >> 3) + ((key0 >> 2) & 1) * 8;
+            char *p = lds + swz_vt(d, key0 >> 3) + ((key0 >> 2) & 1) * 8;
             store8(p, u32x2{v0 | (v1 << 16), v2 | (v3 << 16)});
         }
     }

@@ -4,8 +4,8 @@
 // over the causal window, max-pooling into B = 128-token blocks).
 //
 // K1 (prefill) is a short-K GEMM with a max-pool epilogue, run on bf16 MFMA with
-// fp32 accumulation.  One work-group (up to 8 waves) owns one query block (128
-// queries x G groups = 128*G stacked index rows, contiguous in idx_q[L,G,dI]) and
+// fp32 accumulation.  One work-group (4 waves) owns part of one query block (64
+// or 128 queries x G groups of stacked index rows, contiguous in idx_q[L,G,dI]) and
 // a range of up to 32 key blocks strictly before the query block; the query's
 // own block is never scored because it is always selected.  Index rows stay in
 // registers for the whole range; each 128-key block of idx_k is staged once in
@@ -26,14 +26,17 @@ namespace msa {
 constexpr int kK1Flush = 8;   // key blocks buffered in LDS between flushes
 
 // Work items are ordered key-chunk-major: for key chunk c, query blocks
-// qb in [max(qb0, 32c+1), qb1) each score key blocks [32c, min(32c+32, qb)).
-__device__ __forceinline__ bool k1_item(int64_t item, int qb0, int qb1, int &qb, int &c) {
+// qb in [max(qb0, 32c+1), qb1) -- each split into P parts of 128/P queries --
+// score key blocks [32c, min(32c+32, qb)).
+__device__ __forceinline__ bool k1_item(int64_t item, int qb0, int qb1, int P, int &qb, int &part,
+                                        int &c) {
     for (c = 0;; ++c) {
         const int lo = max(qb0, c * kK1KeyChunk + 1);
         if (lo >= qb1) return false;
-        const int64_t n = qb1 - lo;
+        const int64_t n = (int64_t)(qb1 - lo) * P;
         if (item < n) {
-            qb = lo + (int)item;
+            qb = lo + (int)(item / P);
+            part = (int)(item % P);
             return true;
         }
         item -= n;
@@ -50,23 +53,29 @@ int64_t k1_num_items(int qb0, int qb1) {
     return total;
 }
 
-// Columns per wave: 32 * NT.  G = 1: 4 waves x 32;  G = 2: 8 x 32;  G = 4: 8 x 64;
-// G = 8: 16 x 64.
+// Four waves per work-group, 32*NT index rows per wave; a work-group covers
+// QT = 128*NT/G queries (all G groups) of one query block, P = 128/QT parts.
+//   G = 1: NT 1, 128 queries;  G = 2: NT 1, 64;  G = 4: NT 2, 64;  G = 8: NT 2, 32.
+// Two work-groups fit on a CU (LDS 64 KB key tiles + row maxima each), so one
+// work-group's barrier is covered by the other's MFMAs.
 template <int G> struct K1Tiling {
     static constexpr int NT = G >= 4 ? 2 : 1;
-    static constexpr int WAVES = kBlock * G / (32 * NT);
-    static constexpr int THREADS = WAVES * kWave;
+    static constexpr int ROWS = 4 * 32 * NT;
+    static constexpr int QT = ROWS / G;
+    static constexpr int P = kBlock / QT;
+    static constexpr int THREADS = 256;
 };
 
 template <int G, int DI>
-__global__ __launch_bounds__(K1Tiling<G>::THREADS, 1) void k1_index_pool(
+__global__ __launch_bounds__(256, 2) void k1_index_pool(
     const uint16_t *__restrict__ iq, const uint16_t *__restrict__ ik, float *__restrict__ S,
     int64_t q0, int64_t qend, int nbp, int qb0, int qb1, int64_t n_items) {
     constexpr int NT = K1Tiling<G>::NT;
     constexpr int NTHR = K1Tiling<G>::THREADS;
+    constexpr int P = K1Tiling<G>::P;
     constexpr int CPR = DI / 8;            // 16-byte chunks per index row
     constexpr int KS = DI / 16;            // MFMA K-steps
-    constexpr int NCOL = kBlock * G;       // stacked index rows of the work-group
+    constexpr int NCOL = K1Tiling<G>::ROWS;   // stacked index rows of the work-group
     constexpr int TILE = kBlock * DI * 2;  // bytes of one staged key block
     __shared__ __attribute__((aligned(16))) char lds_k[2][TILE];
     __shared__ float lds_s[kK1Flush][NCOL];
@@ -74,8 +83,8 @@ __global__ __launch_bounds__(K1Tiling<G>::THREADS, 1) void k1_index_pool(
     // XCD-aware order: consecutive logical items (same key chunk) on one XCD.
     const int64_t per = gridDim.x / 8;
     const int64_t item = (blockIdx.x % 8) * per + blockIdx.x / 8;
-    int qb, c;
-    if (item >= n_items || !k1_item(item, qb0, qb1, qb, c)) return;
+    int qb, part, c;
+    if (item >= n_items * P || !k1_item(item, qb0, qb1, P, qb, part, c)) return;
     const int j0 = c * kK1KeyChunk;
     const int j1 = min(j0 + kK1KeyChunk, qb);
 
@@ -84,7 +93,7 @@ __global__ __launch_bounds__(K1Tiling<G>::THREADS, 1) void k1_index_pool(
 
     // B operand: index rows of this wave, kept in registers.
     bf16x8 bq[NT][KS];
-    const int64_t row0 = (int64_t)qb * kBlock * G;   // flattened [L*G] row of column 0
+    const int64_t row0 = ((int64_t)qb * kBlock + part * K1Tiling<G>::QT) * G;   // [L*G] row of column 0
     const int64_t row_end = qend * G;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -97,54 +106,53 @@ __global__ __launch_bounds__(K1Tiling<G>::THREADS, 1) void k1_index_pool(
 
     const char *ikb = reinterpret_cast<const char *>(ik);
     const int64_t blk_bytes = (int64_t)kBlock * DI * 2;
-    constexpr int kRowsPerIter = NTHR / CPR;   // may exceed 128 rows: extra threads idle
-    constexpr int kIters = (kBlock + kRowsPerIter - 1) / kRowsPerIter;
-    {
-        const char *src = ikb + j0 * blk_bytes;
-#pragma unroll
-        for (int it = 0; it < kIters; ++it) {
-            const int row = tid / CPR + it * kRowsPerIter;
-            if (row < kBlock)
-                store16(lds_k[0] + swz<CPR>(row, tid % CPR),
-                        load16(src + row * (DI * 2) + (tid % CPR) * 16));
-        }
-    }
+    // key blocks j < qb are always full, so the tiles need no zero fill
+    stage_rows_direct<CPR, NTHR>(lds_k[0], ikb + j0 * blk_bytes, DI * 2, tid);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int j = j0; j < j1; ++j) {
         const int buf = (j - j0) & 1;
-        // prefetch the next key block into registers
-        u32x4 pre[kIters];
+        // the next key block goes straight into the other LDS buffer (last read in
+        // the previous iteration, before its closing barrier)
         const bool more = j + 1 < j1;
-        if (more) {
-            const char *src = ikb + (j + 1) * blk_bytes;
-#pragma unroll
-            for (int it = 0; it < kIters; ++it) {
-                const int row = tid / CPR + it * kRowsPerIter;
-                if (row < kBlock) pre[it] = load16(src + row * (DI * 2) + (tid % CPR) * 16);
-            }
-        }
+        if (more) stage_rows_direct<CPR, NTHR>(lds_k[buf ^ 1], ikb + (j + 1) * blk_bytes, DI * 2, tid);
         float mx[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) mx[nt] = -INFINITY;
+        // A operands (key rows) of M-tile mt+1 are read from LDS while the MFMAs of
+        // M-tile mt run, so LDS latency is not exposed between MFMAs
+        const char *kt = lds_k[buf];
+        bf16x8 a_cur[KS], a_nxt[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a_cur[ks] = as_bf16x8(load16(kt + swz<CPR>(l32, 2 * ks + hf)));
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
+            if (mt < 3) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    a_nxt[ks] = as_bf16x8(load16(kt + swz<CPR>((mt + 1) * 32 + l32, 2 * ks + hf)));
+            }
+            // one M-tile of operand reads in flight: nothing crosses this point
+            __builtin_amdgcn_sched_barrier(0);
             f32x16 acc[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = as_bf16x8(load16(lds_k[buf] + swz<CPR>(mt * 32 + l32, 2 * ks + hf)));
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma32(a, bq[nt][ks], acc[nt]);
+                for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma32(a_cur[ks], bq[nt][ks], acc[nt]);
             }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 float m = acc[nt][0];
 #pragma unroll
-                for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[nt][r]);
-                mx[nt] = fmaxf(mx[nt], m);
+                for (int r = 1; r < 16; ++r) m = __builtin_fmaxf(m, acc[nt][r]);
+                mx[nt] = __builtin_fmaxf(mx[nt], m);
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) a_cur[ks] = a_nxt[ks];
         }
         const int slot = (j - j0) % kK1Flush;
 #pragma unroll
@@ -152,13 +160,7 @@ __global__ __launch_bounds__(K1Tiling<G>::THREADS, 1) void k1_index_pool(
             const float m = fmaxf(mx[nt], xor_shfl(mx[nt], 32));
             if (hf == 0) lds_s[slot][wave * 32 * NT + nt * 32 + l32] = m;
         }
-        if (more) {
-#pragma unroll
-            for (int it = 0; it < kIters; ++it) {
-                const int row = tid / CPR + it * kRowsPerIter;
-                if (row < kBlock) store16(lds_k[buf ^ 1] + swz<CPR>(row, tid % CPR), pre[it]);
-            }
-        }
+        __builtin_amdgcn_s_waitcnt(0);   // the next tile has landed in LDS
         __syncthreads();
         if (slot == kK1Flush - 1 || j == j1 - 1) {
             const int nj = slot + 1;
@@ -188,7 +190,7 @@ static hipError_t k1_dispatch(const uint16_t *iq, const uint16_t *ik, float *S, 
     const int qb1 = (int)((qend + kBlock - 1) / kBlock);
     const int64_t n = k1_num_items(qb0, qb1);
     if (n == 0) return hipSuccess;
-    const int64_t grid = round_up(n, 8);
+    const int64_t grid = round_up(n * K1Tiling<G>::P, 8);
     hipLaunchKernelGGL((k1_index_pool<G, DI>), dim3((unsigned)grid), dim3(K1Tiling<G>::THREADS), 0,
                        s, iq, ik, S, q0, qend, nbp, qb0, qb1, n);
     return hipGetLastError();

@@ -43,6 +43,7 @@ struct SchedBuffers {
     int *toff;       // [nlists + 1] prefix sum of ceil(count / kK4Queries)
     int *wcnt;       // [G * k3_num_groups(C) * nb] per-work-group counts / prefixes
     int *total;      // [1] number of K4 work items
+    int *items;      // [k4_max_items] list index of every K4 work item
     uint32_t *list;  // [C * G * k] entries (i - q0) << 5 | slot
 };
 hipError_t launch_k3_schedule(const int32_t *ids, int64_t C, int G, int k, int nb,

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void k3_scatter(const int32_t *__restrict__ id
 // One work-group of 1024 threads scans all lists.
 __global__ __launch_bounds__(1024) void k3_scan(const int *__restrict__ counts, int nlists,
                                                 int *__restrict__ offs, int *__restrict__ toff,
-                                                int *__restrict__ total) {
+                                                int *__restrict__ total, int *__restrict__ items) {
     __shared__ int sc[1024], st[1024];
     const int tid = threadIdx.x;
     const int per = (nlists + 1023) / 1024;
@@ -129,10 +129,12 @@ __global__ __launch_bounds__(1024) void k3_scan(const int *__restrict__ counts, 
     int ec = sc[tid] - c_sum, et = st[tid] - t_sum;
     for (int l = beg; l < end; ++l) {
         const int c = counts[l];
+        const int nt = (c + kK4Queries - 1) / kK4Queries;
         offs[l] = ec;
         toff[l] = et;
+        for (int t = 0; t < nt; ++t) items[et + t] = l;   // tile -> list table for K4
         ec += c;
-        et += (c + kK4Queries - 1) / kK4Queries;
+        et += nt;
     }
     if (tid == 1023) {
         offs[nlists] = sc[1023];
@@ -161,7 +163,7 @@ hipError_t launch_k3_schedule(const int32_t *ids, int64_t C, int G, int k, int n
                        sb.wcnt, G, nb, nW, sb.counts);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k3_scan, dim3(1), dim3(1024), 0, s, sb.counts, nlists, sb.offs, sb.toff,
-                       sb.total);
+                       sb.total, sb.items);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k3_scatter, grid, dim3(256), 2 * nb * sizeof(int), s, ids, C, G, k, nb,
                        sb.offs, sb.wcnt, sb.list);
