@@ -113,10 +113,7 @@ __global__ __launch_bounds__(256, 2) void k1_index_pool(
 
     for (int j = j0; j < j1; ++j) {
         const int buf = (j - j0) & 1;
-        // the next key block goes straight into the other LDS buffer (last read in
-        // the previous iteration, before its closing barrier)
         const bool more = j + 1 < j1;
-        if (more) stage_rows_direct<CPR, NTHR>(lds_k[buf ^ 1], ikb + (j + 1) * blk_bytes, DI * 2, tid);
         float mx[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) mx[nt] = -INFINITY;
@@ -133,6 +130,12 @@ __global__ __launch_bounds__(256, 2) void k1_index_pool(
                 for (int ks = 0; ks < KS; ++ks)
                     a_nxt[ks] = as_bf16x8(load16(kt + swz<CPR>((mt + 1) * 32 + l32, 2 * ks + hf)));
             }
+            // The next key block goes straight into the other LDS buffer (last read in
+            // the previous iteration, before its closing barrier).  It is issued after
+            // this block's last operand reads: the compiler cannot tell the two buffers
+            // apart and waits for these loads before any later LDS read.
+            if (mt == 2 && more)
+                stage_rows_direct<CPR, NTHR>(lds_k[buf ^ 1], ikb + (j + 1) * blk_bytes, DI * 2, tid);
             // one M-tile of operand reads in flight: nothing crosses this point
             __builtin_amdgcn_sched_barrier(0);
             f32x16 acc[NT];

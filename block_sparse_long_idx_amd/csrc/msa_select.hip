@@ -8,8 +8,9 @@
 // one 64-bit key (order-preserving float bits in the high word, inverted id in
 // the low word), so "larger score first, smaller id on ties" is plain unsigned
 // order and every key is distinct.
-//   1. each lane streams its strided share of the row and keeps its best key (the
-//      first 1024 scores of a row stay in registers for step 3);
+//   1. each lane streams its share of the row (16-byte loads) and keeps its best
+//      (score, index) with float compares (the first 1024 scores of a row stay in
+//      registers for step 3);
 //   2. a bitonic sort of the 64 lane-best keys across the wave gives tau, the
 //      (k-1)-th largest lane best; every one of the true top k-1 keys is >= tau;
 //   3. a second pass compacts the keys >= tau into a per-wave LDS list (in the
@@ -95,52 +96,71 @@ __global__ __launch_bounds__(256) void k2_select(const float *__restrict__ S, in
         return;
     }
     const float *srow = S + row * nbp;
-
-    // 1. lane-best keys; the first 1024 scores of the row stay in registers
-    constexpr int kCache = 16;
-    float cache[kCache];
-    uint64_t best = 0;
+    // Scores are read 4 per lane per step (16 bytes; rows are 32-byte aligned):
+    // lane l owns elements 4(l + 64 v) + e, visited in increasing index order.
+    // The first 1024 scores of a row stay in registers for step 3.
+    constexpr int kVec = 4;                       // float4 loads per lane kept in registers
+    f32x4 cache[kVec];
+    // 1. lane-best (score, smallest index on equal scores) with float compares
+    float bv = -INFINITY;
+    int bi_idx = 0x7FFFFFFF;
+    auto scan4 = [&](const f32x4 &x, int i0) {
 #pragma unroll
-    for (int t = 0; t < kCache; ++t) {
-        const int idx = lane + kWave * t;
-        cache[t] = idx < n ? srow[idx] : 0.0f;
-        if (idx < n) {
-            const uint64_t key = make_key(cache[t], idx);
-            best = key > best ? key : best;
+        for (int e = 0; e < 4; ++e) {
+            const int idx = i0 + e;
+            if (idx < n && (x[e] > bv || bi_idx == 0x7FFFFFFF)) {
+                bv = x[e];
+                bi_idx = idx;
+            }
         }
+    };
+#pragma unroll
+    for (int t = 0; t < kVec; ++t) {
+        const int i0 = 4 * (lane + kWave * t);
+        cache[t] = i0 < n ? *reinterpret_cast<const f32x4 *>(srow + i0) : f32x4{0, 0, 0, 0};
+        scan4(cache[t], i0);
     }
-    for (int idx = kCache * kWave + lane; idx < n; idx += kWave) {
-        const uint64_t key = make_key(srow[idx], idx);
-        best = key > best ? key : best;
-    }
+    for (int i0 = 4 * (lane + kWave * kVec); i0 < n; i0 += 4 * kWave)
+        scan4(*reinterpret_cast<const f32x4 *>(srow + i0), i0);
+    const uint64_t best = bi_idx == 0x7FFFFFFF ? 0 : make_key(bv, bi_idx);
     // 2. tau = (k-1)-th largest lane best
     const uint64_t sorted = wave_bitonic<true>(best, lane);
     const uint32_t tlo = __shfl((uint32_t)sorted, kk - 1, kWave);
     const uint32_t thi = __shfl((uint32_t)(sorted >> 32), kk - 1, kWave);
     const uint64_t tau = ((uint64_t)thi << 32) | tlo;
+    const int tau_idx = key_id(tau);
+    // score of tau: invert the order-preserving map of float_order_key
+    const uint32_t tau_key = (uint32_t)(tau >> 32);
+    const float tau_v = __uint_as_float((tau_key & 0x80000000u) ? (tau_key & 0x7FFFFFFFu) : ~tau_key);
+    // With 4 consecutive scores per lane, a short row can have fewer than k-1 lanes
+    // holding scores: tau is then the empty key and every score is a candidate.
+    const bool take_all = tau == 0;
 
-    // 3. compact keys >= tau
+    // 3. compact the elements ranked at or above tau (score > tau, or equal score
+    //    and index <= tau's) into the per-wave candidate list
     int cnt = 0;
-    auto consider = [&](bool inrow, float v, int idx) {
-        const uint64_t key = inrow ? make_key(v, idx) : 0;
-        const bool f = inrow && key >= tau;
-        const uint64_t m = __ballot(f);
-        if (f) {
-            const int p = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-            if (p < 64) cand[wave][p] = key;
+    auto consider4 = [&](const f32x4 &x, int i0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int idx = i0 + e;
+            const bool f = idx < n && (take_all || x[e] > tau_v || (x[e] == tau_v && idx <= tau_idx));
+            const uint64_t m = __ballot(f);
+            if (f) {
+                const int p = cnt + (int)__builtin_amdgcn_mbcnt_hi(
+                                        (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+                if (p < 64) cand[wave][p] = make_key(x[e], idx);
+            }
+            cnt += __popcll(m);
         }
-        cnt += __popcll(m);
     };
 #pragma unroll
-    for (int t = 0; t < kCache; ++t) {
-        if (t * kWave >= n) break;
-        const int idx = lane + kWave * t;
-        consider(idx < n, cache[t], idx);
+    for (int t = 0; t < kVec; ++t) {
+        if (4 * kWave * t >= n) break;
+        consider4(cache[t], 4 * (lane + kWave * t));
     }
-    for (int base = kCache * kWave; base < n; base += kWave) {
-        const int idx = base + lane;
-        consider(idx < n, idx < n ? srow[idx] : 0.0f, idx);
+    for (int base = 4 * kWave * kVec; base < n; base += 4 * kWave) {
+        const int i0 = base + 4 * lane;
+        consider4(i0 < n ? *reinterpret_cast<const f32x4 *>(srow + i0) : f32x4{0, 0, 0, 0}, i0);
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");

@@ -269,3 +269,72 @@ def test_chunked_workspace_invariance():
     with pytest.raises(msa.MSAError):
         msa.prefill(d["q"], d["k"], d["v"], d["iq"], d["ik"], kslots=shape.k,
                     workspace=msa._workspace(4096, DEV))
+
+
+def _constructed_select(L, w, k, rows):
+    """idx_k rows w[t] * e_0 and idx_q = e_0 (G = 1, dI = 32): every token score is
+    w[t] exactly, so block scores and ties are fixed by construction."""
+    msa = _msa()
+    dI = 32
+    ik = torch.zeros((L, dI), dtype=torch.bfloat16)
+    ik[:, 0] = torch.as_tensor(w, dtype=torch.float32).to(torch.bfloat16)
+    iq = torch.zeros((L, 1, dI), dtype=torch.bfloat16)
+    iq[:, 0, 0] = 1.0
+    ids = msa.select_blocks(iq.to(DEV), ik.to(DEV), k=k)
+    torch.cuda.synchronize()
+    S = oracle.block_scores(iq, ik, 128, rows=rows)
+    oids, gap = oracle.select(S, rows, 128, k)
+    got = ids.cpu().numpy()[rows]
+    _parity.check_selection_valid(got, rows, k)
+    return got, oids
+
+
+def test_select_ties_and_candidate_overflow_1m():
+    """L = 2^20 (8191 competitors per row at the end): (a) all scores equal, so the
+    smallest ids win; (b) one lane of the selector's row layout holds 128 equal
+    maxima, more than its 64-entry candidate list, forcing the exact fallback."""
+    L, k = 1 << 20, 16
+    rows = np.array([L - 1, L - 128, L // 2, 200000, 4096, 2047])
+    blk = np.arange(L) // 128
+    _say("select ties, L=2^20")
+    got, want = _constructed_select(L, np.ones(L), k, rows)
+    assert (got == want).all()
+    for r, i in enumerate(rows):
+        bi = i // 128
+        assert got[r, 0].tolist() == list(range(min(k - 1, bi))) + [bi] + [-1] * max(0, k - bi - 1)
+    _say("select candidate overflow, L=2^20")
+    w = np.where(blk % 256 < 4, 1000.0, -(blk % 200).astype(np.float64))
+    got, want = _constructed_select(L, w, k, rows)
+    assert (got == want).all()
+
+
+def test_prefill_1m_hot_sampled():
+    """The 1M-token skewed workload in the launch configuration the benchmark times
+    (query chunks of 131072), checked on sampled rows."""
+    wl = synth.WORKLOADS["prefill_L1048576_hot"]
+    s = wl.shape
+    _say("prefill 1M hot: generate on GPU")
+    x = synth.prefill_inputs(s, seed=0, plant=wl.plant, n_plant=wl.n_plant, c=wl.c,
+                             hot_blocks=wl.hot_blocks, device=DEV)
+    msa = _msa()
+    out, ids = msa.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], kslots=s.k,
+                           return_ids=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 256, 37), np.arange(s.L - 128, s.L, 41),
+                                     np.random.default_rng(3).choice(s.L, 40, replace=False)]))
+    _say(f"  oracle on {len(rows)} rows")
+    # host copies: only the sampled q rows are materialised
+    host = {n: x[n].cpu() for n in ("k", "v", "iq", "ik")}
+    hq = torch.empty((s.L, s.H, s.d), dtype=torch.bfloat16)
+    hq[torch.as_tensor(rows)] = x["q"][torch.as_tensor(rows, device=DEV)].cpu()
+    host["q"] = hq
+    st = _parity.prefill_rows_vs_oracle(host, rows, ids[rows].cpu().numpy(),
+                                        out[rows].float().cpu().numpy(), 128, s.k,
+                                        1.0 / math.sqrt(s.d))
+    _say(f"  -> {st}")
+    assert st["id_mismatches"] == 0
+    assert st["max_abs"] < _parity.MAX_ABS and st["mean_abs"] < _parity.MEAN_ABS
+    idn = ids.cpu().numpy()
+    hot = (idn[128 * 5:, :, :4] == np.arange(4)).all(-1).mean()
+    _say(f"  hot blocks 0-3 selected by {hot:.5f} of (query, group) rows")
+    assert hot > 0.995
