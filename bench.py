@@ -157,6 +157,42 @@ def cpu_baseline_decode(x, shape, target_s=15.0):
                       f"{shape.N}"}
 
 
+def dense_gqa_baseline(x, shape, msa_ms, reps=3):
+    """Dense causal GQA attention on the same q/k/v with PyTorch's fused SDPA
+    backends (flash / memory-efficient; the math backend is never allowed, it would
+    materialise L x L).  A library timing for the sparse-vs-dense comparison."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    r = shape.H // shape.G
+    q = x["q"].transpose(0, 1).unsqueeze(0).contiguous()                  # [1, H, L, d]
+    k = x["k"].transpose(0, 1).repeat_interleave(r, dim=0).unsqueeze(0).contiguous()
+    v = x["v"].transpose(0, 1).repeat_interleave(r, dim=0).unsqueeze(0).contiguous()
+    res = {"backend": None, "ms": None, "tflops": None, "speedup_msa_vs_dense": None}
+    for name, be in (("flash", SDPBackend.FLASH_ATTENTION),
+                     ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            with sdpa_kernel([be]):
+                torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+                e1.record()
+                torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            flops = 4.0 * shape.H * shape.d * shape.L * (shape.L + 1) / 2
+            res.update({"backend": name, "ms": ms, "tflops": flops / (ms / 1e3) / 1e12,
+                        "speedup_msa_vs_dense": ms / msa_ms})
+            break
+        except RuntimeError as e:            # backend not available for this shape
+            res["error_" + name] = str(e).splitlines()[0][:160]
+    del q, k, v
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(gib: float):
     """A plain copy of known size: each launch reads and writes exactly n bytes."""
     import torch
@@ -206,6 +242,9 @@ def main():
     ap.add_argument("--workload", default="prefill_L131072")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dense-baseline", choices=["auto", "on", "off"], default="auto",
+                    help="time dense causal GQA attention (PyTorch SDPA, fused backends only) on "
+                         "the same q/k/v; auto = prefill workloads up to L = 131072")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device-to-device copy of GIB GiB (4 times), the "
@@ -345,6 +384,11 @@ def main():
             result["cpu_baseline"] = cpu_baseline_prefill(x, s, args.cpu_seconds)
         else:
             result["cpu_baseline"] = cpu_baseline_decode(x, s, args.cpu_seconds)
+    want_dense = args.dense_baseline == "on" or (
+        args.dense_baseline == "auto" and wl.kind == "prefill" and s.L <= 131072)
+    if want_dense:
+        print("[bench] dense causal GQA baseline (SDPA)", file=sys.stderr, flush=True)
+        result["dense_baseline"] = dense_gqa_baseline(x, s, ms_per_step)
     result["wall_s_timed_region"] = wall_s
     print(json.dumps(result), flush=True)
 
