@@ -4,7 +4,8 @@
 One step = one full pass of the hot path over one batch of seeded synthetic
 input already resident in HBM: for prefill workloads a whole ``msa_prefill``
 (index score + block max-pool, exp-free top-k, scheduling, KV-outer attention,
-combine); for the decode workload one ``msa_decode`` over all sequences.
+combine); for the decode workloads one ``msa_decode`` (or ``msa_decode_paged``)
+over all sequences.
 
 Prints ONE JSON line with the throughput, the roofline position of the kernel
 that dominates the step (its per-launch duration measured in-process with HIP
@@ -79,13 +80,15 @@ def prefill_work(L, H, G, d, dI, k, B=B_BLOCK, list_counts=None):
     }
 
 
-def decode_work(N, Lc, H, G, d, dI, k, B=B_BLOCK):
+def decode_work(N, Lc, H, G, d, dI, k, B=B_BLOCK, paged=False):
     p = Lc - 1
     nb = p // B                                        # competitor blocks per sequence
     nsel = min(k, nb + 1)
     idx_bytes = N * nb * B * dI * 2.0                  # idx-K cache stream
     kv_bytes = N * G * nsel * 2 * B * d * 2.0          # selected K and V blocks
     small = N * (H * d * 2 * 2 + G * dI * 2) + N * G * (nb * 4 * 2 + k * 4)
+    if paged:                                          # block-table reads
+        small += N * (nb + 1) * 4.0 * 2 + N * G * nsel * 4.0 * 2
     part = N * H * nsel * (2 * d + 4) * 2.0
     return {
         "bytes": {"k1d_index_pool": idx_bytes + N * G * nb * 4.0,
@@ -155,6 +158,33 @@ def cpu_baseline_decode(x, shape, target_s=15.0):
             "kind": "oracle",
             "sample": f"{total} of {shape.N} sequences ({total_s:.1f} s wall), scaled to all "
                       f"{shape.N}"}
+
+
+def cpu_baseline_decode_paged(x, shape, target_s=15.0):
+    """The paged oracle on batches of whole sequences: the pages a batch's tables
+    name are copied to the host; the oracle gathers them and decodes the batch."""
+    import oracle
+    lib = oracle.load()
+    q, iq = x["q"].cpu(), x["iq"].cpu()
+    table = x["block_table"]
+    lens = np.asarray(x["seq_len"], np.int64)
+    total, total_s, n_seq = 0, 0.0, 1
+    while total_s < target_s and total < shape.N:
+        seqs = np.arange(total, min(shape.N, total + n_seq))
+        pages = table[seqs[0]:seqs[-1] + 1].long()
+        kp, vp, ikp = (x[name][pages.reshape(-1)].cpu()
+                       for name in ("k_pages", "v_pages", "ik_pages"))
+        local = np.arange(pages.numel(), dtype=np.int32).reshape(pages.shape)
+        t0 = time.perf_counter()
+        oracle.decode_paged(q[seqs[0]:seqs[-1] + 1], iq[seqs[0]:seqs[-1] + 1], kp, vp, ikp, local,
+                            lens[seqs], B_BLOCK, shape.k, lib=lib)
+        total_s += time.perf_counter() - t0
+        total += len(seqs)
+        n_seq = min(16, n_seq * 2)
+    return {"value": total_s / total * shape.N * 1e6, "unit": "us/step",
+            "cores": oracle.num_threads(lib), "kind": "oracle",
+            "sample": f"{total} of {shape.N} sequences ({total_s:.1f} s wall, page gather "
+                      f"included), scaled to all {shape.N}"}
 
 
 def dense_gqa_baseline(x, shape, msa_ms, reps=3):
@@ -279,7 +309,7 @@ def main():
         def step():
             msa.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], kslots=s.k, out=out,
                         ids_out=ids, workspace=ws, return_ids=True)
-    else:
+    elif wl.kind == "decode":
         x = synth.decode_inputs(s, seed=args.seed, device=dev)
         seq_len = torch.tensor(np.asarray(x["seq_len"], np.int32), device=dev)
         out = torch.empty_like(x["q"])
@@ -290,6 +320,23 @@ def main():
         def step():
             msa.decode(x["q"], x["iq"], x["k_cache"], x["v_cache"], x["ik_cache"], seq_len,
                        kslots=s.k, out=out, ids_out=ids, workspace=ws, return_ids=True)
+    else:   # decode over 128-token pages in a seeded random order
+        x = synth.decode_inputs(s, seed=args.seed, device=dev)
+        x.update(synth.paginate(x, B_BLOCK, seed=args.seed))
+        for name in ("k_cache", "v_cache", "ik_cache"):
+            del x[name]
+        torch.cuda.empty_cache()
+        seq_len = torch.tensor(np.asarray(x["seq_len"], np.int32), device=dev)
+        out = torch.empty_like(x["q"])
+        ids = torch.empty((s.N, s.G, s.k), dtype=torch.int32, device=dev)
+        maxb = x["block_table"].shape[1]
+        ws = msa._workspace(msa.workspace_size("decode_paged", N=s.N, max_blocks=maxb, H=s.H,
+                                               G=s.G, d=s.d, dI=s.dI, k=s.k), dev)
+
+        def step():
+            msa.decode_paged(x["q"], x["iq"], x["k_pages"], x["v_pages"], x["ik_pages"],
+                             x["block_table"], seq_len, kslots=s.k, out=out, ids_out=ids,
+                             workspace=ws, return_ids=True)
 
     torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -340,7 +387,7 @@ def main():
         result["algorithmic_flops_per_step"] = work["f_total"]
         result["dense_gqa_flops_per_step"] = work["dense_gqa_flops"]
     else:
-        work = decode_work(s.N, s.Lc, s.H, s.G, s.d, s.dI, s.k)
+        work = decode_work(s.N, s.Lc, s.H, s.G, s.d, s.dI, s.k, paged=wl.kind == "decode_paged")
         result.update({"value": ms_per_step * 1e3, "unit": "us/step", "higher_is_better": False})
         result["config"] = {"workload": wl.name, "N": s.N, "Lc": s.Lc, "H": s.H, "G": s.G,
                             "d": s.d, "dI": s.dI, "B": s.B, "k": s.k}
@@ -382,8 +429,10 @@ def main():
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         if wl.kind == "prefill":
             result["cpu_baseline"] = cpu_baseline_prefill(x, s, args.cpu_seconds)
-        else:
+        elif wl.kind == "decode":
             result["cpu_baseline"] = cpu_baseline_decode(x, s, args.cpu_seconds)
+        else:
+            result["cpu_baseline"] = cpu_baseline_decode_paged(x, s, args.cpu_seconds)
     want_dense = args.dense_baseline == "on" or (
         args.dense_baseline == "auto" and wl.kind == "prefill" and s.L <= 131072)
     if want_dense:

@@ -15,7 +15,8 @@ import os
 
 import torch
 
-__all__ = ["MSAError", "select_blocks", "sparse_attn", "prefill", "decode", "workspace_size",
+__all__ = ["MSAError", "select_blocks", "sparse_attn", "prefill", "decode", "decode_paged",
+           "workspace_size",
            "library_path", "load_library", "timing_enable", "timing_collect", "timing_disable"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +92,11 @@ def load_library():
     lib.msa_decode.argtypes = [P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, i32, i32, f32, P,
                                P, P, sz, P]
     lib.msa_decode.restype = i32
+    lib.msa_decode_paged_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.msa_decode_paged_workspace_size.restype = sz
+    lib.msa_decode_paged.argtypes = [P, P, P, P, P, i64, P, i32, P, i32, i32, i32, i32, i32, i32,
+                                     i32, f32, P, P, P, sz, P]
+    lib.msa_decode_paged.restype = i32
     lib.msa_timing_enable.argtypes = [i32]
     lib.msa_timing_enable.restype = i32
     lib.msa_timing_collect.argtypes = [ctypes.POINTER(_KernelTime), i32, ctypes.POINTER(i32)]
@@ -154,6 +160,9 @@ def workspace_size(kind: str, **kw) -> int:
     if kind == "decode":
         return lib.msa_decode_workspace_size(kw["N"], kw["Lmax"], kw["H"], kw["G"], kw["d"],
                                              kw["dI"], kw.get("B", 128), kw["k"])
+    if kind == "decode_paged":
+        return lib.msa_decode_paged_workspace_size(kw["N"], kw["max_blocks"], kw["H"], kw["G"],
+                                                   kw["d"], kw["dI"], kw.get("B", 128), kw["k"])
     raise ValueError(kind)
 
 
@@ -252,4 +261,43 @@ def decode(q, idx_q, k_cache, v_cache, idx_k_cache, seq_len, kslots: int = 16, B
                         _ptr(seq_len), N, Lmax, H, G, d, dI, B, kslots, _scale(scale, d), _ptr(out),
                         _ptr(ids_out), _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "msa_decode")
+    return (out, ids_out) if return_ids else out
+
+
+def decode_paged(q, idx_q, k_pages, v_pages, idx_k_pages, block_table, seq_len, kslots: int = 16,
+                 B: int = 128, scale=None, return_ids: bool = False, out=None, ids_out=None,
+                 workspace=None):
+    """MSA decode over 128-token cache pages: out [N, H, d] bf16.
+
+    k_pages/v_pages [P, 128, G, d], idx_k_pages [P, 128, dI]; block_table [N, max_blocks]
+    int32 maps each sequence's logical block to its page.
+    """
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(idx_q, "idx_q", torch.bfloat16, 3, dev)
+    _need(k_pages, "k_pages", torch.bfloat16, 4, dev)
+    _need(v_pages, "v_pages", torch.bfloat16, 4, dev)
+    _need(idx_k_pages, "idx_k_pages", torch.bfloat16, 3, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(seq_len, "seq_len", torch.int32, 1, dev)
+    N, H, d = q.shape
+    G, dI = idx_q.shape[1], idx_q.shape[2]
+    npages = k_pages.shape[0]
+    maxb = block_table.shape[1]
+    if (k_pages.shape != (npages, B, G, d) or v_pages.shape != (npages, B, G, d)
+            or idx_k_pages.shape != (npages, B, dI) or block_table.shape[0] != N
+            or seq_len.shape != (N,)):
+        raise MSAError("inconsistent shapes for paged decode inputs")
+    if out is None:
+        out = torch.empty_like(q)
+    if return_ids and ids_out is None:
+        ids_out = torch.empty((N, G, kslots), dtype=torch.int32, device=dev)
+    nbytes = lib.msa_decode_paged_workspace_size(N, maxb, H, G, d, dI, B, kslots)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    st = lib.msa_decode_paged(_ptr(q), _ptr(idx_q), _ptr(k_pages), _ptr(v_pages),
+                              _ptr(idx_k_pages), npages, _ptr(block_table), maxb, _ptr(seq_len),
+                              N, H, G, d, dI, B, kslots, _scale(scale, d), _ptr(out),
+                              _ptr(ids_out), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "msa_decode_paged")
     return (out, ids_out) if return_ids else out

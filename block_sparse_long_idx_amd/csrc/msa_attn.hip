@@ -266,6 +266,7 @@ __global__ __launch_bounds__(256) void k4d_split(const uint16_t *__restrict__ q,
                                                  const uint16_t *__restrict__ vc,
                                                  const int32_t *__restrict__ ids,
                                                  const int32_t *__restrict__ seq_len,
+                                                 const int32_t *__restrict__ table, int maxb,
                                                  int64_t Lmax, int H, int G, int kslots,
                                                  float scale_log2, uint16_t *__restrict__ po,
                                                  float *__restrict__ plse) {
@@ -280,8 +281,11 @@ __global__ __launch_bounds__(256) void k4d_split(const uint16_t *__restrict__ q,
     const int64_t p = (int64_t)seq_len[n] - 1;
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int64_t kv_row_bytes = (int64_t)G * D * 2;
-    const int64_t row0 = (n * Lmax + (int64_t)j * kBlock) * G + g;
-    const int nrows = (int)min<int64_t>(kBlock, Lmax - (int64_t)j * kBlock);
+    // first token row of block j: contiguous cache [N, Lmax, G, D], or its page of
+    // a paged cache [pages, 128, G, D] (a page is always whole)
+    const int64_t tok0 = table ? (int64_t)table[n * maxb + j] * kBlock : n * Lmax + (int64_t)j * kBlock;
+    const int64_t row0 = tok0 * G + g;
+    const int nrows = table ? kBlock : (int)min<int64_t>(kBlock, Lmax - (int64_t)j * kBlock);
     stage_rows<D / 8, true>(lds_k, reinterpret_cast<const char *>(kc + row0 * D), kv_row_bytes,
                             nrows, tid);
     stage_v_transposed<D>(lds_vt, reinterpret_cast<const char *>(vc + row0 * D), kv_row_bytes,
@@ -300,24 +304,24 @@ __global__ __launch_bounds__(256) void k4d_split(const uint16_t *__restrict__ q,
 
 template <int D, int R>
 static hipError_t k4d_dispatch(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
-                               const int32_t *ids, const int32_t *seq_len, int N, int64_t Lmax,
-                               int H, int G, int k, float sl2, uint16_t *po, float *plse,
-                               hipStream_t s) {
+                               const int32_t *ids, const int32_t *seq_len, const int32_t *table,
+                               int maxb, int N, int64_t Lmax, int H, int G, int k, float sl2,
+                               uint16_t *po, float *plse, hipStream_t s) {
     const int64_t grid = (int64_t)N * G * k;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((k4d_split<D, R>), dim3((unsigned)grid), dim3(256), 0, s, q, kc, vc, ids,
-                       seq_len, Lmax, H, G, k, sl2, po, plse);
+                       seq_len, table, maxb, Lmax, H, G, k, sl2, po, plse);
     return hipGetLastError();
 }
 
 hipError_t launch_k4d_split(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
-                            const int32_t *ids, const int32_t *seq_len, int N, int64_t Lmax, int H,
-                            int G, int d, int k, float scale, uint16_t *po, float *plse,
-                            hipStream_t s) {
+                            const int32_t *ids, const int32_t *seq_len, const int32_t *table,
+                            int maxb, int N, int64_t Lmax, int H, int G, int d, int k, float scale,
+                            uint16_t *po, float *plse, hipStream_t s) {
     const float sl2 = scale * kLog2e;
     const int R = H / G;
 #define K4D_CASE(dd, rr) \
-    if (d == dd && R == rr) return k4d_dispatch<dd, rr>(q, kc, vc, ids, seq_len, N, Lmax, H, G, k, sl2, po, plse, s);
+    if (d == dd && R == rr) return k4d_dispatch<dd, rr>(q, kc, vc, ids, seq_len, table, maxb, N, Lmax, H, G, k, sl2, po, plse, s);
     K4D_CASE(64, 1) K4D_CASE(64, 2) K4D_CASE(64, 4) K4D_CASE(64, 8) K4D_CASE(64, 16) K4D_CASE(64, 32)
     K4D_CASE(128, 1) K4D_CASE(128, 2) K4D_CASE(128, 4) K4D_CASE(128, 8) K4D_CASE(128, 16) K4D_CASE(128, 32)
 #undef K4D_CASE

@@ -17,7 +17,9 @@
 //
 // K1d (decode) streams each sequence's idx_k cache once (the HBM-bound part of
 // decode): one wave per 128-key block, 16x16x32 MFMA with the G index heads as
-// the N dimension, operands loaded straight from global memory.
+// the N dimension, operands loaded straight from global memory.  The cache is
+// either contiguous per sequence or paged: with a block table, logical block b of
+// sequence n is the 128-token page table[n][b].
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -215,11 +217,14 @@ hipError_t launch_k1_index_pool(const uint16_t *iq, const uint16_t *ik, float *S
 
 // ---------------------------------------------------------------------------
 // K1d: one wave per (sequence, 128-key block).  grid = (ceil(nbmax/4), N).
+// table == nullptr: ikc is [N, Lmax, DI]; otherwise ikc is [pages, 128, DI] and
+// table[n * maxb + b] names the page of block b (checked by the caller).
 // ---------------------------------------------------------------------------
 template <int G, int DI>
 __global__ __launch_bounds__(256) void k1d_index_pool(const uint16_t *__restrict__ iq,
                                                       const uint16_t *__restrict__ ikc,
                                                       const int32_t *__restrict__ seq_len,
+                                                      const int32_t *__restrict__ table, int maxb,
                                                       float *__restrict__ S, int64_t Lmax,
                                                       int nbp) {
     constexpr int KS = DI / 32;
@@ -237,7 +242,9 @@ __global__ __launch_bounds__(256) void k1d_index_pool(const uint16_t *__restrict
     for (int ks = 0; ks < KS; ++ks)
         bq[ks] = as_bf16x8(l16 < G ? load16(iq + ((int64_t)n * G + l16) * DI + 32 * ks + 8 * qt)
                                    : u32x4{0, 0, 0, 0});
-    const uint16_t *base = ikc + ((int64_t)n * Lmax + (int64_t)b * kBlock) * DI;
+    const int64_t tok0 = table ? (int64_t)table[(int64_t)n * maxb + b] * kBlock
+                               : (int64_t)n * Lmax + (int64_t)b * kBlock;
+    const uint16_t *base = ikc + tok0 * DI;
     u32x4 a[8][KS];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
@@ -259,20 +266,21 @@ __global__ __launch_bounds__(256) void k1d_index_pool(const uint16_t *__restrict
 
 template <int G, int DI>
 static hipError_t k1d_dispatch(const uint16_t *iq, const uint16_t *ikc, const int32_t *seq_len,
-                               float *S, int N, int64_t Lmax, int nbp, hipStream_t s) {
+                               const int32_t *table, int maxb, float *S, int N, int64_t Lmax,
+                               int nbp, hipStream_t s) {
     const int64_t nbmax = (Lmax - 1) / kBlock;   // competitors of the longest sequence
     if (nbmax <= 0 || N <= 0) return hipSuccess;
     dim3 grid((unsigned)((nbmax + 3) / 4), (unsigned)N);
-    hipLaunchKernelGGL((k1d_index_pool<G, DI>), grid, dim3(256), 0, s, iq, ikc, seq_len, S, Lmax,
-                       nbp);
+    hipLaunchKernelGGL((k1d_index_pool<G, DI>), grid, dim3(256), 0, s, iq, ikc, seq_len, table,
+                       maxb, S, Lmax, nbp);
     return hipGetLastError();
 }
 
 hipError_t launch_k1d_index_pool(const uint16_t *iq, const uint16_t *ikc, const int32_t *seq_len,
-                                 float *S, int N, int64_t Lmax, int G, int dI, int nbp,
-                                 hipStream_t s) {
+                                 const int32_t *table, int maxb, float *S, int N, int64_t Lmax,
+                                 int G, int dI, int nbp, hipStream_t s) {
 #define K1D_CASE(g, di) \
-    if (G == g && dI == di) return k1d_dispatch<g, di>(iq, ikc, seq_len, S, N, Lmax, nbp, s);
+    if (G == g && dI == di) return k1d_dispatch<g, di>(iq, ikc, seq_len, table, maxb, S, N, Lmax, nbp, s);
     K1D_CASE(1, 32) K1D_CASE(1, 64) K1D_CASE(1, 128)
     K1D_CASE(2, 32) K1D_CASE(2, 64) K1D_CASE(2, 128)
     K1D_CASE(4, 32) K1D_CASE(4, 64) K1D_CASE(4, 128)

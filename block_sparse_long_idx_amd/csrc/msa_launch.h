@@ -27,9 +27,11 @@ hipError_t launch_k1_index_pool(const uint16_t *iq, const uint16_t *ik, float *S
                                 hipStream_t s);
 
 // K1d: decode block scores S[n*G + g][b] for blocks b < b(seq_len[n]-1).
+// table == nullptr: contiguous cache ikc [N, Lmax, dI]; otherwise a paged cache
+// [pages, 128, dI] with block b of sequence n in page table[n * maxb + b].
 hipError_t launch_k1d_index_pool(const uint16_t *iq, const uint16_t *ikc, const int32_t *seq_len,
-                                 float *S, int N, int64_t Lmax, int G, int dI, int nbp,
-                                 hipStream_t s);
+                                 const int32_t *table, int maxb, float *S, int N, int64_t Lmax,
+                                 int G, int dI, int nbp, hipStream_t s);
 
 // K2: exp-free selection.  Row r of S belongs to query position
 // q0 + r / G (prefill, seq_len == nullptr) or seq_len[r / G] - 1 (decode).
@@ -59,11 +61,17 @@ hipError_t launch_k4_kv_outer(const uint16_t *q, const uint16_t *kx, const uint1
                               int H, int G, int d, int k, float scale, uint16_t *po, float *plse,
                               hipStream_t s);
 
-// K4d: decode split over slots -> partials per (sequence, head, slot).
+// K4d: decode split over slots -> partials per (sequence, head, slot).  Cache
+// addressing as in K1d (kc, vc [N, Lmax, G, d] or pages [pages, 128, G, d]).
 hipError_t launch_k4d_split(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
-                            const int32_t *ids, const int32_t *seq_len, int N, int64_t Lmax, int H,
-                            int G, int d, int k, float scale, uint16_t *po, float *plse,
-                            hipStream_t s);
+                            const int32_t *ids, const int32_t *seq_len, const int32_t *table,
+                            int maxb, int N, int64_t Lmax, int H, int G, int d, int k, float scale,
+                            uint16_t *po, float *plse, hipStream_t s);
+
+// Paged decode: eff_len[n] = seq_len[n] when 1 <= seq_len[n] <= maxb * 128 and
+// every page id the sequence needs is in [0, num_pages), else 0.
+hipError_t launch_page_check(const int32_t *table, int maxb, int64_t num_pages,
+                             const int32_t *seq_len, int N, int32_t *eff_len, hipStream_t s);
 
 // K5: two-phase combine of the partials of `nq` queries into out[nq, H, d].
 // ids [nq, G, k]: a slot is merged when 0 <= id < nb_lim.

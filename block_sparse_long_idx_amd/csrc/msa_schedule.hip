@@ -14,6 +14,9 @@
 // Hot blocks (picked by nearly every query) only cost LDS atomics.  The order of
 // entries inside one work-group's share of a list depends on LDS atomic timing, but
 // no result does: every entry's partial goes to its own (query, head, slot).
+//
+// Also here: the page-table check of paged decode ("MiniMax M3 的采用瓶颈…"
+// §对建设者的影响: paged MSA decode), run before any page is read.
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -27,6 +30,39 @@ __global__ void k_fill_i32(int *p, int64_t n, int v) {
 hipError_t launch_fill_i32(int *p, int64_t n, int value, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, value);
+    return hipGetLastError();
+}
+
+// Paged decode: one work-group per sequence checks the page ids of the blocks it
+// needs (0 .. b(seq_len - 1)) and writes the length the later kernels may use: the
+// sequence's own length, or 0 (no block selected, zero output) when the length is
+// out of range or a needed page id is outside [0, num_pages).
+__global__ __launch_bounds__(256) void k_page_check(const int32_t *__restrict__ table, int maxb,
+                                                    int64_t num_pages,
+                                                    const int32_t *__restrict__ seq_len,
+                                                    int32_t *__restrict__ eff_len) {
+    const int n = blockIdx.x;
+    const int sl = seq_len[n];
+    const bool len_ok = sl >= 1 && (int64_t)sl <= (int64_t)maxb * kBlock;
+    int bad = 0;
+    if (len_ok) {
+        const int nblk = (sl - 1) / kBlock + 1;
+        const int32_t *row = table + (int64_t)n * maxb;
+#pragma unroll 8
+        for (int b = threadIdx.x; b < nblk; b += 256) {
+            const int32_t pg = row[b];
+            bad |= pg < 0 || (int64_t)pg >= num_pages;
+        }
+    }
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) eff_len[n] = (len_ok && !bad) ? sl : 0;
+}
+
+hipError_t launch_page_check(const int32_t *table, int maxb, int64_t num_pages,
+                             const int32_t *seq_len, int N, int32_t *eff_len, hipStream_t s) {
+    if (N <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_page_check, dim3((unsigned)N), dim3(256), 0, s, table, maxb, num_pages,
+                       seq_len, eff_len);
     return hipGetLastError();
 }
 

@@ -141,11 +141,41 @@ MSA_API int msa_decode(const uint16_t *q, const uint16_t *idx_q, const uint16_t 
                uint16_t *out, int32_t *block_ids_out, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Paged decode [SERVE: paged MSA decode; M3-20x §二 (B = 128-token blocks)].
+ * The same computation as msa_decode, with the caches held in fixed 128-token
+ * pages so that every MSA block is exactly one page: logical token t of sequence
+ * n is row t % 128 of page block_table[n * max_blocks + t / 128].  Pages may be
+ * shared between sequences (a common prefix); they are only read.
+ *   q            [N, H, d]                bf16
+ *   idx_q        [N, G, dI]               bf16
+ *   k_pages      [num_pages, 128, G, d]   bf16
+ *   v_pages      [num_pages, 128, G, d]   bf16
+ *   idx_k_pages  [num_pages, 128, dI]     bf16
+ *   block_table  [N, max_blocks] int32 DEVICE  page of each logical block; only
+ *                                 the entries of blocks 0 .. (seq_len[n]-1)/128 are
+ *                                 read, the rest may hold anything
+ *   seq_len      [N] int32 DEVICE  1 <= seq_len[n] <= max_blocks * 128
+ *   out          [N, H, d] bf16 OUT;  block_ids_out [N, G, k] int32 OUT or NULL
+ * A sequence whose length is out of range, or one of whose needed table entries
+ * lies outside [0, num_pages), gets ids all -1 and a zero output row, and none of
+ * its pages is read (the table is checked on the device before any page read).
+ * Requires B == 128 and max_blocks * 128 <= INT32_MAX; other limits as msa_decode.
+ * ------------------------------------------------------------------------- */
+MSA_API size_t msa_decode_paged_workspace_size(int N, int max_blocks, int H, int G, int d, int dI,
+                                               int B, int k);
+MSA_API int msa_decode_paged(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_pages,
+                             const uint16_t *v_pages, const uint16_t *idx_k_pages,
+                             int64_t num_pages, const int32_t *block_table, int max_blocks,
+                             const int32_t *seq_len, int N, int H, int G, int d, int dI, int B,
+                             int kslots, float scale, uint16_t *out, int32_t *block_ids_out,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Optional per-kernel timing (measurement support, process-wide, not
  * thread-safe).  While enabled, every kernel stage the entry points above enqueue
  * is bracketed by a pair of hipEvents recorded on the caller's stream; stages are
  * named "k1_index_pool", "k2_select", "k3_schedule" (its four small kernels as
- * one), "k4_kv_outer", "k5_combine", "k1d_index_pool", "k4d_split".
+ * one), "k4_kv_outer", "k5_combine", "k1d_index_pool", "k4d_split", "page_check".
  *   msa_timing_enable(max_launches): start recording (events for up to
  *       max_launches stages are created up front; further stages are not timed).
  *   msa_timing_collect(out, max_entries, n_out): waits for the recorded events

@@ -180,3 +180,81 @@ def decode_attend(q, k_cache, v_cache, seq_len, ids, B, scale, seqs, lib=None):
                              ids.shape[2], float(scale), _ptr(seqs), len(seqs), _ptr(ids),
                              _ptr(out))
     return out
+
+
+def decode_paged(q, iq, k_pages, v_pages, ik_pages, block_table, seq_len, B, kslots, scale=None,
+                 seqs=None, lib=None):
+    """Paged MSA decode for the listed sequences: (ids, gap, out, valid).
+
+    Token t of sequence n is row t % B of page block_table[n, t // B] (every MSA block
+    is one cache page).  The listed sequences' pages are gathered, in logical
+    order, into contiguous caches, and the contiguous decode above runs on them.  A
+    sequence whose length is outside [1, max_blocks * B] or that needs a page id
+    outside [0, num_pages) is not computed: valid False, ids -1, out 0, gap nan.
+    """
+    q, iq = _u16(q), _u16(iq)
+    kp, vp, ikp = _u16(k_pages), _u16(v_pages), _u16(ik_pages)
+    table = np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table,
+                       dtype=np.int64)
+    lens = np.asarray(seq_len.cpu() if hasattr(seq_len, "cpu") else seq_len, dtype=np.int64)
+    N, H, d = q.shape
+    G, dI = iq.shape[1], iq.shape[2]
+    npages, maxb = kp.shape[0], table.shape[1]
+    seqs = _rows(seqs, N)
+    n_out = len(seqs)
+    ids = np.full((n_out, G, kslots), -1, np.int32)
+    gap = np.full((n_out, G), np.nan, np.float32)
+    out = np.zeros((n_out, H, d), np.float64)
+    pages = [_pages_of(table, lens, n, B, npages) for n in seqs]
+    valid = np.array([p is not None for p in pages], bool)
+    vr = np.nonzero(valid)[0]
+    if len(vr) == 0:
+        return ids, gap, out, valid
+    # gather the valid sequences' pages, in logical order, into one contiguous batch
+    Lc = max(len(pages[r]) for r in vr) * B
+    kc = np.zeros((len(vr), Lc, G, d), np.uint16)
+    vc = np.zeros((len(vr), Lc, G, d), np.uint16)
+    ikc = np.zeros((len(vr), Lc, dI), np.uint16)
+    for j, r in enumerate(vr):
+        n_tok = len(pages[r]) * B
+        kc[j, :n_tok] = kp[pages[r]].reshape(n_tok, G, d)
+        vc[j, :n_tok] = vp[pages[r]].reshape(n_tok, G, d)
+        ikc[j, :n_tok] = ikp[pages[r]].reshape(n_tok, dI)
+    sv = seqs[vr]
+    ids[vr], gap[vr], out[vr] = decode(q[sv], iq[sv], kc, vc, ikc, lens[sv], B, kslots, scale,
+                                       lib=lib)
+    return ids, gap, out, valid
+
+
+def _pages_of(table, lens, n, B, npages):
+    """Page ids of sequence n's blocks 0 .. (len-1)/B in logical order, or None when
+    the length is outside [1, max_blocks * B] or a page id is outside the pool."""
+    Ln = int(lens[n])
+    if Ln < 1 or Ln > table.shape[1] * B:
+        return None
+    pages = table[n, :(Ln - 1) // B + 1]
+    if pages.min() < 0 or pages.max() >= npages:
+        return None
+    return pages
+
+
+def decode_paged_attend(q, k_pages, v_pages, block_table, seq_len, ids, B, scale, seqs,
+                        lib=None):
+    """Paged decode main branch for the listed (valid) sequences with given ids."""
+    q, kp, vp = _u16(q), _u16(k_pages), _u16(v_pages)
+    table = np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table,
+                       dtype=np.int64)
+    lens = np.asarray(seq_len.cpu() if hasattr(seq_len, "cpu") else seq_len, dtype=np.int64)
+    N, H, d = q.shape
+    G = kp.shape[2]
+    ids = np.asarray(ids, np.int32)
+    out = np.zeros((len(seqs), H, d), np.float64)
+    for r, n in enumerate(seqs):
+        pages = _pages_of(table, lens, n, B, kp.shape[0])
+        if pages is None:
+            raise ValueError(f"sequence {n} is not valid")
+        Lc = len(pages) * B
+        out[r] = decode_attend(q[n:n + 1], kp[pages].reshape(1, Lc, G, d),
+                               vp[pages].reshape(1, Lc, G, d), [int(lens[n])], ids[r:r + 1], B,
+                               scale, [0], lib=lib)[0]
+    return out

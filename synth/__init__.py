@@ -66,7 +66,7 @@ class DecodeShape:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "prefill" | "decode"
+    kind: str                 # "prefill" | "decode" | "decode_paged"
     shape: object
     plant: str = "lit"
     n_plant: int = 4
@@ -75,7 +75,8 @@ class Workload:
 
 
 # The five workloads: shapes of the pages' research model (64 query heads,
-# 4 KV heads, B = 128, k = 16) with head/index dims 128, plus the tiny case.
+# 4 KV heads, B = 128, k = 16) with head/index dims 128, plus the tiny case; and
+# the decode workload again with its caches in shuffled 128-token pages.
 WORKLOADS = {
     "tiny_prefill_L4096": Workload("tiny_prefill_L4096", "prefill",
                                    PrefillShape(L=4096, H=8, G=2, d=64, dI=32, B=128, k=4)),
@@ -88,6 +89,9 @@ WORKLOADS = {
     "prefill_L1048576_hot": Workload("prefill_L1048576_hot", "prefill",
                                      PrefillShape(L=1048576, H=64, G=4, d=128, dI=128),
                                      plant="hot", n_plant=0, c=3.0, hot_blocks=(0, 1, 2, 3)),
+    "decode_paged_N64_L262144": Workload("decode_paged_N64_L262144", "decode_paged",
+                                         DecodeShape(N=64, Lc=262144, H=64, G=4, d=128,
+                                                     dI=128)),
 }
 
 
@@ -225,3 +229,41 @@ def decode_inputs(shape: DecodeShape, seed: int, plant: str = "lit", n_plant: in
     out["seq_len"] = seq_len
     out["planted"] = planted
     return out
+
+
+def paginate(x: dict, B: int, seed: int, extra_pages: int = 0) -> dict:
+    """Re-lay the contiguous decode caches of ``decode_inputs`` as B-token pages.
+
+    Logical block b of sequence n goes to page ``block_table[n, b]``; the pages are
+    a seeded random permutation of all N * ceil(Lc / B) blocks, followed by
+    ``extra_pages`` pages of N(0,1) data that no table entry names.  A cache whose
+    length is not a multiple of B is zero-padded to whole pages.  Returns
+    k_pages/v_pages [P, B, G, d], ik_pages [P, B, dI] (bf16) and block_table
+    [N, ceil(Lc / B)] (int32), on the caches' device.
+    """
+    kc, vc, ikc = x["k_cache"], x["v_cache"], x["ik_cache"]
+    N, Lc, G, d = kc.shape
+    dI = ikc.shape[2]
+    nblk = (Lc + B - 1) // B
+    pad = nblk * B - Lc
+    dev = kc.device
+    gen = torch.Generator().manual_seed(_seed(seed, T_PLANT, 7))
+    perm = torch.randperm(N * nblk, generator=gen).to(dev)
+    P = N * nblk + extra_pages
+
+    def lay(cache, row_shape, tid):
+        pages = randn_bf16((P, B) + row_shape, seed, tid, dev) if extra_pages else \
+            torch.empty((P, B) + row_shape, dtype=cache.dtype, device=dev)
+        blocks = cache
+        if pad:
+            blocks = torch.cat([cache, torch.zeros((N, pad) + row_shape, dtype=cache.dtype,
+                                                   device=dev)], dim=1)
+        pages[perm] = blocks.reshape((N * nblk, B) + row_shape)
+        return pages
+
+    return {
+        "k_pages": lay(kc, (G, d), 11),
+        "v_pages": lay(vc, (G, d), 12),
+        "ik_pages": lay(ikc, (dI,), 13),
+        "block_table": perm.view(N, nblk).to(torch.int32),
+    }

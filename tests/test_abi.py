@@ -33,8 +33,10 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for want in ("msa_select_blocks", "msa_sparse_attn", "msa_prefill", "msa_decode",
-                 "msa_select_blocks_workspace_size", "msa_sparse_attn_workspace_size",
-                 "msa_prefill_workspace_size", "msa_decode_workspace_size", "msa_status_string"):
+                 "msa_decode_paged", "msa_select_blocks_workspace_size",
+                 "msa_sparse_attn_workspace_size", "msa_prefill_workspace_size",
+                 "msa_decode_workspace_size", "msa_decode_paged_workspace_size",
+                 "msa_status_string"):
         assert want in names
 
 
@@ -64,6 +66,11 @@ def test_workspace_sizes(lib):
     s3 = lib.msa_prefill_workspace_size(1048576, 64, 4, 128, 128, 128, 16)
     assert s2 > 0 and s3 < 4 * s2 + (1 << 34)
     assert lib.msa_decode_workspace_size(64, 262144, 64, 4, 128, 128, 128, 16) > 0
+    # paged decode: the contiguous decode workspace at Lmax = max_blocks * B, plus one
+    # checked length per sequence
+    wp = lib.msa_decode_paged_workspace_size(64, 2048, 64, 4, 128, 128, 128, 16)
+    assert wp >= lib.msa_decode_workspace_size(64, 262144, 64, 4, 128, 128, 128, 16) + 64 * 4
+    assert lib.msa_decode_paged_workspace_size(0, 2048, 64, 4, 128, 128, 128, 16) == 0
 
 
 P = ctypes.c_void_p
@@ -127,3 +134,26 @@ def test_binding_fails_loudly_without_gpu_tensors():
     x = torch.zeros(4, 2, 32, dtype=torch.bfloat16)
     with pytest.raises(msa.MSAError):
         msa.select_blocks(x, torch.zeros(4, 32, dtype=torch.bfloat16), k=4)
+
+
+def test_paged_decode_arguments(lib):
+    f, ws, big, s = _fake(), P(0x100000), ctypes.c_size_t(1 << 40), None
+    zero = ctypes.c_float(0)
+
+    def call(q=f, table=f, seq_len=f, N=2, npages=16, maxb=8, H=8, G=2, d=64, dI=32, B=128, k=4,
+             ws_=ws, nbytes=big):
+        return lib.msa_decode_paged(q, f, f, f, f, npages, table, maxb, seq_len, N, H, G, d, dI, B,
+                                    k, zero, f, None, ws_, nbytes, s)
+
+    assert call(N=0, q=None, table=None, seq_len=None) == OK      # empty batch: nothing to do
+    assert call(table=None) == INVALID
+    assert call(seq_len=None) == INVALID
+    assert call(npages=0) == INVALID
+    assert call(maxb=0) == INVALID
+    assert call(H=6, G=4) == INVALID
+    assert call(B=64) == UNSUPPORTED        # a page is one 128-token MSA block
+    assert call(d=96) == UNSUPPORTED
+    assert call(k=33) == UNSUPPORTED
+    assert call(maxb=1 << 24) == UNSUPPORTED  # max_blocks * 128 must fit in int32
+    assert call(nbytes=ctypes.c_size_t(64)) == WS_SMALL
+    assert call(ws_=P(0x100010)) == WS_SMALL

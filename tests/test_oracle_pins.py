@@ -341,9 +341,60 @@ def check_prefix_and_decode(lib):
         assert np.array_equal(outd[n], out[sl - 1])
 
 
+# --------------------------------------------------------------------------
+# 10. Paged decode ("MiniMax M3 的采用瓶颈…" §对建设者的影响: paged MSA decode) is
+#     decode on the cache that the block table spells out: pages laid out by an
+#     independent seeded permutation (synth.paginate) must give the contiguous
+#     decode bit for bit; a table that points two sequences at the same pages must
+#     give decode on caches whose prefixes were copied in contiguous form; a bad
+#     page id or length marks the sequence invalid.
+# --------------------------------------------------------------------------
+def check_paged_decode(lib):
+    B, k = 16, 4
+    sh = synth.DecodeShape(N=4, Lc=150, H=4, G=2, d=16, dI=8, B=B, k=k)
+    seq_len = np.array([150, 1, 97, 64], np.int64)
+    x = synth.decode_inputs(sh, seed=21, seq_len=seq_len)
+    pg = synth.paginate(x, B, seed=21, extra_pages=5)
+    scale = 1.0 / math.sqrt(sh.d)
+    ids, gap, out = oracle.decode(x["q"], x["iq"], x["k_cache"], x["v_cache"], x["ik_cache"],
+                                  seq_len, B, k, scale, lib=lib)
+    idsp, gapp, outp, valid = oracle.decode_paged(x["q"], x["iq"], pg["k_pages"], pg["v_pages"],
+                                                  pg["ik_pages"], pg["block_table"], seq_len, B,
+                                                  k, scale, lib=lib)
+    assert valid.all()
+    assert np.array_equal(idsp, ids) and np.array_equal(outp, out)
+    # sequence 2 shares sequence 0's first 3 pages
+    table = pg["block_table"].clone()
+    table[2, :3] = table[0, :3]
+    kc, vc, ikc = x["k_cache"].clone(), x["v_cache"].clone(), x["ik_cache"].clone()
+    kc[2, :3 * B], vc[2, :3 * B], ikc[2, :3 * B] = kc[0, :3 * B], vc[0, :3 * B], ikc[0, :3 * B]
+    ids2, _, out2 = oracle.decode(x["q"], x["iq"], kc, vc, ikc, seq_len, B, k, scale, lib=lib)
+    idsp2, _, outp2, _ = oracle.decode_paged(x["q"], x["iq"], pg["k_pages"], pg["v_pages"],
+                                             pg["ik_pages"], table, seq_len, B, k, scale, lib=lib)
+    assert np.array_equal(idsp2, ids2) and np.array_equal(outp2, out2)
+    assert not np.array_equal(out2[2], out[2])
+    # a page id out of range, a length past the table: invalid, ids -1, zero output
+    npages = pg["k_pages"].shape[0]
+    table[3, 1] = npages
+    bad_len = seq_len.copy()
+    bad_len[1] = table.shape[1] * B + 1
+    idsp3, _, outp3, valid3 = oracle.decode_paged(x["q"], x["iq"], pg["k_pages"], pg["v_pages"],
+                                                  pg["ik_pages"], table, bad_len, B, k, scale,
+                                                  lib=lib)
+    assert list(valid3) == [True, False, True, False]
+    assert (idsp3[[1, 3]] == -1).all() and not outp3[[1, 3]].any()
+    # an entry past the sequence's last block is never read
+    table[0, -1] = -7
+    short = seq_len.copy()
+    short[0] = (table.shape[1] - 1) * B
+    _, _, _, valid4 = oracle.decode_paged(x["q"], x["iq"], pg["k_pages"], pg["v_pages"],
+                                          pg["ik_pages"], table, short, B, k, scale, lib=lib)
+    assert valid4[0]
+
+
 PINS = [check_dense_equivalence, check_local_only, check_masked_attention, check_exp_free,
         check_constructed, check_tie_break, check_brute_force, check_invariants,
-        check_properties, check_prefix_and_decode]
+        check_properties, check_prefix_and_decode, check_paged_decode]
 
 
 @pytest.mark.parametrize("check", PINS, ids=[c.__name__ for c in PINS])
@@ -352,7 +403,7 @@ def test_pin(check):
 
 
 # --------------------------------------------------------------------------
-# 10. Mutation test: plausible mistakes planted in copies of the oracle source
+# 11. Mutation test: plausible mistakes planted in copies of the oracle source
 #     (on the CPU) must each fail at least one of the pins above.
 # --------------------------------------------------------------------------
 MUTANTS = {

@@ -242,6 +242,119 @@ def test_decode_full_size_subset():
     _decode_check(shape, seq_len, seed=0, seqs=np.array([0, 1, 17, 31, 48, 63]), device=DEV)
 
 
+# ----------------------------- paged decode ---------------------------------
+def _compact_pages(pg, table, seqs, seq_len, B=128):
+    """CPU copies of only the pages the listed sequences need, with their table
+    rows renumbered; entries outside [0, num_pages) stay out of range."""
+    npages = pg["k_pages"].shape[0]
+    rows = table[torch.as_tensor(seqs, dtype=torch.long, device=table.device)].long()
+    need = []
+    for r, n in enumerate(seqs):
+        nblk = max(int(seq_len[n]) - 1, 0) // B + 1
+        need.append(rows[r, :nblk])
+    need = torch.cat(need)
+    uniq = torch.unique(need[(need >= 0) & (need < npages)])
+    sub = {name: pg[name][uniq].cpu() for name in ("k_pages", "v_pages", "ik_pages")}
+    pos = torch.searchsorted(uniq, rows.clamp(0, npages - 1))
+    inb = (rows >= 0) & (rows < npages)
+    hit = inb & (uniq[pos.clamp(max=len(uniq) - 1)] == rows)
+    sub_table = torch.where(hit, pos, torch.full_like(pos, -1)).to(torch.int32).cpu()
+    return sub, sub_table
+
+
+def _paged_check(shape, seq_len, seed, share=(), bad=(), seqs=None, device="cpu",
+                 extra_pages=3):
+    """msa.decode_paged vs the paged oracle on the listed sequences; without
+    shared or bad pages also bitwise against msa.decode on the contiguous caches."""
+    msa = _msa()
+    _say(f"paged decode N={shape.N} Lmax={shape.Lc} seq_len[:8]={list(seq_len[:8])} "
+         f"share={list(share)} bad={list(bad)} seed={seed}")
+    seq_len = np.asarray(seq_len, np.int64)
+    x = synth.decode_inputs(shape, seed=seed, seq_len=np.clip(seq_len, 1, shape.Lc),
+                            device=device)
+    pg = synth.paginate({n: x[n] for n in ("k_cache", "v_cache", "ik_cache")}, 128, seed,
+                        extra_pages=extra_pages)
+    table = pg["block_table"].clone()
+    for dst, src, m in share:
+        table[dst, :m] = table[src, :m]
+    for n, b, val in bad:
+        table[n, b] = val
+    g = {n: t.to(DEV) for n, t in pg.items()}
+    table_d = table.to(DEV)
+    q, iq = x["q"].to(DEV), x["iq"].to(DEV)
+    sl = torch.tensor(seq_len.astype(np.int32), device=DEV)
+    out, ids = msa.decode_paged(q, iq, g["k_pages"], g["v_pages"], g["ik_pages"], table_d, sl,
+                                kslots=shape.k, return_ids=True)
+    torch.cuda.synchronize()
+    if not share and not bad:
+        kc, vc, ikc = (x[n].to(DEV) for n in ("k_cache", "v_cache", "ik_cache"))
+        out_c, ids_c = msa.decode(q, iq, kc, vc, ikc, sl, kslots=shape.k, return_ids=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ids_c)
+        assert torch.equal(out.view(torch.int16), out_c.view(torch.int16))
+        del kc, vc, ikc
+    out = out.float().cpu().numpy()
+    ids = ids.cpu().numpy()
+    if seqs is None:
+        seqs = np.arange(shape.N)
+    sub, sub_table = _compact_pages(g, table_d, seqs, seq_len)
+    scale = 1.0 / math.sqrt(shape.d)
+    oids, gap, oout, valid = oracle.decode_paged(x["q"][seqs], x["iq"][seqs], sub["k_pages"],
+                                                 sub["v_pages"], sub["ik_pages"], sub_table,
+                                                 seq_len[seqs], 128, shape.k, scale)
+    vs = seqs[valid]
+    for n in seqs[~valid]:
+        assert (ids[n] == -1).all() and (out[n] == 0).all()
+    if len(vs) == 0:
+        return
+    _parity.check_selection_valid(ids[vs], seq_len[vs] - 1, shape.k)
+    tie, nmis = _parity.compare_ids(ids[vs], oids[valid], gap[valid])
+    ref = oout[valid].copy()
+    if tie.any():
+        # near-tie sequences: attend the GPU's own selection
+        tr = np.nonzero(tie.any(axis=1))[0]
+        ref[tr] = oracle.decode_paged_attend(x["q"][seqs], sub["k_pages"], sub["v_pages"],
+                                             sub_table, seq_len[seqs], ids[vs[tr]], 128, scale,
+                                             np.nonzero(valid)[0][tr])
+    mx, mean = _parity.compare_out(out[vs], ref)
+    _say(f"  -> valid {len(vs)}/{len(seqs)} near_ties {int(tie.sum())} mismatches {nmis} "
+         f"max {mx:.3e} mean {mean:.3e}")
+    assert nmis == 0
+    assert mx < _parity.MAX_ABS and mean < _parity.MEAN_ABS
+
+
+def test_paged_decode_small():
+    shape = synth.DecodeShape(N=8, Lc=2000, H=64, G=4, d=128, dI=128, B=128, k=16)
+    _paged_check(shape, np.array([1, 127, 128, 129, 2000, 1500, 640, 1999]), seed=3)
+
+
+def test_paged_decode_tiny_dims():
+    shape = synth.DecodeShape(N=5, Lc=4096, H=8, G=2, d=64, dI=32, B=128, k=4)
+    _paged_check(shape, np.array([4096, 3000, 129, 640, 1]), seed=4, extra_pages=0)
+
+
+def test_paged_decode_shared_and_bad_pages():
+    """Sequences 1 and 2 reuse sequence 0's first pages (a common prefix); sequence 3
+    names a page past the pool, sequence 4 a negative one, sequence 5 is longer than
+    its table, sequence 6 has length 0: those four get ids -1 and zero rows."""
+    shape = synth.DecodeShape(N=8, Lc=3000, H=16, G=4, d=128, dI=128, B=128, k=8)
+    seq_len = np.array([3000, 2500, 1000, 2000, 700, 3000, 0, 1234])
+    Lc_blocks = (shape.Lc + 127) // 128
+    seq_len[5] = Lc_blocks * 128 + 1
+    npages = shape.N * Lc_blocks + 2
+    _paged_check(shape, seq_len, seed=5, share=[(1, 0, 12), (2, 0, 7)],
+                 bad=[(3, 4, npages), (4, 0, -3)], extra_pages=2)
+
+
+def test_paged_decode_full_size():
+    """64 sequences x 262144 cached tokens in 131072 shuffled pages: bitwise equal to
+    contiguous decode for every sequence, and the oracle on 4 of them."""
+    wl = synth.WORKLOADS["decode_N64_L262144"]
+    shape = wl.shape
+    _paged_check(shape, np.full(shape.N, shape.Lc), seed=0, seqs=np.array([0, 21, 42, 63]),
+                 device=DEV, extra_pages=0)
+
+
 def test_chunked_workspace_invariance():
     """A smaller workspace makes the library split the queries into several chunks;
     every row's result must be bitwise the same as with one chunk."""
