@@ -80,18 +80,20 @@ def prefill_work(L, H, G, d, dI, k, B=B_BLOCK, list_counts=None):
     }
 
 
-def decode_work(N, Lc, H, G, d, dI, k, B=B_BLOCK, paged=False):
+def decode_work(N, Lc, H, G, d, dI, k, B=B_BLOCK, paged=False, fp8idx=False):
     p = Lc - 1
     nb = p // B                                        # competitor blocks per sequence
     nsel = min(k, nb + 1)
-    idx_bytes = N * nb * B * dI * 2.0                  # idx-K cache stream
+    # idx-K cache stream: bf16, or E4M3 bytes plus one fp32 scale per token
+    idx_bytes = N * nb * B * (dI + 4.0 if fp8idx else dI * 2.0)
     kv_bytes = N * G * nsel * 2 * B * d * 2.0          # selected K and V blocks
     small = N * (H * d * 2 * 2 + G * dI * 2) + N * G * (nb * 4 * 2 + k * 4)
     if paged:                                          # block-table reads
         small += N * (nb + 1) * 4.0 * 2 + N * G * nsel * 4.0 * 2
     part = N * H * nsel * (2 * d + 4) * 2.0
+    k1d = "k1d_index_pool_fp8" if fp8idx else "k1d_index_pool"
     return {
-        "bytes": {"k1d_index_pool": idx_bytes + N * G * nb * 4.0,
+        "bytes": {k1d: idx_bytes + N * G * nb * 4.0,
                   "k4d_split": kv_bytes + N * H * nsel * (d * 2 + 2 * d + 4),
                   "k2_select": N * G * (nb * 4.0 + k * 4), "k5_combine": part / 2 + N * H * d * 2},
         "total_bytes": idx_bytes + kv_bytes + small + part,
@@ -133,8 +135,11 @@ def cpu_baseline_prefill(x, shape, target_s=15.0):
 
 
 def cpu_baseline_decode(x, shape, target_s=15.0):
+    """The decode oracle on batches of whole sequences (E4M3 index-key variant when
+    the workload's index cache is FP8)."""
     import oracle
     lib = oracle.load()
+    fp8 = "ik8" in x
     t_copy = time.perf_counter()
     n_seq = 1
     host = None
@@ -143,12 +148,20 @@ def cpu_baseline_decode(x, shape, target_s=15.0):
         seqs = np.arange(total, min(shape.N, total + n_seq))
         if host is None:
             host = {n: x[n].cpu() for n in ("q", "iq")}
-        kc = x["k_cache"][seqs[0]:seqs[-1] + 1].cpu()
-        vc = x["v_cache"][seqs[0]:seqs[-1] + 1].cpu()
-        ikc = x["ik_cache"][seqs[0]:seqs[-1] + 1].cpu()
+        sl = slice(seqs[0], seqs[-1] + 1)
+        kc = x["k_cache"][sl].cpu()
+        vc = x["v_cache"][sl].cpu()
+        if fp8:
+            ik8, iks = x["ik8"][sl].cpu(), x["ik_scale"][sl].cpu()
+        else:
+            ikc = x["ik_cache"][sl].cpu()
         t0 = time.perf_counter()
-        oracle.decode(host["q"][seqs[0]:seqs[-1] + 1], host["iq"][seqs[0]:seqs[-1] + 1], kc, vc,
-                      ikc, np.asarray(x["seq_len"])[seqs], B_BLOCK, shape.k, lib=lib)
+        if fp8:
+            oracle.decode_fp8idx(host["q"][sl], host["iq"][sl], kc, vc, ik8, iks,
+                                 np.asarray(x["seq_len"])[seqs], B_BLOCK, shape.k, lib=lib)
+        else:
+            oracle.decode(host["q"][sl], host["iq"][sl], kc, vc, ikc,
+                          np.asarray(x["seq_len"])[seqs], B_BLOCK, shape.k, lib=lib)
         total_s += time.perf_counter() - t0
         total += len(seqs)
         n_seq = min(16, n_seq * 2)
@@ -320,6 +333,21 @@ def main():
         def step():
             msa.decode(x["q"], x["iq"], x["k_cache"], x["v_cache"], x["ik_cache"], seq_len,
                        kslots=s.k, out=out, ids_out=ids, workspace=ws, return_ids=True)
+    elif wl.kind == "decode_fp8idx":   # index-key cache as E4M3 bytes + per-token scales
+        x = synth.decode_inputs(s, seed=args.seed, device=dev)
+        x["ik8"], x["ik_scale"] = msa.quantize_idx_k_e4m3(x["ik_cache"])
+        del x["ik_cache"]
+        torch.cuda.empty_cache()
+        seq_len = torch.tensor(np.asarray(x["seq_len"], np.int32), device=dev)
+        out = torch.empty_like(x["q"])
+        ids = torch.empty((s.N, s.G, s.k), dtype=torch.int32, device=dev)
+        ws = msa._workspace(msa.workspace_size("decode", N=s.N, Lmax=s.Lc, H=s.H, G=s.G, d=s.d,
+                                               dI=s.dI, k=s.k), dev)
+
+        def step():
+            msa.decode_fp8idx(x["q"], x["iq"], x["k_cache"], x["v_cache"], x["ik8"],
+                              x["ik_scale"], seq_len, kslots=s.k, out=out, ids_out=ids,
+                              workspace=ws, return_ids=True)
     else:   # decode over 128-token pages in a seeded random order
         x = synth.decode_inputs(s, seed=args.seed, device=dev)
         x.update(synth.paginate(x, B_BLOCK, seed=args.seed))
@@ -387,7 +415,8 @@ def main():
         result["algorithmic_flops_per_step"] = work["f_total"]
         result["dense_gqa_flops_per_step"] = work["dense_gqa_flops"]
     else:
-        work = decode_work(s.N, s.Lc, s.H, s.G, s.d, s.dI, s.k, paged=wl.kind == "decode_paged")
+        work = decode_work(s.N, s.Lc, s.H, s.G, s.d, s.dI, s.k, paged=wl.kind == "decode_paged",
+                           fp8idx=wl.kind == "decode_fp8idx")
         result.update({"value": ms_per_step * 1e3, "unit": "us/step", "higher_is_better": False})
         result["config"] = {"workload": wl.name, "N": s.N, "Lc": s.Lc, "H": s.H, "G": s.G,
                             "d": s.d, "dI": s.dI, "B": s.B, "k": s.k}
@@ -429,7 +458,7 @@ def main():
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         if wl.kind == "prefill":
             result["cpu_baseline"] = cpu_baseline_prefill(x, s, args.cpu_seconds)
-        elif wl.kind == "decode":
+        elif wl.kind in ("decode", "decode_fp8idx"):
             result["cpu_baseline"] = cpu_baseline_decode(x, s, args.cpu_seconds)
         else:
             result["cpu_baseline"] = cpu_baseline_decode_paged(x, s, args.cpu_seconds)

@@ -16,7 +16,7 @@ import os
 import torch
 
 __all__ = ["MSAError", "select_blocks", "sparse_attn", "prefill", "decode", "decode_paged",
-           "workspace_size",
+           "decode_fp8idx", "quantize_idx_k_e4m3", "workspace_size",
            "library_path", "load_library", "timing_enable", "timing_collect", "timing_disable"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -47,9 +47,9 @@ def timing_enable(max_launches: int = 4096):
 def timing_collect() -> dict:
     """Wait for the recorded stages; {stage: (launches, total_ms)}; clears the record."""
     lib = load_library()
-    buf = (_KernelTime * 16)()
+    buf = (_KernelTime * 32)()
     n = ctypes.c_int(0)
-    _check(lib.msa_timing_collect(buf, 16, ctypes.byref(n)), "msa_timing_collect")
+    _check(lib.msa_timing_collect(buf, 32, ctypes.byref(n)), "msa_timing_collect")
     return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(n.value)}
 
 
@@ -97,6 +97,11 @@ def load_library():
     lib.msa_decode_paged.argtypes = [P, P, P, P, P, i64, P, i32, P, i32, i32, i32, i32, i32, i32,
                                      i32, f32, P, P, P, sz, P]
     lib.msa_decode_paged.restype = i32
+    lib.msa_decode_fp8idx.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, i32, i32,
+                                      f32, P, P, P, sz, P]
+    lib.msa_decode_fp8idx.restype = i32
+    lib.msa_quantize_idx_k_e4m3.argtypes = [P, i64, i32, P, P, P]
+    lib.msa_quantize_idx_k_e4m3.restype = i32
     lib.msa_timing_enable.argtypes = [i32]
     lib.msa_timing_enable.restype = i32
     lib.msa_timing_collect.argtypes = [ctypes.POINTER(_KernelTime), i32, ctypes.POINTER(i32)]
@@ -300,4 +305,57 @@ def decode_paged(q, idx_q, k_pages, v_pages, idx_k_pages, block_table, seq_len, 
                               N, H, G, d, dI, B, kslots, _scale(scale, d), _ptr(out),
                               _ptr(ids_out), _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "msa_decode_paged")
+    return (out, ids_out) if return_ids else out
+
+
+def quantize_idx_k_e4m3(idx_k, out=None, scale_out=None):
+    """Index-key rows [..., dI] bf16 -> (E4M3 bytes [..., dI] uint8, scales [...] fp32)."""
+    lib = load_library()
+    if not isinstance(idx_k, torch.Tensor) or idx_k.dtype != torch.bfloat16 or not idx_k.is_cuda:
+        raise MSAError("idx_k must be a bf16 GPU tensor")
+    if not idx_k.is_contiguous():
+        raise MSAError("idx_k must be contiguous")
+    dI = idx_k.shape[-1]
+    rows = idx_k.numel() // max(dI, 1)
+    if out is None:
+        out = torch.empty(idx_k.shape, dtype=torch.uint8, device=idx_k.device)
+    if scale_out is None:
+        scale_out = torch.empty(idx_k.shape[:-1], dtype=torch.float32, device=idx_k.device)
+    st = lib.msa_quantize_idx_k_e4m3(_ptr(idx_k), rows, dI, _ptr(out), _ptr(scale_out),
+                                     _stream(idx_k.device))
+    _check(st, "msa_quantize_idx_k_e4m3")
+    return out, scale_out
+
+
+def decode_fp8idx(q, idx_q, k_cache, v_cache, idx_k_e4m3, idx_k_scale, seq_len, kslots: int = 16,
+                  B: int = 128, scale=None, return_ids: bool = False, out=None, ids_out=None,
+                  workspace=None):
+    """MSA decode with an E4M3 index-key cache [N, Lmax, dI] (uint8) + scales [N, Lmax]."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(idx_q, "idx_q", torch.bfloat16, 3, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _need(idx_k_e4m3, "idx_k_e4m3", torch.uint8, 3, dev)
+    _need(idx_k_scale, "idx_k_scale", torch.float32, 2, dev)
+    _need(seq_len, "seq_len", torch.int32, 1, dev)
+    N, H, d = q.shape
+    G, dI = idx_q.shape[1], idx_q.shape[2]
+    Lmax = k_cache.shape[1]
+    if (k_cache.shape != (N, Lmax, G, d) or v_cache.shape != (N, Lmax, G, d)
+            or idx_k_e4m3.shape != (N, Lmax, dI) or idx_k_scale.shape != (N, Lmax)
+            or seq_len.shape != (N,)):
+        raise MSAError("inconsistent shapes for FP8 decode inputs")
+    if out is None:
+        out = torch.empty_like(q)
+    if return_ids and ids_out is None:
+        ids_out = torch.empty((N, G, kslots), dtype=torch.int32, device=dev)
+    nbytes = lib.msa_decode_workspace_size(N, Lmax, H, G, d, dI, B, kslots)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    st = lib.msa_decode_fp8idx(_ptr(q), _ptr(idx_q), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(idx_k_e4m3), _ptr(idx_k_scale), _ptr(seq_len), N, Lmax, H, G,
+                               d, dI, B, kslots, _scale(scale, d), _ptr(out), _ptr(ids_out),
+                               _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "msa_decode_fp8idx")
     return (out, ids_out) if return_ids else out

@@ -8,7 +8,8 @@
 // the chunking.  Per chunk:
 //   K1 index score + block max-pool -> K2 exp-free top-k -> K3 schedule ->
 //   K4 KV-outer attention -> K5 combine.
-// Decode: K1d -> K2 -> K4d -> K5 (paged decode: page-table check first).
+// Decode: K1d -> K2 -> K4d -> K5 (paged decode: page-table check first; FP8
+// index-key cache: the E4M3 variant of K1d).
 // The compute entry points never allocate device memory, free or synchronise;
 // only the optional timing calls at the end create events and synchronise.
 #include <math.h>
@@ -126,10 +127,11 @@ struct TimedLaunch {
     int name;
     hipEvent_t start, stop;
 };
-enum StageName { kK1, kK2, kK3, kK4, kK5, kK1d, kK4d, kKpc, kNumStages };
+enum StageName { kK1, kK2, kK3, kK4, kK5, kK1d, kK4d, kKpc, kK1d8, kQuant, kNumStages };
 const char *const kStageNames[kNumStages] = {"k1_index_pool", "k2_select", "k3_schedule",
                                              "k4_kv_outer", "k5_combine", "k1d_index_pool",
-                                             "k4d_split", "page_check"};
+                                             "k4d_split", "page_check", "k1d_index_pool_fp8",
+                                             "quantize_e4m3"};
 struct Timing {
     bool on = false;
     int cap = 0, used = 0;
@@ -378,6 +380,52 @@ int msa_decode_paged(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k
     MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, eff_len, Lmax, ids, s));
     MSA_TIMED(kK4d, launch_k4d_split(q, k_pages, v_pages, ids, eff_len, block_table, max_blocks, N,
                                      Lmax, H, G, d, kslots, scale, po, plse, s));
+    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, s));
+    return MSA_OK;
+}
+
+// ----------------------- FP8 (E4M3) index-key cache ------------------------
+int msa_quantize_idx_k_e4m3(const uint16_t *idx_k, int64_t rows, int dI, uint8_t *idx_k_e4m3,
+                            float *idx_k_scale, void *stream) {
+    if (rows < 0 || dI <= 0) return MSA_ERR_INVALID_ARG;
+    if (rows == 0) return MSA_OK;
+    if (!idx_k || !idx_k_e4m3 || !idx_k_scale) return MSA_ERR_INVALID_ARG;
+    if (dI != 32 && dI != 64 && dI != 128) return MSA_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    MSA_TIMED(kQuant, launch_quant_e4m3(idx_k, rows, dI, idx_k_e4m3, idx_k_scale, s));
+    return MSA_OK;
+}
+
+int msa_decode_fp8idx(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache,
+                      const uint16_t *v_cache, const uint8_t *idx_k_e4m3, const float *idx_k_scale,
+                      const int32_t *seq_len, int N, int64_t Lmax, int H, int G, int d, int dI,
+                      int B, int kslots, float scale, uint16_t *out, int32_t *block_ids_out,
+                      void *ws, size_t ws_bytes, void *stream) {
+    if (N < 0 || Lmax < 0 || H <= 0 || G <= 0 || d <= 0 || dI <= 0 || B <= 0 || kslots < 1 ||
+        H % G)
+        return MSA_ERR_INVALID_ARG;
+    if (N == 0) return MSA_OK;
+    if (Lmax == 0 || !q || !idx_q || !k_cache || !v_cache || !idx_k_e4m3 || !idx_k_scale ||
+        !seq_len || !out)
+        return MSA_ERR_INVALID_ARG;
+    if (B != kBlock || !d_ok(d) || !r_ok(H, G) || !index_ok(G, dI) || kslots > 32)
+        return MSA_ERR_UNSUPPORTED;
+    const int st = check_ws(ws, ws_bytes, msa_decode_workspace_size(N, Lmax, H, G, d, dI, B, kslots));
+    if (st != MSA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    scale = default_scale(scale, d);
+    const int nbp = nb_padded(Lmax);
+    Carver c(ws);
+    float *S = c.take<float>((int64_t)N * G * nbp);
+    int32_t *ids_ws = c.take<int32_t>((int64_t)N * G * kslots);
+    uint16_t *po = c.take<uint16_t>((int64_t)N * H * kslots * d);
+    float *plse = c.take<float>((int64_t)N * H * kslots);
+    int32_t *ids = block_ids_out ? block_ids_out : ids_ws;
+    MSA_TIMED(kK1d8, launch_k1d_index_pool_fp8(idx_q, idx_k_e4m3, idx_k_scale, seq_len, S, N, Lmax,
+                                               G, dI, nbp, s));
+    MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, seq_len, Lmax, ids, s));
+    MSA_TIMED(kK4d, launch_k4d_split(q, k_cache, v_cache, ids, seq_len, nullptr, 0, N, Lmax, H, G,
+                                     d, kslots, scale, po, plse, s));
     MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, s));
     return MSA_OK;
 }

@@ -289,4 +289,176 @@ hipError_t launch_k1d_index_pool(const uint16_t *iq, const uint16_t *ikc, const 
     return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------
+// K1d over an FP8 index-key cache: bytes ik8[N, Lmax, DI] in the OCP E4M3 encoding
+// and one fp32 scale per token, ksc[N, Lmax]; the score of token t is
+// ksc[t] * (iq . e4m3(ik8[t])).  Half the bytes of the bf16 cache per key.  Each
+// E4M3 value is exact in bf16, so bytes are widened in registers
+// (v_cvt_scalef32_pk_bf16_fp8, scale 1) and the bf16 MFMA of K1d runs unchanged;
+// the token scale multiplies the fp32 dot product before the block max.  The
+// contraction index is relabelled so that a lane's key bytes are contiguous: in
+// MFMA step ks, quarter qt of the wave holds elements 8*KS*qt + 8*ks .. +7 of
+// both operands.
+// ---------------------------------------------------------------------------
+template <int G, int DI>
+__global__ __launch_bounds__(256) void k1d_index_pool_fp8(const uint16_t *__restrict__ iq,
+                                                          const uint8_t *__restrict__ ik8,
+                                                          const float *__restrict__ ksc,
+                                                          const int32_t *__restrict__ seq_len,
+                                                          float *__restrict__ S, int64_t Lmax,
+                                                          int nbp, int sc_aligned) {
+    constexpr int KS = DI / 32;
+    constexpr int SPAN = 8 * KS;          // contiguous key bytes per lane and token
+    const int n = blockIdx.y;
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int b = blockIdx.x * 4 + wave;
+    const int sl = seq_len[n];
+    if (sl < 1 || sl > Lmax) return;
+    const int ncomp = (sl - 1) / kBlock;
+    if (b >= ncomp) return;
+    const int l16 = lane & 15, qt = lane >> 4;
+
+    bf16x8 bq[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        bq[ks] = as_bf16x8(l16 < G ? load16(iq + ((int64_t)n * G + l16) * DI + SPAN * qt + 8 * ks)
+                                   : u32x4{0, 0, 0, 0});
+    const int64_t tok0 = (int64_t)n * Lmax + (int64_t)b * kBlock;
+    const uint8_t *base = ik8 + tok0 * DI + SPAN * qt;
+    // raw[mt][w]: dword w of this lane's SPAN bytes of token mt*16 + l16
+    uint32_t raw[8][SPAN / 4];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+        const uint8_t *p = base + (mt * 16 + l16) * DI;
+        if constexpr (SPAN >= 16) {
+#pragma unroll
+            for (int c = 0; c < SPAN / 16; ++c) {
+                const u32x4 v = load16(p + 16 * c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) raw[mt][4 * c + e] = v[e];
+            }
+        } else {
+            const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
+            raw[mt][0] = v[0];
+            raw[mt][1] = v[1];
+        }
+    }
+    // token scales of this lane's accumulator rows: tokens mt*16 + 4*qt + r
+    const float *sp = ksc + tok0 + 4 * qt;
+    float m = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+        f32x4 acc = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 a;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t w = raw[mt][2 * ks + h];
+                const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+                const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+                a[4 * h + 0] = lo[0];
+                a[4 * h + 1] = lo[1];
+                a[4 * h + 2] = hi[0];
+                a[4 * h + 3] = hi[1];
+            }
+            acc = mfma16(a, bq[ks], acc);
+        }
+        const float *p = sp + mt * 16;
+        const f32x4 sc = sc_aligned ? *reinterpret_cast<const f32x4 *>(p)
+                                    : f32x4{p[0], p[1], p[2], p[3]};
+        m = fmaxf(m, fmaxf(fmaxf(acc[0] * sc[0], acc[1] * sc[1]),
+                           fmaxf(acc[2] * sc[2], acc[3] * sc[3])));
+    }
+    m = fmaxf(m, xor_shfl(m, 16));
+    m = fmaxf(m, xor_shfl(m, 32));
+    if (lane < G) S[((int64_t)n * G + lane) * nbp + b] = m;
+}
+
+template <int G, int DI>
+static hipError_t k1d8_dispatch(const uint16_t *iq, const uint8_t *ik8, const float *ksc,
+                                const int32_t *seq_len, float *S, int N, int64_t Lmax, int nbp,
+                                hipStream_t s) {
+    const int64_t nbmax = (Lmax - 1) / kBlock;
+    if (nbmax <= 0 || N <= 0) return hipSuccess;
+    const int aligned = (Lmax % 4 == 0) && (reinterpret_cast<uintptr_t>(ksc) % 16 == 0);
+    dim3 grid((unsigned)((nbmax + 3) / 4), (unsigned)N);
+    hipLaunchKernelGGL((k1d_index_pool_fp8<G, DI>), grid, dim3(256), 0, s, iq, ik8, ksc, seq_len, S,
+                       Lmax, nbp, aligned);
+    return hipGetLastError();
+}
+
+hipError_t launch_k1d_index_pool_fp8(const uint16_t *iq, const uint8_t *ik8, const float *ksc,
+                                     const int32_t *seq_len, float *S, int N, int64_t Lmax, int G,
+                                     int dI, int nbp, hipStream_t s) {
+#define K1D8_CASE(g, di) \
+    if (G == g && dI == di) return k1d8_dispatch<g, di>(iq, ik8, ksc, seq_len, S, N, Lmax, nbp, s);
+    K1D8_CASE(1, 32) K1D8_CASE(1, 64) K1D8_CASE(1, 128)
+    K1D8_CASE(2, 32) K1D8_CASE(2, 64) K1D8_CASE(2, 128)
+    K1D8_CASE(4, 32) K1D8_CASE(4, 64) K1D8_CASE(4, 128)
+    K1D8_CASE(8, 32) K1D8_CASE(8, 64)
+#undef K1D8_CASE
+    return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Index-key cache writer: per-row power-of-two scale and E4M3 rounding.  For a
+// row x of DI bf16 values: scale = 2^e with e the smallest integer such that
+// max|x| <= 448 * 2^e (e = 0 for a zero row); each byte is the E4M3 value nearest
+// to x / scale (ties to the even code), which the hardware conversion
+// v_cvt_pk_fp8_f32 produces in round-to-nearest-even mode.  DI/8 threads per row,
+// 8 values (16 bytes in, 8 bytes out) per thread.
+// ---------------------------------------------------------------------------
+template <int DI>
+__global__ __launch_bounds__(256) void k_quant_e4m3(const uint16_t *__restrict__ x, int64_t rows,
+                                                    uint8_t *__restrict__ out,
+                                                    float *__restrict__ scale) {
+    constexpr int TPR = DI / 8;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = t / TPR;
+    const int sub = (int)(t % TPR);
+    const bool active = row < rows;
+    float v[8];
+    float amax = 0.0f;
+    if (active) {
+        const u32x4 w = load16(x + row * DI + 8 * sub);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
+            v[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    }
+    // row maximum over the TPR threads of the row (aligned groups of lanes)
+#pragma unroll
+    for (int m = 1; m < TPR; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+    if (!active) return;
+    int e = 0;
+    if (amax > 0.0f) {
+        int ex;
+        const float fr = frexpf(amax / 448.0f, &ex);   // amax/448 = fr * 2^ex, fr in [0.5, 1)
+        e = fr == 0.5f ? ex - 1 : ex;
+    }
+    uint32_t lo = 0, hi = 0;
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[0], -e), ldexpf(v[1], -e), lo, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[2], -e), ldexpf(v[3], -e), lo, true);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4], -e), ldexpf(v[5], -e), hi, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[6], -e), ldexpf(v[7], -e), hi, true);
+    store8(out + row * DI + 8 * sub, u32x2{lo, hi});
+    if (sub == 0) scale[row] = ldexpf(1.0f, e);
+}
+
+hipError_t launch_quant_e4m3(const uint16_t *x, int64_t rows, int dI, uint8_t *out, float *scale,
+                             hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    const int64_t threads = rows * (dI / 8);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (dI == 32) hipLaunchKernelGGL(k_quant_e4m3<32>, grid, dim3(256), 0, s, x, rows, out, scale);
+    else if (dI == 64) hipLaunchKernelGGL(k_quant_e4m3<64>, grid, dim3(256), 0, s, x, rows, out, scale);
+    else if (dI == 128) hipLaunchKernelGGL(k_quant_e4m3<128>, grid, dim3(256), 0, s, x, rows, out, scale);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 }  // namespace msa

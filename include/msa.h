@@ -171,11 +171,40 @@ MSA_API int msa_decode_paged(const uint16_t *q, const uint16_t *idx_q, const uin
                              void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Decode with an FP8 index-key cache [M3.1 kernel list: the index QK of decode
+ * runs on FP8 keys; SERVE: index scoring].  Identical to msa_decode except that
+ * the index keys are stored in the OCP 8-bit floating point E4M3 encoding with one
+ * fp32 scale per token, halving the bytes of the decode index stream:
+ *   idx_k_e4m3  [N, Lmax, dI] uint8 DEVICE  E4M3 bytes
+ *   idx_k_scale [N, Lmax]     fp32 DEVICE   > 0
+ * The index key of token t is idx_k_scale[t] * e4m3(idx_k_e4m3[t, :]) and its
+ * score is idx_k_scale[t] * (idx_q . e4m3(...)), the dot product accumulated in
+ * fp32 from exact bf16 x E4M3 products.  Selection and attention then proceed as
+ * in msa_decode (K/V caches stay bf16).  Workspace: msa_decode_workspace_size.
+ * ------------------------------------------------------------------------- */
+MSA_API int msa_decode_fp8idx(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache,
+                              const uint16_t *v_cache, const uint8_t *idx_k_e4m3,
+                              const float *idx_k_scale, const int32_t *seq_len, int N,
+                              int64_t Lmax, int H, int G, int d, int dI, int B, int kslots,
+                              float scale, uint16_t *out, int32_t *block_ids_out, void *ws,
+                              size_t ws_bytes, void *stream);
+
+/* Index-key cache writer for msa_decode_fp8idx: rows [rows, dI] bf16 (dI in
+ * {32, 64, 128}) -> E4M3 bytes [rows, dI] and scales [rows].  Per row: scale = 2^e
+ * with e the smallest integer such that max|x| <= 448 * 2^e (1 for an all-zero
+ * row); byte = the E4M3 value nearest to x / scale, ties to the even code, sign of
+ * x kept.  Power-of-two scales make every dequantised key exact in bf16.  Input
+ * values must be finite.  Stream-ordered, no workspace. */
+MSA_API int msa_quantize_idx_k_e4m3(const uint16_t *idx_k, int64_t rows, int dI,
+                                    uint8_t *idx_k_e4m3, float *idx_k_scale, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Optional per-kernel timing (measurement support, process-wide, not
  * thread-safe).  While enabled, every kernel stage the entry points above enqueue
  * is bracketed by a pair of hipEvents recorded on the caller's stream; stages are
  * named "k1_index_pool", "k2_select", "k3_schedule" (its four small kernels as
- * one), "k4_kv_outer", "k5_combine", "k1d_index_pool", "k4d_split", "page_check".
+ * one), "k4_kv_outer", "k5_combine", "k1d_index_pool", "k4d_split", "page_check",
+ * "k1d_index_pool_fp8", "quantize_e4m3".
  *   msa_timing_enable(max_launches): start recording (events for up to
  *       max_launches stages are created up front; further stages are not timed).
  *   msa_timing_collect(out, max_entries, n_out): waits for the recorded events

@@ -48,8 +48,12 @@ def load(path: str | None = None):
                                   P, i64, P, P, P]
     lib.oracle_decode_attend.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, i32, f64, P, i64,
                                          P, P]
+    lib.oracle_e4m3_table.argtypes = [P]
+    lib.oracle_decode_fp8idx.argtypes = [P, P, P, P, P, P, P, i64, i32, i32, i32, i32, i32, i32,
+                                         f64, P, i64, P, P, P]
     for f in (lib.oracle_block_scores, lib.oracle_select, lib.oracle_attend,
-              lib.oracle_prefill_rows, lib.oracle_decode, lib.oracle_decode_attend):
+              lib.oracle_prefill_rows, lib.oracle_decode, lib.oracle_decode_attend,
+              lib.oracle_e4m3_table, lib.oracle_decode_fp8idx):
         f.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
@@ -258,3 +262,73 @@ def decode_paged_attend(q, k_pages, v_pages, block_table, seq_len, ids, B, scale
                                vp[pages].reshape(1, Lc, G, d), [int(lens[n])], ids[r:r + 1], B,
                                scale, [0], lib=lib)[0]
     return out
+
+
+# --------------------------------------------------------------------------
+# FP8 (OCP E4M3) index-key cache for decode
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_table(lib=None) -> np.ndarray:
+    """Value of each of the 256 E4M3 bytes (NaN for the two NaN patterns)."""
+    lib = lib or load()
+    out = np.empty(256, np.float64)
+    lib.oracle_e4m3_table(_ptr(out))
+    return out
+
+
+def quantize_e4m3_rows(x, lib=None):
+    """Per-row power-of-two scaling + E4M3 rounding of bf16 rows [..., dI].
+
+    For each row: amax = max |x|; scale = 2^e with e the smallest integer such
+    that amax <= 448 * 2^e (e = 0 for an all-zero row); every element is x / scale
+    (exact) rounded to the nearest E4M3 value, ties to the even code (last bit 0);
+    the sign bit is the sign of x.  Returns (bytes uint8 [..., dI], scale fp32 [...]).
+    """
+    table = e4m3_table(lib)
+    mags = table[:127]                       # codes 0x00..0x7E: 0 .. 448 ascending
+    xv = _u16(x).astype(np.uint32) << 16
+    xf = xv.view(np.float32).astype(np.float64)
+    amax = np.abs(xf).max(axis=-1)
+    e = np.zeros(amax.shape, np.int64)
+    nz = amax > 0
+    # smallest e with amax <= 448 * 2^e
+    m, ex = np.frexp(amax[nz] / E4M3_MAX)    # amax/448 = m * 2^ex, m in [0.5, 1)
+    e[nz] = np.where(m == 0.5, ex - 1, ex)
+    scale = np.ldexp(1.0, e)
+    y = np.abs(xf) / scale[..., None]
+    hi = np.searchsorted(mags, y, side="left").clip(0, 126)   # first value >= y
+    lo = (hi - 1).clip(0, 126)
+    d_hi = mags[hi] - y
+    d_lo = y - mags[lo]
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code |= (np.signbit(xf).astype(np.uint8) << 7)
+    return code, scale.astype(np.float32)
+
+
+def decode_fp8idx(q, iq, k_cache, v_cache, ik8, kscale, seq_len, B, kslots, scale=None,
+                  seqs=None, lib=None):
+    """Decode with an E4M3 index-key cache: (ids, gap, out)."""
+    lib = lib or load()
+    q, iq = _u16(q), _u16(iq)
+    kc, vc = _u16(k_cache), _u16(v_cache)
+    ik8 = np.ascontiguousarray(ik8.cpu().numpy() if hasattr(ik8, "cpu") else ik8, np.uint8)
+    ks = np.ascontiguousarray(kscale.cpu().numpy() if hasattr(kscale, "cpu") else kscale,
+                              np.float32)
+    N, H, d = q.shape
+    G, dI = iq.shape[1], iq.shape[2]
+    Lmax = kc.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    seq_len = np.ascontiguousarray(np.asarray(seq_len, dtype=np.int64))
+    seqs = _rows(seqs, N)
+    n = len(seqs)
+    ids = np.empty((n, G, kslots), np.int32)
+    gap = np.empty((n, G), np.float32)
+    out = np.empty((n, H, d), np.float64)
+    lib.oracle_decode_fp8idx(_ptr(q), _ptr(iq), _ptr(kc), _ptr(vc), _ptr(ik8), _ptr(ks),
+                             _ptr(seq_len), Lmax, H, G, d, dI, B, kslots, float(scale),
+                             _ptr(seqs), n, _ptr(ids), _ptr(gap), _ptr(out))
+    return ids, gap, out

@@ -45,6 +45,8 @@
  *   prefill: q[L,H,d]  k[L,G,d]  v[L,G,d]  iq[L,G,dI]  ik[L,dI]
  *   decode : q[N,H,d]  iq[N,G,dI]  kc[N,Lmax,G,d]  vc[N,Lmax,G,d]
  *            ikc[N,Lmax,dI]  seq_len[N]; the query is the last cached token.
+ *   decode with an FP8 index-key cache: ik8[N,Lmax,dI] E4M3 bytes plus
+ *            kscale[N,Lmax] fp32 (key = scale * value), in place of ikc.
  * Rows are processed in parallel with OpenMP; each row is independent.
  */
 #include <math.h>
@@ -85,6 +87,51 @@ static void row_block_scores(const uint16_t *iq_row, const uint16_t *ik,
                 double s = 0.0;
                 for (int c = 0; c < dI; ++c)
                     s += bf16_to_double(qv[c]) * bf16_to_double(kv[c]);
+                if (s > best) best = s;
+            }
+            S_out[(int64_t)g * nb + b] = (float)best;   /* one rounding to fp32 */
+        }
+    }
+}
+
+/* ---- step 1 + 2 over an FP8 index-key cache (decode variant) -------------
+ * Index keys held as OCP 8-bit floating point E4M3 bytes with one positive fp32
+ * scale per token: key t is scale[t] * e4m3(ik8[t*dI + c]).  E4M3 (OCP 8-bit
+ * floating point specification, "OFP8"): 1 sign bit, 4 exponent bits with bias 7,
+ * 3 mantissa bits; exponent field 0 holds subnormals (m/8) * 2^-6; the patterns
+ * S.1111.111 are NaN; there are no infinities; the largest finite value is 448. */
+static double e4m3_to_double(uint8_t x)
+{
+    int sgn = x >> 7, e = (x >> 3) & 15, m = x & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m / 8.0, -6);
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sgn ? -v : v;
+}
+
+static void row_block_scores_fp8(const uint16_t *iq_row, const uint8_t *ik8,
+                                 const float *kscale, int64_t i, int64_t L, int G, int dI,
+                                 int B, float *S_out)
+{
+    int64_t nb = (L + B - 1) / B;
+    int64_t bi = i / B;
+    for (int g = 0; g < G; ++g) {
+        const uint16_t *qv = iq_row + (int64_t)g * dI;
+        for (int64_t b = 0; b < nb; ++b) {
+            if (b > bi) {
+                S_out[(int64_t)g * nb + b] = -INFINITY;
+                continue;
+            }
+            double best = -INFINITY;
+            int64_t t_end = (b + 1) * B;
+            if (t_end > i + 1) t_end = i + 1;            /* causal window t <= i */
+            for (int64_t t = b * B; t < t_end; ++t) {
+                const uint8_t *kv = ik8 + t * dI;
+                double s = 0.0;
+                for (int c = 0; c < dI; ++c)
+                    s += bf16_to_double(qv[c]) * e4m3_to_double(kv[c]);
+                s *= (double)kscale[t];                  /* the token's scale */
                 if (s > best) best = s;
             }
             S_out[(int64_t)g * nb + b] = (float)best;   /* one rounding to fp32 */
@@ -286,6 +333,37 @@ void oracle_decode_attend(const uint16_t *q, const uint16_t *kc, const uint16_t 
         int64_t Ln = seq_len[n];
         row_attend(q + n * H * d, kc + n * Lmax * G * d, vc + n * Lmax * G * d, ids + r * G * k,
                    Ln - 1, Ln, H, G, d, B, k, scale, out + r * H * d);
+    }
+}
+
+/* The value of every E4M3 byte (index = the byte), NaN for the NaN patterns. */
+void oracle_e4m3_table(double *out)
+{
+    for (int x = 0; x < 256; ++x) out[x] = e4m3_to_double((uint8_t)x);
+}
+
+/* Decode with an FP8 index-key cache: ik8[N,Lmax,dI] E4M3 bytes and
+ * kscale[N,Lmax] fp32; everything else as oracle_decode. */
+void oracle_decode_fp8idx(const uint16_t *q, const uint16_t *iq, const uint16_t *kc,
+                          const uint16_t *vc, const uint8_t *ik8, const float *kscale,
+                          const int64_t *seq_len, int64_t Lmax, int H, int G, int d, int dI,
+                          int B, int k, double scale, const int64_t *seqs, int64_t nseqs,
+                          int32_t *ids, float *gap, double *out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nseqs; ++r) {
+        int64_t n = seqs[r];
+        int64_t Ln = seq_len[n];
+        int64_t i = Ln - 1;
+        int64_t nb = (Ln + B - 1) / B;
+        float *S = (float *)malloc(sizeof(float) * (size_t)(G * nb));
+        row_block_scores_fp8(iq + n * G * dI, ik8 + n * Lmax * dI, kscale + n * Lmax, i, Ln, G,
+                             dI, B, S);
+        for (int g = 0; g < G; ++g)
+            select_one(S + g * nb, i / B, k, ids + (r * G + g) * k, gap + r * G + g);
+        row_attend(q + n * H * d, kc + n * Lmax * G * d, vc + n * Lmax * G * d, ids + r * G * k,
+                   i, Ln, H, G, d, B, k, scale, out + r * H * d);
+        free(S);
     }
 }
 

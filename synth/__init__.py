@@ -66,7 +66,7 @@ class DecodeShape:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "prefill" | "decode" | "decode_paged"
+    kind: str                 # "prefill" | "decode" | "decode_paged" | "decode_fp8idx"
     shape: object
     plant: str = "lit"
     n_plant: int = 4
@@ -76,7 +76,8 @@ class Workload:
 
 # The five workloads: shapes of the pages' research model (64 query heads,
 # 4 KV heads, B = 128, k = 16) with head/index dims 128, plus the tiny case; and
-# the decode workload again with its caches in shuffled 128-token pages.
+# the decode workload again, with its caches in shuffled 128-token pages, and with
+# its index-key cache held as E4M3 bytes plus per-token scales.
 WORKLOADS = {
     "tiny_prefill_L4096": Workload("tiny_prefill_L4096", "prefill",
                                    PrefillShape(L=4096, H=8, G=2, d=64, dI=32, B=128, k=4)),
@@ -92,6 +93,9 @@ WORKLOADS = {
     "decode_paged_N64_L262144": Workload("decode_paged_N64_L262144", "decode_paged",
                                          DecodeShape(N=64, Lc=262144, H=64, G=4, d=128,
                                                      dI=128)),
+    "decode_fp8idx_N64_L262144": Workload("decode_fp8idx_N64_L262144", "decode_fp8idx",
+                                          DecodeShape(N=64, Lc=262144, H=64, G=4, d=128,
+                                                      dI=128)),
 }
 
 

@@ -33,7 +33,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for want in ("msa_select_blocks", "msa_sparse_attn", "msa_prefill", "msa_decode",
-                 "msa_decode_paged", "msa_select_blocks_workspace_size",
+                 "msa_decode_paged", "msa_decode_fp8idx", "msa_quantize_idx_k_e4m3",
+                 "msa_select_blocks_workspace_size",
                  "msa_sparse_attn_workspace_size", "msa_prefill_workspace_size",
                  "msa_decode_workspace_size", "msa_decode_paged_workspace_size",
                  "msa_status_string"):
@@ -157,3 +158,26 @@ def test_paged_decode_arguments(lib):
     assert call(maxb=1 << 24) == UNSUPPORTED  # max_blocks * 128 must fit in int32
     assert call(nbytes=ctypes.c_size_t(64)) == WS_SMALL
     assert call(ws_=P(0x100010)) == WS_SMALL
+
+
+def test_fp8_decode_and_quantizer_arguments(lib):
+    f, ws, big, s = _fake(), P(0x100000), ctypes.c_size_t(1 << 40), None
+    zero = ctypes.c_float(0)
+
+    def call(q=f, ik8=f, sc=f, N=2, Lmax=1024, H=8, G=2, d=64, dI=32, B=128, k=4, nbytes=big):
+        return lib.msa_decode_fp8idx(q, f, f, f, ik8, sc, f, N, Lmax, H, G, d, dI, B, k, zero, f,
+                                     None, ws, nbytes, s)
+
+    assert call(N=0, q=None, ik8=None, sc=None) == OK
+    assert call(ik8=None) == INVALID
+    assert call(sc=None) == INVALID
+    assert call(Lmax=0) == INVALID
+    assert call(B=64) == UNSUPPORTED
+    assert call(dI=48) == UNSUPPORTED
+    assert call(nbytes=ctypes.c_size_t(16)) == WS_SMALL
+    # cache writer
+    assert lib.msa_quantize_idx_k_e4m3(None, 0, 128, None, None, s) == OK
+    assert lib.msa_quantize_idx_k_e4m3(None, 10, 128, f, f, s) == INVALID
+    assert lib.msa_quantize_idx_k_e4m3(f, 10, 128, f, None, s) == INVALID
+    assert lib.msa_quantize_idx_k_e4m3(f, -1, 128, f, f, s) == INVALID
+    assert lib.msa_quantize_idx_k_e4m3(f, 10, 96, f, f, s) == UNSUPPORTED

@@ -392,9 +392,90 @@ def check_paged_decode(lib):
     assert valid4[0]
 
 
+# --------------------------------------------------------------------------
+# 11. FP8 index-key cache.  E4M3 is the OCP 8-bit floating point encoding; the
+#     library routine torch.float8_e4m3fn implements the same encoding, so it
+#     pins the oracle's byte decoding (all 256 bytes) and its round-to-nearest-
+#     even quantizer (random rows over a wide range of magnitudes, every midpoint
+#     between neighbouring values).  With power-of-two scales the dequantised keys
+#     are exact in bf16, so FP8 decode must equal bf16 decode on them; a scale
+#     other than a power of two multiplies the token's score.
+# --------------------------------------------------------------------------
+def _e4m3_ref(x):
+    return torch.as_tensor(x, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def check_e4m3(lib):
+    table = oracle.e4m3_table(lib)
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(table), np.isnan(ref))
+    assert np.array_equal(table[~np.isnan(table)], ref[~np.isnan(ref)])
+    rng = np.random.default_rng(3)
+    x = torch.tensor(rng.standard_normal((300, 64)) * np.exp(rng.uniform(-25, 25, (300, 1))),
+                     dtype=torch.float32).to(torch.bfloat16)
+    x[0] = 0
+    x[1] = x[1] / x[1].abs().max().float().item() * 100
+    x[1, 7] = -448 * 2.0 ** 5            # amax exactly 448 * 2^5 -> scale 2^5
+    codes, sc = oracle.quantize_e4m3_rows(x, lib)
+    xf = x.double().numpy()
+    amax = np.abs(xf).max(axis=1)
+    assert sc[0] == 1.0 and sc[1] == 32.0
+    assert (amax <= 448.0 * sc).all() and (amax[2:] > 224.0 * sc[2:]).all()
+    assert np.all(np.log2(sc) == np.round(np.log2(sc)))
+    assert np.array_equal(codes, _e4m3_ref(xf / sc[:, None]))
+    mags = table[:127]
+    mid = (mags[:-1] + mags[1:]) / 2
+    rows = np.zeros((2 * len(mid), 2))
+    rows[:, 0] = np.concatenate([mid, -mid])
+    rows[:, 1] = 448.0
+    codes2, sc2 = oracle.quantize_e4m3_rows(_bf16(rows), lib)
+    assert (sc2 == 1.0).all()
+    assert np.array_equal(codes2, _e4m3_ref(rows))
+
+
+def check_fp8_decode(lib):
+    B, k = 16, 4
+    sh = synth.DecodeShape(N=4, Lc=200, H=4, G=2, d=16, dI=8, B=B, k=k)
+    seq_len = np.array([200, 1, 97, 150], np.int64)
+    x = synth.decode_inputs(sh, seed=23, seq_len=seq_len)
+    # token magnitudes spread over 2^-6 .. 2^6 so the per-token scales differ
+    rng = np.random.default_rng(23)
+    mag = torch.tensor(np.exp2(rng.integers(-6, 7, (sh.N, sh.Lc, 1))), dtype=torch.float32)
+    ikx = (x["ik_cache"].float() * mag).to(torch.bfloat16)
+    codes, sc = oracle.quantize_e4m3_rows(ikx, lib)
+    assert len(np.unique(sc)) > 5
+    table = oracle.e4m3_table(lib)
+    deq = _bf16(table[codes] * sc[..., None])
+    assert np.array_equal(deq.double().numpy(), table[codes] * sc[..., None])   # exact in bf16
+    scale = 1.0 / math.sqrt(sh.d)
+    ids8, gap8, out8 = oracle.decode_fp8idx(x["q"], x["iq"], x["k_cache"], x["v_cache"], codes,
+                                            sc, seq_len, B, k, scale, lib=lib)
+    ids, gap, out = oracle.decode(x["q"], x["iq"], x["k_cache"], x["v_cache"], deq, seq_len, B,
+                                  k, scale, lib=lib)
+    assert np.array_equal(ids8, ids) and np.array_equal(out8, out)
+    np.testing.assert_array_equal(gap8, gap)
+    # a non-power-of-two scale multiplies the score: two blocks holding the same
+    # bytes, the one with the larger scale wins (the query's dot product is > 0)
+    N1, L1, dI = 1, 5 * B, 8
+    q1 = torch.zeros((1, 2, 4), dtype=torch.bfloat16)
+    iq1 = _bf16(np.ones((1, 1, dI)))
+    kv1 = torch.zeros((1, L1, 1, 4), dtype=torch.bfloat16)
+    ik8 = np.full((1, L1, dI), 0x30, np.uint8)          # e4m3 0x30 = 1.0
+    ks = np.ones((1, L1), np.float32)
+    ks[0, 1 * B:2 * B] = 1.25
+    ks[0, 3 * B:4 * B] = 1.5
+    ids1, _, _ = oracle.decode_fp8idx(q1, iq1, kv1, kv1, ik8, ks, [L1], B, 2, 1.0, lib=lib)
+    assert list(ids1[0, 0]) == [3, 4]
+    ks[0, 3 * B + 7] = 0.5                                 # max over the block still 1.5
+    ks[0, 1 * B + 9] = 1.75
+    ids2, _, _ = oracle.decode_fp8idx(q1, iq1, kv1, kv1, ik8, ks, [L1], B, 2, 1.0, lib=lib)
+    assert list(ids2[0, 0]) == [1, 4]
+
+
 PINS = [check_dense_equivalence, check_local_only, check_masked_attention, check_exp_free,
         check_constructed, check_tie_break, check_brute_force, check_invariants,
-        check_properties, check_prefix_and_decode, check_paged_decode]
+        check_properties, check_prefix_and_decode, check_paged_decode, check_e4m3,
+        check_fp8_decode]
 
 
 @pytest.mark.parametrize("check", PINS, ids=[c.__name__ for c in PINS])
@@ -403,7 +484,7 @@ def test_pin(check):
 
 
 # --------------------------------------------------------------------------
-# 11. Mutation test: plausible mistakes planted in copies of the oracle source
+# 12. Mutation test: plausible mistakes planted in copies of the oracle source
 #     (on the CPU) must each fail at least one of the pins above.
 # --------------------------------------------------------------------------
 MUTANTS = {
@@ -429,6 +510,12 @@ MUTANTS = {
                           "const uint16_t *kt = kk + (tok[u] * G) * d;"),
     "no_max_subtraction_sign": ("z[u] = exp(z[u] - m);", "z[u] = exp(m - z[u]);"),
     "blocks_after_query_compete": ("int64_t ncand = bi;", "int64_t ncand = bi + 1;"),
+    "e4m3_exponent_bias": ("else v = ldexp(1.0 + (double)m / 8.0, e - 7);",
+                           "else v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "e4m3_subnormal_scale": ("if (e == 0) v = ldexp((double)m / 8.0, -6);",
+                             "if (e == 0) v = ldexp((double)m / 8.0, -7);"),
+    "fp8_token_scale_ignored": ("s *= (double)kscale[t];", "s *= 1.0;"),
+    "fp8_scale_of_wrong_token": ("s *= (double)kscale[t];", "s *= (double)kscale[b * B];"),
 }
 
 
@@ -454,3 +541,15 @@ def test_mutant_is_caught(name, tmp_path):
         except Exception as e:  # a crash of the mutant also counts as caught
             caught.append(f"{check.__name__}:{type(e).__name__}")
     assert caught, f"mutant {name} passed every pin"
+
+
+def test_torch_e4m3_route_matches_oracle_quantizer():
+    """The torch route (frexp + float8_e4m3fn cast) that prepares full-size FP8
+    caches on the GPU in the parity tests gives the oracle quantizer's bytes."""
+    rng = np.random.default_rng(11)
+    x = torch.tensor(rng.standard_normal((3000, 128)) * np.exp(rng.uniform(-30, 30, (3000, 1))),
+                     dtype=torch.float32).to(torch.bfloat16)
+    x[0] = 0
+    c1, s1 = oracle.quantize_e4m3_rows(x)
+    c2, s2 = _refs.e4m3_rows_torch(x)
+    assert np.array_equal(c1, c2.numpy()) and np.array_equal(s1, s2.numpy())

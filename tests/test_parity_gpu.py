@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import synth
-from tests import _parity
+from tests import _parity, _refs
 
 pytestmark = pytest.mark.gpu
 
@@ -353,6 +353,126 @@ def test_paged_decode_full_size():
     shape = wl.shape
     _paged_check(shape, np.full(shape.N, shape.Lc), seed=0, seqs=np.array([0, 21, 42, 63]),
                  device=DEV, extra_pages=0)
+
+
+# --------------------------- FP8 index-key cache -----------------------------
+@pytest.mark.parametrize("dI", [32, 64, 128])
+def test_quantize_e4m3_vs_oracle(dI):
+    """The library's cache writer gives the oracle quantizer's bytes and scales:
+    rows over a wide range of magnitudes, an all-zero row, a row whose maximum is
+    exactly 448 * 2^3, and rows holding every midpoint between E4M3 neighbours."""
+    msa = _msa()
+    rng = np.random.default_rng(dI)
+    x = torch.tensor(rng.standard_normal((4099, dI)) * np.exp(rng.uniform(-30, 30, (4099, 1))),
+                     dtype=torch.float32).to(torch.bfloat16)
+    x[0] = 0
+    x[1] = 0
+    x[1, 3] = -448.0 * 8
+    x[1, 4] = 17.0
+    mags = oracle.e4m3_table()[:127]
+    mid = torch.tensor(np.concatenate([(mags[:-1] + mags[1:]) / 2, -(mags[:-1] + mags[1:]) / 2]),
+                       dtype=torch.float32)
+    rows = torch.zeros((len(mid), dI))
+    rows[:, 0] = mid
+    rows[:, 1] = 448.0
+    x = torch.cat([x, rows.to(torch.bfloat16)])
+    _say(f"quantize e4m3 rows={x.shape[0]} dI={dI}")
+    codes, sc = msa.quantize_idx_k_e4m3(x.to(DEV))
+    torch.cuda.synchronize()
+    oc, osc = oracle.quantize_e4m3_rows(x)
+    bad = (codes.cpu().numpy() != oc).any(axis=1)
+    _say(f"  -> rows with differing bytes {int(bad.sum())}, scales equal "
+         f"{np.array_equal(sc.cpu().numpy(), osc)}")
+    assert not bad.any()
+    assert np.array_equal(sc.cpu().numpy(), osc)
+
+
+def _fp8_decode_check(shape, seq_len, seed, seqs=None, device="cpu", spread=False,
+                      scale_factor=1.0):
+    """msa.decode_fp8idx vs oracle.decode_fp8idx.  The E4M3 cache is written by the
+    oracle quantizer (CPU inputs) or by the torch route (inputs on the GPU); with
+    `spread` each token's keys are first scaled by a random power of two, and
+    `scale_factor` multiplies every stored scale (scales need not be powers of two)."""
+    msa = _msa()
+    _say(f"fp8 decode N={shape.N} Lmax={shape.Lc} seq_len[:8]={list(seq_len[:8])} seed={seed} "
+         f"spread={spread} scale_factor={scale_factor}")
+    seq_len = np.asarray(seq_len, np.int64)
+    x = synth.decode_inputs(shape, seed=seed, seq_len=np.clip(seq_len, 1, shape.Lc), device=device)
+    ik = x["ik_cache"]
+    if spread:
+        rng = np.random.default_rng(seed)
+        mag = torch.tensor(np.exp2(rng.integers(-8, 9, (shape.N, shape.Lc, 1))),
+                           dtype=torch.float32, device=ik.device)
+        ik = (ik.float() * mag).to(torch.bfloat16)
+    if device == "cpu":
+        c, sc = oracle.quantize_e4m3_rows(ik)
+        codes, ksc = torch.from_numpy(c), torch.from_numpy(sc)
+    else:
+        codes, ksc = _refs.e4m3_rows_torch(ik)
+        # the torch route agrees with the oracle quantizer on a sample of rows
+        rows = torch.randint(0, shape.Lc, (512,), generator=torch.Generator().manual_seed(seed))
+        oc, osc = oracle.quantize_e4m3_rows(ik[0, rows.to(ik.device)].cpu())
+        assert np.array_equal(codes[0, rows.to(ik.device)].cpu().numpy(), oc)
+    del ik
+    ksc = ksc * scale_factor
+    sl = torch.tensor(seq_len.astype(np.int32), device=DEV)
+    g = {n: x[n].to(DEV) for n in ("q", "iq", "k_cache", "v_cache", "ik_cache")}
+    out, ids = msa.decode_fp8idx(g["q"], g["iq"], g["k_cache"], g["v_cache"], codes.to(DEV),
+                                 ksc.to(DEV), sl, kslots=shape.k, return_ids=True)
+    out_b, ids_b = msa.decode(g["q"], g["iq"], g["k_cache"], g["v_cache"], g["ik_cache"], sl,
+                              kslots=shape.k, return_ids=True)
+    torch.cuda.synchronize()
+    valid = (seq_len >= 1) & (seq_len <= shape.Lc)
+    same = (ids == ids_b).all(dim=-1).cpu().numpy()[valid]
+    out = out.float().cpu().numpy()
+    ids = ids.cpu().numpy()
+    if seqs is None:
+        seqs = np.nonzero(valid)[0]
+    scale = 1.0 / math.sqrt(shape.d)
+    sub = torch.as_tensor(seqs)
+    kc, vc = x["k_cache"][sub.to(x["k_cache"].device)].cpu(), x["v_cache"][sub.to(x["k_cache"].device)].cpu()
+    lens = np.clip(seq_len[seqs], 1, shape.Lc)
+    oids, gap, oout = oracle.decode_fp8idx(x["q"][sub.to(x["q"].device)], x["iq"][sub.to(x["q"].device)],
+                                           kc, vc, codes[sub.to(codes.device)].cpu(),
+                                           ksc[sub.to(ksc.device)].cpu(), lens, 128, shape.k, scale)
+    pos = lens - 1
+    _parity.check_selection_valid(ids[seqs], pos, shape.k)
+    tie, nmis = _parity.compare_ids(ids[seqs], oids, gap)
+    ref = oout.copy()
+    if tie.any():
+        tr = np.nonzero(tie.any(axis=1))[0]
+        ref[tr] = oracle.decode_attend(x["q"][sub.to(x["q"].device)], kc, vc, lens, ids[seqs[tr]],
+                                       128, scale, tr)
+    mx, mean = _parity.compare_out(out[seqs], ref)
+    _say(f"  -> near_ties {int(tie.sum())} mismatches {nmis} max {mx:.3e} mean {mean:.3e}; "
+         f"(seq, group) selections equal to the bf16 cache's: {same.mean():.4f}")
+    assert nmis == 0
+    assert mx < _parity.MAX_ABS and mean < _parity.MEAN_ABS
+    for n in np.nonzero(~valid)[0]:
+        assert (ids[n] == -1).all() and (out[n] == 0).all()
+
+
+def test_fp8_decode_small_ragged():
+    shape = synth.DecodeShape(N=8, Lc=2000, H=64, G=4, d=128, dI=128, B=128, k=16)
+    _fp8_decode_check(shape, np.array([1, 127, 128, 129, 2000, 1500, 0, 2001]), seed=6)
+
+
+def test_fp8_decode_spread_scales():
+    shape = synth.DecodeShape(N=6, Lc=4093, H=16, G=4, d=128, dI=64, B=128, k=8)
+    _fp8_decode_check(shape, np.array([4093, 3000, 129, 640, 1, 2222]), seed=7, spread=True,
+                      scale_factor=1.37)
+
+
+def test_fp8_decode_tiny_dims():
+    shape = synth.DecodeShape(N=5, Lc=4096, H=8, G=2, d=64, dI=32, B=128, k=4)
+    _fp8_decode_check(shape, np.array([4096, 3000, 129, 640, 1]), seed=8, spread=True)
+
+
+def test_fp8_decode_full_size_subset():
+    """64 sequences x 262144 cached tokens with an E4M3 index-key cache; oracle on 4."""
+    shape = synth.WORKLOADS["decode_N64_L262144"].shape
+    _fp8_decode_check(shape, np.full(shape.N, shape.Lc), seed=0, seqs=np.array([0, 21, 42, 63]),
+                      device=DEV)
 
 
 def test_chunked_workspace_invariance():
