@@ -101,6 +101,17 @@ def decode_work(N, Lc, H, G, d, dI, k, B=B_BLOCK, paged=False, fp8idx=False):
     }
 
 
+def _add_work(a, b):
+    """Sum of two prefill_work records (work of a batch of sequences)."""
+    out = {}
+    for key, val in a.items():
+        if isinstance(val, dict):
+            out[key] = {k_: val[k_] + b[key][k_] for k_ in val}
+        else:
+            out[key] = val + b[key]
+    return out
+
+
 # --------------------------------------------------------------------------
 def _sample_rows(L, n, seed=0):
     rng = np.random.default_rng(seed)
@@ -322,6 +333,30 @@ def main():
         def step():
             msa.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], kslots=s.k, out=out,
                         ids_out=ids, workspace=ws, return_ids=True)
+    elif wl.kind == "prefill_varlen":
+        parts = [synth.prefill_inputs(s, seed=args.seed + b, plant=wl.plant, n_plant=wl.n_plant,
+                                      c=wl.c, device=dev) for b in range(wl.batch)]
+        x = {n: torch.cat([p_[n] for p_ in parts]) for n in ("q", "k", "v", "iq", "ik")}
+        del parts
+        T = wl.batch * s.L
+        out = torch.empty_like(x["q"])
+        ids = torch.empty((T, s.G, s.k), dtype=torch.int32, device=dev)
+        ws = msa._workspace(msa.workspace_size("prefill", L=s.L, H=s.H, G=s.G, d=s.d, dI=s.dI,
+                                               k=s.k), dev)
+        if wl.chunk:       # one sequence, `chunk` new tokens per call over the cached prefix
+            calls = []
+            for P in range(0, s.L, wl.chunk):
+                C = min(wl.chunk, s.L - P)
+                calls.append((x["q"][P:P + C], x["iq"][P:P + C], x["k"][:P + C], x["v"][:P + C],
+                              x["ik"][:P + C], [0, C], [0, P + C], out[P:P + C], ids[P:P + C]))
+        else:              # the whole batch in one call
+            cu = [b * s.L for b in range(wl.batch + 1)]
+            calls = [(x["q"], x["iq"], x["k"], x["v"], x["ik"], cu, cu, out, ids)]
+
+        def step():
+            for qq, iqq, kk, vv, ikk, cq, ckv, oo, ii in calls:
+                msa.prefill_varlen(qq, kk, vv, iqq, ikk, cq, ckv, kslots=s.k, out=oo, ids_out=ii,
+                                   workspace=ws, return_ids=True)
     elif wl.kind == "decode":
         x = synth.decode_inputs(s, seed=args.seed, device=dev)
         seq_len = torch.tensor(np.asarray(x["seq_len"], np.int32), device=dev)
@@ -398,19 +433,24 @@ def main():
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "ms_per_step": ms_per_step, "scaling": "weak", "vs_baseline": None,
               "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, planted blocks)"}
-    if wl.kind == "prefill":
-        counts = None
-        idn = ids.cpu().numpy()
-        valid = idn >= 0
-        g_idx = np.broadcast_to(np.arange(s.G)[None, :, None], idn.shape)
-        counts = np.bincount((g_idx[valid] * ((s.L + 127) // 128) + idn[valid]).ravel(),
-                             minlength=s.G * ((s.L + 127) // 128))
-        work = prefill_work(s.L, s.H, s.G, s.d, s.dI, s.k, list_counts=counts)
-        result.update({"value": s.L / (ms_per_step / 1e3), "unit": "tokens/s",
+    if wl.kind in ("prefill", "prefill_varlen"):
+        nseq = wl.batch
+        idn = ids.cpu().numpy().reshape(nseq, s.L, s.G, s.k)
+        work = None
+        for b in range(nseq):
+            valid = idn[b] >= 0
+            g_idx = np.broadcast_to(np.arange(s.G)[None, :, None], idn[b].shape)
+            counts = np.bincount((g_idx[valid] * ((s.L + 127) // 128) + idn[b][valid]).ravel(),
+                                 minlength=s.G * ((s.L + 127) // 128))
+            w_b = prefill_work(s.L, s.H, s.G, s.d, s.dI, s.k, list_counts=counts)
+            work = w_b if work is None else _add_work(work, w_b)
+        result.update({"value": nseq * s.L / (ms_per_step / 1e3), "unit": "tokens/s",
                        "higher_is_better": True})
         result["config"] = {"workload": wl.name, "L": s.L, "H": s.H, "G": s.G, "d": s.d,
                             "dI": s.dI, "B": s.B, "k": s.k, "planting": wl.plant,
                             "query_chunk": min(-(-s.L // 128) * 128, 131072)}
+        if wl.kind == "prefill_varlen":
+            result["config"].update({"sequences": nseq, "new_tokens_per_call": wl.chunk or s.L})
         result["step_mfma_frac"] = work["f_total"] / (ms_per_step / 1e3) / PEAK_BF16_FLOPS
         result["algorithmic_flops_per_step"] = work["f_total"]
         result["dense_gqa_flops_per_step"] = work["dense_gqa_flops"]
@@ -456,8 +496,10 @@ def main():
     # ---- CPU oracle baseline (rank 0, N=1) ------------------------------------
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        if wl.kind == "prefill":
-            result["cpu_baseline"] = cpu_baseline_prefill(x, s, args.cpu_seconds)
+        if wl.kind in ("prefill", "prefill_varlen"):
+            # rows of the first sequence (every sequence has the same shape)
+            x0 = {n: x[n][:s.L] for n in ("q", "k", "v", "iq", "ik")}
+            result["cpu_baseline"] = cpu_baseline_prefill(x0, s, args.cpu_seconds)
         elif wl.kind in ("decode", "decode_fp8idx"):
             result["cpu_baseline"] = cpu_baseline_decode(x, s, args.cpu_seconds)
         else:

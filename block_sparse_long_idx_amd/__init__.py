@@ -15,7 +15,8 @@ import os
 
 import torch
 
-__all__ = ["MSAError", "select_blocks", "sparse_attn", "prefill", "decode", "decode_paged",
+__all__ = ["MSAError", "select_blocks", "sparse_attn", "prefill", "prefill_varlen", "decode",
+           "decode_paged",
            "decode_fp8idx", "quantize_idx_k_e4m3", "workspace_size",
            "library_path", "load_library", "timing_enable", "timing_collect", "timing_disable"]
 
@@ -97,6 +98,9 @@ def load_library():
     lib.msa_decode_paged.argtypes = [P, P, P, P, P, i64, P, i32, P, i32, i32, i32, i32, i32, i32,
                                      i32, f32, P, P, P, sz, P]
     lib.msa_decode_paged.restype = i32
+    lib.msa_prefill_varlen.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                       f32, P, P, P, sz, P]
+    lib.msa_prefill_varlen.restype = i32
     lib.msa_decode_fp8idx.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, i32, i32,
                                       f32, P, P, P, sz, P]
     lib.msa_decode_fp8idx.restype = i32
@@ -358,4 +362,45 @@ def decode_fp8idx(q, idx_q, k_cache, v_cache, idx_k_e4m3, idx_k_scale, seq_len, 
                                d, dI, B, kslots, _scale(scale, d), _ptr(out), _ptr(ids_out),
                                _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "msa_decode_fp8idx")
+    return (out, ids_out) if return_ids else out
+
+
+def prefill_varlen(q, k, v, idx_q, idx_k, cu_q, cu_kv, kslots: int = 16, B: int = 128, scale=None,
+                   return_ids: bool = False, out=None, ids_out=None, workspace=None):
+    """Packed batch of causal sequences, each possibly continuing a cached prefix.
+
+    q [sum C, H, d], idx_q [sum C, G, dI] hold the new tokens; k, v [sum L, G, d] and
+    idx_k [sum L, dI] hold every token (prefix + new).  cu_q / cu_kv: offsets (host
+    sequences of ints, nseq + 1 each).  Sequence s's prefix length L - C must be a
+    multiple of 128.
+    """
+    import numpy as np
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    for name, t, nd in (("k", k, 3), ("v", v, 3), ("idx_q", idx_q, 3), ("idx_k", idx_k, 2)):
+        _need(t, name, torch.bfloat16, nd, dev)
+    cq = np.ascontiguousarray(np.asarray(cu_q, dtype=np.int64))
+    ckv = np.ascontiguousarray(np.asarray(cu_kv, dtype=np.int64))
+    nseq = len(cq) - 1
+    if nseq < 0 or len(ckv) != nseq + 1:
+        raise MSAError("cu_q and cu_kv must hold nseq + 1 offsets each")
+    Tq, H, d = q.shape
+    G, dI = idx_q.shape[1], idx_q.shape[2]
+    Tkv = k.shape[0]
+    if (idx_q.shape[0] != Tq or k.shape != (Tkv, G, d) or v.shape != (Tkv, G, d)
+            or idx_k.shape != (Tkv, dI) or (nseq > 0 and (cq[-1] > Tq or ckv[-1] > Tkv))):
+        raise MSAError("inconsistent shapes for varlen prefill inputs")
+    if out is None:
+        out = torch.empty_like(q)
+    if return_ids and ids_out is None:
+        ids_out = torch.empty((Tq, G, kslots), dtype=torch.int32, device=dev)
+    max_L = int((ckv[1:] - ckv[:-1]).max()) if nseq > 0 else 0
+    nbytes = lib.msa_prefill_workspace_size(max(max_L, 1), H, G, d, dI, B, kslots)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    st = lib.msa_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(idx_q), _ptr(idx_k),
+                                cq.ctypes.data, ckv.ctypes.data, nseq, H, G, d, dI, B, kslots,
+                                _scale(scale, d), _ptr(out), _ptr(ids_out), _ptr(ws), ws.numel(),
+                                _stream(dev))
+    _check(st, "msa_prefill_varlen")
     return (out, ids_out) if return_ids else out

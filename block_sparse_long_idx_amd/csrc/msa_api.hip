@@ -255,6 +255,50 @@ size_t msa_prefill_workspace_size(int64_t L, int H, int G, int d, int dI, int B,
     return prefill_bytes(chunk_of(L), L, H, G, d, k);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Queries [P, L) of one causal sequence of L tokens (P a multiple of the chunk
+// granularity): K1..K5 per query chunk.  q, idx_q, out and ids are addressed by
+// absolute position (row i of the sequence at q + i*H*d); only rows >= P are
+// ever dereferenced, so a caller that holds the new rows only passes pointers
+// shifted back by P rows.  ids == nullptr: ids live in the workspace.
+int prefill_range(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *idx_q,
+                  const uint16_t *idx_k, int64_t L, int64_t P, int H, int G, int d, int dI,
+                  int kslots, float scale, uint16_t *out, int32_t *ids, void *ws, size_t ws_bytes,
+                  hipStream_t s) {
+    const int64_t C = fit_chunk(L, ws_bytes,
+                                [&](int64_t c) { return prefill_bytes(c, L, H, G, d, kslots); });
+    if (C == 0) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    const int nbp = nb_padded(L);
+    Carver c(ws);
+    float *S = c.take<float>(C * G * nbp);
+    int32_t *ids_ws = c.take<int32_t>(C * G * kslots);
+    const AttnWs w = carve_attn(c, C, H, G, d, kslots, (int)nblocks(L));
+    for (int64_t q0 = P; q0 < L; q0 += C) {
+        const int64_t qend = std::min(L, q0 + C);
+        int32_t *ids_c = ids ? ids + q0 * G * kslots : ids_ws;
+        MSA_TIMED(kK1, launch_k1_index_pool(idx_q, idx_k, S, L, q0, qend, G, dI, nbp, s));
+        MSA_TIMED(kK2, launch_k2_select(S, nbp, (qend - q0) * G, G, kslots, q0, nullptr, 0, ids_c, s));
+        const int rc = attn_chunk(q, k, v, ids_c, L, q0, qend, H, G, d, kslots, scale, out, w, s);
+        if (rc != MSA_OK) return rc;
+    }
+    return MSA_OK;
+}
+
+// Address of row -rows (rows may be negative) of a row-major array starting at p;
+// prefill_range never dereferences it below p.
+template <typename T>
+T *rows_back(T *p, int64_t rows, int64_t row_elems) {
+    const intptr_t bytes = (intptr_t)(rows * row_elems) * (intptr_t)sizeof(T);
+    return reinterpret_cast<T *>(reinterpret_cast<intptr_t>(p) - bytes);
+}
+
+}  // namespace
+
+extern "C" {
+
 int msa_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *idx_q,
                 const uint16_t *idx_k, int64_t L, int H, int G, int d, int dI, int B, int kslots,
                 float scale, uint16_t *out, int32_t *block_ids_out, void *ws, size_t ws_bytes,
@@ -267,22 +311,52 @@ int msa_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
         L > kMaxPrefillLen)
         return MSA_ERR_UNSUPPORTED;
     if (check_ptr(ws) != MSA_OK) return MSA_ERR_WORKSPACE_TOO_SMALL;
-    const int64_t C = fit_chunk(L, ws_bytes,
-                                [&](int64_t c) { return prefill_bytes(c, L, H, G, d, kslots); });
-    if (C == 0) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    if (fit_chunk(L, ws_bytes, [&](int64_t c) { return prefill_bytes(c, L, H, G, d, kslots); }) == 0)
+        return MSA_ERR_WORKSPACE_TOO_SMALL;
+    return prefill_range(q, k, v, idx_q, idx_k, L, 0, H, G, d, dI, kslots, default_scale(scale, d),
+                         out, block_ids_out, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+// ------------------------ varlen / prefix prefill -------------------------
+int msa_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                       const uint16_t *idx_q, const uint16_t *idx_k, const int64_t *cu_q,
+                       const int64_t *cu_kv, int nseq, int H, int G, int d, int dI, int B,
+                       int kslots, float scale, uint16_t *out, int32_t *block_ids_out, void *ws,
+                       size_t ws_bytes, void *stream) {
+    if (nseq < 0 || H <= 0 || G <= 0 || d <= 0 || dI <= 0 || B <= 0 || kslots < 1 || H % G)
+        return MSA_ERR_INVALID_ARG;
+    if (nseq == 0) return MSA_OK;
+    if (!cu_q || !cu_kv) return MSA_ERR_INVALID_ARG;
+    if (B != kBlock || !d_ok(d) || !r_ok(H, G) || !index_ok(G, dI) || kslots > 32)
+        return MSA_ERR_UNSUPPORTED;
+    int64_t total_q = 0, max_L = 0;
+    for (int sq = 0; sq < nseq; ++sq) {
+        const int64_t C = cu_q[sq + 1] - cu_q[sq], L = cu_kv[sq + 1] - cu_kv[sq];
+        if (cu_q[sq] < 0 || cu_kv[sq] < 0 || C < 0 || L < C) return MSA_ERR_INVALID_ARG;
+        if (C > 0 && (L > kMaxPrefillLen || (L - C) % kBlock)) return MSA_ERR_UNSUPPORTED;
+        total_q += C;
+        if (C > 0) max_L = std::max(max_L, L);
+    }
+    if (total_q == 0) return MSA_OK;
+    if (!q || !k || !v || !idx_q || !idx_k || !out) return MSA_ERR_INVALID_ARG;
+    if (check_ptr(ws) != MSA_OK) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    // every sequence must fit at least one 128-query chunk (the longest needs most)
+    if (fit_chunk(max_L, ws_bytes,
+                  [&](int64_t c) { return prefill_bytes(c, max_L, H, G, d, kslots); }) == 0)
+        return MSA_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     scale = default_scale(scale, d);
-    const int nbp = nb_padded(L);
-    Carver c(ws);
-    float *S = c.take<float>(C * G * nbp);
-    int32_t *ids_ws = c.take<int32_t>(C * G * kslots);
-    const AttnWs w = carve_attn(c, C, H, G, d, kslots, (int)nblocks(L));
-    for (int64_t q0 = 0; q0 < L; q0 += C) {
-        const int64_t qend = std::min(L, q0 + C);
-        int32_t *ids_c = block_ids_out ? block_ids_out + q0 * G * kslots : ids_ws;
-        MSA_TIMED(kK1, launch_k1_index_pool(idx_q, idx_k, S, L, q0, qend, G, dI, nbp, s));
-        MSA_TIMED(kK2, launch_k2_select(S, nbp, (qend - q0) * G, G, kslots, q0, nullptr, 0, ids_c, s));
-        const int rc = attn_chunk(q, k, v, ids_c, L, q0, qend, H, G, d, kslots, scale, out, w, s);
+    for (int sq = 0; sq < nseq; ++sq) {
+        const int64_t C = cu_q[sq + 1] - cu_q[sq], L = cu_kv[sq + 1] - cu_kv[sq], P = L - C;
+        if (C == 0) continue;
+        // queries are the last C tokens of the sequence: shift the new-token arrays back
+        // by P rows so that row i of the sequence is addressed at its absolute position
+        const int64_t back = P - cu_q[sq];
+        int32_t *ids = block_ids_out ? rows_back(block_ids_out, back, (int64_t)G * kslots) : nullptr;
+        const int rc = prefill_range(rows_back(q, back, (int64_t)H * d), k + cu_kv[sq] * G * d,
+                                     v + cu_kv[sq] * G * d, rows_back(idx_q, back, (int64_t)G * dI),
+                                     idx_k + cu_kv[sq] * dI, L, P, H, G, d, dI, kslots, scale,
+                                     rows_back(out, back, (int64_t)H * d), ids, ws, ws_bytes, s);
         if (rc != MSA_OK) return rc;
     }
     return MSA_OK;

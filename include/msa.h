@@ -118,6 +118,31 @@ MSA_API int msa_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                 void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Varlen / prefix prefill [M3-20x §二 (causal window per sequence); SERVE
+ * 对建设者的影响: cache management around the sparse kernel].  A batch of nseq
+ * independent causal sequences, packed token-major.  Sequence s holds
+ * Ls = cu_kv[s+1] - cu_kv[s] tokens, of which the last Cs = cu_q[s+1] - cu_q[s]
+ * are new: its first Ps = Ls - Cs tokens are an existing prefix whose K, V and
+ * index keys are in the cache.  The new tokens are prefilled exactly as rows
+ * Ps .. Ls-1 of msa_prefill over the whole sequence (bitwise the same results).
+ *   q     [sum Cs, H, d]   idx_q [sum Cs, G, dI]   (new tokens only)
+ *   k, v  [sum Ls, G, d]   idx_k [sum Ls, dI]      (prefix + new tokens)
+ *   out   [sum Cs, H, d] OUT;  block_ids_out [sum Cs, G, k] OUT or NULL
+ *   cu_q, cu_kv: HOST int64 arrays of nseq + 1 offsets (non-decreasing).
+ * Requires Ps % 128 == 0 (whole prefix blocks) and Ls <= 1048576 for every
+ * sequence with new tokens, else MSA_ERR_UNSUPPORTED; Cs > Ls or a negative
+ * offset is MSA_ERR_INVALID_ARG.  Workspace: at least one
+ * 128-query chunk of msa_prefill_workspace_size(max Ls, ...); the size for the
+ * longest sequence is the preferred one.  Sequences run one after another on
+ * `stream` (each in query chunks, like msa_prefill).
+ * ------------------------------------------------------------------------- */
+MSA_API int msa_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                               const uint16_t *idx_q, const uint16_t *idx_k, const int64_t *cu_q,
+                               const int64_t *cu_kv, int nseq, int H, int G, int d, int dI, int B,
+                               int kslots, float scale, uint16_t *out, int32_t *block_ids_out,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Decode [M3-20x §二, §四 decode result; SERVE: paged MSA decode].  N independent
  * sequences; sequence n holds seq_len[n] cached tokens and its query is the LAST
  * cached token, position p = seq_len[n] - 1 (the new token is already inserted).

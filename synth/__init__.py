@@ -66,18 +66,22 @@ class DecodeShape:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "prefill" | "decode" | "decode_paged" | "decode_fp8idx"
+    kind: str                 # "prefill" | "prefill_varlen" | "decode" | "decode_paged" | "decode_fp8idx"
     shape: object
     plant: str = "lit"
     n_plant: int = 4
     c: float = 2.0
     hot_blocks: tuple = field(default_factory=tuple)
+    batch: int = 1            # prefill_varlen: sequences of shape.L tokens packed in one call
+    chunk: int = 0            # prefill_varlen: new tokens per call over the growing prefix (0: all)
 
 
 # The five workloads: shapes of the pages' research model (64 query heads,
 # 4 KV heads, B = 128, k = 16) with head/index dims 128, plus the tiny case; and
 # the decode workload again, with its caches in shuffled 128-token pages, and with
-# its index-key cache held as E4M3 bytes plus per-token scales.
+# its index-key cache held as E4M3 bytes plus per-token scales; and two packed /
+# chunked prefills (8 sequences of 16384 tokens in one call; the 128K sequence
+# prefilled 16384 new tokens at a time over its growing cached prefix).
 WORKLOADS = {
     "tiny_prefill_L4096": Workload("tiny_prefill_L4096", "prefill",
                                    PrefillShape(L=4096, H=8, G=2, d=64, dI=32, B=128, k=4)),
@@ -90,6 +94,11 @@ WORKLOADS = {
     "prefill_L1048576_hot": Workload("prefill_L1048576_hot", "prefill",
                                      PrefillShape(L=1048576, H=64, G=4, d=128, dI=128),
                                      plant="hot", n_plant=0, c=3.0, hot_blocks=(0, 1, 2, 3)),
+    "prefill_varlen_8x16384": Workload("prefill_varlen_8x16384", "prefill_varlen",
+                                       PrefillShape(L=16384, H=64, G=4, d=128, dI=128), batch=8),
+    "prefill_chunked_L131072_C16384": Workload("prefill_chunked_L131072_C16384", "prefill_varlen",
+                                               PrefillShape(L=131072, H=64, G=4, d=128, dI=128),
+                                               chunk=16384),
     "decode_paged_N64_L262144": Workload("decode_paged_N64_L262144", "decode_paged",
                                          DecodeShape(N=64, Lc=262144, H=64, G=4, d=128,
                                                      dI=128)),

@@ -32,7 +32,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for want in ("msa_select_blocks", "msa_sparse_attn", "msa_prefill", "msa_decode",
+    for want in ("msa_select_blocks", "msa_sparse_attn", "msa_prefill", "msa_prefill_varlen",
+                 "msa_decode",
                  "msa_decode_paged", "msa_decode_fp8idx", "msa_quantize_idx_k_e4m3",
                  "msa_select_blocks_workspace_size",
                  "msa_sparse_attn_workspace_size", "msa_prefill_workspace_size",
@@ -181,3 +182,26 @@ def test_fp8_decode_and_quantizer_arguments(lib):
     assert lib.msa_quantize_idx_k_e4m3(f, 10, 128, f, None, s) == INVALID
     assert lib.msa_quantize_idx_k_e4m3(f, -1, 128, f, f, s) == INVALID
     assert lib.msa_quantize_idx_k_e4m3(f, 10, 96, f, f, s) == UNSUPPORTED
+
+
+def test_varlen_prefill_arguments(lib):
+    f, ws, big, s = _fake(), P(0x100000), ctypes.c_size_t(1 << 40), None
+    zero = ctypes.c_float(0)
+    I64 = ctypes.c_int64
+
+    def call(cu_q, cu_kv, nseq=None, q=f, H=8, G=2, d=64, dI=32, B=128, k=4, nbytes=big):
+        n = len(cu_q) - 1 if nseq is None else nseq
+        aq = (I64 * len(cu_q))(*cu_q) if cu_q is not None else None
+        akv = (I64 * len(cu_kv))(*cu_kv) if cu_kv is not None else None
+        return lib.msa_prefill_varlen(q, f, f, f, f, aq, akv, n, H, G, d, dI, B, k, zero, f, None,
+                                      ws, nbytes, s)
+
+    assert call(None, None, nseq=0) == OK
+    assert call([0, 0, 0], [0, 300, 600], q=None) == OK        # no new tokens: nothing to do
+    assert call(None, [0, 10], nseq=1) == INVALID
+    assert call([0, 300], [0, 200]) == INVALID                 # more new tokens than tokens
+    assert call([0, 10, 5], [0, 10, 20]) == INVALID            # decreasing offsets
+    assert call([0, 100], [0, 200]) == UNSUPPORTED             # prefix of 100: not whole blocks
+    assert call([0, 100], [0, 1048576 + 228]) == UNSUPPORTED   # longer than 2^20 tokens
+    assert call([0, 100], [0, 100], B=64) == UNSUPPORTED
+    assert call([0, 100], [0, 100], nbytes=ctypes.c_size_t(64)) == WS_SMALL

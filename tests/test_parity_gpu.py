@@ -242,6 +242,88 @@ def test_decode_full_size_subset():
     _decode_check(shape, seq_len, seed=0, seqs=np.array([0, 1, 17, 31, 48, 63]), device=DEV)
 
 
+# ------------------------- varlen / prefix prefill ---------------------------
+def _cat_inputs(parts):
+    return {n: torch.cat([p[n] for p in parts]) for n in ("q", "k", "v", "iq", "ik")}
+
+
+def test_prefill_varlen_batch():
+    """Five packed sequences without prefix: each equals its own msa_prefill bitwise
+    and matches the oracle on every row."""
+    msa = _msa()
+    lens = [1000, 128, 1, 4097, 3000]
+    shapes = [synth.PrefillShape(L=L, H=16, G=4, d=128, dI=128, B=128, k=8) for L in lens]
+    xs = [synth.prefill_inputs(sh, seed=30 + i) for i, sh in enumerate(shapes)]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    _say(f"varlen prefill lens={lens}")
+    c = {n: t.to(DEV) for n, t in _cat_inputs(xs).items()}
+    out, ids = msa.prefill_varlen(c["q"], c["k"], c["v"], c["iq"], c["ik"], cu, cu, kslots=8,
+                                  return_ids=True)
+    torch.cuda.synchronize()
+    for i, (sh, x) in enumerate(zip(shapes, xs)):
+        sl = slice(int(cu[i]), int(cu[i + 1]))
+        o1, i1 = _prefill_gpu(x, sh.k)
+        assert torch.equal(ids[sl], i1)
+        assert torch.equal(out[sl].view(torch.int16), o1.view(torch.int16))
+        st = _parity.prefill_rows_vs_oracle(x, np.arange(sh.L), i1.cpu().numpy(),
+                                            o1.float().cpu().numpy(), 128, sh.k,
+                                            1.0 / math.sqrt(sh.d))
+        _say(f"  seq {i} L={sh.L} -> {st}")
+        assert st["id_mismatches"] == 0
+        assert st["max_abs"] < _parity.MAX_ABS and st["mean_abs"] < _parity.MEAN_ABS
+
+
+def test_prefill_with_cached_prefix():
+    """Chunked prefill over cached prefixes (first P tokens' K/V/idx-K already in the
+    cache, only the last L - P tokens are queries): rows P.. of the whole-sequence
+    prefill, bitwise, and the oracle on those rows."""
+    msa = _msa()
+    lens, prefixes = [5000, 2048, 700, 1300], [1024, 1920, 0, 1280]
+    shapes = [synth.PrefillShape(L=L, H=16, G=4, d=128, dI=128, B=128, k=8) for L in lens]
+    xs = [synth.prefill_inputs(sh, seed=40 + i) for i, sh in enumerate(shapes)]
+    _say(f"prefix prefill lens={lens} prefixes={prefixes}")
+    new = [{"q": x["q"][P:], "iq": x["iq"][P:]} for x, P in zip(xs, prefixes)]
+    cu_q = np.concatenate([[0], np.cumsum([L - P for L, P in zip(lens, prefixes)])])
+    cu_kv = np.concatenate([[0], np.cumsum(lens)])
+    q = torch.cat([n_["q"] for n_ in new]).to(DEV)
+    iq = torch.cat([n_["iq"] for n_ in new]).to(DEV)
+    kk = torch.cat([x["k"] for x in xs]).to(DEV)
+    vv = torch.cat([x["v"] for x in xs]).to(DEV)
+    ik = torch.cat([x["ik"] for x in xs]).to(DEV)
+    out, ids = msa.prefill_varlen(q, kk, vv, iq, ik, cu_q, cu_kv, kslots=8, return_ids=True)
+    torch.cuda.synchronize()
+    for i, (sh, x, P) in enumerate(zip(shapes, xs, prefixes)):
+        sl = slice(int(cu_q[i]), int(cu_q[i + 1]))
+        o1, i1 = _prefill_gpu(x, sh.k)
+        assert torch.equal(ids[sl], i1[P:])
+        assert torch.equal(out[sl].view(torch.int16), o1[P:].view(torch.int16))
+        rows = np.arange(P, sh.L)
+        st = _parity.prefill_rows_vs_oracle(x, rows, ids[sl].cpu().numpy(),
+                                            out[sl].float().cpu().numpy(), 128, sh.k,
+                                            1.0 / math.sqrt(sh.d))
+        _say(f"  seq {i} L={sh.L} P={P} -> {st}")
+        assert st["id_mismatches"] == 0
+        assert st["max_abs"] < _parity.MAX_ABS and st["mean_abs"] < _parity.MEAN_ABS
+
+
+def test_prefix_prefill_32k_matches_whole():
+    """L = 32768 with the first 16384 tokens cached: bitwise the second half of the
+    whole-sequence prefill (a property that holds at any size)."""
+    msa = _msa()
+    wl = synth.WORKLOADS["prefill_L32768"]
+    sh = wl.shape
+    P = 16384
+    x = synth.prefill_inputs(sh, seed=1, device=DEV)
+    _say(f"prefix prefill L={sh.L} P={P}")
+    o1, i1 = msa.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], kslots=sh.k, return_ids=True)
+    out, ids = msa.prefill_varlen(x["q"][P:].contiguous(), x["k"], x["v"],
+                                  x["iq"][P:].contiguous(), x["ik"], [0, sh.L - P], [0, sh.L],
+                                  kslots=sh.k, return_ids=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, i1[P:])
+    assert torch.equal(out.view(torch.int16), o1[P:].view(torch.int16))
+
+
 # ----------------------------- paged decode ---------------------------------
 def _compact_pages(pg, table, seqs, seq_len, B=128):
     """CPU copies of only the pages the listed sequences need, with their table
