@@ -12,7 +12,8 @@
 //     computes S^T = K Q^T, the block-local softmax (causal mask only in the query's
 //     own block), O^T = V^T P^T, and writes the normalised partial o (bf16) and its
 //     log2-sum-exp (fp32) to the entry's own (query, head, slot) location.
-// K4d (decode, split over slots): one work item per (sequence, group, slot).
+// K4d (decode, split over slots): one work item per (sequence, group, slot); a
+//     work-group takes several items and loads the next one's K/V while it attends.
 // K5  (combine, both paths): per (query, head) the partials of its valid slots are
 //     merged with the log-sum-exp rule  out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M),
 //     M = max_s lse_s -- the merge that keeps the softmax exact.
@@ -29,16 +30,20 @@ namespace msa {
 
 // A-operand row m of an S^T M-tile holds key pi(m) = m with bits 2 and 3 swapped:
 //   pi(m) = 16*(m>>4) + 8*((m>>2)&1) + 4*((m>>3)&1) + (m&3).
-// K tiles are staged with that permutation applied (stage_rows<.., true>), so the
+// K tiles are staged with that permutation applied (KVStage), so the
 // MFMA operand reads are plain row reads.
 
 // Q operand of one lane's column: D/16 chunks of 8 values (K-step ks takes chunk 2ks+hf).
+// qrow must be a readable row even for an inactive column (the load is not
+// branched around; its value is then replaced by zero).
 template <int D>
 __device__ __forceinline__ void load_q(bf16x8 (&qb)[D / 16], const uint16_t *qrow, bool active,
                                        int hf) {
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-        qb[ks] = as_bf16x8(active ? load16(qrow + (2 * ks + hf) * 8) : u32x4{0, 0, 0, 0});
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const u32x4 v = load16(qrow + (2 * ks + hf) * 8);
+        qb[ks] = as_bf16x8(active ? v : u32x4{0, 0, 0, 0});
+    }
 }
 
 // One pass of 32 columns of a wave over a staged block.  Lane column = l % 32.
@@ -188,12 +193,15 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     load_q<D>(qb, q + ((q0 + (entry >> 5)) * H + hh) * D, act, hf);
 
     if (tid < cnt) lds_e[tid] = list[begin + tid];
-    const int64_t kv_row_bytes = (int64_t)G * D * 2;
+    const int kv_row_bytes = G * D * 2;
     const char *ksrc = reinterpret_cast<const char *>(kx + ((int64_t)j * kBlock * G + g) * D);
     const char *vsrc = reinterpret_cast<const char *>(vx + ((int64_t)j * kBlock * G + g) * D);
     const int nrows = (int)min<int64_t>(kBlock, L - (int64_t)j * kBlock);
-    stage_rows<D / 8, true>(lds_k, ksrc, kv_row_bytes, nrows, tid);
-    stage_v_transposed<D>(lds_vt, vsrc, kv_row_bytes, nrows, tid);
+    {
+        KVStage<D> st;
+        st.load(ksrc, vsrc, kv_row_bytes, nrows, tid);
+        st.store(lds_k, lds_vt, tid);
+    }
     __syncthreads();
 
     constexpr int STEP = 4 * QPW;
@@ -261,7 +269,7 @@ hipError_t launch_k4_kv_outer(const uint16_t *q, const uint16_t *kx, const uint1
 // K4d: decode, one work-group per (sequence, group, slot).
 // ---------------------------------------------------------------------------
 template <int D, int R>
-__global__ __launch_bounds__(256) void k4d_split(const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(256, 2) void k4d_split(const uint16_t *__restrict__ q,
                                                  const uint16_t *__restrict__ kc,
                                                  const uint16_t *__restrict__ vc,
                                                  const int32_t *__restrict__ ids,
@@ -269,37 +277,82 @@ __global__ __launch_bounds__(256) void k4d_split(const uint16_t *__restrict__ q,
                                                  const int32_t *__restrict__ table, int maxb,
                                                  int64_t Lmax, int H, int G, int kslots,
                                                  float scale_log2, uint16_t *__restrict__ po,
-                                                 float *__restrict__ plse) {
+                                                 float *__restrict__ plse, int64_t n_items) {
     __shared__ __attribute__((aligned(16))) char lds_k[kBlock * D * 2];
     __shared__ __attribute__((aligned(16))) char lds_vt[D * kBlock * 2];
-    const int64_t item = blockIdx.x;
-    const int64_t n = item / ((int64_t)G * kslots);
-    const int g = (int)((item / kslots) % G);
-    const int s = (int)(item % kslots);
-    const int j = ids[(n * G + g) * kslots + s];
-    if (j < 0) return;
-    const int64_t p = (int64_t)seq_len[n] - 1;
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-    const int64_t kv_row_bytes = (int64_t)G * D * 2;
-    // first token row of block j: contiguous cache [N, Lmax, G, D], or its page of
-    // a paged cache [pages, 128, G, D] (a page is always whole)
-    const int64_t tok0 = table ? (int64_t)table[n * maxb + j] * kBlock : n * Lmax + (int64_t)j * kBlock;
-    const int64_t row0 = tok0 * G + g;
-    const int nrows = table ? kBlock : (int)min<int64_t>(kBlock, Lmax - (int64_t)j * kBlock);
-    stage_rows<D / 8, true>(lds_k, reinterpret_cast<const char *>(kc + row0 * D), kv_row_bytes,
-                            nrows, tid);
-    stage_v_transposed<D>(lds_vt, reinterpret_cast<const char *>(vc + row0 * D), kv_row_bytes,
-                          nrows, tid);
-    __syncthreads();
-    if (wave != 0) return;
-    const int l32 = lane & 31;
-    const bool active = l32 < R;
-    const int64_t hh = (int64_t)g * R + (active ? l32 : 0);
-    const int64_t prow = (n * H + hh) * kslots + s;
-    const int64_t lrow = ((n * G + g) * kslots + s) * R + (active ? l32 : 0);
-    bf16x8 qb[D / 16];
-    load_q<D>(qb, q + (n * H + hh) * D, active, lane >> 5);
-    attend_pass<D>(lds_k, lds_vt, j, qb, active, p, po + prow * D, plse + lrow, scale_log2, lane);
+    const int kv_row_bytes = G * D * 2;
+    // Items (sequence, group, slot) with a valid id, visited with stride gridDim.x.
+    // The next item's K/V loads are issued before the current item is attended, so
+    // the memory latency of one overlaps the attention of the other.
+    auto next_valid = [&](int64_t it) {
+        for (; it < n_items; it += gridDim.x)
+            if (ids[it] >= 0) return it;
+        return n_items;
+    };
+    // item -> first K/V element of its block: contiguous cache [N, Lmax, G, D], or the
+    // block's page of a paged cache [pages, 128, G, D] (a page is always whole)
+    auto kv_src = [&](int64_t it, int &nrows) {
+        const int64_t n = it / ((int64_t)G * kslots);
+        const int g = (int)((it / kslots) % G);
+        const int j = ids[it];
+        const int64_t tok0 =
+            table ? (int64_t)table[n * maxb + j] * kBlock : n * Lmax + (int64_t)j * kBlock;
+        nrows = table ? kBlock : (int)min<int64_t>(kBlock, Lmax - (int64_t)j * kBlock);
+        return (tok0 * G + g) * D;
+    };
+    // Roles by wave: waves 2-3 stage K/V (store the current item, then load the next
+    // into registers), wave 0 attends, wave 1 only keeps the barrier count.  Every
+    // role walks the same item sequence and meets the same two barriers per item;
+    // the roles' code paths are disjoint, so the staging registers are never live
+    // during the attention.
+    const int64_t first = next_valid(blockIdx.x);
+    if (first >= n_items) return;
+    if (wave >= 2) {
+        const int stid = tid - 2 * kWave;
+        KVStage<D, 2 * kWave> st;
+        int64_t item = first;
+        int nrows;
+        int64_t off = kv_src(item, nrows);
+        st.load(reinterpret_cast<const char *>(kc + off), reinterpret_cast<const char *>(vc + off),
+                kv_row_bytes, nrows, stid);
+        while (item < n_items) {
+            st.store(lds_k, lds_vt, stid);
+            __syncthreads();                       // (A) the item is in LDS
+            const int64_t nxt = next_valid(item + gridDim.x);
+            if (nxt < n_items) {
+                off = kv_src(nxt, nrows);
+                st.load(reinterpret_cast<const char *>(kc + off),
+                        reinterpret_cast<const char *>(vc + off), kv_row_bytes, nrows, stid);
+            }
+            __syncthreads();                       // (B) the item's attention is done
+            item = nxt;
+        }
+    } else if (wave == 0) {
+        for (int64_t item = first; item < n_items; item = next_valid(item + gridDim.x)) {
+            __syncthreads();                       // (A)
+            const int64_t n = item / ((int64_t)G * kslots);
+            const int g = (int)((item / kslots) % G);
+            const int s = (int)(item % kslots);
+            const int j = ids[item];
+            const int64_t p = (int64_t)seq_len[n] - 1;
+            const int l32 = lane & 31;
+            const bool active = l32 < R;
+            const int64_t hh = (int64_t)g * R + (active ? l32 : 0);
+            const int64_t prow = (n * H + hh) * kslots + s;
+            const int64_t lrow = ((n * G + g) * kslots + s) * R + (active ? l32 : 0);
+            bf16x8 qb[D / 16];
+            load_q<D>(qb, q + (n * H + hh) * D, active, lane >> 5);
+            attend_pass<D>(lds_k, lds_vt, j, qb, active, p, po + prow * D, plse + lrow,
+                           scale_log2, lane);
+            __syncthreads();                       // (B)
+        }
+    } else {
+        for (int64_t item = first; item < n_items; item = next_valid(item + gridDim.x)) {
+            __syncthreads();                       // (A)
+            __syncthreads();                       // (B)
+        }
+    }
 }
 
 template <int D, int R>
@@ -307,10 +360,12 @@ static hipError_t k4d_dispatch(const uint16_t *q, const uint16_t *kc, const uint
                                const int32_t *ids, const int32_t *seq_len, const int32_t *table,
                                int maxb, int N, int64_t Lmax, int H, int G, int k, float sl2,
                                uint16_t *po, float *plse, hipStream_t s) {
-    const int64_t grid = (int64_t)N * G * k;
-    if (grid == 0) return hipSuccess;
+    const int64_t n_items = (int64_t)N * G * k;
+    if (n_items == 0) return hipSuccess;
+    // two work-groups per CU (64 KB of LDS each), a few items per work-group
+    const int64_t grid = n_items < 512 ? n_items : 512;
     hipLaunchKernelGGL((k4d_split<D, R>), dim3((unsigned)grid), dim3(256), 0, s, q, kc, vc, ids,
-                       seq_len, table, maxb, Lmax, H, G, k, sl2, po, plse);
+                       seq_len, table, maxb, Lmax, H, G, k, sl2, po, plse, n_items);
     return hipGetLastError();
 }
 

@@ -77,31 +77,6 @@ __device__ __forceinline__ int swz(int row, int chunk) {
     return row * (CPR * 16) + ((chunk ^ (row & kMask)) << 4);
 }
 
-// Copy a 128-row tile of CPR 16-byte chunks per row from global rows at
-// `src + row*stride_bytes` (rows >= nrows are zero-filled) into swizzled LDS.
-// Called by all 256 threads of a work-group.
-// With SwapBits23, source row t is stored at LDS row t with bits 2 and 3 swapped
-// (an involution), so that reading LDS row m yields source row pi(m).
-template <int CPR, bool SwapBits23 = false>
-__device__ __forceinline__ void stage_rows(char *lds, const char *src, int64_t stride_bytes,
-                                           int nrows, int tid) {
-    constexpr int kRowsPerIter = 256 / CPR;
-    constexpr int kIters = kBlock / kRowsPerIter;
-    const int c = tid % CPR;
-    u32x4 regs[kIters];
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-        const int row = tid / CPR + it * kRowsPerIter;
-        regs[it] = (row < nrows) ? load16(src + row * stride_bytes + c * 16) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-        const int row = tid / CPR + it * kRowsPerIter;
-        const int lrow = SwapBits23 ? ((row & ~12) | ((row & 4) << 1) | ((row & 8) >> 1)) : row;
-        store16(lds + swz<CPR>(lrow, c), regs[it]);
-    }
-}
-
 typedef void __attribute__((address_space(3))) *lds_ptr_t;
 
 // Direct global -> LDS copy (global_load_lds_dwordx4, no registers) of a full
@@ -136,36 +111,72 @@ __device__ __forceinline__ int swz_vt(int d, int chunk) {
     return d * 256 + ((chunk ^ (d & 15) ^ ((d >> 4) & 7)) << 4);
 }
 
-// Stage V (128 keys x D values, rows at `src + key*stride_bytes`) TRANSPOSED into
-// LDS as D rows of 128 keys (swz_vt layout).  Keys >= nrows are 0.
-template <int D>
-__device__ __forceinline__ void stage_v_transposed(char *lds, const char *src,
-                                                   int64_t stride_bytes, int nrows, int tid) {
-    constexpr int CPR = D / 8;                   // 16-byte chunks of d per V row
-    constexpr int kQuadsPerIter = 256 / CPR;     // key quads covered per iteration
-    constexpr int kIters = (kBlock / 4) / kQuadsPerIter;
-    const int dc = tid % CPR;
+// One KV block staged through registers: K (rows permuted by swapping bits 2 and 3,
+// swz<D/8> layout) and V transposed (swz_vt layout), from rows at
+// `ksrc/vsrc + key*stride_bytes`; keys >= nrows (1 <= nrows <= 128) are zero.
+// load() issues every global load of both tiles with no branch around any load
+// (out-of-range keys re-read row nrows-1 and are replaced by zero at store time),
+// so a block costs one memory round trip; store() writes LDS.  Between the two the
+// caller may do other work (the loads stay in flight).  NTHR threads (tid in
+// [0, NTHR)) take part.
+template <int D, int NTHR = 256>
+struct KVStage {
+    static constexpr int CPR = D / 8;
+    static constexpr int kRowsPerIter = NTHR / CPR;
+    static_assert(kBlock % (4 * kRowsPerIter) == 0, "block must split evenly");
+    static constexpr int kKIters = kBlock / kRowsPerIter;          // K chunks per thread
+    static constexpr int kVIters = (kBlock / 4) / kRowsPerIter;    // V key quads per thread
+    u32x4 kr[kKIters], vr[kVIters][4];
+    int last;
+
+    // ksrc / vsrc are the same for every thread; offsets within the block are 32-bit
+    // (at most 127 rows of stride_bytes <= 2 KiB), one address register per load.
+    __device__ __forceinline__ void load(const char *ksrc, const char *vsrc, int stride_bytes,
+                                         int nrows, int tid) {
+        const int c = tid % CPR;
+        last = nrows - 1;
 #pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-        const int kq = tid / CPR + it * kQuadsPerIter;   // keys 4kq .. 4kq+3
-        u32x4 r[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int key = 4 * kq + kk;
-            r[kk] = (key < nrows) ? load16(src + key * stride_bytes + dc * 16) : u32x4{0, 0, 0, 0};
+        for (int it = 0; it < kKIters; ++it) {
+            const int row = tid / CPR + it * kRowsPerIter;
+            kr[it] = load16(ksrc + (uint32_t)(min(row, last) * stride_bytes + c * 16));
         }
-        // element e of chunk dc is d = 8*dc + e; gather the 4 keys for each d
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1, sh = (e & 1) * 16;
-            uint32_t v0 = (r[0][w] >> sh) & 0xFFFFu, v1 = (r[1][w] >> sh) & 0xFFFFu;
-            uint32_t v2 = (r[2][w] >> sh) & 0xFFFFu, v3 = (r[3][w] >> sh) & 0xFFFFu;
-            const int d = 8 * dc + e;
-            const int key0 = 4 * kq;
-            char *p = lds + swz_vt(d, key0 >> 3) + ((key0 >> 2) & 1) * 8;
-            store8(p, u32x2{v0 | (v1 << 16), v2 | (v3 << 16)});
+        for (int it = 0; it < kVIters; ++it) {
+            const int kq = tid / CPR + it * kRowsPerIter;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                vr[it][kk] = load16(vsrc + (uint32_t)(min(4 * kq + kk, last) * stride_bytes + c * 16));
         }
     }
-}
+
+    __device__ __forceinline__ void store(char *lds_k, char *lds_vt, int tid) const {
+        const int c = tid % CPR;
+        const u32x4 zero = {0, 0, 0, 0};
+#pragma unroll
+        for (int it = 0; it < kKIters; ++it) {
+            const int row = tid / CPR + it * kRowsPerIter;
+            const int lrow = (row & ~12) | ((row & 4) << 1) | ((row & 8) >> 1);
+            store16(lds_k + swz<CPR>(lrow, c), row <= last ? kr[it] : zero);
+        }
+#pragma unroll
+        for (int it = 0; it < kVIters; ++it) {
+            const int kq = tid / CPR + it * kRowsPerIter;
+            u32x4 r[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) r[kk] = 4 * kq + kk <= last ? vr[it][kk] : zero;
+            // element e of chunk c is d = 8c + e; gather the 4 keys for each d
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int w = e >> 1, sh = (e & 1) * 16;
+                const uint32_t v0 = (r[0][w] >> sh) & 0xFFFFu, v1 = (r[1][w] >> sh) & 0xFFFFu;
+                const uint32_t v2 = (r[2][w] >> sh) & 0xFFFFu, v3 = (r[3][w] >> sh) & 0xFFFFu;
+                const int d = 8 * c + e;
+                const int key0 = 4 * kq;
+                char *p = lds_vt + swz_vt(d, key0 >> 3) + ((key0 >> 2) & 1) * 8;
+                store8(p, u32x2{v0 | (v1 << 16), v2 | (v3 << 16)});
+            }
+        }
+    }
+};
 
 }  // namespace msa
