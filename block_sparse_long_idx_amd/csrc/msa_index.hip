@@ -292,7 +292,8 @@ hipError_t launch_k1d_index_pool(const uint16_t *iq, const uint16_t *ikc, const 
 // ---------------------------------------------------------------------------
 // K1d over an FP8 index-key cache: bytes ik8[N, Lmax, DI] in the OCP E4M3 encoding
 // and one fp32 scale per token, ksc[N, Lmax]; the score of token t is
-// ksc[t] * (iq . e4m3(ik8[t])).  Half the bytes of the bf16 cache per key.  Each
+// ksc[t] * (iq . e4m3(ik8[t])).  Half the bytes of the bf16 cache per key.  One
+// wave scores BPW consecutive blocks, requesting all their bytes up front.  Each
 // E4M3 value is exact in bf16, so bytes are widened in registers
 // (v_cvt_scalef32_pk_bf16_fp8, scale 1) and the bf16 MFMA of K1d runs unchanged;
 // the token scale multiplies the fp32 dot product before the block max.  The
@@ -300,7 +301,7 @@ hipError_t launch_k1d_index_pool(const uint16_t *iq, const uint16_t *ikc, const 
 // MFMA step ks, quarter qt of the wave holds elements 8*KS*qt + 8*ks .. +7 of
 // both operands.
 // ---------------------------------------------------------------------------
-template <int G, int DI>
+template <int G, int DI, int BPW>
 __global__ __launch_bounds__(256) void k1d_index_pool_fp8(const uint16_t *__restrict__ iq,
                                                           const uint8_t *__restrict__ ik8,
                                                           const float *__restrict__ ksc,
@@ -311,11 +312,11 @@ __global__ __launch_bounds__(256) void k1d_index_pool_fp8(const uint16_t *__rest
     constexpr int SPAN = 8 * KS;          // contiguous key bytes per lane and token
     const int n = blockIdx.y;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
-    const int b = blockIdx.x * 4 + wave;
+    const int b0 = (blockIdx.x * 4 + wave) * BPW;   // this wave's first block
     const int sl = seq_len[n];
     if (sl < 1 || sl > Lmax) return;
     const int ncomp = (sl - 1) / kBlock;
-    if (b >= ncomp) return;
+    if (b0 >= ncomp) return;
     const int l16 = lane & 15, qt = lane >> 4;
 
     bf16x8 bq[KS];
@@ -323,56 +324,66 @@ __global__ __launch_bounds__(256) void k1d_index_pool_fp8(const uint16_t *__rest
     for (int ks = 0; ks < KS; ++ks)
         bq[ks] = as_bf16x8(l16 < G ? load16(iq + ((int64_t)n * G + l16) * DI + SPAN * qt + 8 * ks)
                                    : u32x4{0, 0, 0, 0});
-    const int64_t tok0 = (int64_t)n * Lmax + (int64_t)b * kBlock;
-    const uint8_t *base = ik8 + tok0 * DI + SPAN * qt;
-    // raw[mt][w]: dword w of this lane's SPAN bytes of token mt*16 + l16
-    uint32_t raw[8][SPAN / 4];
+    // raw[bb][mt][w]: dword w of this lane's SPAN bytes of token mt*16 + l16 of block
+    // b0 + bb; every block's bytes are requested before any is converted
+    uint32_t raw[BPW][8][SPAN / 4];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-        const uint8_t *p = base + (mt * 16 + l16) * DI;
-        if constexpr (SPAN >= 16) {
+    for (int bb = 0; bb < BPW; ++bb) {
+        // a block past the sequence's competitors re-reads the first block (discarded)
+        const int b = b0 + bb < ncomp ? b0 + bb : b0;
+        const uint8_t *base = ik8 + ((int64_t)n * Lmax + (int64_t)b * kBlock) * DI + SPAN * qt;
 #pragma unroll
-            for (int c = 0; c < SPAN / 16; ++c) {
-                const u32x4 v = load16(p + 16 * c);
+        for (int mt = 0; mt < 8; ++mt) {
+            const uint8_t *p = base + (mt * 16 + l16) * DI;
+            if constexpr (SPAN >= 16) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) raw[mt][4 * c + e] = v[e];
+                for (int c = 0; c < SPAN / 16; ++c) {
+                    const u32x4 v = load16(p + 16 * c);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) raw[bb][mt][4 * c + e] = v[e];
+                }
+            } else {
+                const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
+                raw[bb][mt][0] = v[0];
+                raw[bb][mt][1] = v[1];
             }
-        } else {
-            const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
-            raw[mt][0] = v[0];
-            raw[mt][1] = v[1];
         }
     }
-    // token scales of this lane's accumulator rows: tokens mt*16 + 4*qt + r
-    const float *sp = ksc + tok0 + 4 * qt;
-    float m = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-        f32x4 acc = f32x4{};
+    for (int bb = 0; bb < BPW; ++bb) {
+        const int b = b0 + bb;
+        if (b >= ncomp) break;
+        // token scales of this lane's accumulator rows: tokens mt*16 + 4*qt + r
+        const float *sp = ksc + (int64_t)n * Lmax + (int64_t)b * kBlock + 4 * qt;
+        float m = -INFINITY;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 a;
+        for (int mt = 0; mt < 8; ++mt) {
+            f32x4 acc = f32x4{};
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint32_t w = raw[mt][2 * ks + h];
-                const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-                const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
-                a[4 * h + 0] = lo[0];
-                a[4 * h + 1] = lo[1];
-                a[4 * h + 2] = hi[0];
-                a[4 * h + 3] = hi[1];
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8 a;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t w = raw[bb][mt][2 * ks + h];
+                    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+                    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+                    a[4 * h + 0] = lo[0];
+                    a[4 * h + 1] = lo[1];
+                    a[4 * h + 2] = hi[0];
+                    a[4 * h + 3] = hi[1];
+                }
+                acc = mfma16(a, bq[ks], acc);
             }
-            acc = mfma16(a, bq[ks], acc);
+            const float *p = sp + mt * 16;
+            const f32x4 sc = sc_aligned ? *reinterpret_cast<const f32x4 *>(p)
+                                        : f32x4{p[0], p[1], p[2], p[3]};
+            m = fmaxf(m, fmaxf(fmaxf(acc[0] * sc[0], acc[1] * sc[1]),
+                               fmaxf(acc[2] * sc[2], acc[3] * sc[3])));
         }
-        const float *p = sp + mt * 16;
-        const f32x4 sc = sc_aligned ? *reinterpret_cast<const f32x4 *>(p)
-                                    : f32x4{p[0], p[1], p[2], p[3]};
-        m = fmaxf(m, fmaxf(fmaxf(acc[0] * sc[0], acc[1] * sc[1]),
-                           fmaxf(acc[2] * sc[2], acc[3] * sc[3])));
+        m = fmaxf(m, xor_shfl(m, 16));
+        m = fmaxf(m, xor_shfl(m, 32));
+        if (lane < G) S[((int64_t)n * G + lane) * nbp + b] = m;
     }
-    m = fmaxf(m, xor_shfl(m, 16));
-    m = fmaxf(m, xor_shfl(m, 32));
-    if (lane < G) S[((int64_t)n * G + lane) * nbp + b] = m;
 }
 
 template <int G, int DI>
@@ -382,9 +393,12 @@ static hipError_t k1d8_dispatch(const uint16_t *iq, const uint8_t *ik8, const fl
     const int64_t nbmax = (Lmax - 1) / kBlock;
     if (nbmax <= 0 || N <= 0) return hipSuccess;
     const int aligned = (Lmax % 4 == 0) && (reinterpret_cast<uintptr_t>(ksc) % 16 == 0);
-    dim3 grid((unsigned)((nbmax + 3) / 4), (unsigned)N);
-    hipLaunchKernelGGL((k1d_index_pool_fp8<G, DI>), grid, dim3(256), 0, s, iq, ik8, ksc, seq_len, S,
-                       Lmax, nbp, aligned);
+    // two blocks per wave: 32 KB in flight per wave at 2 waves per SIMD (measured
+    // faster than one block at 3 waves per SIMD, and than four at one wave)
+    constexpr int BPW = 2;
+    dim3 grid((unsigned)((nbmax + 4 * BPW - 1) / (4 * BPW)), (unsigned)N);
+    hipLaunchKernelGGL((k1d_index_pool_fp8<G, DI, BPW>), grid, dim3(256), 0, s, iq, ik8, ksc,
+                       seq_len, S, Lmax, nbp, aligned);
     return hipGetLastError();
 }
 
