@@ -132,6 +132,18 @@ def test_shape_grid(H, G, d, dI, k):
     _full_check(shape, seed=6)
 
 
+@pytest.mark.parametrize("H,G,d,dI,k", [
+    (16, 8, 64, 64, 6),      # eight groups (32 queries per K1 work-group)
+    (32, 1, 128, 128, 5),    # one group
+    (8, 2, 64, 32, 7),       # index dim 32
+])
+def test_shape_grid_long(H, G, d, dI, k):
+    """Long enough (97 blocks, four key chunks of K1) that every group really
+    selects k-1 of many competitors."""
+    shape = synth.PrefillShape(L=12345, H=H, G=G, d=d, dI=dI, B=128, k=k)
+    _full_check(shape, seed=16, rows=_sample_rows(shape.L, 1200, 16))
+
+
 def test_determinism():
     x = synth.prefill_inputs(TINY, seed=7)
     _say("determinism")
@@ -232,6 +244,12 @@ def test_decode_small_ragged():
 def test_decode_tiny_dims():
     shape = synth.DecodeShape(N=5, Lc=4096, H=8, G=2, d=64, dI=32, B=128, k=4)
     _decode_check(shape, np.array([4096, 3000, 129, 640, 1]), seed=1)
+
+
+@pytest.mark.parametrize("H,G,d,dI,k", [(64, 8, 64, 64, 8), (16, 1, 128, 128, 16)])
+def test_decode_other_groupings(H, G, d, dI, k):
+    shape = synth.DecodeShape(N=6, Lc=20000, H=H, G=G, d=d, dI=dI, B=128, k=k)
+    _decode_check(shape, np.array([20000, 17000, 129, 2048, 1, 9999]), seed=12)
 
 
 def test_decode_full_size_subset():
