@@ -113,6 +113,20 @@ def _add_work(a, b):
 
 
 # --------------------------------------------------------------------------
+def _host():
+    """What the CPU baseline ran on: visible cores and the CPU model."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
 def _sample_rows(L, n, seed=0):
     rng = np.random.default_rng(seed)
     return np.sort(rng.choice(L, size=min(n, L), replace=False))
@@ -409,16 +423,20 @@ def main():
 
     # ---- timed region: exactly K steps --------------------------------------
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: the K-step total and each step's time
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
+    ev[0].record()
+    for i in range(args.steps):
         step()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ms_per_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    median_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else \
+        0.5 * (step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
 
     # ---- per-kernel breakdown: the same K steps with stage events -----------
     msa.timing_enable(64 * args.steps + 64)
@@ -431,7 +449,8 @@ def main():
     dominant = max(kernels, key=lambda k_: kernels[k_]["ms_per_step"])
 
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-              "ms_per_step": ms_per_step, "scaling": "weak", "vs_baseline": None,
+              "ms_per_step": ms_per_step, "ms_per_step_median": median_ms,
+              "ms_per_step_min": step_ms[0], "scaling": "weak", "vs_baseline": None,
               "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, planted blocks)"}
     if wl.kind in ("prefill", "prefill_varlen"):
         nseq = wl.batch
@@ -504,6 +523,7 @@ def main():
             result["cpu_baseline"] = cpu_baseline_decode(x, s, args.cpu_seconds)
         else:
             result["cpu_baseline"] = cpu_baseline_decode_paged(x, s, args.cpu_seconds)
+        result["cpu_baseline"]["host"] = _host()
     want_dense = args.dense_baseline == "on" or (
         args.dense_baseline == "auto" and wl.kind == "prefill" and s.L <= 131072)
     if want_dense:
