@@ -210,12 +210,20 @@ def cpu_baseline_decode_paged(x, shape, target_s=15.0):
     while total_s < target_s and total < shape.N:
         seqs = np.arange(total, min(shape.N, total + n_seq))
         pages = table[seqs[0]:seqs[-1] + 1].long()
-        kp, vp, ikp = (x[name][pages.reshape(-1)].cpu()
-                       for name in ("k_pages", "v_pages", "ik_pages"))
         local = np.arange(pages.numel(), dtype=np.int32).reshape(pages.shape)
-        t0 = time.perf_counter()
-        oracle.decode_paged(q[seqs[0]:seqs[-1] + 1], iq[seqs[0]:seqs[-1] + 1], kp, vp, ikp, local,
-                            lens[seqs], B_BLOCK, shape.k, lib=lib)
+        sl = slice(seqs[0], seqs[-1] + 1)
+        if "ik8_pages" in x:
+            kp, vp, ik8p, kscp = (x[name][pages.reshape(-1)].cpu() for name in
+                                  ("k_pages", "v_pages", "ik8_pages", "ik_scale_pages"))
+            t0 = time.perf_counter()
+            oracle.decode_paged_fp8idx(q[sl], iq[sl], kp, vp, ik8p, kscp, local, lens[seqs],
+                                       B_BLOCK, shape.k, lib=lib)
+        else:
+            kp, vp, ikp = (x[name][pages.reshape(-1)].cpu()
+                           for name in ("k_pages", "v_pages", "ik_pages"))
+            t0 = time.perf_counter()
+            oracle.decode_paged(q[sl], iq[sl], kp, vp, ikp, local, lens[seqs], B_BLOCK, shape.k,
+                                lib=lib)
         total_s += time.perf_counter() - t0
         total += len(seqs)
         n_seq = min(16, n_seq * 2)
@@ -398,10 +406,15 @@ def main():
                               x["ik_scale"], seq_len, kslots=s.k, out=out, ids_out=ids,
                               workspace=ws, return_ids=True)
     else:   # decode over 128-token pages in a seeded random order
+        e4m3 = wl.kind == "decode_paged_fp8idx"
         x = synth.decode_inputs(s, seed=args.seed, device=dev)
-        x.update(synth.paginate(x, B_BLOCK, seed=args.seed))
-        for name in ("k_cache", "v_cache", "ik_cache"):
-            del x[name]
+        names = ("k_cache", "v_cache", "ik_cache")
+        if e4m3:
+            x["ik8"], x["ik_scale"] = msa.quantize_idx_k_e4m3(x["ik_cache"])
+            names = ("k_cache", "v_cache", "ik8", "ik_scale")
+        x.update(synth.paginate(x, B_BLOCK, seed=args.seed, names=names))
+        for name in ("k_cache", "v_cache", "ik_cache", "ik8", "ik_scale"):
+            x.pop(name, None)
         torch.cuda.empty_cache()
         seq_len = torch.tensor(np.asarray(x["seq_len"], np.int32), device=dev)
         out = torch.empty_like(x["q"])
@@ -411,9 +424,15 @@ def main():
                                                G=s.G, d=s.d, dI=s.dI, k=s.k), dev)
 
         def step():
-            msa.decode_paged(x["q"], x["iq"], x["k_pages"], x["v_pages"], x["ik_pages"],
-                             x["block_table"], seq_len, kslots=s.k, out=out, ids_out=ids,
-                             workspace=ws, return_ids=True)
+            if e4m3:
+                msa.decode_paged_fp8idx(x["q"], x["iq"], x["k_pages"], x["v_pages"],
+                                        x["ik8_pages"], x["ik_scale_pages"], x["block_table"],
+                                        seq_len, kslots=s.k, out=out, ids_out=ids, workspace=ws,
+                                        return_ids=True)
+            else:
+                msa.decode_paged(x["q"], x["iq"], x["k_pages"], x["v_pages"], x["ik_pages"],
+                                 x["block_table"], seq_len, kslots=s.k, out=out, ids_out=ids,
+                                 workspace=ws, return_ids=True)
 
     torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -474,8 +493,9 @@ def main():
         result["algorithmic_flops_per_step"] = work["f_total"]
         result["dense_gqa_flops_per_step"] = work["dense_gqa_flops"]
     else:
-        work = decode_work(s.N, s.Lc, s.H, s.G, s.d, s.dI, s.k, paged=wl.kind == "decode_paged",
-                           fp8idx=wl.kind == "decode_fp8idx")
+        work = decode_work(s.N, s.Lc, s.H, s.G, s.d, s.dI, s.k,
+                           paged=wl.kind in ("decode_paged", "decode_paged_fp8idx"),
+                           fp8idx=wl.kind in ("decode_fp8idx", "decode_paged_fp8idx"))
         result.update({"value": ms_per_step * 1e3, "unit": "us/step", "higher_is_better": False})
         result["config"] = {"workload": wl.name, "N": s.N, "Lc": s.Lc, "H": s.H, "G": s.G,
                             "d": s.d, "dI": s.dI, "B": s.B, "k": s.k}

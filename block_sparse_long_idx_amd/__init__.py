@@ -17,7 +17,7 @@ import torch
 
 __all__ = ["MSAError", "select_blocks", "sparse_attn", "prefill", "prefill_varlen", "decode",
            "decode_paged",
-           "decode_fp8idx", "quantize_idx_k_e4m3", "workspace_size",
+           "decode_fp8idx", "decode_paged_fp8idx", "quantize_idx_k_e4m3", "workspace_size",
            "library_path", "load_library", "timing_enable", "timing_collect", "timing_disable"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -104,6 +104,9 @@ def load_library():
     lib.msa_decode_fp8idx.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, i32, i32,
                                       f32, P, P, P, sz, P]
     lib.msa_decode_fp8idx.restype = i32
+    lib.msa_decode_paged_fp8idx.argtypes = [P, P, P, P, P, P, i64, P, i32, P, i32, i32, i32, i32,
+                                            i32, i32, i32, f32, P, P, P, sz, P]
+    lib.msa_decode_paged_fp8idx.restype = i32
     lib.msa_quantize_idx_k_e4m3.argtypes = [P, i64, i32, P, P, P]
     lib.msa_quantize_idx_k_e4m3.restype = i32
     lib.msa_timing_enable.argtypes = [i32]
@@ -403,4 +406,42 @@ def prefill_varlen(q, k, v, idx_q, idx_k, cu_q, cu_kv, kslots: int = 16, B: int 
                                 _scale(scale, d), _ptr(out), _ptr(ids_out), _ptr(ws), ws.numel(),
                                 _stream(dev))
     _check(st, "msa_prefill_varlen")
+    return (out, ids_out) if return_ids else out
+
+
+def decode_paged_fp8idx(q, idx_q, k_pages, v_pages, idx_k_pages_e4m3, idx_k_scale_pages,
+                        block_table, seq_len, kslots: int = 16, B: int = 128, scale=None,
+                        return_ids: bool = False, out=None, ids_out=None, workspace=None):
+    """Paged decode with E4M3 index-key pages [P, 128, dI] (uint8) + scales [P, 128]."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(idx_q, "idx_q", torch.bfloat16, 3, dev)
+    _need(k_pages, "k_pages", torch.bfloat16, 4, dev)
+    _need(v_pages, "v_pages", torch.bfloat16, 4, dev)
+    _need(idx_k_pages_e4m3, "idx_k_pages_e4m3", torch.uint8, 3, dev)
+    _need(idx_k_scale_pages, "idx_k_scale_pages", torch.float32, 2, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(seq_len, "seq_len", torch.int32, 1, dev)
+    N, H, d = q.shape
+    G, dI = idx_q.shape[1], idx_q.shape[2]
+    npages = k_pages.shape[0]
+    maxb = block_table.shape[1]
+    if (k_pages.shape != (npages, B, G, d) or v_pages.shape != (npages, B, G, d)
+            or idx_k_pages_e4m3.shape != (npages, B, dI)
+            or idx_k_scale_pages.shape != (npages, B) or block_table.shape[0] != N
+            or seq_len.shape != (N,)):
+        raise MSAError("inconsistent shapes for paged FP8 decode inputs")
+    if out is None:
+        out = torch.empty_like(q)
+    if return_ids and ids_out is None:
+        ids_out = torch.empty((N, G, kslots), dtype=torch.int32, device=dev)
+    nbytes = lib.msa_decode_paged_workspace_size(N, maxb, H, G, d, dI, B, kslots)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    st = lib.msa_decode_paged_fp8idx(_ptr(q), _ptr(idx_q), _ptr(k_pages), _ptr(v_pages),
+                                     _ptr(idx_k_pages_e4m3), _ptr(idx_k_scale_pages), npages,
+                                     _ptr(block_table), maxb, _ptr(seq_len), N, H, G, d, dI, B,
+                                     kslots, _scale(scale, d), _ptr(out), _ptr(ids_out), _ptr(ws),
+                                     ws.numel(), _stream(dev))
+    _check(st, "msa_decode_paged_fp8idx")
     return (out, ids_out) if return_ids else out

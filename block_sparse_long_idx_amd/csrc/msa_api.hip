@@ -495,11 +495,53 @@ int msa_decode_fp8idx(const uint16_t *q, const uint16_t *idx_q, const uint16_t *
     uint16_t *po = c.take<uint16_t>((int64_t)N * H * kslots * d);
     float *plse = c.take<float>((int64_t)N * H * kslots);
     int32_t *ids = block_ids_out ? block_ids_out : ids_ws;
-    MSA_TIMED(kK1d8, launch_k1d_index_pool_fp8(idx_q, idx_k_e4m3, idx_k_scale, seq_len, S, N, Lmax,
-                                               G, dI, nbp, s));
+    MSA_TIMED(kK1d8, launch_k1d_index_pool_fp8(idx_q, idx_k_e4m3, idx_k_scale, seq_len, nullptr, 0,
+                                               S, N, Lmax, G, dI, nbp, s));
     MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, seq_len, Lmax, ids, s));
     MSA_TIMED(kK4d, launch_k4d_split(q, k_cache, v_cache, ids, seq_len, nullptr, 0, N, Lmax, H, G,
                                      d, kslots, scale, po, plse, s));
+    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, s));
+    return MSA_OK;
+}
+
+int msa_decode_paged_fp8idx(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_pages,
+                            const uint16_t *v_pages, const uint8_t *idx_k_pages_e4m3,
+                            const float *idx_k_scale_pages, int64_t num_pages,
+                            const int32_t *block_table, int max_blocks, const int32_t *seq_len,
+                            int N, int H, int G, int d, int dI, int B, int kslots, float scale,
+                            uint16_t *out, int32_t *block_ids_out, void *ws, size_t ws_bytes,
+                            void *stream) {
+    if (N < 0 || num_pages < 0 || max_blocks < 0 || H <= 0 || G <= 0 || d <= 0 || dI <= 0 ||
+        B <= 0 || kslots < 1 || H % G)
+        return MSA_ERR_INVALID_ARG;
+    if (N == 0) return MSA_OK;
+    if (max_blocks == 0 || num_pages == 0 || !q || !idx_q || !k_pages || !v_pages ||
+        !idx_k_pages_e4m3 || !idx_k_scale_pages || !block_table || !seq_len || !out)
+        return MSA_ERR_INVALID_ARG;
+    if (B != kBlock || !d_ok(d) || !r_ok(H, G) || !index_ok(G, dI) || kslots > 32 ||
+        (int64_t)max_blocks * B > INT32_MAX)
+        return MSA_ERR_UNSUPPORTED;
+    const int st = check_ws(ws, ws_bytes,
+                            msa_decode_paged_workspace_size(N, max_blocks, H, G, d, dI, B, kslots));
+    if (st != MSA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    scale = default_scale(scale, d);
+    const int64_t Lmax = (int64_t)max_blocks * B;
+    const int nbp = nb_padded(Lmax);
+    Carver c(ws);
+    float *S = c.take<float>((int64_t)N * G * nbp);
+    int32_t *ids_ws = c.take<int32_t>((int64_t)N * G * kslots);
+    uint16_t *po = c.take<uint16_t>((int64_t)N * H * kslots * d);
+    float *plse = c.take<float>((int64_t)N * H * kslots);
+    int32_t *eff_len = c.take<int32_t>(N);
+    int32_t *ids = block_ids_out ? block_ids_out : ids_ws;
+    // every later stage sees only lengths whose pages were checked
+    MSA_TIMED(kKpc, launch_page_check(block_table, max_blocks, num_pages, seq_len, N, eff_len, s));
+    MSA_TIMED(kK1d8, launch_k1d_index_pool_fp8(idx_q, idx_k_pages_e4m3, idx_k_scale_pages, eff_len,
+                                               block_table, max_blocks, S, N, Lmax, G, dI, nbp, s));
+    MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, eff_len, Lmax, ids, s));
+    MSA_TIMED(kK4d, launch_k4d_split(q, k_pages, v_pages, ids, eff_len, block_table, max_blocks, N,
+                                     Lmax, H, G, d, kslots, scale, po, plse, s));
     MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, s));
     return MSA_OK;
 }

@@ -306,10 +306,16 @@ __global__ __launch_bounds__(256) void k1d_index_pool_fp8(const uint16_t *__rest
                                                           const uint8_t *__restrict__ ik8,
                                                           const float *__restrict__ ksc,
                                                           const int32_t *__restrict__ seq_len,
-                                                          float *__restrict__ S, int64_t Lmax,
-                                                          int nbp, int sc_aligned) {
+                                                          const int32_t *__restrict__ table,
+                                                          int maxb, float *__restrict__ S,
+                                                          int64_t Lmax, int nbp, int sc_aligned) {
     constexpr int KS = DI / 32;
     constexpr int SPAN = 8 * KS;          // contiguous key bytes per lane and token
+    // first token row of block b: contiguous caches [N, Lmax, ...], or the block's
+    // page of paged caches [pages, 128, ...]
+    auto tok0 = [&](int64_t n, int b) {
+        return table ? (int64_t)table[n * maxb + b] * kBlock : n * Lmax + (int64_t)b * kBlock;
+    };
     const int n = blockIdx.y;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int b0 = (blockIdx.x * 4 + wave) * BPW;   // this wave's first block
@@ -331,7 +337,7 @@ __global__ __launch_bounds__(256) void k1d_index_pool_fp8(const uint16_t *__rest
     for (int bb = 0; bb < BPW; ++bb) {
         // a block past the sequence's competitors re-reads the first block (discarded)
         const int b = b0 + bb < ncomp ? b0 + bb : b0;
-        const uint8_t *base = ik8 + ((int64_t)n * Lmax + (int64_t)b * kBlock) * DI + SPAN * qt;
+        const uint8_t *base = ik8 + tok0(n, b) * DI + SPAN * qt;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             const uint8_t *p = base + (mt * 16 + l16) * DI;
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(256) void k1d_index_pool_fp8(const uint16_t *__rest
         const int b = b0 + bb;
         if (b >= ncomp) break;
         // token scales of this lane's accumulator rows: tokens mt*16 + 4*qt + r
-        const float *sp = ksc + (int64_t)n * Lmax + (int64_t)b * kBlock + 4 * qt;
+        const float *sp = ksc + tok0(n, b) + 4 * qt;
         float m = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
@@ -388,25 +394,28 @@ __global__ __launch_bounds__(256) void k1d_index_pool_fp8(const uint16_t *__rest
 
 template <int G, int DI>
 static hipError_t k1d8_dispatch(const uint16_t *iq, const uint8_t *ik8, const float *ksc,
-                                const int32_t *seq_len, float *S, int N, int64_t Lmax, int nbp,
-                                hipStream_t s) {
+                                const int32_t *seq_len, const int32_t *table, int maxb, float *S,
+                                int N, int64_t Lmax, int nbp, hipStream_t s) {
     const int64_t nbmax = (Lmax - 1) / kBlock;
     if (nbmax <= 0 || N <= 0) return hipSuccess;
-    const int aligned = (Lmax % 4 == 0) && (reinterpret_cast<uintptr_t>(ksc) % 16 == 0);
+    // 16-byte scale loads need every block's scales 16-byte aligned (pages of 128
+    // scales always are)
+    const int aligned = (table || Lmax % 4 == 0) && (reinterpret_cast<uintptr_t>(ksc) % 16 == 0);
     // two blocks per wave: 32 KB in flight per wave at 2 waves per SIMD (measured
     // faster than one block at 3 waves per SIMD, and than four at one wave)
     constexpr int BPW = 2;
     dim3 grid((unsigned)((nbmax + 4 * BPW - 1) / (4 * BPW)), (unsigned)N);
     hipLaunchKernelGGL((k1d_index_pool_fp8<G, DI, BPW>), grid, dim3(256), 0, s, iq, ik8, ksc,
-                       seq_len, S, Lmax, nbp, aligned);
+                       seq_len, table, maxb, S, Lmax, nbp, aligned);
     return hipGetLastError();
 }
 
 hipError_t launch_k1d_index_pool_fp8(const uint16_t *iq, const uint8_t *ik8, const float *ksc,
-                                     const int32_t *seq_len, float *S, int N, int64_t Lmax, int G,
-                                     int dI, int nbp, hipStream_t s) {
+                                     const int32_t *seq_len, const int32_t *table, int maxb,
+                                     float *S, int N, int64_t Lmax, int G, int dI, int nbp,
+                                     hipStream_t s) {
 #define K1D8_CASE(g, di) \
-    if (G == g && dI == di) return k1d8_dispatch<g, di>(iq, ik8, ksc, seq_len, S, N, Lmax, nbp, s);
+    if (G == g && dI == di) return k1d8_dispatch<g, di>(iq, ik8, ksc, seq_len, table, maxb, S, N, Lmax, nbp, s);
     K1D8_CASE(1, 32) K1D8_CASE(1, 64) K1D8_CASE(1, 128)
     K1D8_CASE(2, 32) K1D8_CASE(2, 64) K1D8_CASE(2, 128)
     K1D8_CASE(4, 32) K1D8_CASE(4, 64) K1D8_CASE(4, 128)

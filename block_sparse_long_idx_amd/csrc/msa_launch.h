@@ -35,9 +35,11 @@ hipError_t launch_k1d_index_pool(const uint16_t *iq, const uint16_t *ikc, const 
 
 // K1d over an FP8 (E4M3) index-key cache ik8 [N, Lmax, dI] with per-token fp32
 // scales ksc [N, Lmax]: score = ksc[t] * (iq . e4m3(ik8[t])).
+// table != nullptr: paged caches ik8 [pages, 128, dI], ksc [pages, 128] (as K1d).
 hipError_t launch_k1d_index_pool_fp8(const uint16_t *iq, const uint8_t *ik8, const float *ksc,
-                                     const int32_t *seq_len, float *S, int N, int64_t Lmax, int G,
-                                     int dI, int nbp, hipStream_t s);
+                                     const int32_t *seq_len, const int32_t *table, int maxb,
+                                     float *S, int N, int64_t Lmax, int G, int dI, int nbp,
+                                     hipStream_t s);
 
 // Index-key cache writer: rows [rows, dI] bf16 -> E4M3 bytes + power-of-two scales.
 hipError_t launch_quant_e4m3(const uint16_t *x, int64_t rows, int dI, uint8_t *out, float *scale,

@@ -214,6 +214,24 @@ MSA_API int msa_decode_fp8idx(const uint16_t *q, const uint16_t *idx_q, const ui
                               float scale, uint16_t *out, int32_t *block_ids_out, void *ws,
                               size_t ws_bytes, void *stream);
 
+/* Paged decode with an E4M3 index-key cache: the caches of msa_decode_paged, with
+ * the index keys in pages of E4M3 bytes and their per-token scales,
+ *   idx_k_pages_e4m3   [num_pages, 128, dI] uint8
+ *   idx_k_scale_pages  [num_pages, 128]     fp32 > 0
+ * addressed through the same block table (the index key of logical token t of
+ * sequence n is scale * e4m3(bytes) of row t % 128 of page block_table[n][t/128]).
+ * Scores, selection, attention, the page check and the error behaviour are those
+ * of msa_decode_fp8idx and msa_decode_paged.  Workspace:
+ * msa_decode_paged_workspace_size. */
+MSA_API int msa_decode_paged_fp8idx(const uint16_t *q, const uint16_t *idx_q,
+                                    const uint16_t *k_pages, const uint16_t *v_pages,
+                                    const uint8_t *idx_k_pages_e4m3, const float *idx_k_scale_pages,
+                                    int64_t num_pages, const int32_t *block_table, int max_blocks,
+                                    const int32_t *seq_len, int N, int H, int G, int d, int dI,
+                                    int B, int kslots, float scale, uint16_t *out,
+                                    int32_t *block_ids_out, void *ws, size_t ws_bytes,
+                                    void *stream);
+
 /* Index-key cache writer for msa_decode_fp8idx: rows [rows, dI] bf16 (dI in
  * {32, 64, 128}) -> E4M3 bytes [rows, dI] and scales [rows].  Per row: scale = 2^e
  * with e the smallest integer such that max|x| <= 448 * 2^e (1 for an all-zero

@@ -332,3 +332,49 @@ def decode_fp8idx(q, iq, k_cache, v_cache, ik8, kscale, seq_len, B, kslots, scal
                              _ptr(seq_len), Lmax, H, G, d, dI, B, kslots, float(scale),
                              _ptr(seqs), n, _ptr(ids), _ptr(gap), _ptr(out))
     return ids, gap, out
+
+
+def decode_paged_fp8idx(q, iq, k_pages, v_pages, ik8_pages, ksc_pages, block_table, seq_len, B,
+                        kslots, scale=None, seqs=None, lib=None):
+    """Paged decode with E4M3 index-key pages: (ids, gap, out, valid).
+
+    The listed sequences' pages (K, V, E4M3 index bytes and their scales) are
+    gathered in logical order into contiguous caches and decode_fp8idx runs on
+    them; invalid sequences as in decode_paged.
+    """
+    q, iq = _u16(q), _u16(iq)
+    kp, vp = _u16(k_pages), _u16(v_pages)
+    ik8p = np.ascontiguousarray(ik8_pages.cpu().numpy() if hasattr(ik8_pages, "cpu")
+                                else ik8_pages, np.uint8)
+    kscp = np.ascontiguousarray(ksc_pages.cpu().numpy() if hasattr(ksc_pages, "cpu")
+                                else ksc_pages, np.float32)
+    table = np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table,
+                       dtype=np.int64)
+    lens = np.asarray(seq_len.cpu() if hasattr(seq_len, "cpu") else seq_len, dtype=np.int64)
+    N, H, d = q.shape
+    G, dI = iq.shape[1], iq.shape[2]
+    seqs = _rows(seqs, N)
+    n_out = len(seqs)
+    ids = np.full((n_out, G, kslots), -1, np.int32)
+    gap = np.full((n_out, G), np.nan, np.float32)
+    out = np.zeros((n_out, H, d), np.float64)
+    pages = [_pages_of(table, lens, n, B, kp.shape[0]) for n in seqs]
+    valid = np.array([p is not None for p in pages], bool)
+    vr = np.nonzero(valid)[0]
+    if len(vr) == 0:
+        return ids, gap, out, valid
+    Lc = max(len(pages[r]) for r in vr) * B
+    kc = np.zeros((len(vr), Lc, G, d), np.uint16)
+    vc = np.zeros((len(vr), Lc, G, d), np.uint16)
+    ik8 = np.zeros((len(vr), Lc, dI), np.uint8)
+    ksc = np.ones((len(vr), Lc), np.float32)
+    for j, r in enumerate(vr):
+        n_tok = len(pages[r]) * B
+        kc[j, :n_tok] = kp[pages[r]].reshape(n_tok, G, d)
+        vc[j, :n_tok] = vp[pages[r]].reshape(n_tok, G, d)
+        ik8[j, :n_tok] = ik8p[pages[r]].reshape(n_tok, dI)
+        ksc[j, :n_tok] = kscp[pages[r]].reshape(n_tok)
+    sv = seqs[vr]
+    ids[vr], gap[vr], out[vr] = decode_fp8idx(q[sv], iq[sv], kc, vc, ik8, ksc, lens[sv], B,
+                                              kslots, scale, lib=lib)
+    return ids, gap, out, valid

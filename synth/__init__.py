@@ -66,7 +66,8 @@ class DecodeShape:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "prefill" | "prefill_varlen" | "decode" | "decode_paged" | "decode_fp8idx"
+    kind: str                 # "prefill" | "prefill_varlen" | "decode" | "decode_paged" |
+                              # "decode_fp8idx" | "decode_paged_fp8idx"
     shape: object
     plant: str = "lit"
     n_plant: int = 4
@@ -105,6 +106,10 @@ WORKLOADS = {
     "decode_fp8idx_N64_L262144": Workload("decode_fp8idx_N64_L262144", "decode_fp8idx",
                                           DecodeShape(N=64, Lc=262144, H=64, G=4, d=128,
                                                       dI=128)),
+    "decode_paged_fp8idx_N64_L262144": Workload("decode_paged_fp8idx_N64_L262144",
+                                                "decode_paged_fp8idx",
+                                                DecodeShape(N=64, Lc=262144, H=64, G=4, d=128,
+                                                            dI=128)),
 }
 
 
@@ -244,29 +249,34 @@ def decode_inputs(shape: DecodeShape, seed: int, plant: str = "lit", n_plant: in
     return out
 
 
-def paginate(x: dict, B: int, seed: int, extra_pages: int = 0) -> dict:
-    """Re-lay the contiguous decode caches of ``decode_inputs`` as B-token pages.
+def paginate(x: dict, B: int, seed: int, extra_pages: int = 0,
+             names=("k_cache", "v_cache", "ik_cache")) -> dict:
+    """Re-lay per-sequence caches [N, Lc, ...] (default: those of ``decode_inputs``)
+    as B-token pages, every cache with the same page order.
 
     Logical block b of sequence n goes to page ``block_table[n, b]``; the pages are
     a seeded random permutation of all N * ceil(Lc / B) blocks, followed by
-    ``extra_pages`` pages of N(0,1) data that no table entry names.  A cache whose
-    length is not a multiple of B is zero-padded to whole pages.  Returns
-    k_pages/v_pages [P, B, G, d], ik_pages [P, B, dI] (bf16) and block_table
-    [N, ceil(Lc / B)] (int32), on the caches' device.
+    ``extra_pages`` pages that no table entry names (N(0,1) for bf16 caches, zero
+    otherwise).  A cache whose length is not a multiple of B is zero-padded to whole
+    pages.  Returns, for each cache "<x>_cache" or "<x>", a pages tensor
+    "<x>_pages" [P, B, ...] on the caches' device, and block_table [N, ceil(Lc / B)]
+    (int32).
     """
-    kc, vc, ikc = x["k_cache"], x["v_cache"], x["ik_cache"]
-    N, Lc, G, d = kc.shape
-    dI = ikc.shape[2]
+    first = x[names[0]]
+    N, Lc = first.shape[0], first.shape[1]
     nblk = (Lc + B - 1) // B
     pad = nblk * B - Lc
-    dev = kc.device
+    dev = first.device
     gen = torch.Generator().manual_seed(_seed(seed, T_PLANT, 7))
     perm = torch.randperm(N * nblk, generator=gen).to(dev)
     P = N * nblk + extra_pages
 
-    def lay(cache, row_shape, tid):
-        pages = randn_bf16((P, B) + row_shape, seed, tid, dev) if extra_pages else \
-            torch.empty((P, B) + row_shape, dtype=cache.dtype, device=dev)
+    def lay(cache, tid):
+        row_shape = tuple(cache.shape[2:])
+        if extra_pages and cache.dtype == torch.bfloat16:
+            pages = randn_bf16((P, B) + row_shape, seed, tid, dev)
+        else:
+            pages = torch.zeros((P, B) + row_shape, dtype=cache.dtype, device=dev)
         blocks = cache
         if pad:
             blocks = torch.cat([cache, torch.zeros((N, pad) + row_shape, dtype=cache.dtype,
@@ -274,9 +284,8 @@ def paginate(x: dict, B: int, seed: int, extra_pages: int = 0) -> dict:
         pages[perm] = blocks.reshape((N * nblk, B) + row_shape)
         return pages
 
-    return {
-        "k_pages": lay(kc, (G, d), 11),
-        "v_pages": lay(vc, (G, d), 12),
-        "ik_pages": lay(ikc, (dI,), 13),
-        "block_table": perm.view(N, nblk).to(torch.int32),
-    }
+    out = {"block_table": perm.view(N, nblk).to(torch.int32)}
+    for i, name in enumerate(names):
+        key = (name[:-len("_cache")] if name.endswith("_cache") else name) + "_pages"
+        out[key] = lay(x[name], 11 + i)
+    return out

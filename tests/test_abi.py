@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     names = _declared()
     for want in ("msa_select_blocks", "msa_sparse_attn", "msa_prefill", "msa_prefill_varlen",
                  "msa_decode",
-                 "msa_decode_paged", "msa_decode_fp8idx", "msa_quantize_idx_k_e4m3",
+                 "msa_decode_paged", "msa_decode_fp8idx", "msa_decode_paged_fp8idx",
+                 "msa_quantize_idx_k_e4m3",
                  "msa_select_blocks_workspace_size",
                  "msa_sparse_attn_workspace_size", "msa_prefill_workspace_size",
                  "msa_decode_workspace_size", "msa_decode_paged_workspace_size",
@@ -205,3 +206,21 @@ def test_varlen_prefill_arguments(lib):
     assert call([0, 100], [0, 1048576 + 228]) == UNSUPPORTED   # longer than 2^20 tokens
     assert call([0, 100], [0, 100], B=64) == UNSUPPORTED
     assert call([0, 100], [0, 100], nbytes=ctypes.c_size_t(64)) == WS_SMALL
+
+
+def test_paged_fp8_decode_arguments(lib):
+    f, ws, big, s = _fake(), P(0x100000), ctypes.c_size_t(1 << 40), None
+    zero = ctypes.c_float(0)
+
+    def call(ik8=f, sc=f, table=f, N=2, npages=16, maxb=8, B=128, dI=32, nbytes=big):
+        return lib.msa_decode_paged_fp8idx(f, f, f, f, ik8, sc, npages, table, maxb, f, N, 8, 2,
+                                           64, dI, B, 4, zero, f, None, ws, nbytes, s)
+
+    assert call(N=0, ik8=None, sc=None, table=None) == OK
+    assert call(ik8=None) == INVALID
+    assert call(sc=None) == INVALID
+    assert call(table=None) == INVALID
+    assert call(npages=0) == INVALID
+    assert call(B=64) == UNSUPPORTED
+    assert call(dI=48) == UNSUPPORTED
+    assert call(nbytes=ctypes.c_size_t(64)) == WS_SMALL

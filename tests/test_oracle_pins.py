@@ -472,10 +472,31 @@ def check_fp8_decode(lib):
     assert list(ids2[0, 0]) == [1, 4]
 
 
+def check_paged_fp8_decode(lib):
+    """Paged decode over E4M3 index-key pages equals the contiguous E4M3 decode on
+    the caches an independent seeded page permutation scatters."""
+    B, k = 16, 4
+    sh = synth.DecodeShape(N=3, Lc=170, H=4, G=2, d=16, dI=8, B=B, k=k)
+    seq_len = np.array([170, 33, 120], np.int64)
+    x = synth.decode_inputs(sh, seed=27, seq_len=seq_len)
+    codes, sc = oracle.quantize_e4m3_rows(x["ik_cache"], lib)
+    x["ik8"], x["ik_scale"] = torch.from_numpy(codes), torch.from_numpy(sc * 1.5)
+    pg = synth.paginate(x, B, seed=27, extra_pages=2,
+                        names=("k_cache", "v_cache", "ik8", "ik_scale"))
+    scale = 1.0 / math.sqrt(sh.d)
+    ids, gap, out = oracle.decode_fp8idx(x["q"], x["iq"], x["k_cache"], x["v_cache"], x["ik8"],
+                                         x["ik_scale"], seq_len, B, k, scale, lib=lib)
+    idsp, gapp, outp, valid = oracle.decode_paged_fp8idx(
+        x["q"], x["iq"], pg["k_pages"], pg["v_pages"], pg["ik8_pages"], pg["ik_scale_pages"],
+        pg["block_table"], seq_len, B, k, scale, lib=lib)
+    assert valid.all()
+    assert np.array_equal(idsp, ids) and np.array_equal(outp, out)
+
+
 PINS = [check_dense_equivalence, check_local_only, check_masked_attention, check_exp_free,
         check_constructed, check_tie_break, check_brute_force, check_invariants,
         check_properties, check_prefix_and_decode, check_paged_decode, check_e4m3,
-        check_fp8_decode]
+        check_fp8_decode, check_paged_fp8_decode]
 
 
 @pytest.mark.parametrize("check", PINS, ids=[c.__name__ for c in PINS])

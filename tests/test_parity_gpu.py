@@ -575,6 +575,58 @@ def test_fp8_decode_full_size_subset():
                       device=DEV)
 
 
+def test_paged_fp8_decode():
+    """Paged decode over E4M3 index-key pages: the oracle on a ragged batch (with a
+    bad page id and a too-long sequence), and bitwise equality with the contiguous
+    E4M3 decode on the full-size workload."""
+    msa = _msa()
+    # ragged batch vs the oracle
+    shape = synth.DecodeShape(N=6, Lc=3000, H=16, G=4, d=128, dI=128, B=128, k=8)
+    seq_len = np.array([3000, 2500, 129, 1, 2000, 3000])
+    x = synth.decode_inputs(shape, seed=14, seq_len=np.clip(seq_len, 1, shape.Lc))
+    codes, sc = oracle.quantize_e4m3_rows(x["ik_cache"])
+    x["ik8"], x["ik_scale"] = torch.from_numpy(codes), torch.from_numpy(sc)
+    pg = synth.paginate(x, 128, seed=14, extra_pages=2,
+                        names=("k_cache", "v_cache", "ik8", "ik_scale"))
+    table = pg["block_table"].clone()
+    table[4, 3] = pg["k_pages"].shape[0]               # a page past the pool
+    seq_len[5] = table.shape[1] * 128 + 1              # longer than its table
+    _say(f"paged fp8 decode N={shape.N} seq_len={list(seq_len)}")
+    g = {n: t.to(DEV) for n, t in pg.items()}
+    sl = torch.tensor(seq_len.astype(np.int32), device=DEV)
+    out, ids = msa.decode_paged_fp8idx(x["q"].to(DEV), x["iq"].to(DEV), g["k_pages"],
+                                       g["v_pages"], g["ik8_pages"], g["ik_scale_pages"],
+                                       table.to(DEV), sl, kslots=shape.k, return_ids=True)
+    torch.cuda.synchronize()
+    out, ids = out.float().cpu().numpy(), ids.cpu().numpy()
+    scale = 1.0 / math.sqrt(shape.d)
+    oids, gap, oout, valid = oracle.decode_paged_fp8idx(
+        x["q"], x["iq"], pg["k_pages"], pg["v_pages"], pg["ik8_pages"], pg["ik_scale_pages"],
+        table, seq_len, 128, shape.k, scale)
+    assert list(valid) == [True, True, True, True, False, False]
+    vs = np.nonzero(valid)[0]
+    tie, nmis = _parity.compare_ids(ids[vs], oids[vs], gap[vs])
+    assert not tie.any() and nmis == 0
+    mx, mean = _parity.compare_out(out[vs], oout[vs])
+    _say(f"  -> mismatches {nmis} max {mx:.3e} mean {mean:.3e}")
+    assert mx < _parity.MAX_ABS and mean < _parity.MEAN_ABS
+    assert (ids[~valid] == -1).all() and (out[~valid] == 0).all()
+    # full size: paged == contiguous, bitwise
+    shape = synth.WORKLOADS["decode_N64_L262144"].shape
+    x = synth.decode_inputs(shape, seed=3, device=DEV)
+    x["ik8"], x["ik_scale"] = _refs.e4m3_rows_torch(x["ik_cache"])
+    sl = torch.tensor(np.asarray(x["seq_len"], np.int32), device=DEV)
+    o1, i1 = msa.decode_fp8idx(x["q"], x["iq"], x["k_cache"], x["v_cache"], x["ik8"],
+                               x["ik_scale"], sl, kslots=shape.k, return_ids=True)
+    pg = synth.paginate(x, 128, seed=3, names=("k_cache", "v_cache", "ik8", "ik_scale"))
+    o2, i2 = msa.decode_paged_fp8idx(x["q"], x["iq"], pg["k_pages"], pg["v_pages"],
+                                     pg["ik8_pages"], pg["ik_scale_pages"], pg["block_table"], sl,
+                                     kslots=shape.k, return_ids=True)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
 def test_chunked_workspace_invariance():
     """A smaller workspace makes the library split the queries into several chunks;
     every row's result must be bitwise the same as with one chunk."""
