@@ -656,15 +656,9 @@ def test_chunked_workspace_invariance():
                     workspace=msa._workspace(4096, DEV))
 
 
-def _constructed_select(L, w, k, rows):
-    """idx_k rows w[t] * e_0 and idx_q = e_0 (G = 1, dI = 32): every token score is
-    w[t] exactly, so block scores and ties are fixed by construction."""
+def _select_vs_oracle(iq, ik, k, rows):
+    """select_blocks on the GPU and the oracle's selection for the same rows."""
     msa = _msa()
-    dI = 32
-    ik = torch.zeros((L, dI), dtype=torch.bfloat16)
-    ik[:, 0] = torch.as_tensor(w, dtype=torch.float32).to(torch.bfloat16)
-    iq = torch.zeros((L, 1, dI), dtype=torch.bfloat16)
-    iq[:, 0, 0] = 1.0
     ids = msa.select_blocks(iq.to(DEV), ik.to(DEV), k=k)
     torch.cuda.synchronize()
     S = oracle.block_scores(iq, ik, 128, rows=rows)
@@ -674,10 +668,22 @@ def _constructed_select(L, w, k, rows):
     return got, oids
 
 
-def test_select_ties_and_candidate_overflow_1m():
+def _constructed_select(L, w, k, rows):
+    """idx_k rows w[t] * e_0 and idx_q = e_0 (G = 1, dI = 32): every token score is
+    w[t] exactly, so block scores and ties are fixed by construction."""
+    dI = 32
+    ik = torch.zeros((L, dI), dtype=torch.bfloat16)
+    ik[:, 0] = torch.as_tensor(w, dtype=torch.float32).to(torch.bfloat16)
+    iq = torch.zeros((L, 1, dI), dtype=torch.bfloat16)
+    iq[:, 0, 0] = 1.0
+    return _select_vs_oracle(iq, ik, k, rows)
+
+
+def test_select_ties_and_spread_maxima_1m():
     """L = 2^20 (8191 competitors per row at the end): (a) all scores equal, so the
-    smallest ids win; (b) one lane of the selector's row layout holds 128 equal
-    maxima, more than its 64-entry candidate list, forcing the exact fallback."""
+    smallest ids win; (b) 128 equal maxima spread along the row (four in every 256
+    blocks), so the tie between the register-held head and the streamed rest of
+    the row decides the selection."""
     L, k = 1 << 20, 16
     rows = np.array([L - 1, L - 128, L // 2, 200000, 4096, 2047])
     blk = np.arange(L) // 128
@@ -687,10 +693,61 @@ def test_select_ties_and_candidate_overflow_1m():
     for r, i in enumerate(rows):
         bi = i // 128
         assert got[r, 0].tolist() == list(range(min(k - 1, bi))) + [bi] + [-1] * max(0, k - bi - 1)
-    _say("select candidate overflow, L=2^20")
+    _say("select spread maxima, L=2^20")
     w = np.where(blk % 256 < 4, 1000.0, -(blk % 200).astype(np.float64))
     got, want = _constructed_select(L, w, k, rows)
     assert (got == want).all()
+
+
+# Row lengths (competitor counts b(i)) around the selector's layout: 4 scores per
+# lane, a 1024-score register head, 256-score streaming steps, a 64-entry list.
+_ADV_NB = [16, 17, 18, 31, 32, 59, 60, 61, 63, 64, 65, 127, 255, 256, 257, 511, 1023, 1024,
+           1025, 1279, 1280, 1281, 2047]
+_ADV_PATTERNS = ["normal", "equal", "inc", "dec", "mod3", "few", "spikes", "inc_head_dec"]
+
+
+@pytest.mark.parametrize("pattern", _ADV_PATTERNS)
+def test_select_constructed_block_scores(pattern):
+    """Block scores fixed by construction (G = 1, dI = 32, L = 262144): one peak token
+    per block at a block-dependent offset, the block's other tokens strictly lower.
+    Increasing scores make every streamed score beat the running threshold (the
+    candidate list is cut again and again); decreasing ones admit nothing after the
+    head; equal, mod3 and few-valued scores tie heavily (the equal rows overflow the
+    list from the head alone).  Ids must equal the oracle's exactly for k = 4, 16, 32."""
+    nb, dI = 2048, 32
+    L = nb * 128
+    rng = np.random.default_rng(7)
+    b = np.arange(nb)
+    w = {"normal": rng.standard_normal(nb), "equal": np.ones(nb), "inc": b, "dec": -b,
+         "mod3": b % 3, "few": rng.integers(0, 4, nb),
+         "spikes": np.where(b % 256 < 4, 1000, -(b % 200)),
+         "inc_head_dec": np.where(b < 1024, b, -b)}[pattern]
+    t = np.arange(L)
+    blk, off = t // 128, t % 128
+    peak = off == (blk * 37) % 128
+    ik = torch.zeros((L, dI), dtype=torch.bfloat16)
+    iq = torch.zeros((L, 1, dI), dtype=torch.bfloat16)
+    iq[:, 0, 0] = 1.0
+    if pattern == "normal":
+        wb = torch.as_tensor(w, dtype=torch.float32).to(torch.bfloat16).float().numpy()[blk]
+        other = wb - 1.0 - (off % 5)                   # strictly below the peak after bf16 rounding
+        ik[:, 0] = torch.as_tensor(np.where(peak, wb, other), dtype=torch.float32).to(torch.bfloat16)
+    else:
+        # integer scores as hi + lo (hi a multiple of 256, lo in [-5, 255]): both exact
+        # in bf16, and their sum exact in fp32
+        wb = np.asarray(w, dtype=np.int64)[blk]
+        lo = np.mod(wb, 256)
+        hi = wb - lo
+        lo = np.where(peak, lo, lo - 1 - off % 5)
+        ik[:, 0] = torch.as_tensor(hi, dtype=torch.float32).to(torch.bfloat16)
+        ik[:, 1] = torch.as_tensor(lo, dtype=torch.float32).to(torch.bfloat16)
+        iq[:, 0, 1] = 1.0
+    rows = np.array([n * 128 + (n * 13) % 128 for n in _ADV_NB])
+    for k in (4, 16, 32):
+        _say(f"select constructed {pattern} k={k}")
+        got, want = _select_vs_oracle(iq, ik, k, rows)
+        bad = np.nonzero((got != want).any(-1))[0]
+        assert len(bad) == 0, f"rows with b(i) = {[_ADV_NB[j] for j in bad]} differ"
 
 
 def test_prefill_1m_hot_sampled():
