@@ -284,25 +284,30 @@ def copy_calibration(gib: float):
 
 
 def _load_traffic(kernel: str, workload: str):
-    """HBM traffic per launch from committed rocprofv3 counter summaries, if any
-    are recorded for this kernel, workload and the current kernel sources."""
+    """HBM traffic per launch from a committed rocprofv3 counter summary, if one is
+    recorded for this kernel and workload and the source files it names (those
+    that decide the kernel's code, launch and work list) are unchanged."""
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", f"traffic_{kernel}_{workload}.md")
     if not os.path.exists(path):
         return None
-    src = os.path.join(here, "block_sparse_long_idx_amd", "csrc")
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(src)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(src, f), "rb").read())
-    digest = h.hexdigest()[:16]
     rec = {}
     for line in open(path):
         if ":" in line and line.strip().startswith("-"):
             key, _, val = line.strip("- \n").partition(":")
             rec[key.strip()] = val.strip()
-    if rec.get("sources_sha256_16") != digest:
+    files = rec.get("sources", "").split()
+    if not files:
+        return None
+    src = os.path.join(here, "block_sparse_long_idx_amd", "csrc")
+    h = hashlib.sha256()
+    for f in files:
+        fp = os.path.join(src, f)
+        if not os.path.exists(fp):
+            return None
+        h.update(open(fp, "rb").read())
+    if rec.get("sources_sha256_16") != h.hexdigest()[:16]:
         return None
     try:
         return float(rec["hbm_bytes_per_launch"])
