@@ -50,12 +50,13 @@ __device__ __forceinline__ void load_q(bf16x8 (&qb)[D / 16], const uint16_t *qro
 //   qb     : the column's q row as the B operand (see load_q)
 //   qpos   : the column's token position (its causal limit in its own block)
 //   j      : the staged KV block
-//   orow / lse_dst : destination of the column's partial (written when active)
-template <int D>
+//   emit   : receives the column's normalised partial as bf16 16-byte chunks --
+//            w[u] holds chunk 4(u/2) + 2(u%2) + hf of the row (elements 8c .. 8c+7) --
+//            and its log2-sum-exp, and writes them
+template <int D, typename Emit>
 __device__ __forceinline__ void attend_pass(const char *lds_k, const char *lds_vt, int j,
                                             const bf16x8 (&qb)[D / 16], bool active, int64_t qpos,
-                                            uint16_t *orow, float *lse_dst, float scale_log2,
-                                            int lane) {
+                                            float scale_log2, int lane, Emit emit) {
     constexpr int KS = D / 16;   // K-steps of S^T over d
     constexpr int CPR = D / 8;
     constexpr int MD = D / 32;   // M-tiles of O^T over d
@@ -131,9 +132,10 @@ __device__ __forceinline__ void attend_pass(const char *lds_k, const char *lds_v
         __builtin_amdgcn_sched_barrier(0);
     }
     // normalise, pack to bf16, and swap half-rows between the lane halves
-    // (v_permlane32_swap) so each lane stores 8 consecutive d values (16 bytes):
+    // (v_permlane32_swap) so each lane holds 8 consecutive d values (16 bytes):
     // before, lane half hf holds d = 16q + 4hf + {0..3} and 16q + 8 + 4hf + {0..3}
     const float inv = 1.0f / sum;
+    u32x4 w[D / 16];
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
 #pragma unroll
@@ -146,12 +148,56 @@ __device__ __forceinline__ void attend_pass(const char *lds_k, const char *lds_v
             uint32_t b1 = pack_bf16x2(acc[r0 + 6] * inv, acc[r0 + 7] * inv);
             const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
             const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-            // lower half now holds d = 16q2 + 0..7, upper half d = 16q2 + 8..15
-            if (active)
-                store16(orow + 32 * md + 16 * q2 + 8 * hf, u32x4{s0[0], s1[0], s0[1], s1[1]});
+            // lower half now holds d = 32md + 16q2 + 0..7, upper half 32md + 16q2 + 8..15
+            w[2 * md + q2] = u32x4{s0[0], s1[0], s0[1], s1[1]};
         }
     }
-    if (active && hf == 0) *lse_dst = mx * scale_log2 + __log2f(sum);
+    emit(w, mx * scale_log2 + __log2f(sum));
+}
+
+// Writes the 32 partial rows of a pass (row = MFMA column, 2D bytes) through the
+// wave's LDS staging buffer, 8 rows per round, so that every global store writes
+// whole rows (CR = D/8 lanes x 16 bytes per row) rather than 32-byte pieces of 32
+// rows: scattered 32-byte writes cost HBM write bandwidth.  w is attend_pass's
+// chunk layout; row_dst(row) is the destination of a row, nullptr if inactive.
+// The row pitch is padded by 32 bytes so the staging writes are bank-conflict free.
+template <int D>
+constexpr int kStageBytes = 8 * (2 * D + 32);
+
+template <int D, typename RowDst>
+__device__ __forceinline__ void store_rows_staged(char *stg, const u32x4 (&w)[D / 16], int lane,
+                                                  RowDst row_dst) {
+    constexpr int CR = D / 8;
+    constexpr int PITCH = 2 * D + 32;
+    constexpr int NR = 8 * CR / kWave;    // chunks a lane moves per round
+    const int l32 = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if ((l32 >> 3) == r) {
+#pragma unroll
+            for (int u = 0; u < D / 16; ++u) {
+                const int c = 4 * (u >> 1) + 2 * (u & 1) + hf;
+                *reinterpret_cast<u32x4 *>(stg + (l32 & 7) * PITCH + 16 * c) = w[u];
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        u32x4 v[NR];
+#pragma unroll
+        for (int x = 0; x < NR; ++x) {
+            const int idx = x * kWave + lane;
+            v[x] = *reinterpret_cast<const u32x4 *>(stg + (idx / CR) * PITCH + 16 * (idx % CR));
+        }
+        // every lane has read this round's rows before the next round overwrites them
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+        for (int x = 0; x < NR; ++x) {
+            const int idx = x * kWave + lane;
+            uint16_t *dst = row_dst(8 * r + idx / CR);
+            if (dst) store16(dst + 8 * (idx % CR), v[x]);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -168,6 +214,10 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     __shared__ __attribute__((aligned(16))) char lds_vt[D * kBlock * 2];
     static_assert(kK4Queries <= 256, "one entry per thread is staged");
     __shared__ uint32_t lds_e[kK4Queries];                   // the item's (query, slot) entries
+    // Whole-row partial stores through LDS; the d = 128, R = 4 build runs out of
+    // registers with them (it spills), so it keeps the per-lane 16-byte stores.
+    constexpr bool kStaged = !(D == 128 && R == 4);
+    __shared__ __attribute__((aligned(16))) char lds_stg[4][kStaged ? kStageBytes<D> : 16];
     const int per = gridDim.x / 8;
     const int x = (blockIdx.x % 8) * per + blockIdx.x / 8;   // XCD-contiguous items
     if (x >= *total) return;
@@ -220,10 +270,28 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
 
         const int64_t il = entry >> 5;
         const int s = entry & 31;
-        const int64_t prow = (il * H + hh) * kslots + s;
         const int64_t lrow = ((il * G + g) * kslots + s) * R + h;
-        attend_pass<D>(lds_k, lds_vt, j, qb, act, q0 + il, po + prow * D, plse + lrow, scale_log2,
-                       lane);
+        const int pbase = base;
+        const uint32_t pentry = entry;
+        attend_pass<D>(lds_k, lds_vt, j, qb, act, q0 + il, scale_log2, lane,
+                       [&](const u32x4 (&w)[D / 16], float lse) {
+                           if (act && hf == 0) plse[lrow] = lse;
+                           if constexpr (kStaged) {
+                               // row = column: query col / R of the pass, head col % R
+                               store_rows_staged<D>(lds_stg[wave], w, lane, [&](int col) -> uint16_t * {
+                                   const int qa = col / R;
+                                   const uint32_t e = __shfl(pentry, qa * R, kWave);
+                                   if (pbase + qa >= cnt) return nullptr;
+                                   return po + (((int64_t)(e >> 5) * H + (int64_t)g * R + col % R) *
+                                                    kslots + (e & 31)) * D;
+                               });
+                           } else if (act) {
+                               uint16_t *orow = po + ((il * H + hh) * kslots + s) * D;
+#pragma unroll
+                               for (int u = 0; u < D / 16; ++u)
+                                   store16(orow + 8 * (4 * (u >> 1) + 2 * (u & 1) + hf), w[u]);
+                           }
+                       });
         base = nbase;
         act = nact;
         entry = nentry;
@@ -343,8 +411,15 @@ __global__ __launch_bounds__(256, 2) void k4d_split(const uint16_t *__restrict__
             const int64_t lrow = ((n * G + g) * kslots + s) * R + (active ? l32 : 0);
             bf16x8 qb[D / 16];
             load_q<D>(qb, q + (n * H + hh) * D, active, lane >> 5);
-            attend_pass<D>(lds_k, lds_vt, j, qb, active, p, po + prow * D, plse + lrow,
-                           scale_log2, lane);
+            const int hf = lane >> 5;
+            attend_pass<D>(lds_k, lds_vt, j, qb, active, p, scale_log2, lane,
+                           [&](const u32x4 (&w)[D / 16], float lse) {
+                               if (!active) return;
+#pragma unroll
+                               for (int u = 0; u < D / 16; ++u)
+                                   store16(po + prow * D + 8 * (4 * (u >> 1) + 2 * (u & 1) + hf), w[u]);
+                               if (hf == 0) plse[lrow] = lse;
+                           });
             __syncthreads();                       // (B)
         }
     } else {
