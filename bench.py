@@ -368,8 +368,9 @@ def main():
         T = wl.batch * s.L
         out = torch.empty_like(x["q"])
         ids = torch.empty((T, s.G, s.k), dtype=torch.int32, device=dev)
-        ws = msa._workspace(msa.workspace_size("prefill", L=s.L, H=s.H, G=s.G, d=s.d, dI=s.dI,
-                                               k=s.k), dev)
+        cu_all = [b * s.L for b in range(wl.batch + 1)]
+        ws = msa._workspace(msa.workspace_size("prefill_varlen", cu_q=cu_all, cu_kv=cu_all, H=s.H,
+                                               G=s.G, d=s.d, dI=s.dI, k=s.k), dev)
         if wl.chunk:       # one sequence, `chunk` new tokens per call over the cached prefix
             calls = []
             for P in range(0, s.L, wl.chunk):

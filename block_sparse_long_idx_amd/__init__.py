@@ -101,6 +101,8 @@ def load_library():
     lib.msa_prefill_varlen.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
                                        f32, P, P, P, sz, P]
     lib.msa_prefill_varlen.restype = i32
+    lib.msa_prefill_varlen_workspace_size.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32]
+    lib.msa_prefill_varlen_workspace_size.restype = sz
     lib.msa_decode_fp8idx.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, i32, i32,
                                       f32, P, P, P, sz, P]
     lib.msa_decode_fp8idx.restype = i32
@@ -175,6 +177,13 @@ def workspace_size(kind: str, **kw) -> int:
     if kind == "decode_paged":
         return lib.msa_decode_paged_workspace_size(kw["N"], kw["max_blocks"], kw["H"], kw["G"],
                                                    kw["d"], kw["dI"], kw.get("B", 128), kw["k"])
+    if kind == "prefill_varlen":
+        import numpy as np
+        cq = np.ascontiguousarray(np.asarray(kw["cu_q"], dtype=np.int64))
+        ckv = np.ascontiguousarray(np.asarray(kw["cu_kv"], dtype=np.int64))
+        return lib.msa_prefill_varlen_workspace_size(cq.ctypes.data, ckv.ctypes.data, len(cq) - 1,
+                                                     kw["H"], kw["G"], kw["d"], kw["dI"],
+                                                     kw.get("B", 128), kw["k"])
     raise ValueError(kind)
 
 
@@ -398,8 +407,8 @@ def prefill_varlen(q, k, v, idx_q, idx_k, cu_q, cu_kv, kslots: int = 16, B: int 
         out = torch.empty_like(q)
     if return_ids and ids_out is None:
         ids_out = torch.empty((Tq, G, kslots), dtype=torch.int32, device=dev)
-    max_L = int((ckv[1:] - ckv[:-1]).max()) if nseq > 0 else 0
-    nbytes = lib.msa_prefill_workspace_size(max(max_L, 1), H, G, d, dI, B, kslots)
+    nbytes = lib.msa_prefill_varlen_workspace_size(cq.ctypes.data, ckv.ctypes.data, nseq, H, G, d,
+                                                   dI, B, kslots)
     ws = workspace if workspace is not None else _workspace(nbytes, dev)
     st = lib.msa_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(idx_q), _ptr(idx_k),
                                 cq.ctypes.data, ckv.ctypes.data, nseq, H, G, d, dI, B, kslots,

@@ -165,9 +165,12 @@ int attn_chunk(const uint16_t *q, const uint16_t *kx, const uint16_t *vx, const 
                uint16_t *out, const AttnWs &w, hipStream_t s) {
     const int64_t C = qend - q0;
     const int nbc = (int)((qend - 1) / kBlock + 1);
-    MSA_TIMED(kK3, launch_k3_schedule(ids_c, C, G, k, nbc, w.sb, s));
-    MSA_TIMED(kK4, launch_k4_kv_outer(q, kx, vx, w.sb, nbc, L, q0, C, H, G, d, k, scale, w.po, w.plse, s));
-    MSA_TIMED(kK5, launch_k5_combine(w.po, w.plse, ids_c, C, H, G, d, k, nbc, out + q0 * H * d, s));
+    const BatchMap single;
+    MSA_TIMED(kK3, launch_k3_schedule(ids_c, C, G, k, nbc, w.sb, single, s));
+    MSA_TIMED(kK4, launch_k4_kv_outer(q, kx, vx, w.sb, nbc, L, q0, C, H, G, d, k, scale, w.po, w.plse,
+                                      single, s));
+    MSA_TIMED(kK5, launch_k5_combine(w.po, w.plse, ids_c, C, H, G, d, k, nbc, out + q0 * H * d,
+                                     single, s));
     return MSA_OK;
 }
 
@@ -295,6 +298,126 @@ T *rows_back(T *p, int64_t rows, int64_t row_elems) {
     return reinterpret_cast<T *>(reinterpret_cast<intptr_t>(p) - bytes);
 }
 
+// ------------------- varlen prefill: batches of sequences -------------------
+// Short sequences are prefilled together: K1 ... K5 run once over the rows of a
+// batch of up to kBatchMaxSeq sequences, so that a batch of short prompts costs a
+// few launches instead of a few per sequence.  Results are identical to
+// prefilling every sequence on its own.
+
+// Workspace of one batch: `rows` new tokens over `blocks` KV blocks, block-score
+// rows of nbp entries.
+size_t batch_bytes(int64_t rows, int64_t blocks, int nbp, int H, int G, int d, int k) {
+    Carver c(nullptr);
+    c.take<float>(rows * G * nbp);
+    c.take<int32_t>(rows * G * k);
+    for (int m = 0; m < 3; ++m) c.take<int32_t>(rows);
+    for (int m = 0; m < 2; ++m) c.take<int32_t>(blocks);
+    c.take<BatchTable>(1);
+    carve_attn(c, rows, H, G, d, k, (int)blocks);
+    return c.used;
+}
+
+// Greedy batching, in sequence order: a sequence with at most kBatchMaxNew new
+// tokens joins the open batch while the batch stays within kBatchMaxSeq sequences,
+// kChunkQ rows, kBatchMaxBlocks blocks and `ws_limit` bytes; a longer sequence
+// runs alone (measured: alone, the q rows of one long sequence stay in the
+// last-level cache across the attention's 16 re-reads of each row, which beats
+// the saved launches from about 16384 new tokens on).  Sequences without new
+// tokens are skipped.  Calls run(batch) for every batch in order (the caller
+// prefills a single-member batch as an ordinary sequence, chunked if need be).
+constexpr int64_t kBatchMaxNew = 8192;
+struct BatchPlan {
+    int members[kBatchMaxSeq];
+    int n = 0;
+    bool solo = false;       // the first member runs alone
+    int64_t rows = 0, blocks = 0;
+    int nbp = 8;
+};
+template <typename Run>
+int plan_batches(const int64_t *cu_q, const int64_t *cu_kv, int nseq, int H, int G, int d, int k,
+                 size_t ws_limit, bool allow_batch, Run run) {
+    BatchPlan b;
+    for (int sq = 0; sq < nseq; ++sq) {
+        const int64_t C = cu_q[sq + 1] - cu_q[sq], L = cu_kv[sq + 1] - cu_kv[sq];
+        if (C == 0) continue;
+        const bool batchable = allow_batch && C <= kBatchMaxNew;
+        if (b.n > 0) {
+            const int64_t rows = b.rows + C, blocks = b.blocks + nblocks(L);
+            const int nbp = std::max(b.nbp, nb_padded(L));
+            const bool join = batchable && !b.solo && b.n < kBatchMaxSeq && rows <= kChunkQ &&
+                              blocks <= kBatchMaxBlocks &&
+                              batch_bytes(rows, blocks, nbp, H, G, d, k) <= ws_limit;
+            if (!join) {
+                const int rc = run(b);
+                if (rc != MSA_OK) return rc;
+                b = BatchPlan{};
+            }
+        }
+        if (b.n == 0) b.solo = !batchable;
+        b.members[b.n++] = sq;
+        b.rows += C;
+        b.blocks += nblocks(L);
+        b.nbp = std::max(b.nbp, nb_padded(L));
+    }
+    return b.n > 0 ? run(b) : MSA_OK;
+}
+
+int run_batch(const BatchPlan &b, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+              const uint16_t *idx_q, const uint16_t *idx_k, const int64_t *cu_q,
+              const int64_t *cu_kv, int H, int G, int d, int dI, int kslots, float scale,
+              uint16_t *out, int32_t *block_ids_out, void *ws, hipStream_t s) {
+    BatchTable t;
+    t.n = b.n;
+    t.rows = (int)b.rows;
+    t.blocks = (int)b.blocks;
+    const int64_t q_base = cu_q[b.members[0]];
+    int64_t maxL = 0, blk = 0, k1wg = 0;
+    for (int m = 0; m < b.n; ++m) {
+        const int sq = b.members[m];
+        const int64_t L = cu_kv[sq + 1] - cu_kv[sq], C = cu_q[sq + 1] - cu_q[sq];
+        t.q_off[m] = (int)(cu_q[sq] - q_base);
+        t.blk_off[m] = (int)blk;
+        t.k1_off[m] = (int)k1wg;
+        t.kv_off[m] = (int)cu_kv[sq];
+        t.kv_len[m] = (int)L;
+        blk += nblocks(L);
+        k1wg += k1_num_workgroups(L - C, L, G);
+        maxL = std::max(maxL, L);
+    }
+    t.q_off[b.n] = t.rows;
+    t.blk_off[b.n] = t.blocks;
+    t.k1_off[b.n] = (int)k1wg;
+    const int64_t rows = b.rows;
+    const int nbp = b.nbp;
+    Carver c(ws);
+    float *S = c.take<float>(rows * G * nbp);
+    int32_t *ids_ws = c.take<int32_t>(rows * G * kslots);
+    int32_t *row_len = c.take<int32_t>(rows);
+    int32_t *row_kvpos = c.take<int32_t>(rows);
+    int32_t *row_blk0 = c.take<int32_t>(rows);
+    int32_t *blk_tok0 = c.take<int32_t>(b.blocks);
+    int32_t *blk_rows = c.take<int32_t>(b.blocks);
+    BatchTable *dtab = c.take<BatchTable>(1);
+    const AttnWs w = carve_attn(c, rows, H, G, d, kslots, (int)b.blocks);
+    int32_t *ids = block_ids_out ? block_ids_out + q_base * G * kslots : ids_ws;
+    BatchMap bm;
+    bm.row_len = row_len;
+    bm.row_kvpos = row_kvpos;
+    bm.row_blk0 = row_blk0;
+    bm.blk_tok0 = blk_tok0;
+    bm.blk_rows = blk_rows;
+    MSA_TIMED(kK3, launch_batch_setup(t, dtab, row_len, row_kvpos, row_blk0, blk_tok0, blk_rows, s));
+    MSA_TIMED(kK1, launch_k1_index_pool_batch(idx_q + q_base * G * dI, idx_k, S, t, dtab, G, dI,
+                                              nbp, s));
+    MSA_TIMED(kK2, launch_k2_select(S, nbp, rows * G, G, kslots, 0, row_len, maxL, ids, s));
+    MSA_TIMED(kK3, launch_k3_schedule(ids, rows, G, kslots, (int)b.blocks, w.sb, bm, s));
+    MSA_TIMED(kK4, launch_k4_kv_outer(q + q_base * H * d, k, v, w.sb, (int)b.blocks, 0, 0, rows, H,
+                                      G, d, kslots, scale, w.po, w.plse, bm, s));
+    MSA_TIMED(kK5, launch_k5_combine(w.po, w.plse, ids, rows, H, G, d, kslots, 0,
+                                     out + q_base * H * d, bm, s));
+    return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -346,20 +469,44 @@ int msa_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         return MSA_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     scale = default_scale(scale, d);
-    for (int sq = 0; sq < nseq; ++sq) {
+    // batches address K/V tokens with 32-bit offsets
+    const bool allow_batch = cu_kv[nseq] < (int64_t)INT32_MAX - kBlock;
+    auto one_sequence = [&](int sq) {
         const int64_t C = cu_q[sq + 1] - cu_q[sq], L = cu_kv[sq + 1] - cu_kv[sq], P = L - C;
-        if (C == 0) continue;
         // queries are the last C tokens of the sequence: shift the new-token arrays back
         // by P rows so that row i of the sequence is addressed at its absolute position
         const int64_t back = P - cu_q[sq];
         int32_t *ids = block_ids_out ? rows_back(block_ids_out, back, (int64_t)G * kslots) : nullptr;
-        const int rc = prefill_range(rows_back(q, back, (int64_t)H * d), k + cu_kv[sq] * G * d,
-                                     v + cu_kv[sq] * G * d, rows_back(idx_q, back, (int64_t)G * dI),
-                                     idx_k + cu_kv[sq] * dI, L, P, H, G, d, dI, kslots, scale,
-                                     rows_back(out, back, (int64_t)H * d), ids, ws, ws_bytes, s);
-        if (rc != MSA_OK) return rc;
+        return prefill_range(rows_back(q, back, (int64_t)H * d), k + cu_kv[sq] * G * d,
+                             v + cu_kv[sq] * G * d, rows_back(idx_q, back, (int64_t)G * dI),
+                             idx_k + cu_kv[sq] * dI, L, P, H, G, d, dI, kslots, scale,
+                             rows_back(out, back, (int64_t)H * d), ids, ws, ws_bytes, s);
+    };
+    return plan_batches(cu_q, cu_kv, nseq, H, G, d, kslots, ws_bytes, allow_batch,
+                        [&](const BatchPlan &b) {
+                            if (b.n == 1) return one_sequence(b.members[0]);
+                            return run_batch(b, q, k, v, idx_q, idx_k, cu_q, cu_kv, H, G, d, dI,
+                                             kslots, scale, out, block_ids_out, ws, s);
+                        });
+}
+
+size_t msa_prefill_varlen_workspace_size(const int64_t *cu_q, const int64_t *cu_kv, int nseq,
+                                         int H, int G, int d, int dI, int B, int k) {
+    (void)dI; (void)B;
+    if (nseq <= 0 || !cu_q || !cu_kv || G <= 0 || H <= 0 || d <= 0 || k <= 0) return 0;
+    size_t need = 0;
+    for (int sq = 0; sq < nseq; ++sq) {
+        const int64_t C = cu_q[sq + 1] - cu_q[sq], L = cu_kv[sq + 1] - cu_kv[sq];
+        if (C <= 0 || L < C) continue;
+        need = std::max(need, prefill_bytes(chunk_of(L), L, H, G, d, k));
     }
-    return MSA_OK;
+    // the batches formed when the workspace is not the limit
+    plan_batches(cu_q, cu_kv, nseq, H, G, d, k, SIZE_MAX, cu_kv[nseq] < (int64_t)INT32_MAX - kBlock,
+                 [&](const BatchPlan &b) {
+                     if (b.n > 1) need = std::max(need, batch_bytes(b.rows, b.blocks, b.nbp, H, G, d, k));
+                     return MSA_OK;
+                 });
+    return need;
 }
 
 // -------------------------------- decode ----------------------------------
@@ -402,7 +549,7 @@ int msa_decode(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache
     MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, seq_len, Lmax, ids, s));
     MSA_TIMED(kK4d, launch_k4d_split(q, k_cache, v_cache, ids, seq_len, nullptr, 0, N, Lmax, H, G,
                                      d, kslots, scale, po, plse, s));
-    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, s));
+    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, BatchMap{}, s));
     return MSA_OK;
 }
 
@@ -454,7 +601,7 @@ int msa_decode_paged(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k
     MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, eff_len, Lmax, ids, s));
     MSA_TIMED(kK4d, launch_k4d_split(q, k_pages, v_pages, ids, eff_len, block_table, max_blocks, N,
                                      Lmax, H, G, d, kslots, scale, po, plse, s));
-    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, s));
+    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, BatchMap{}, s));
     return MSA_OK;
 }
 
@@ -500,7 +647,7 @@ int msa_decode_fp8idx(const uint16_t *q, const uint16_t *idx_q, const uint16_t *
     MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, seq_len, Lmax, ids, s));
     MSA_TIMED(kK4d, launch_k4d_split(q, k_cache, v_cache, ids, seq_len, nullptr, 0, N, Lmax, H, G,
                                      d, kslots, scale, po, plse, s));
-    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, s));
+    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, BatchMap{}, s));
     return MSA_OK;
 }
 
@@ -542,7 +689,7 @@ int msa_decode_paged_fp8idx(const uint16_t *q, const uint16_t *idx_q, const uint
     MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, eff_len, Lmax, ids, s));
     MSA_TIMED(kK4d, launch_k4d_split(q, k_pages, v_pages, ids, eff_len, block_table, max_blocks, N,
                                      Lmax, H, G, d, kslots, scale, po, plse, s));
-    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, s));
+    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, BatchMap{}, s));
     return MSA_OK;
 }
 

@@ -48,14 +48,14 @@ __device__ __forceinline__ void load_q(bf16x8 (&qb)[D / 16], const uint16_t *qro
 
 // One pass of 32 columns of a wave over a staged block.  Lane column = l % 32.
 //   qb     : the column's q row as the B operand (see load_q)
-//   qpos   : the column's token position (its causal limit in its own block)
-//   j      : the staged KV block
+//   rel    : the column's token position minus the staged block's first position;
+//            0 <= rel < 128 marks the query's own block, whose keys past it are masked
 //   emit   : receives the column's normalised partial as bf16 16-byte chunks --
 //            w[u] holds chunk 4(u/2) + 2(u%2) + hf of the row (elements 8c .. 8c+7) --
 //            and its log2-sum-exp, and writes them
 template <int D, typename Emit>
-__device__ __forceinline__ void attend_pass(const char *lds_k, const char *lds_vt, int j,
-                                            const bf16x8 (&qb)[D / 16], bool active, int64_t qpos,
+__device__ __forceinline__ void attend_pass(const char *lds_k, const char *lds_vt,
+                                            const bf16x8 (&qb)[D / 16], bool active, int64_t rel,
                                             float scale_log2, int lane, Emit emit) {
     constexpr int KS = D / 16;   // K-steps of S^T over d
     constexpr int CPR = D / 8;
@@ -76,9 +76,9 @@ __device__ __forceinline__ void attend_pass(const char *lds_k, const char *lds_v
     }
     // causal mask inside the query's own block (skipped by waves holding no such
     // query); register r of M-tile mt holds key 32mt + 16(ip/2) + 8hf + 4(ip%2) + jj
-    const bool local = active && (qpos / kBlock == j);
+    const bool local = active && rel < kBlock;
     if (__ballot(local)) {
-        const int lim = local ? (int)(qpos - (int64_t)j * kBlock) - 8 * hf : kBlock;
+        const int lim = local ? (int)rel - 8 * hf : kBlock;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -203,13 +203,13 @@ __device__ __forceinline__ void store_rows_staged(char *stg, const u32x4 (&w)[D 
 // ---------------------------------------------------------------------------
 // K4: KV-outer sparse attention over the scheduled lists.
 // ---------------------------------------------------------------------------
-template <int D, int R>
+template <int D, int R, bool BATCH>
 __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kx,
     const uint16_t *__restrict__ vx, const int *__restrict__ offs, const int *__restrict__ toff,
     const int *__restrict__ total, const int *__restrict__ items,
     const uint32_t *__restrict__ list, int nb, int64_t L, int64_t q0, int H, int G, int kslots,
-    float scale_log2, uint16_t *__restrict__ po, float *__restrict__ plse) {
+    float scale_log2, uint16_t *__restrict__ po, float *__restrict__ plse, const BatchMap bm) {
     __shared__ __attribute__((aligned(16))) char lds_k[kBlock * D * 2];
     __shared__ __attribute__((aligned(16))) char lds_vt[D * kBlock * 2];
     static_assert(kK4Queries <= 256, "one entry per thread is staged");
@@ -218,11 +218,23 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     // registers with them (it spills), so it keeps the per-lane 16-byte stores.
     constexpr bool kStaged = !(D == 128 && R == 4);
     __shared__ __attribute__((aligned(16))) char lds_stg[4][kStaged ? kStageBytes<D> : 16];
-    const int per = gridDim.x / 8;
-    const int x = (blockIdx.x % 8) * per + blockIdx.x / 8;   // XCD-contiguous items
-    if (x >= *total) return;
+    // XCD-aware order: work-group b runs on XCD b % 8, which takes a contiguous eighth
+    // of the items actually scheduled (the grid is only an upper bound on them)
+    const int tot = *total;
+    const int per = (tot + 7) / 8;
+    if ((int)(blockIdx.x / 8) >= per) return;
+    const int x = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    if (x >= tot) return;
     const int li = items[x];                                 // list of this tile
     const int g = li / nb, j = li % nb;
+    // the block's first token (single sequence: block j; batch: global block j)
+    const int64_t blk0 = BATCH ? (int64_t)bm.blk_tok0[j] : (int64_t)j * kBlock;
+    // batch: position of an entry's query relative to the block's first token,
+    // fetched with the entry two passes ahead (a single sequence computes it)
+    auto rel_of = [&](bool on, uint32_t e) -> int {
+        if constexpr (BATCH) return on ? bm.row_kvpos[e >> 5] - (int)blk0 : 0;
+        else return 0;
+    };
     const int t = x - toff[li];
     const int begin = offs[li] + t * kK4Queries;
     const int cnt = min(kK4Queries, offs[li + 1] - begin);
@@ -241,12 +253,13 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     uint32_t entry = act ? list[begin + base + a] : 0u;
     bf16x8 qb[D / 16];
     load_q<D>(qb, q + ((q0 + (entry >> 5)) * H + hh) * D, act, hf);
+    int rel = rel_of(act, entry);
 
     if (tid < cnt) lds_e[tid] = list[begin + tid];
     const int kv_row_bytes = G * D * 2;
-    const char *ksrc = reinterpret_cast<const char *>(kx + ((int64_t)j * kBlock * G + g) * D);
-    const char *vsrc = reinterpret_cast<const char *>(vx + ((int64_t)j * kBlock * G + g) * D);
-    const int nrows = (int)min<int64_t>(kBlock, L - (int64_t)j * kBlock);
+    const char *ksrc = reinterpret_cast<const char *>(kx + (blk0 * G + g) * D);
+    const char *vsrc = reinterpret_cast<const char *>(vx + (blk0 * G + g) * D);
+    const int nrows = BATCH ? bm.blk_rows[j] : (int)min<int64_t>(kBlock, L - blk0);
     {
         KVStage<D> st;
         st.load(ksrc, vsrc, kv_row_bytes, nrows, tid);
@@ -260,6 +273,7 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     uint32_t nentry = nact ? lds_e[nbase + a] : 0u;
     bf16x8 qn[D / 16];
     load_q<D>(qn, q + ((q0 + (nentry >> 5)) * H + hh) * D, nact, hf);
+    int nrel = rel_of(nact, nentry);
 
     while (base < cnt) {
         const int fbase = nbase + STEP;
@@ -267,13 +281,14 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
         const uint32_t fentry = fact ? lds_e[fbase + a] : 0u;
         bf16x8 qf[D / 16];
         load_q<D>(qf, q + ((q0 + (fentry >> 5)) * H + hh) * D, fact, hf);
+        const int frel = rel_of(fact, fentry);
 
         const int64_t il = entry >> 5;
         const int s = entry & 31;
         const int64_t lrow = ((il * G + g) * kslots + s) * R + h;
         const int pbase = base;
         const uint32_t pentry = entry;
-        attend_pass<D>(lds_k, lds_vt, j, qb, act, q0 + il, scale_log2, lane,
+        attend_pass<D>(lds_k, lds_vt, qb, act, BATCH ? (int64_t)rel : q0 + il - blk0, scale_log2, lane,
                        [&](const u32x4 (&w)[D / 16], float lse) {
                            if (act && hf == 0) plse[lrow] = lse;
                            if constexpr (kStaged) {
@@ -295,8 +310,10 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
         base = nbase;
         act = nact;
         entry = nentry;
+        rel = nrel;
         nbase = fbase;
         nact = fact;
+        nrel = frel;
         nentry = fentry;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
@@ -310,23 +327,28 @@ template <int D, int R>
 static hipError_t k4_dispatch(const uint16_t *q, const uint16_t *kx, const uint16_t *vx,
                               const SchedBuffers &sb, int nb, int64_t L, int64_t q0, int64_t C,
                               int H, int G, int k, float scale_log2, uint16_t *po, float *plse,
-                              hipStream_t s) {
+                              const BatchMap &bm, hipStream_t s) {
     const int64_t grid = round_up(k4_max_items(C, G, k, nb), 8);
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((k4_kv_outer<D, R>), dim3((unsigned)grid), dim3(256), 0, s, q, kx, vx,
-                       sb.offs, sb.toff, sb.total, sb.items, sb.list, nb, L, q0, H, G, k,
-                       scale_log2, po, plse);
+    if (bm.row_kvpos)
+        hipLaunchKernelGGL((k4_kv_outer<D, R, true>), dim3((unsigned)grid), dim3(256), 0, s, q, kx,
+                           vx, sb.offs, sb.toff, sb.total, sb.items, sb.list, nb, L, q0, H, G, k,
+                           scale_log2, po, plse, bm);
+    else
+        hipLaunchKernelGGL((k4_kv_outer<D, R, false>), dim3((unsigned)grid), dim3(256), 0, s, q, kx,
+                           vx, sb.offs, sb.toff, sb.total, sb.items, sb.list, nb, L, q0, H, G, k,
+                           scale_log2, po, plse, bm);
     return hipGetLastError();
 }
 
 hipError_t launch_k4_kv_outer(const uint16_t *q, const uint16_t *kx, const uint16_t *vx,
                               const SchedBuffers &sb, int nb, int64_t L, int64_t q0, int64_t C,
                               int H, int G, int d, int k, float scale, uint16_t *po, float *plse,
-                              hipStream_t s) {
+                              const BatchMap &bm, hipStream_t s) {
     const float sl2 = scale * kLog2e;
     const int R = H / G;
 #define K4_CASE(dd, rr) \
-    if (d == dd && R == rr) return k4_dispatch<dd, rr>(q, kx, vx, sb, nb, L, q0, C, H, G, k, sl2, po, plse, s);
+    if (d == dd && R == rr) return k4_dispatch<dd, rr>(q, kx, vx, sb, nb, L, q0, C, H, G, k, sl2, po, plse, bm, s);
     K4_CASE(64, 1) K4_CASE(64, 2) K4_CASE(64, 4) K4_CASE(64, 8) K4_CASE(64, 16) K4_CASE(64, 32)
     K4_CASE(128, 1) K4_CASE(128, 2) K4_CASE(128, 4) K4_CASE(128, 8) K4_CASE(128, 16) K4_CASE(128, 32)
 #undef K4_CASE
@@ -412,7 +434,7 @@ __global__ __launch_bounds__(256, 2) void k4d_split(const uint16_t *__restrict__
             bf16x8 qb[D / 16];
             load_q<D>(qb, q + (n * H + hh) * D, active, lane >> 5);
             const int hf = lane >> 5;
-            attend_pass<D>(lds_k, lds_vt, j, qb, active, p, scale_log2, lane,
+            attend_pass<D>(lds_k, lds_vt, qb, active, p - (int64_t)j * kBlock, scale_log2, lane,
                            [&](const u32x4 (&w)[D / 16], float lse) {
                                if (!active) return;
 #pragma unroll
@@ -459,17 +481,18 @@ hipError_t launch_k4d_split(const uint16_t *q, const uint16_t *kc, const uint16_
 }
 
 // ---------------------------------------------------------------------------
-// K5: combine.  D/8 threads per (query, head), 8 d values per thread.  All KMAX
-// slot partials of a thread are requested at once (every slot location exists in
-// the workspace); slots are merged only when 0 <= id < nb_lim -- the rule K3 used
-// to build the lists -- so stale workspace contents never enter the result.
+// K5: combine.  D/8 threads per (query, head), 8 d values per thread.  The partials
+// of all valid slots of a thread are requested at once; a slot is valid when
+// 0 <= id < nb_lim -- the rule K3 used to build the lists -- so stale workspace
+// contents never enter the result, and padding slots (rows with fewer than k
+// selectable blocks) cost no memory traffic.
 // ---------------------------------------------------------------------------
 template <int D, int KMAX>
 __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ po,
                                                   const float *__restrict__ plse,
                                                   const int32_t *__restrict__ ids, int64_t nq,
                                                   int H, int G, int kslots, int nb_lim,
-                                                  uint16_t *__restrict__ out) {
+                                                  uint16_t *__restrict__ out, const BatchMap bm) {
     constexpr int TPH = D / 8;
     constexpr int PPW = 256 / TPH;
     const int64_t ih = (int64_t)blockIdx.x * PPW + threadIdx.x / TPH;
@@ -480,6 +503,8 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
     const int g = h / (H / G);
     const int R = H / G;
     const int32_t *idr = ids + (i * G + g) * kslots;
+    // batch: ids are local to the row's sequence and valid up to its own block
+    if (bm.row_len) nb_lim = (bm.row_len[i] - 1) / kBlock + 1;
     const float *lr = plse + (i * G + g) * kslots * R + (h - g * R);   // slot s at lr[s * R]
     const uint16_t *pr = po + ih * kslots * D + sub * 8;
     u32x4 v[KMAX];
@@ -498,8 +523,8 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
         }
 #pragma unroll
         for (int s = 0; s < KMAX; ++s) {
-            l[s] = lr[s * R];
-            v[s] = load16(pr + s * D);
+            l[s] = ok[s] ? lr[s * R] : 0.0f;
+            v[s] = ok[s] ? load16(pr + s * D) : u32x4{0, 0, 0, 0};
         }
     } else {
 #pragma unroll
@@ -507,8 +532,8 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
             if (s < kslots) {
                 const int id = idr[s];
                 ok[s] = id >= 0 && id < nb_lim;
-                l[s] = lr[s * R];
-                v[s] = load16(pr + s * D);
+                l[s] = ok[s] ? lr[s * R] : 0.0f;
+                v[s] = ok[s] ? load16(pr + s * D) : u32x4{0, 0, 0, 0};
             } else {
                 ok[s] = false;
             }
@@ -541,26 +566,26 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
 template <int D>
 static hipError_t k5_dispatch(const uint16_t *po, const float *plse, const int32_t *ids,
                               int64_t nq, int H, int G, int k, int nb_lim, uint16_t *out,
-                              hipStream_t s) {
+                              const BatchMap &bm, hipStream_t s) {
     constexpr int PPW = 256 / (D / 8);
     const dim3 grid((unsigned)((nq * H + PPW - 1) / PPW));
     if (k <= 4)
-        hipLaunchKernelGGL((k5_combine<D, 4>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out);
+        hipLaunchKernelGGL((k5_combine<D, 4>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
     else if (k <= 8)
-        hipLaunchKernelGGL((k5_combine<D, 8>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out);
+        hipLaunchKernelGGL((k5_combine<D, 8>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
     else if (k <= 16)
-        hipLaunchKernelGGL((k5_combine<D, 16>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out);
+        hipLaunchKernelGGL((k5_combine<D, 16>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
     else
-        hipLaunchKernelGGL((k5_combine<D, 32>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out);
+        hipLaunchKernelGGL((k5_combine<D, 32>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
     return hipGetLastError();
 }
 
 hipError_t launch_k5_combine(const uint16_t *po, const float *plse, const int32_t *ids, int64_t nq,
                              int H, int G, int d, int k, int nb_lim, uint16_t *out,
-                             hipStream_t s) {
+                             const BatchMap &bm, hipStream_t s) {
     if (nq <= 0) return hipSuccess;
-    if (d == 64) return k5_dispatch<64>(po, plse, ids, nq, H, G, k, nb_lim, out, s);
-    if (d == 128) return k5_dispatch<128>(po, plse, ids, nq, H, G, k, nb_lim, out, s);
+    if (d == 64) return k5_dispatch<64>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, s);
+    if (d == 128) return k5_dispatch<128>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, s);
     return hipErrorInvalidValue;
 }
 

@@ -68,10 +68,14 @@ template <int G> struct K1Tiling {
     static constexpr int THREADS = 256;
 };
 
-template <int G, int DI>
+// BATCH: the work-groups of several sequences in one launch; tab (device copy of
+// the batch table) gives each sequence's first work-group, rows and tokens, and
+// the work-group rebases iq, ik, S and its query range on its own sequence.
+template <int G, int DI, bool BATCH>
 __global__ __launch_bounds__(256, 2) void k1_index_pool(
     const uint16_t *__restrict__ iq, const uint16_t *__restrict__ ik, float *__restrict__ S,
-    int64_t q0, int64_t qend, int nbp, int qb0, int qb1, int64_t n_items) {
+    int64_t q0, int64_t qend, int nbp, int qb0, int qb1, int64_t n_items,
+    const BatchTable *__restrict__ tab) {
     constexpr int NT = K1Tiling<G>::NT;
     constexpr int NTHR = K1Tiling<G>::THREADS;
     constexpr int P = K1Tiling<G>::P;
@@ -84,9 +88,32 @@ __global__ __launch_bounds__(256, 2) void k1_index_pool(
 
     // XCD-aware order: consecutive logical items (same key chunk) on one XCD.
     const int64_t per = gridDim.x / 8;
-    const int64_t item = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    int64_t item = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    if constexpr (BATCH) {
+        if (item >= tab->k1_off[tab->n]) return;
+        int lo = 0, hi = tab->n;   // the sequence: largest sq with k1_off[sq] <= item
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (tab->k1_off[mid] <= item) lo = mid;
+            else hi = mid;
+        }
+        const int sq = lo;
+        const int64_t L = tab->kv_len[sq];
+        const int64_t P0 = L - (tab->q_off[sq + 1] - tab->q_off[sq]);   // cached prefix
+        q0 = P0;
+        qend = L;
+        qb0 = (int)(P0 / kBlock);
+        qb1 = (int)((L + kBlock - 1) / kBlock);
+        // the row of query position p is batch row q_off + p - P0
+        iq += ((int64_t)tab->q_off[sq] - P0) * G * DI;
+        ik += (int64_t)tab->kv_off[sq] * DI;
+        S += (int64_t)tab->q_off[sq] * G * nbp;
+        item -= tab->k1_off[sq];
+    } else {
+        if (item >= n_items * P) return;
+    }
     int qb, part, c;
-    if (item >= n_items * P || !k1_item(item, qb0, qb1, P, qb, part, c)) return;
+    if (!k1_item(item, qb0, qb1, P, qb, part, c)) return;
     const int j0 = c * kK1KeyChunk;
     const int j1 = min(j0 + kK1KeyChunk, qb);
 
@@ -196,9 +223,44 @@ static hipError_t k1_dispatch(const uint16_t *iq, const uint16_t *ik, float *S, 
     const int64_t n = k1_num_items(qb0, qb1);
     if (n == 0) return hipSuccess;
     const int64_t grid = round_up(n * K1Tiling<G>::P, 8);
-    hipLaunchKernelGGL((k1_index_pool<G, DI>), dim3((unsigned)grid), dim3(K1Tiling<G>::THREADS), 0,
-                       s, iq, ik, S, q0, qend, nbp, qb0, qb1, n);
+    hipLaunchKernelGGL((k1_index_pool<G, DI, false>), dim3((unsigned)grid), dim3(K1Tiling<G>::THREADS),
+                       0, s, iq, ik, S, q0, qend, nbp, qb0, qb1, n, nullptr);
     return hipGetLastError();
+}
+
+template <int G, int DI>
+static hipError_t k1_dispatch_batch(const uint16_t *iq, const uint16_t *ik, float *S,
+                                    const BatchTable &t, const BatchTable *dtab, int nbp,
+                                    hipStream_t s) {
+    const int64_t grid = round_up(t.k1_off[t.n], 8);
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((k1_index_pool<G, DI, true>), dim3((unsigned)grid), dim3(K1Tiling<G>::THREADS),
+                       0, s, iq, ik, S, 0, 0, nbp, 0, 0, 0, dtab);
+    return hipGetLastError();
+}
+
+int64_t k1_num_workgroups(int64_t q0, int64_t qend, int G) {
+    const int qb0 = (int)(q0 / kBlock), qb1 = (int)((qend + kBlock - 1) / kBlock);
+    const int64_t n = k1_num_items(qb0, qb1);
+    switch (G) {
+    case 1: return n * K1Tiling<1>::P;
+    case 2: return n * K1Tiling<2>::P;
+    case 4: return n * K1Tiling<4>::P;
+    default: return n * K1Tiling<8>::P;
+    }
+}
+
+hipError_t launch_k1_index_pool_batch(const uint16_t *iq, const uint16_t *ik, float *S,
+                                      const BatchTable &t, const BatchTable *dtab, int G, int dI,
+                                      int nbp, hipStream_t s) {
+#define K1B_CASE(g, di) \
+    if (G == g && dI == di) return k1_dispatch_batch<g, di>(iq, ik, S, t, dtab, nbp, s);
+    K1B_CASE(1, 32) K1B_CASE(1, 64) K1B_CASE(1, 128)
+    K1B_CASE(2, 32) K1B_CASE(2, 64) K1B_CASE(2, 128)
+    K1B_CASE(4, 32) K1B_CASE(4, 64) K1B_CASE(4, 128)
+    K1B_CASE(8, 32) K1B_CASE(8, 64)
+#undef K1B_CASE
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_k1_index_pool(const uint16_t *iq, const uint16_t *ik, float *S, int64_t L,

@@ -50,7 +50,43 @@ hipError_t launch_quant_e4m3(const uint16_t *x, int64_t rows, int dI, uint8_t *o
 hipError_t launch_k2_select(const float *S, int nbp, int64_t nrows, int G, int k, int64_t q0,
                             const int32_t *seq_len, int64_t Lmax, int32_t *ids, hipStream_t s);
 
+// A packed batch of sequences run as one set of launches (varlen prefill).  Row r
+// of the batch is a new token of one sequence; the batch's KV blocks are numbered
+// sequence after sequence ("global" blocks).  Built on the device by
+// launch_batch_setup; a BatchMap of null pointers means a single sequence.
+struct BatchMap {
+    const int32_t *row_len = nullptr;    // [rows] position of the row's token + 1
+    const int32_t *row_kvpos = nullptr;  // [rows] absolute index of that token in k / v
+    const int32_t *row_blk0 = nullptr;   // [rows] global number of its sequence's block 0
+    const int32_t *blk_tok0 = nullptr;   // [blocks] absolute first token of a global block
+    const int32_t *blk_rows = nullptr;   // [blocks] tokens in the block (<= 128)
+};
+constexpr int kBatchMaxSeq = 128;        // sequences per batched launch set
+constexpr int kBatchMaxBlocks = 8192;    // global blocks per batched launch set
+// Host description of a batch, passed by value to the setup kernel (2.6 KB), which
+// also copies it to device memory for K1.
+struct BatchTable {
+    int n = 0, rows = 0, blocks = 0;
+    int q_off[kBatchMaxSeq + 1];     // first row of each sequence; q_off[n] = rows
+    int blk_off[kBatchMaxSeq + 1];   // first global block; blk_off[n] = blocks
+    int k1_off[kBatchMaxSeq + 1];    // first K1 work-group of each sequence
+    int kv_off[kBatchMaxSeq];        // absolute first K/V token of each sequence
+    int kv_len[kBatchMaxSeq];        // its tokens, cached prefix + new
+};
+hipError_t launch_batch_setup(const BatchTable &t, BatchTable *dtab, int32_t *row_len,
+                              int32_t *row_kvpos, int32_t *row_blk0, int32_t *blk_tok0,
+                              int32_t *blk_rows, hipStream_t s);
+// K1 over a batch: the work-groups of every sequence in one launch.  iq holds the
+// batch's rows, ik all tokens; S rows follow the batch rows.
+hipError_t launch_k1_index_pool_batch(const uint16_t *iq, const uint16_t *ik, float *S,
+                                      const BatchTable &t, const BatchTable *dtab, int G, int dI,
+                                      int nbp, hipStream_t s);
+// K1 work-groups of the queries [q0, qend) of one sequence.
+int64_t k1_num_workgroups(int64_t q0, int64_t qend, int G);
+
 // K3: invert query-major ids of queries [q0, q0 + C) into per-(g, block) lists.
+// With a batch map, ids are local to each row's sequence and lists are per global
+// block; an id is scheduled when 0 <= id <= b(row) (batch) or 0 <= id < nb.
 struct SchedBuffers {
     int *counts;     // [nlists]
     int *offs;       // [nlists + 1]
@@ -61,17 +97,18 @@ struct SchedBuffers {
     uint32_t *list;  // [C * G * k] entries (i - q0) << 5 | slot
 };
 hipError_t launch_k3_schedule(const int32_t *ids, int64_t C, int G, int k, int nb,
-                              const SchedBuffers &sb, hipStream_t s);
+                              const SchedBuffers &sb, const BatchMap &bm, hipStream_t s);
 int64_t k4_max_items(int64_t C, int G, int k, int nb);
 int k3_num_groups(int64_t C);
 
 // K4: KV-outer attention over the scheduled lists -> partials per (query, head,
 // slot): po [(i*H + h)*k + slot][d] bf16 (normalised o), plse [((i*G + g)*k + slot)*R
-// + h % R] fp32 (log2-sum-exp of the scaled scores).
+// + h % R] fp32 (log2-sum-exp of the scaled scores).  With a batch map, q holds the
+// batch's rows (q0 = 0) and the lists are per global block.
 hipError_t launch_k4_kv_outer(const uint16_t *q, const uint16_t *kx, const uint16_t *vx,
                               const SchedBuffers &sb, int nb, int64_t L, int64_t q0, int64_t C,
                               int H, int G, int d, int k, float scale, uint16_t *po, float *plse,
-                              hipStream_t s);
+                              const BatchMap &bm, hipStream_t s);
 
 // K4d: decode split over slots -> partials per (sequence, head, slot).  Cache
 // addressing as in K1d (kc, vc [N, Lmax, G, d] or pages [pages, 128, G, d]).
@@ -86,10 +123,11 @@ hipError_t launch_page_check(const int32_t *table, int maxb, int64_t num_pages,
                              const int32_t *seq_len, int N, int32_t *eff_len, hipStream_t s);
 
 // K5: two-phase combine of the partials of `nq` queries into out[nq, H, d].
-// ids [nq, G, k]: a slot is merged when 0 <= id < nb_lim.
+// ids [nq, G, k]: a slot is merged when 0 <= id < nb_lim, or with a batch map when
+// 0 <= id <= b(row) -- the rule K3 scheduled by.
 hipError_t launch_k5_combine(const uint16_t *po, const float *plse, const int32_t *ids, int64_t nq,
                              int H, int G, int d, int k, int nb_lim, uint16_t *out,
-                             hipStream_t s);
+                             const BatchMap &bm, hipStream_t s);
 
 // Fill n ints with a value (used instead of hipMemsetAsync so calls stay capturable).
 hipError_t launch_fill_i32(int *p, int64_t n, int value, hipStream_t s);

@@ -66,26 +66,85 @@ hipError_t launch_page_check(const int32_t *table, int maxb, int64_t num_pages,
     return hipGetLastError();
 }
 
+// Batched varlen prefill: per-row and per-global-block tables from the batch's
+// host description (one thread per row and per block; the sequence is found by
+// binary search over the offsets, which live in the kernel-argument segment).
+__global__ __launch_bounds__(256) void k_batch_setup(const BatchTable t, BatchTable *__restrict__ dtab,
+                                                     int32_t *__restrict__ row_len,
+                                                     int32_t *__restrict__ row_kvpos,
+                                                     int32_t *__restrict__ row_blk0,
+                                                     int32_t *__restrict__ blk_tok0,
+                                                     int32_t *__restrict__ blk_rows) {
+    const BatchTable *tp = &t;
+    const int x = blockIdx.x * 256 + threadIdx.x;
+    if (blockIdx.x == 0) {   // device copy of the table, one int per thread and step
+        const int *src = reinterpret_cast<const int *>(tp);
+        int *dst = reinterpret_cast<int *>(dtab);
+        for (int w = threadIdx.x; w < (int)(sizeof(BatchTable) / sizeof(int)); w += 256)
+            dst[w] = src[w];
+    }
+    auto seq_of = [&](const int *off, int v) {   // largest s with off[s] <= v
+        int lo = 0, hi = tp->n;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (off[mid] <= v) lo = mid;
+            else hi = mid;
+        }
+        return lo;
+    };
+    if (x < tp->rows) {
+        const int sq = seq_of(tp->q_off, x);
+        const int newc = tp->q_off[sq + 1] - tp->q_off[sq];
+        const int pos = tp->kv_len[sq] - newc + (x - tp->q_off[sq]);
+        row_len[x] = pos + 1;
+        row_kvpos[x] = tp->kv_off[sq] + pos;
+        row_blk0[x] = tp->blk_off[sq];
+    }
+    if (x < tp->blocks) {
+        const int sq = seq_of(tp->blk_off, x);
+        const int j = x - tp->blk_off[sq];
+        blk_tok0[x] = tp->kv_off[sq] + j * kBlock;
+        blk_rows[x] = min(kBlock, tp->kv_len[sq] - j * kBlock);
+    }
+}
+
+hipError_t launch_batch_setup(const BatchTable &t, BatchTable *dtab, int32_t *row_len,
+                              int32_t *row_kvpos, int32_t *row_blk0, int32_t *blk_tok0,
+                              int32_t *blk_rows, hipStream_t s) {
+    const int n = t.rows > t.blocks ? t.rows : t.blocks;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_batch_setup, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, t, dtab,
+                       row_len, row_kvpos, row_blk0, blk_tok0, blk_rows);
+    return hipGetLastError();
+}
+
 // Entries of one work-group: queries [w*kK3Queries, (w+1)*kK3Queries) of the chunk,
-// group g, all k slots; entry e -> query w*kK3Queries + e / k, slot e % k.
+// group g, all k slots; entry e -> query w*kK3Queries + e / k, slot e % k.  Returns
+// the entry's list block, or -1 for an id that is not scheduled: outside [0, nb),
+// or in a batch outside [0, b(row)] (then the list block is the global one).
 __device__ __forceinline__ int entry_block(const int32_t *ids, int64_t C, int G, int k, int nb,
-                                           int g, int64_t i, int s) {
+                                           const BatchMap &bm, int g, int64_t i, int s) {
     if (i >= C) return -1;
     const int id = ids[(i * G + g) * k + s];
-    return (id >= 0 && id < nb) ? id : -1;   // ids outside [0, nb) are ignored
+    if (bm.row_len) {
+        const int own = (bm.row_len[i] - 1) / kBlock;
+        return (id >= 0 && id <= own) ? bm.row_blk0[i] + id : -1;
+    }
+    return (id >= 0 && id < nb) ? id : -1;
 }
 
 // Count pass: per-work-group histogram in LDS, written (zeros included) to
 // wcnt[(g * nW + w) * nb + b].  No global atomics.
 __global__ __launch_bounds__(256) void k3_count(const int32_t *__restrict__ ids, int64_t C, int G,
-                                                int k, int nb, int *__restrict__ wcnt) {
+                                                int k, int nb, const BatchMap bm,
+                                                int *__restrict__ wcnt) {
     extern __shared__ int lds_cnt[];
     const int w = blockIdx.x, g = blockIdx.y, nW = gridDim.x;
     for (int b = threadIdx.x; b < nb; b += 256) lds_cnt[b] = 0;
     __syncthreads();
     const int64_t i0 = (int64_t)w * kK3Queries;
     for (int e = threadIdx.x; e < kK3Queries * k; e += 256) {
-        const int id = entry_block(ids, C, G, k, nb, g, i0 + e / k, e % k);
+        const int id = entry_block(ids, C, G, k, nb, bm, g, i0 + e / k, e % k);
         if (id >= 0) atomicAdd(&lds_cnt[id], 1);
     }
     __syncthreads();
@@ -113,7 +172,8 @@ __global__ __launch_bounds__(256) void k3_colscan(int *__restrict__ wcnt, int G,
 // Scatter pass: each work-group places its entries at
 // offs[list] + (entries of earlier work-groups) + (rank inside this work-group).
 __global__ __launch_bounds__(256) void k3_scatter(const int32_t *__restrict__ ids, int64_t C, int G,
-                                                  int k, int nb, const int *__restrict__ offs,
+                                                  int k, int nb, const BatchMap bm,
+                                                  const int *__restrict__ offs,
                                                   const int *__restrict__ wcnt,
                                                   uint32_t *__restrict__ list) {
     extern __shared__ int lds[];
@@ -130,7 +190,7 @@ __global__ __launch_bounds__(256) void k3_scatter(const int32_t *__restrict__ id
     for (int e = threadIdx.x; e < kK3Queries * k; e += 256) {
         const int64_t i = i0 + e / k;
         const int s = e % k;
-        const int id = entry_block(ids, C, G, k, nb, g, i, s);
+        const int id = entry_block(ids, C, G, k, nb, bm, g, i, s);
         if (id < 0) continue;
         const int r = atomicAdd(&rank[id], 1);
         list[base[id] + r] = ((uint32_t)i << 5) | (uint32_t)s;
@@ -188,12 +248,13 @@ int64_t k4_max_items(int64_t C, int G, int k, int nb) {
 int k3_num_groups(int64_t C) { return (int)((C + kK3Queries - 1) / kK3Queries); }
 
 hipError_t launch_k3_schedule(const int32_t *ids, int64_t C, int G, int k, int nb,
-                              const SchedBuffers &sb, hipStream_t s) {
+                              const SchedBuffers &sb, const BatchMap &bm, hipStream_t s) {
     const int nlists = G * nb;
     const int nW = k3_num_groups(C);
     hipError_t e;
     const dim3 grid((unsigned)nW, (unsigned)G);
-    hipLaunchKernelGGL(k3_count, grid, dim3(256), nb * sizeof(int), s, ids, C, G, k, nb, sb.wcnt);
+    hipLaunchKernelGGL(k3_count, grid, dim3(256), nb * sizeof(int), s, ids, C, G, k, nb, bm,
+                       sb.wcnt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k3_colscan, dim3((unsigned)((nlists + 255) / 256)), dim3(256), 0, s,
                        sb.wcnt, G, nb, nW, sb.counts);
@@ -201,7 +262,7 @@ hipError_t launch_k3_schedule(const int32_t *ids, int64_t C, int G, int k, int n
     hipLaunchKernelGGL(k3_scan, dim3(1), dim3(1024), 0, s, sb.counts, nlists, sb.offs, sb.toff,
                        sb.total, sb.items);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k3_scatter, grid, dim3(256), 2 * nb * sizeof(int), s, ids, C, G, k, nb,
+    hipLaunchKernelGGL(k3_scatter, grid, dim3(256), 2 * nb * sizeof(int), s, ids, C, G, k, nb, bm,
                        sb.offs, sb.wcnt, sb.list);
     return hipGetLastError();
 }

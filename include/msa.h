@@ -131,11 +131,20 @@ MSA_API int msa_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  *   cu_q, cu_kv: HOST int64 arrays of nseq + 1 offsets (non-decreasing).
  * Requires Ps % 128 == 0 (whole prefix blocks) and Ls <= 1048576 for every
  * sequence with new tokens, else MSA_ERR_UNSUPPORTED; Cs > Ls or a negative
- * offset is MSA_ERR_INVALID_ARG.  Workspace: at least one
- * 128-query chunk of msa_prefill_workspace_size(max Ls, ...); the size for the
- * longest sequence is the preferred one.  Sequences run one after another on
- * `stream` (each in query chunks, like msa_prefill).
+ * offset is MSA_ERR_INVALID_ARG.
+ * Consecutive sequences of at most 8192 new tokens are prefilled together in
+ * batches (up to 128 sequences, 131072 new tokens and 8192 KV blocks per batch,
+ * as far as the workspace holds them), every kernel of the path launched once per
+ * batch.  Longer sequences,
+ * and any that no batch can take, run alone in query chunks like msa_prefill.
+ * The results do not depend on the batching.
+ * Workspace: msa_prefill_varlen_workspace_size gives the size at which every
+ * batch is formed; the minimum is one 128-query chunk of
+ * msa_prefill_workspace_size(max Ls, ...) (then every sequence runs alone).
  * ------------------------------------------------------------------------- */
+MSA_API size_t msa_prefill_varlen_workspace_size(const int64_t *cu_q, const int64_t *cu_kv,
+                                                 int nseq, int H, int G, int d, int dI, int B,
+                                                 int k);
 MSA_API int msa_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const uint16_t *idx_q, const uint16_t *idx_k, const int64_t *cu_q,
                                const int64_t *cu_kv, int nseq, int H, int G, int d, int dI, int B,

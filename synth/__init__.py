@@ -80,9 +80,10 @@ class Workload:
 # The five workloads: shapes of the pages' research model (64 query heads,
 # 4 KV heads, B = 128, k = 16) with head/index dims 128, plus the tiny case; and
 # the decode workload again, with its caches in shuffled 128-token pages, and with
-# its index-key cache held as E4M3 bytes plus per-token scales; and two packed /
-# chunked prefills (8 sequences of 16384 tokens in one call; the 128K sequence
-# prefilled 16384 new tokens at a time over its growing cached prefix).
+# its index-key cache held as E4M3 bytes plus per-token scales; and packed /
+# chunked prefills (8 sequences of 16384 tokens in one call; 256 prompts of 512
+# tokens in one call; the 128K sequence prefilled 16384 new tokens at a time over
+# its growing cached prefix).
 WORKLOADS = {
     "tiny_prefill_L4096": Workload("tiny_prefill_L4096", "prefill",
                                    PrefillShape(L=4096, H=8, G=2, d=64, dI=32, B=128, k=4)),
@@ -97,6 +98,8 @@ WORKLOADS = {
                                      plant="hot", n_plant=0, c=3.0, hot_blocks=(0, 1, 2, 3)),
     "prefill_varlen_8x16384": Workload("prefill_varlen_8x16384", "prefill_varlen",
                                        PrefillShape(L=16384, H=64, G=4, d=128, dI=128), batch=8),
+    "prefill_varlen_256x512": Workload("prefill_varlen_256x512", "prefill_varlen",
+                                       PrefillShape(L=512, H=64, G=4, d=128, dI=128), batch=256),
     "prefill_chunked_L131072_C16384": Workload("prefill_chunked_L131072_C16384", "prefill_varlen",
                                                PrefillShape(L=131072, H=64, G=4, d=128, dI=128),
                                                chunk=16384),

@@ -208,6 +208,31 @@ def test_varlen_prefill_arguments(lib):
     assert call([0, 100], [0, 100], nbytes=ctypes.c_size_t(64)) == WS_SMALL
 
 
+def test_varlen_workspace_size(lib):
+    """The varlen workspace size is host arithmetic: the single-sequence size for one
+    sequence, and the size of the largest batch (at most 128 sequences) otherwise."""
+    I64 = ctypes.c_int64
+
+    def ws(cu_q, cu_kv, H=16, G=4, d=128, dI=128, k=8):
+        aq, akv = (I64 * len(cu_q))(*cu_q), (I64 * len(cu_kv))(*cu_kv)
+        return lib.msa_prefill_varlen_workspace_size(aq, akv, len(cu_q) - 1, H, G, d, dI, 128, k)
+
+    def single(L):
+        return lib.msa_prefill_workspace_size(L, 16, 4, 128, 128, 128, 8)
+
+    assert lib.msa_prefill_varlen_workspace_size(None, None, 0, 16, 4, 128, 128, 128, 8) == 0
+    assert ws([0, 5000], [0, 5000]) == single(5000)
+    cu = [512 * i for i in range(65)]              # 64 sequences of 512 tokens, one batch
+    assert ws(cu, cu) > single(512)
+    assert ws(cu, cu) >= 64 * 512 * 16 * 8 * 128 * 2   # the partials of every row
+    cu2 = [512 * i for i in range(201)]            # 200 sequences: batches of 128 and 72
+    assert ws(cu2, cu2) == ws(cu2[:129], cu2[:129])
+    # a sequence with nothing new adds nothing
+    assert ws([0, 0, 300], [0, 4096, 4396]) == ws([0, 300], [0, 300])
+    # more than 8192 new tokens: that sequence runs alone, with its own workspace size
+    assert ws([0, 20000, 20500, 21000], [0, 20000, 20500, 21000]) == single(20000)
+
+
 def test_paged_fp8_decode_arguments(lib):
     f, ws, big, s = _fake(), P(0x100000), ctypes.c_size_t(1 << 40), None
     zero = ctypes.c_float(0)

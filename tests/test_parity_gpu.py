@@ -324,6 +324,109 @@ def test_prefill_with_cached_prefix():
         assert st["max_abs"] < _parity.MAX_ABS and st["mean_abs"] < _parity.MEAN_ABS
 
 
+def _packed_case(lens, prefixes, shape_kw, seed):
+    """Packed varlen inputs: new tokens of every sequence (q, idx_q) and all tokens
+    (k, v, idx_k), plus the per-sequence whole inputs."""
+    shapes = [synth.PrefillShape(L=L, B=128, **shape_kw) for L in lens]
+    xs = [synth.prefill_inputs(sh, seed=seed + i) for i, sh in enumerate(shapes)]
+    cu_q = np.concatenate([[0], np.cumsum([L - P for L, P in zip(lens, prefixes)])])
+    cu_kv = np.concatenate([[0], np.cumsum(lens)])
+    packed = {
+        "q": torch.cat([x["q"][P:] for x, P in zip(xs, prefixes)]).to(DEV),
+        "iq": torch.cat([x["iq"][P:] for x, P in zip(xs, prefixes)]).to(DEV),
+        "k": torch.cat([x["k"] for x in xs]).to(DEV),
+        "v": torch.cat([x["v"] for x in xs]).to(DEV),
+        "ik": torch.cat([x["ik"] for x in xs]).to(DEV),
+    }
+    return shapes, xs, cu_q, cu_kv, packed
+
+
+def _varlen(c, cu_q, cu_kv, k, workspace=None):
+    msa = _msa()
+    out, ids = msa.prefill_varlen(c["q"], c["k"], c["v"], c["iq"], c["ik"], cu_q, cu_kv, kslots=k,
+                                  return_ids=True, workspace=workspace)
+    torch.cuda.synchronize()
+    return out, ids
+
+
+def _short_batch(n, seed, max_len=700):
+    """n sequence lengths in [1, max_len] (boundary lengths first) and prefixes: every
+    third sequence longer than 128 tokens continues a cached prefix of whole blocks."""
+    rng = np.random.default_rng(seed)
+    lens = [1, 127, 128, 129, 255, 256, 257, 640] + list(rng.integers(1, max_len + 1, n - 8))
+    prefixes = [(int(rng.integers(1, L // 128 + 1)) * 128 if (i % 3 == 0 and L > 128) else 0)
+                for i, L in enumerate(lens)]
+    prefixes = [P if P < L else P - 128 for P, L in zip(prefixes, lens)]
+    return [int(L) for L in lens], prefixes
+
+
+def test_prefill_varlen_many_short_sequences():
+    """150 sequences of 1 to 700 tokens, a third of them continuing a cached prefix:
+    two batches (128 and 22 sequences) of one launch set each.  Every sequence's rows
+    equal its own whole-sequence prefill bitwise; sampled rows match the oracle."""
+    kw = dict(H=16, G=4, d=128, dI=128, k=8)
+    lens, prefixes = _short_batch(150, seed=61)
+    _say(f"varlen 150 short sequences, {sum(lens)} tokens, {sum(L - P for L, P in zip(lens, prefixes))} new")
+    shapes, xs, cu_q, cu_kv, c = _packed_case(lens, prefixes, kw, seed=600)
+    out, ids = _varlen(c, cu_q, cu_kv, kw["k"])
+    checked = 0
+    for i, (sh, x, P) in enumerate(zip(shapes, xs, prefixes)):
+        sl = slice(int(cu_q[i]), int(cu_q[i + 1]))
+        o1, i1 = _prefill_gpu(x, sh.k)
+        assert torch.equal(ids[sl], i1[P:]), f"sequence {i} (L={sh.L}, P={P}): ids"
+        assert torch.equal(out[sl].view(torch.int16), o1[P:].view(torch.int16)), \
+            f"sequence {i} (L={sh.L}, P={P}): out"
+        if i % 10 == 0:
+            rows = np.unique(np.array([P, (P + sh.L) // 2, sh.L - 1]))
+            st = _parity.prefill_rows_vs_oracle(x, rows, i1.cpu().numpy()[rows],
+                                                o1.float().cpu().numpy()[rows], 128, sh.k,
+                                                1.0 / math.sqrt(sh.d))
+            assert st["id_mismatches"] == 0
+            assert st["max_abs"] < _parity.MAX_ABS and st["mean_abs"] < _parity.MEAN_ABS
+            checked += len(rows)
+    _say(f"  150 sequences bitwise equal to their own prefill; {checked} rows vs the oracle")
+
+
+def test_prefill_varlen_batching_is_invisible():
+    """The same packed batch with three workspaces -- the full size (every batch
+    formed), a third of it (smaller batches) and the minimum (every sequence alone)
+    -- gives bitwise the same outputs and ids; also for d = 64, dI = 32, G = 2."""
+    msa = _msa()
+    for kw, seed in ((dict(H=16, G=4, d=128, dI=128, k=8), 700),
+                     (dict(H=8, G=2, d=64, dI=32, k=4), 800)):
+        lens, prefixes = _short_batch(40, seed=seed, max_len=1500)
+        shapes, xs, cu_q, cu_kv, c = _packed_case(lens, prefixes, kw, seed=seed)
+        full = msa.workspace_size("prefill_varlen", cu_q=cu_q, cu_kv=cu_kv, **kw)
+        single = msa.workspace_size("prefill", L=max(lens), **kw)
+        o_ref, i_ref = _varlen(c, cu_q, cu_kv, kw["k"])
+        for nbytes in (full // 3, min(single, full // 8)):
+            _say(f"varlen {kw} workspace {nbytes} of {full}")
+            o, i = _varlen(c, cu_q, cu_kv, kw["k"], workspace=msa._workspace(nbytes, DEV))
+            assert torch.equal(i, i_ref)
+            assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+        # and the first sequences against their own prefill
+        for j in range(4):
+            sl = slice(int(cu_q[j]), int(cu_q[j + 1]))
+            o1, i1 = _prefill_gpu(xs[j], shapes[j].k)
+            assert torch.equal(o_ref[sl].view(torch.int16), o1[prefixes[j]:].view(torch.int16))
+
+
+def test_prefill_varlen_long_and_short_mixed():
+    """Short sequences around one with more than 8192 new tokens: batches {300, 500},
+    the long one alone, then {100, 200, 1}.  Every sequence's rows equal its own
+    whole-sequence prefill bitwise."""
+    kw = dict(H=16, G=4, d=128, dI=128, k=8)
+    lens, prefixes = [300, 500, 9000, 100, 200, 1], [0, 384, 256, 0, 128, 0]
+    shapes, xs, cu_q, cu_kv, c = _packed_case(lens, prefixes, kw, seed=900)
+    _say(f"varlen mixed lens={lens} prefixes={prefixes}")
+    out, ids = _varlen(c, cu_q, cu_kv, kw["k"])
+    for i, (sh, x, P) in enumerate(zip(shapes, xs, prefixes)):
+        sl = slice(int(cu_q[i]), int(cu_q[i + 1]))
+        o1, i1 = _prefill_gpu(x, sh.k)
+        assert torch.equal(ids[sl], i1[P:]), f"sequence {i}: ids"
+        assert torch.equal(out[sl].view(torch.int16), o1[P:].view(torch.int16)), f"sequence {i}"
+
+
 def test_prefix_prefill_32k_matches_whole():
     """L = 32768 with the first 16384 tokens cached: bitwise the second half of the
     whole-sequence prefill (a property that holds at any size)."""
