@@ -427,6 +427,40 @@ def test_prefill_varlen_long_and_short_mixed():
         assert torch.equal(out[sl].view(torch.int16), o1[P:].view(torch.int16)), f"sequence {i}"
 
 
+def test_prefill_varlen_256x512_bench_config():
+    """The benchmark's packed-prompt workload in its launch configuration: 256 prompts
+    of 512 tokens (H = 64, G = 4, d = dI = 128, k = 16), two batches of 128, the
+    workspace sized by msa_prefill_varlen_workspace_size.  Sampled prompts equal
+    their own prefill bitwise; sampled rows match the oracle."""
+    msa = _msa()
+    wl = synth.WORKLOADS["prefill_varlen_256x512"]
+    s = wl.shape
+    _say("varlen 256 x 512 (benchmark configuration)")
+    parts = [synth.prefill_inputs(s, seed=b, plant=wl.plant, n_plant=wl.n_plant, c=wl.c,
+                                  device=DEV) for b in range(wl.batch)]
+    c = {n: torch.cat([p_[n] for p_ in parts]) for n in ("q", "k", "v", "iq", "ik")}
+    cu = [b * s.L for b in range(wl.batch + 1)]
+    ws = msa._workspace(msa.workspace_size("prefill_varlen", cu_q=cu, cu_kv=cu, H=s.H, G=s.G,
+                                           d=s.d, dI=s.dI, k=s.k), DEV)
+    out, ids = _varlen(c, cu, cu, s.k, workspace=ws)
+    for b in (0, 1, 127, 128, 200, 255):
+        sl = slice(cu[b], cu[b + 1])
+        o1, i1 = msa.prefill(parts[b]["q"], parts[b]["k"], parts[b]["v"], parts[b]["iq"],
+                             parts[b]["ik"], kslots=s.k, return_ids=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ids[sl], i1) and torch.equal(out[sl].view(torch.int16),
+                                                        o1.view(torch.int16)), f"prompt {b}"
+        if b in (0, 200):
+            host = {n: parts[b][n].cpu() for n in ("q", "k", "v", "iq", "ik")}
+            rows = np.array([0, 127, 128, 300, 511])
+            st = _parity.prefill_rows_vs_oracle(host, rows, i1.cpu().numpy()[rows],
+                                                o1.float().cpu().numpy()[rows], 128, s.k,
+                                                1.0 / math.sqrt(s.d))
+            _say(f"  prompt {b} -> {st}")
+            assert st["id_mismatches"] == 0
+            assert st["max_abs"] < _parity.MAX_ABS and st["mean_abs"] < _parity.MEAN_ABS
+
+
 def test_prefix_prefill_32k_matches_whole():
     """L = 32768 with the first 16384 tokens cached: bitwise the second half of the
     whole-sequence prefill (a property that holds at any size)."""
