@@ -218,12 +218,15 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     // registers with them (it spills), so it keeps the per-lane 16-byte stores.
     constexpr bool kStaged = !(D == 128 && R == 4);
     __shared__ __attribute__((aligned(16))) char lds_stg[4][kStaged ? kStageBytes<D> : 16];
-    // XCD-aware order: work-group b runs on XCD b % 8, which takes a contiguous eighth
-    // of the items actually scheduled (the grid is only an upper bound on them)
+    // XCD-aware order: work-group b runs on XCD b % 8.  Runs of kK4Run consecutive
+    // items (tiles of the same lists: the K/V block stays in that XCD's L2) go to
+    // the XCDs in turn, so at any time all XCDs work on neighbouring lists -- one
+    // group's q rows, a working set the last-level cache holds in good part, where
+    // contiguous eighths per XCD would span all groups' rows.  Work-groups past the
+    // items actually scheduled (the grid is an upper bound) exit.
     const int tot = *total;
-    const int per = (tot + 7) / 8;
-    if ((int)(blockIdx.x / 8) >= per) return;
-    const int x = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    const int run = blockIdx.x / 8;
+    const int x = ((run / kK4Run) * 8 + (int)(blockIdx.x % 8)) * kK4Run + run % kK4Run;
     if (x >= tot) return;
     const int li = items[x];                                 // list of this tile
     const int g = li / nb, j = li % nb;
@@ -328,7 +331,7 @@ static hipError_t k4_dispatch(const uint16_t *q, const uint16_t *kx, const uint1
                               const SchedBuffers &sb, int nb, int64_t L, int64_t q0, int64_t C,
                               int H, int G, int k, float scale_log2, uint16_t *po, float *plse,
                               const BatchMap &bm, hipStream_t s) {
-    const int64_t grid = round_up(k4_max_items(C, G, k, nb), 8);
+    const int64_t grid = round_up(k4_max_items(C, G, k, nb), 8 * kK4Run);
     if (grid == 0) return hipSuccess;
     if (bm.row_kvpos)
         hipLaunchKernelGGL((k4_kv_outer<D, R, true>), dim3((unsigned)grid), dim3(256), 0, s, q, kx,

@@ -12,6 +12,8 @@ constexpr int kBlock = 128;   // tokens per MSA block (B)
 constexpr int kK1KeyChunk = 32;
 // Queries per K4 work item (one staged K/V block serves up to this many queries).
 constexpr int kK4Queries = 128;
+// Consecutive K4 work items that one XCD takes before the next XCD's turn.
+constexpr int kK4Run = 16;
 // Queries whose entries one K3 work-group sorts.
 constexpr int kK3Queries = 2048;
 
