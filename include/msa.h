@@ -32,7 +32,10 @@
  *     queries) and fail with MSA_ERR_WORKSPACE_TOO_SMALL only when not even one
  *     128-query chunk fits.  msa_decode needs its full workspace size.
  *     The library never allocates device memory and never synchronises; all work is
- *     enqueued on `stream` (a hipStream_t passed as void*, NULL = default stream).
+ *     enqueued on `stream` (a hipStream_t passed as void*, NULL = default stream)
+ *     as kernel launches only (no memset or copy), so a call may be captured into a
+ *     HIP graph and replayed; a replay reads the buffers as they are at replay time
+ *     (for msa_prefill_varlen the host offsets are read at capture).
  *   - Return value: an msa_status.  Every argument is validated BEFORE anything is
  *     launched; on an error nothing is launched and no output is written.  Faults
  *     inside kernels surface at the caller's next synchronisation of `stream`.
