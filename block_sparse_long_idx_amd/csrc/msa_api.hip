@@ -59,7 +59,10 @@ AttnWs carve_attn(Carver &c, int64_t C, int H, int G, int d, int k, int nb) {
     w.sb.toff = c.take<int>(lists + 1);
     w.sb.wcnt = c.take<int>((int64_t)k3_num_groups(C) * lists);
     w.sb.total = c.take<int>(1);
-    w.sb.items = c.take<int>(k4_max_items(C, G, k, nb));
+    const int64_t max_items = k4_max_items(C, G, k, nb);
+    w.sb.items = c.take<int>(max_items);
+    w.sb.order = c.take<int>(max_items);
+    w.sb.tcnt = c.take<int>(k3_tile_groups(max_items) * kK3Buckets);
     w.sb.list = c.take<uint32_t>(C * G * k);
     w.po = c.take<uint16_t>(C * H * k * d);
     w.plse = c.take<float>(C * H * k);

@@ -195,7 +195,7 @@ __device__ __forceinline__ void store_rows_staged(char *stg, const u32x4 (&w)[D 
         for (int x = 0; x < NR; ++x) {
             const int idx = x * kWave + lane;
             uint16_t *dst = row_dst(8 * r + idx / CR);
-            if (dst) store16(dst + 8 * (idx % CR), v[x]);
+            if (dst) store16_stream(dst + 8 * (idx % CR), v[x]);
         }
     }
 }
@@ -207,7 +207,7 @@ template <int D, int R, bool BATCH>
 __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kx,
     const uint16_t *__restrict__ vx, const int *__restrict__ offs, const int *__restrict__ toff,
-    const int *__restrict__ total, const int *__restrict__ items,
+    const int *__restrict__ total, const int *__restrict__ items, const int *__restrict__ order,
     const uint32_t *__restrict__ list, int nb, int64_t L, int64_t q0, int H, int G, int kslots,
     float scale_log2, uint16_t *__restrict__ po, float *__restrict__ plse, const BatchMap bm) {
     __shared__ __attribute__((aligned(16))) char lds_k[kBlock * D * 2];
@@ -219,16 +219,18 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     constexpr bool kStaged = !(D == 128 && R == 4);
     __shared__ __attribute__((aligned(16))) char lds_stg[4][kStaged ? kStageBytes<D> : 16];
     // XCD-aware order: work-group b runs on XCD b % 8.  Runs of kK4Run consecutive
-    // items (tiles of the same lists: the K/V block stays in that XCD's L2) go to
-    // the XCDs in turn, so at any time all XCDs work on neighbouring lists -- one
-    // group's q rows, a working set the last-level cache holds in good part, where
-    // contiguous eighths per XCD would span all groups' rows.  Work-groups past the
+    // items of the run order (one group, first entries in one query window) go to
+    // the XCDs in turn, so at any time all XCDs gather the q rows of one narrow range
+    // of queries, which the last-level cache holds across their re-reads, where
+    // contiguous eighths per XCD would span the whole chunk.  Work-groups past the
     // items actually scheduled (the grid is an upper bound) exit.
     const int tot = *total;
     const int run = blockIdx.x / 8;
     const int x = ((run / kK4Run) * 8 + (int)(blockIdx.x % 8)) * kK4Run + run % kK4Run;
     if (x >= tot) return;
-    const int li = items[x];                                 // list of this tile
+    const int u = order[x];                                  // the work item (tile)
+    if ((unsigned)u >= (unsigned)tot) return;                // (order is a permutation)
+    const int li = items[u];                                 // list of this tile
     const int g = li / nb, j = li % nb;
     // the block's first token (single sequence: block j; batch: global block j)
     const int64_t blk0 = BATCH ? (int64_t)bm.blk_tok0[j] : (int64_t)j * kBlock;
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
         if constexpr (BATCH) return on ? bm.row_kvpos[e >> 5] - (int)blk0 : 0;
         else return 0;
     };
-    const int t = x - toff[li];
+    const int t = u - toff[li];
     const int begin = offs[li] + t * kK4Queries;
     const int cnt = min(kK4Queries, offs[li + 1] - begin);
 
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
                                uint16_t *orow = po + ((il * H + hh) * kslots + s) * D;
 #pragma unroll
                                for (int u = 0; u < D / 16; ++u)
-                                   store16(orow + 8 * (4 * (u >> 1) + 2 * (u & 1) + hf), w[u]);
+                                   store16_stream(orow + 8 * (4 * (u >> 1) + 2 * (u & 1) + hf), w[u]);
                            }
                        });
         base = nbase;
@@ -335,11 +337,11 @@ static hipError_t k4_dispatch(const uint16_t *q, const uint16_t *kx, const uint1
     if (grid == 0) return hipSuccess;
     if (bm.row_kvpos)
         hipLaunchKernelGGL((k4_kv_outer<D, R, true>), dim3((unsigned)grid), dim3(256), 0, s, q, kx,
-                           vx, sb.offs, sb.toff, sb.total, sb.items, sb.list, nb, L, q0, H, G, k,
+                           vx, sb.offs, sb.toff, sb.total, sb.items, sb.order, sb.list, nb, L, q0, H, G, k,
                            scale_log2, po, plse, bm);
     else
         hipLaunchKernelGGL((k4_kv_outer<D, R, false>), dim3((unsigned)grid), dim3(256), 0, s, q, kx,
-                           vx, sb.offs, sb.toff, sb.total, sb.items, sb.list, nb, L, q0, H, G, k,
+                           vx, sb.offs, sb.toff, sb.total, sb.items, sb.order, sb.list, nb, L, q0, H, G, k,
                            scale_log2, po, plse, bm);
     return hipGetLastError();
 }
@@ -442,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void k4d_split(const uint16_t *__restrict__
                                if (!active) return;
 #pragma unroll
                                for (int u = 0; u < D / 16; ++u)
-                                   store16(po + prow * D + 8 * (4 * (u >> 1) + 2 * (u & 1) + hf), w[u]);
+                                   store16_stream(po + prow * D + 8 * (4 * (u >> 1) + 2 * (u & 1) + hf), w[u]);
                                if (hf == 0) plse[lrow] = lse;
                            });
             __syncthreads();                       // (B)
@@ -527,7 +529,7 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
 #pragma unroll
         for (int s = 0; s < KMAX; ++s) {
             l[s] = ok[s] ? lr[s * R] : 0.0f;
-            v[s] = ok[s] ? load16(pr + s * D) : u32x4{0, 0, 0, 0};
+            v[s] = ok[s] ? load16_stream(pr + s * D) : u32x4{0, 0, 0, 0};
         }
     } else {
 #pragma unroll
@@ -536,7 +538,7 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
                 const int id = idr[s];
                 ok[s] = id >= 0 && id < nb_lim;
                 l[s] = ok[s] ? lr[s * R] : 0.0f;
-                v[s] = ok[s] ? load16(pr + s * D) : u32x4{0, 0, 0, 0};
+                v[s] = ok[s] ? load16_stream(pr + s * D) : u32x4{0, 0, 0, 0};
             } else {
                 ok[s] = false;
             }
@@ -563,7 +565,7 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
     u32x4 r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-    store16(out + ih * D + sub * 8, r);
+    store16_stream(out + ih * D + sub * 8, r);
 }
 
 template <int D>

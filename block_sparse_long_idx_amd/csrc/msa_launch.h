@@ -16,6 +16,10 @@ constexpr int kK4Queries = 128;
 constexpr int kK4Run = 16;
 // Queries whose entries one K3 work-group sorts.
 constexpr int kK3Queries = 2048;
+// K4 work items that one work-group of K3's tile-ordering passes handles, and the
+// most (group, query window) buckets those passes sort the items into.
+constexpr int kK3Tiles = 4096;
+constexpr int kK3Buckets = 2048;
 
 // Round n up to a multiple of m.
 inline int64_t round_up(int64_t n, int64_t m) { return (n + m - 1) / m * m; }
@@ -96,12 +100,15 @@ struct SchedBuffers {
     int *wcnt;       // [G * k3_num_groups(C) * nb] per-work-group counts / prefixes
     int *total;      // [1] number of K4 work items
     int *items;      // [k4_max_items] list index of every K4 work item
+    int *order;      // [k4_max_items] K4's run order: work items by (group, first query)
+    int *tcnt;       // [k3_tile_groups(k4_max_items) * kK3Buckets] bucket counts / bases
     uint32_t *list;  // [C * G * k] entries (i - q0) << 5 | slot
 };
 hipError_t launch_k3_schedule(const int32_t *ids, int64_t C, int G, int k, int nb,
                               const SchedBuffers &sb, const BatchMap &bm, hipStream_t s);
 int64_t k4_max_items(int64_t C, int G, int k, int nb);
 int k3_num_groups(int64_t C);
+int64_t k3_tile_groups(int64_t max_items);
 
 // K4: KV-outer attention over the scheduled lists -> partials per (query, head,
 // slot): po [(i*H + h)*k + slot][d] bf16 (normalised o), plse [((i*G + g)*k + slot)*R

@@ -15,6 +15,16 @@
 // entries inside one work-group's share of a list depends on LDS atomic timing, but
 // no result does: every entry's partial goes to its own (query, head, slot).
 //
+// Then K4's run order: the work items (tiles of 128 entries of one list) sorted by
+// group and by the window of 2^sh queries that holds their first entry, by the same
+// counting sort over work-groups of kK3Tiles items:
+//   tile_count    per-work-group bucket histogram
+//   tile_scan     bucket-major, work-group-minor exclusive prefix (the bases)
+//   tile_scatter  order[base + rank] = item
+// Run in that order, the items in flight at any time gather the q rows of a narrow
+// range of queries, which the last-level cache holds across their 16 re-reads
+// (one per selected block), where the list order spreads them over the whole chunk.
+//
 // Also here: the page-table check of paged decode ("MiniMax M3 的采用瓶颈…"
 // §对建设者的影响: paged MSA decode), run before any page is read.
 #include "msa_device.h"
@@ -239,6 +249,84 @@ __global__ __launch_bounds__(1024) void k3_scan(const int *__restrict__ counts, 
     }
 }
 
+// Bucket of K4 work item u: its group and the query window of its first entry.
+__device__ __forceinline__ int tile_bucket(int u, const int *offs, const int *toff,
+                                           const int *items, const uint32_t *list, int nb,
+                                           int sh, int nw) {
+    const int li = items[u];
+    const int first = offs[li] + (u - toff[li]) * kK4Queries;
+    return (li / nb) * nw + (int)((list[first] >> 5) >> sh);
+}
+
+// Histogram of the buckets of items [w*kK3Tiles, (w+1)*kK3Tiles), zeros included.
+__global__ __launch_bounds__(256) void k3_tile_count(const int *__restrict__ offs,
+                                                     const int *__restrict__ toff,
+                                                     const int *__restrict__ total,
+                                                     const int *__restrict__ items,
+                                                     const uint32_t *__restrict__ list, int nb,
+                                                     int sh, int nw, int nbk,
+                                                     int *__restrict__ tcnt) {
+    __shared__ int lds_h[kK3Buckets];
+    for (int b = threadIdx.x; b < nbk; b += 256) lds_h[b] = 0;
+    __syncthreads();
+    const int u0 = blockIdx.x * kK3Tiles, u1 = min(u0 + kK3Tiles, *total);
+    for (int u = u0 + (int)threadIdx.x; u < u1; u += 256)
+        atomicAdd(&lds_h[tile_bucket(u, offs, toff, items, list, nb, sh, nw)], 1);
+    __syncthreads();
+    int *dst = tcnt + (int64_t)blockIdx.x * nbk;
+    for (int b = threadIdx.x; b < nbk; b += 256) dst[b] = lds_h[b];
+}
+
+// One work-group of 1024 threads: tcnt[w][b] <- (items in buckets < b) + (items of
+// bucket b in work-groups < w).  Thread t owns a contiguous range of buckets.
+__global__ __launch_bounds__(1024) void k3_tile_scan(int *__restrict__ tcnt, int nW, int nbk) {
+    __shared__ int sc[1024];
+    const int tid = threadIdx.x;
+    const int per = (nbk + 1023) / 1024;
+    const int beg = min(tid * per, nbk), end = min(beg + per, nbk);
+    int sum = 0;
+    for (int b = beg; b < end; ++b)
+        for (int w = 0; w < nW; ++w) sum += tcnt[(int64_t)w * nbk + b];
+    sc[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int a = tid >= off ? sc[tid - off] : 0;
+        __syncthreads();
+        sc[tid] += a;
+        __syncthreads();
+    }
+    int run = sc[tid] - sum;
+    for (int b = beg; b < end; ++b)
+        for (int w = 0; w < nW; ++w) {
+            int *p = tcnt + (int64_t)w * nbk + b;
+            const int c = *p;
+            *p = run;
+            run += c;
+        }
+}
+
+// Each work-group places its items at their bucket's base plus a rank in LDS (the
+// order inside one bucket and work-group follows LDS atomic timing; no result
+// depends on the run order).
+__global__ __launch_bounds__(256) void k3_tile_scatter(const int *__restrict__ offs,
+                                                       const int *__restrict__ toff,
+                                                       const int *__restrict__ total,
+                                                       const int *__restrict__ items,
+                                                       const uint32_t *__restrict__ list, int nb,
+                                                       int sh, int nw, int nbk,
+                                                       const int *__restrict__ tcnt,
+                                                       int *__restrict__ order) {
+    __shared__ int lds_base[kK3Buckets];
+    const int *src = tcnt + (int64_t)blockIdx.x * nbk;
+    for (int b = threadIdx.x; b < nbk; b += 256) lds_base[b] = src[b];
+    __syncthreads();
+    const int u0 = blockIdx.x * kK3Tiles, u1 = min(u0 + kK3Tiles, *total);
+    for (int u = u0 + (int)threadIdx.x; u < u1; u += 256)
+        order[atomicAdd(&lds_base[tile_bucket(u, offs, toff, items, list, nb, sh, nw)], 1)] = u;
+}
+
+int64_t k3_tile_groups(int64_t max_items) { return (max_items + kK3Tiles - 1) / kK3Tiles; }
+
 int64_t k4_max_items(int64_t C, int G, int k, int nb) {
     const int64_t entries = C * G * k;
     const int64_t lists = (int64_t)G * nb;
@@ -264,6 +352,23 @@ hipError_t launch_k3_schedule(const int32_t *ids, int64_t C, int G, int k, int n
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k3_scatter, grid, dim3(256), 2 * nb * sizeof(int), s, ids, C, G, k, nb, bm,
                        sb.offs, sb.wcnt, sb.list);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    // K4's run order: query windows of 2^sh rows, the smallest (at least 512) for
+    // which the G * (windows) buckets fit in kK3Buckets.
+    int sh = 9;
+    while ((int64_t)G * ((C + (1ll << sh) - 1) >> sh) > kK3Buckets) ++sh;
+    const int nw = (int)((C + (1ll << sh) - 1) >> sh);
+    const int nbk = G * nw;
+    const int64_t nTW = k3_tile_groups(k4_max_items(C, G, k, nb));
+    if (nTW == 0) return hipSuccess;
+    hipLaunchKernelGGL(k3_tile_count, dim3((unsigned)nTW), dim3(256), 0, s, sb.offs, sb.toff,
+                       sb.total, sb.items, sb.list, nb, sh, nw, nbk, sb.tcnt);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k3_tile_scan, dim3(1), dim3(1024), 0, s, sb.tcnt, (int)nTW, nbk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k3_tile_scatter, dim3((unsigned)nTW), dim3(256), 0, s, sb.offs, sb.toff,
+                       sb.total, sb.items, sb.list, nb, sh, nw, nbk, sb.tcnt, sb.order);
     return hipGetLastError();
 }
 
