@@ -16,7 +16,7 @@
 // no result does: every entry's partial goes to its own (query, head, slot).
 //
 // Then K4's run order: the work items (tiles of 128 entries of one list) sorted by
-// group and by the window of 2^sh queries that holds their first entry, by the same
+// group and by the window of 2^sh queries that holds their middle entry, by the same
 // counting sort over work-groups of kK3Tiles items:
 //   tile_count    per-work-group bucket histogram
 //   tile_scan     bucket-major, work-group-minor exclusive prefix (the bases)
@@ -249,13 +249,14 @@ __global__ __launch_bounds__(1024) void k3_scan(const int *__restrict__ counts, 
     }
 }
 
-// Bucket of K4 work item u: its group and the query window of its first entry.
+// Bucket of K4 work item u: its group and the query window of its middle entry.
 __device__ __forceinline__ int tile_bucket(int u, const int *offs, const int *toff,
                                            const int *items, const uint32_t *list, int nb,
                                            int sh, int nw) {
     const int li = items[u];
     const int first = offs[li] + (u - toff[li]) * kK4Queries;
-    return (li / nb) * nw + (int)((list[first] >> 5) >> sh);
+    const int mid = first + min(kK4Queries, offs[li + 1] - first) / 2;
+    return (li / nb) * nw + (int)((list[mid] >> 5) >> sh);
 }
 
 // Histogram of the buckets of items [w*kK3Tiles, (w+1)*kK3Tiles), zeros included.
