@@ -49,9 +49,9 @@ __device__ __forceinline__ u32x4 load16(const void *p) {
 }
 __device__ __forceinline__ void store16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 // Streaming forms (the `nt` cache policy) for data that one pass writes and a later
-// kernel reads once: partial rows, their combine, the output.  They keep such
-// streams from displacing data that is re-read meanwhile (K4's q rows and K/V
-// blocks) in the caches.
+// kernel reads once: partial rows, their combine, the output, the block scores the
+// selector reads.  They keep such streams from displacing data that is re-read
+// meanwhile (K4's q rows and K/V blocks) in the caches.
 __device__ __forceinline__ u32x4 load16_stream(const void *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }

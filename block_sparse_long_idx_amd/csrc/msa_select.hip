@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void k2_select(const float *__restrict__ S, in
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int i0 = 4 * (lane + kWave * t);
-        const f32x4 x = i0 < n ? *reinterpret_cast<const f32x4 *>(srow + i0)
+        const f32x4 x = i0 < n ? __builtin_bit_cast(f32x4, load16_stream(srow + i0))
                                : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256) void k2_select(const float *__restrict__ S, in
 #pragma unroll
         for (int u = 0; u < kStream; ++u) {
             const int i0 = base + 4 * (lane + kWave * u);
-            x[u] = i0 < n ? *reinterpret_cast<const f32x4 *>(srow + i0)
+            x[u] = i0 < n ? __builtin_bit_cast(f32x4, load16_stream(srow + i0))
                           : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
