@@ -34,8 +34,14 @@ namespace msa {
 // MFMA operand reads are plain row reads.
 
 // Q operand of one lane's column: D/16 chunks of 8 values (K-step ks takes chunk 2ks+hf).
-// qrow must be a readable row even for an inactive column (the load is not
-// branched around; its value is then replaced by zero).
+// load_q_raw leaves the loaded registers untouched until the MFMAs read them;
+// load_q also zeroes an inactive column (qrow must be readable either way: the load
+// is not branched around).
+template <int D>
+__device__ __forceinline__ void load_q_raw(bf16x8 (&qb)[D / 16], const uint16_t *qrow, int hf) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qb[ks] = as_bf16x8(load16(qrow + (2 * ks + hf) * 8));
+}
 template <int D>
 __device__ __forceinline__ void load_q(bf16x8 (&qb)[D / 16], const uint16_t *qrow, bool active,
                                        int hf) {
@@ -250,15 +256,34 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     const int a = l32 / R, h = l32 % R;
     const int64_t hh = (int64_t)g * R + h;
 
-    // the first pass's q rows are requested before the K/V staging, the second's
-    // right after it; every pass then prefetches the pass two ahead (entries come
-    // from LDS, so those loads issue without waiting)
-    int base = wave * QPW;
-    bool act = base + a < cnt;
-    uint32_t entry = act ? list[begin + base + a] : 0u;
-    bf16x8 qb[D / 16];
-    load_q<D>(qb, q + ((q0 + (entry >> 5)) * H + hh) * D, act, hf);
-    int rel = rel_of(act, entry);
+    // Pass p of a wave covers entries wave*QPW + p*STEP + (column / R).  Its q rows
+    // (and entry, and in a batch its position) are requested at the start of pass
+    // p - 1 and consumed -- an empty asm statement that reads the registers --
+    // after that pass's arithmetic and before its partial rows are stored.  Loads
+    // and stores share one counter, and the stores sit in branches that may be
+    // skipped, so any later first use of the loaded registers (the copy at the
+    // loop's end) would wait for every partial row just stored.  The loaded rows
+    // are used unmasked: an inactive column reads a valid row (that of entry 0)
+    // and its result is discarded.  The first pass's rows are requested before the
+    // K/V staging.
+    constexpr int STEP = 4 * QPW;
+    const int first_e = wave * QPW;
+    const int npass = first_e < cnt ? (cnt - first_e + STEP - 1) / STEP : 0;
+    struct PassIn {
+        bool act;
+        uint32_t entry;
+        int rel;
+    };
+    auto request = [&](int pass, bool from_lds, PassIn &in, bf16x8 (&qr)[D / 16]) {
+        const int e = first_e + pass * STEP + a;
+        in.act = e < cnt;
+        in.entry = in.act ? (from_lds ? lds_e[e] : list[begin + e]) : 0u;
+        load_q_raw<D>(qr, q + ((q0 + (in.entry >> 5)) * H + hh) * D, hf);
+        in.rel = rel_of(in.act, in.entry);
+    };
+    PassIn in0;
+    bf16x8 qr0[D / 16];
+    request(0, false, in0, qr0);
 
     if (tid < cnt) lds_e[tid] = list[begin + tid];
     const int kv_row_bytes = G * D * 2;
@@ -272,29 +297,19 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     }
     __syncthreads();
 
-    constexpr int STEP = 4 * QPW;
-    int nbase = base + STEP;
-    bool nact = nbase + a < cnt;
-    uint32_t nentry = nact ? lds_e[nbase + a] : 0u;
-    bf16x8 qn[D / 16];
-    load_q<D>(qn, q + ((q0 + (nentry >> 5)) * H + hh) * D, nact, hf);
-    int nrel = rel_of(nact, nentry);
-
-    while (base < cnt) {
-        const int fbase = nbase + STEP;
-        const bool fact = fbase + a < cnt;
-        const uint32_t fentry = fact ? lds_e[fbase + a] : 0u;
-        bf16x8 qf[D / 16];
-        load_q<D>(qf, q + ((q0 + (fentry >> 5)) * H + hh) * D, fact, hf);
-        const int frel = rel_of(fact, fentry);
-
-        const int64_t il = entry >> 5;
-        const int s = entry & 31;
+    auto attend = [&](int pass, const PassIn &in, const bf16x8 (&qr)[D / 16],
+                      const PassIn &nin, const bf16x8 (&nqr)[D / 16]) {
+        const int64_t il = in.entry >> 5;
+        const int s = in.entry & 31;
         const int64_t lrow = ((il * G + g) * kslots + s) * R + h;
-        const int pbase = base;
-        const uint32_t pentry = entry;
-        attend_pass<D>(lds_k, lds_vt, qb, act, BATCH ? (int64_t)rel : q0 + il - blk0, scale_log2, lane,
-                       [&](const u32x4 (&w)[D / 16], float lse) {
+        const int pbase = first_e + pass * STEP;
+        const uint32_t pentry = in.entry;
+        const bool act = in.act;
+        attend_pass<D>(lds_k, lds_vt, qr, act, BATCH ? (int64_t)in.rel : q0 + il - blk0,
+                       scale_log2, lane, [&](const u32x4 (&w)[D / 16], float lse) {
+#pragma unroll
+                           for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(nqr[ks]));
+                           asm volatile("" ::"v"(nin.entry), "v"(nin.rel));
                            if (act && hf == 0) plse[lrow] = lse;
                            if constexpr (kStaged) {
                                // row = column: query col / R of the pass, head col % R
@@ -312,19 +327,15 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
                                    store16_stream(orow + 8 * (4 * (u >> 1) + 2 * (u & 1) + hf), w[u]);
                            }
                        });
-        base = nbase;
-        act = nact;
-        entry = nentry;
-        rel = nrel;
-        nbase = fbase;
-        nact = fact;
-        nrel = frel;
-        nentry = fentry;
+    };
+    for (int p = 0; p < npass; ++p) {
+        PassIn in1;
+        bf16x8 qr1[D / 16];
+        request(p + 1, true, in1, qr1);
+        attend(p, in0, qr0, in1, qr1);
+        in0 = in1;
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            qb[ks] = qn[ks];
-            qn[ks] = qf[ks];
-        }
+        for (int ks = 0; ks < D / 16; ++ks) qr0[ks] = qr1[ks];
     }
 }
 
