@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     // the block's first token (single sequence: block j; batch: global block j)
     const int64_t blk0 = BATCH ? (int64_t)bm.blk_tok0[j] : (int64_t)j * kBlock;
     // batch: position of an entry's query relative to the block's first token,
-    // fetched with the entry two passes ahead (a single sequence computes it)
+    // fetched with the entry one pass ahead (a single sequence computes it)
     auto rel_of = [&](bool on, uint32_t e) -> int {
         if constexpr (BATCH) return on ? bm.row_kvpos[e >> 5] - (int)blk0 : 0;
         else return 0;
