@@ -34,22 +34,12 @@ namespace msa {
 // MFMA operand reads are plain row reads.
 
 // Q operand of one lane's column: D/16 chunks of 8 values (K-step ks takes chunk 2ks+hf).
-// load_q_raw leaves the loaded registers untouched until the MFMAs read them;
-// load_q also zeroes an inactive column (qrow must be readable either way: the load
-// is not branched around).
+// The loaded registers are left untouched until the MFMAs read them (no select on
+// the value): the first use of a load is where the wait for it lands.
 template <int D>
-__device__ __forceinline__ void load_q_raw(bf16x8 (&qb)[D / 16], const uint16_t *qrow, int hf) {
+__device__ __forceinline__ void load_q(bf16x8 (&qb)[D / 16], const uint16_t *qrow, int hf) {
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qb[ks] = as_bf16x8(load16(qrow + (2 * ks + hf) * 8));
-}
-template <int D>
-__device__ __forceinline__ void load_q(bf16x8 (&qb)[D / 16], const uint16_t *qrow, bool active,
-                                       int hf) {
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 v = load16(qrow + (2 * ks + hf) * 8);
-        qb[ks] = as_bf16x8(active ? v : u32x4{0, 0, 0, 0});
-    }
 }
 
 // One pass of 32 columns of a wave over a staged block.  Lane column = l % 32.
@@ -278,7 +268,7 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
         const int e = first_e + pass * STEP + a;
         in.act = e < cnt;
         in.entry = in.act ? (from_lds ? lds_e[e] : list[begin + e]) : 0u;
-        load_q_raw<D>(qr, q + ((q0 + (in.entry >> 5)) * H + hh) * D, hf);
+        load_q<D>(qr, q + ((q0 + (in.entry >> 5)) * H + hh) * D, hf);
         in.rel = rel_of(in.act, in.entry);
     };
     PassIn in0;
@@ -435,21 +425,28 @@ __global__ __launch_bounds__(256, 2) void k4d_split(const uint16_t *__restrict__
             item = nxt;
         }
     } else if (wave == 0) {
-        for (int64_t item = first; item < n_items; item = next_valid(item + gridDim.x)) {
+        // The q rows of an item are requested before barrier (B) of the previous one,
+        // so their latency overlaps the stagers' LDS stores.  An inactive lane reads
+        // the group's first head row and its result is discarded.
+        const int l32 = lane & 31, hf = lane >> 5;
+        const bool active = l32 < R;
+        auto q_row = [&](int64_t it) {
+            const int64_t n = it / ((int64_t)G * kslots);
+            const int g = (int)((it / kslots) % G);
+            return q + (n * H + (int64_t)g * R + (active ? l32 : 0)) * D;
+        };
+        bf16x8 qb[D / 16];
+        load_q<D>(qb, q_row(first), hf);
+        for (int64_t item = first; item < n_items;) {
             __syncthreads();                       // (A)
             const int64_t n = item / ((int64_t)G * kslots);
             const int g = (int)((item / kslots) % G);
             const int s = (int)(item % kslots);
             const int j = ids[item];
             const int64_t p = (int64_t)seq_len[n] - 1;
-            const int l32 = lane & 31;
-            const bool active = l32 < R;
             const int64_t hh = (int64_t)g * R + (active ? l32 : 0);
             const int64_t prow = (n * H + hh) * kslots + s;
             const int64_t lrow = ((n * G + g) * kslots + s) * R + (active ? l32 : 0);
-            bf16x8 qb[D / 16];
-            load_q<D>(qb, q + (n * H + hh) * D, active, lane >> 5);
-            const int hf = lane >> 5;
             attend_pass<D>(lds_k, lds_vt, qb, active, p - (int64_t)j * kBlock, scale_log2, lane,
                            [&](const u32x4 (&w)[D / 16], float lse) {
                                if (!active) return;
@@ -458,7 +455,10 @@ __global__ __launch_bounds__(256, 2) void k4d_split(const uint16_t *__restrict__
                                    store16_stream(po + prow * D + 8 * (4 * (u >> 1) + 2 * (u & 1) + hf), w[u]);
                                if (hf == 0) plse[lrow] = lse;
                            });
+            const int64_t nxt = next_valid(item + gridDim.x);
+            if (nxt < n_items) load_q<D>(qb, q_row(nxt), hf);
             __syncthreads();                       // (B)
+            item = nxt;
         }
     } else {
         for (int64_t item = first; item < n_items; item = next_valid(item + gridDim.x)) {
