@@ -271,11 +271,14 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
         load_q<D>(qr, q + ((q0 + (in.entry >> 5)) * H + hh) * D, hf);
         in.rel = rel_of(in.act, in.entry);
     };
+    // the item's entries (one per thread, for LDS) are requested with the first
+    // pass's, so that one wait covers both before the q rows and K/V are requested
+    const uint32_t my_e = tid < cnt ? list[begin + tid] : 0u;
     PassIn in0;
     bf16x8 qr0[D / 16];
     request(0, false, in0, qr0);
 
-    if (tid < cnt) lds_e[tid] = list[begin + tid];
+    if (tid < cnt) lds_e[tid] = my_e;
     const int kv_row_bytes = G * D * 2;
     const char *ksrc = reinterpret_cast<const char *>(kx + (blk0 * G + g) * D);
     const char *vsrc = reinterpret_cast<const char *>(vx + (blk0 * G + g) * D);
