@@ -295,9 +295,13 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
         const int64_t il = in.entry >> 5;
         const int s = in.entry & 31;
         const int64_t lrow = ((il * G + g) * kslots + s) * R + h;
-        const int pbase = first_e + pass * STEP;
-        const uint32_t pentry = in.entry;
         const bool act = in.act;
+        // partial row of this lane's column (32 bits: the launcher checks that every
+        // row index fits), or ~0 for an inactive column; the staged stores fetch
+        // each row's index from the lane that owns its column
+        const uint32_t my_row =
+            act ? ((uint32_t)il * (uint32_t)H + (uint32_t)hh) * (uint32_t)kslots + (uint32_t)s
+                : ~0u;
         attend_pass<D>(lds_k, lds_vt, qr, act, BATCH ? (int64_t)in.rel : q0 + il - blk0,
                        scale_log2, lane, [&](const u32x4 (&w)[D / 16], float lse) {
 #pragma unroll
@@ -307,11 +311,8 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
                            if constexpr (kStaged) {
                                // row = column: query col / R of the pass, head col % R
                                store_rows_staged<D>(lds_stg[wave], w, lane, [&](int col) -> uint16_t * {
-                                   const int qa = col / R;
-                                   const uint32_t e = __shfl(pentry, qa * R, kWave);
-                                   if (pbase + qa >= cnt) return nullptr;
-                                   return po + (((int64_t)(e >> 5) * H + (int64_t)g * R + col % R) *
-                                                    kslots + (e & 31)) * D;
+                                   const uint32_t row = (uint32_t)__shfl((int)my_row, col, kWave);
+                                   return row == ~0u ? nullptr : po + (size_t)row * D;
                                });
                            } else if (act) {
                                uint16_t *orow = po + ((il * H + hh) * kslots + s) * D;
@@ -356,6 +357,8 @@ hipError_t launch_k4_kv_outer(const uint16_t *q, const uint16_t *kx, const uint1
                               const BatchMap &bm, hipStream_t s) {
     const float sl2 = scale * kLog2e;
     const int R = H / G;
+    // partial rows are indexed with 32 bits inside the kernel (~0 marks none)
+    if (C * H * (int64_t)k >= (int64_t)UINT32_MAX) return hipErrorInvalidValue;
 #define K4_CASE(dd, rr) \
     if (d == dd && R == rr) return k4_dispatch<dd, rr>(q, kx, vx, sb, nb, L, q0, C, H, G, k, sl2, po, plse, bm, s);
     K4_CASE(64, 1) K4_CASE(64, 2) K4_CASE(64, 4) K4_CASE(64, 8) K4_CASE(64, 16) K4_CASE(64, 32)
