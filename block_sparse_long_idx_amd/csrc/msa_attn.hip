@@ -296,9 +296,9 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
         const int s = in.entry & 31;
         const int64_t lrow = ((il * G + g) * kslots + s) * R + h;
         const bool act = in.act;
-        // partial row of this lane's column (32 bits: the launcher checks that every
-        // row index fits), or ~0 for an inactive column; the staged stores fetch
-        // each row's index from the lane that owns its column
+        // partial row of this lane's column (32 bits: every row index fits, see the
+        // launcher), or ~0 for an inactive column; the staged stores fetch each
+        // row's index from the lane that owns its column
         const uint32_t my_row =
             act ? ((uint32_t)il * (uint32_t)H + (uint32_t)hh) * (uint32_t)kslots + (uint32_t)s
                 : ~0u;
@@ -357,7 +357,9 @@ hipError_t launch_k4_kv_outer(const uint16_t *q, const uint16_t *kx, const uint1
                               const BatchMap &bm, hipStream_t s) {
     const float sl2 = scale * kLog2e;
     const int R = H / G;
-    // partial rows are indexed with 32 bits inside the kernel (~0 marks none)
+    // partial rows are indexed with 32 bits inside the kernel (~0 marks none); the
+    // entry points keep C <= 131072 rows per launch, H <= 256 and k <= 32, so
+    // C * H * k < 2^30 -- this check only guards the assumption
     if (C * H * (int64_t)k >= (int64_t)UINT32_MAX) return hipErrorInvalidValue;
 #define K4_CASE(dd, rr) \
     if (d == dd && R == rr) return k4_dispatch<dd, rr>(q, kx, vx, sb, nb, L, q0, C, H, G, k, sl2, po, plse, bm, s);
