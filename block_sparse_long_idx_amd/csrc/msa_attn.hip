@@ -210,10 +210,8 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     __shared__ __attribute__((aligned(16))) char lds_vt[D * kBlock * 2];
     static_assert(kK4Queries <= 256, "one entry per thread is staged");
     __shared__ uint32_t lds_e[kK4Queries];                   // the item's (query, slot) entries
-    // Whole-row partial stores through LDS; the d = 128, R = 4 build runs out of
-    // registers with them (it spills), so it keeps the per-lane 16-byte stores.
-    constexpr bool kStaged = !(D == 128 && R == 4);
-    __shared__ __attribute__((aligned(16))) char lds_stg[4][kStaged ? kStageBytes<D> : 16];
+    // whole-row partial stores go through a per-wave LDS staging buffer
+    __shared__ __attribute__((aligned(16))) char lds_stg[4][kStageBytes<D>];
     // XCD-aware order: work-group b runs on XCD b % 8.  Runs of kK4Run consecutive
     // items of the run order (one group, first entries in one query window) go to
     // the XCDs in turn, so at any time all XCDs gather the q rows of one narrow range
@@ -308,18 +306,11 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
                            for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(nqr[ks]));
                            asm volatile("" ::"v"(nin.entry), "v"(nin.rel));
                            if (act && hf == 0) plse[lrow] = lse;
-                           if constexpr (kStaged) {
-                               // row = column: query col / R of the pass, head col % R
-                               store_rows_staged<D>(lds_stg[wave], w, lane, [&](int col) -> uint16_t * {
-                                   const uint32_t row = (uint32_t)__shfl((int)my_row, col, kWave);
-                                   return row == ~0u ? nullptr : po + (size_t)row * D;
-                               });
-                           } else if (act) {
-                               uint16_t *orow = po + ((il * H + hh) * kslots + s) * D;
-#pragma unroll
-                               for (int u = 0; u < D / 16; ++u)
-                                   store16_stream(orow + 8 * (4 * (u >> 1) + 2 * (u & 1) + hf), w[u]);
-                           }
+                           // row = column: query col / R of the pass, head col % R
+                           store_rows_staged<D>(lds_stg[wave], w, lane, [&](int col) -> uint16_t * {
+                               const uint32_t row = (uint32_t)__shfl((int)my_row, col, kWave);
+                               return row == ~0u ? nullptr : po + (size_t)row * D;
+                           });
                        });
     };
     for (int p = 0; p < npass; ++p) {
