@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     // whole-row partial stores go through a per-wave LDS staging buffer
     __shared__ __attribute__((aligned(16))) char lds_stg[4][kStageBytes<D>];
     // XCD-aware order: work-group b runs on XCD b % 8.  Runs of kK4Run consecutive
-    // items of the run order (one group, first entries in one query window) go to
+    // items of the run order (one group, middle entries in one query window) go to
     // the XCDs in turn, so at any time all XCDs gather the q rows of one narrow range
     // of queries, which the last-level cache holds across their re-reads, where
     // contiguous eighths per XCD would span the whole chunk.  Work-groups past the

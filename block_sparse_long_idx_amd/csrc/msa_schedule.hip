@@ -22,8 +22,10 @@
 //   tile_scan     bucket-major, work-group-minor exclusive prefix (the bases)
 //   tile_scatter  order[base + rank] = item
 // Run in that order, the items in flight at any time gather the q rows of a narrow
-// range of queries, which the last-level cache holds across their 16 re-reads
-// (one per selected block), where the list order spreads them over the whole chunk.
+// range of queries, which the last-level cache holds across much of their 16
+// re-reads (one per selected block) -- K4 writes its partial rows with streaming
+// stores, so they do not displace them -- where the list order spreads those reads
+// over the whole chunk.
 //
 // Also here: the page-table check of paged decode ("MiniMax M3 的采用瓶颈…"
 // §对建设者的影响: paged MSA decode), run before any page is read.

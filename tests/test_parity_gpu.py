@@ -200,6 +200,30 @@ def test_prefill_128k_sampled():
     _parity.check_selection_valid(ids.cpu().numpy(), np.arange(shape.L), shape.k)
 
 
+@pytest.mark.parametrize("H,G,d,dI,k", [
+    (32, 8, 64, 64, 8),       # eight index groups, d = 64, four heads per group
+    (64, 2, 128, 64, 32),     # 32 heads per group, index dim 64, k = 32 slots
+])
+def test_shape_grid_64k_sampled(H, G, d, dI, k):
+    """Other head groupings at a length where every K1 work-group scores full key
+    chunks and K4 runs many tiles per list; inputs drawn on the GPU, oracle on
+    sampled rows."""
+    shape = synth.PrefillShape(L=65536, H=H, G=G, d=d, dI=dI, B=128, k=k)
+    _say(f"prefill L={shape.L} H={H} G={G} d={d} dI={dI} k={k}: generate on GPU")
+    x = synth.prefill_inputs(shape, seed=21, device=DEV)
+    out, ids = _msa().prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], kslots=k,
+                              return_ids=True)
+    torch.cuda.synchronize()
+    rows = _sample_rows(shape.L, 160, 21)
+    st = _parity.prefill_rows_vs_oracle(x, rows, ids[rows].cpu().numpy(),
+                                        out[rows].float().cpu().numpy(), 128, k,
+                                        1.0 / math.sqrt(d))
+    _say(f"  -> {st}")
+    assert st["id_mismatches"] == 0
+    assert st["max_abs"] < _parity.MAX_ABS and st["mean_abs"] < _parity.MEAN_ABS
+    _parity.check_selection_valid(ids.cpu().numpy(), np.arange(shape.L), k)
+
+
 # ------------------------------- decode ------------------------------------
 def _decode_check(shape, seq_len, seed, seqs=None, device="cpu"):
     msa = _msa()
@@ -250,6 +274,12 @@ def test_decode_tiny_dims():
 def test_decode_other_groupings(H, G, d, dI, k):
     shape = synth.DecodeShape(N=6, Lc=20000, H=H, G=G, d=d, dI=dI, B=128, k=k)
     _decode_check(shape, np.array([20000, 17000, 129, 2048, 1, 9999]), seed=12)
+
+
+def test_decode_k32_ragged():
+    """k = 32 slots (4096 keys per query) over ragged lengths."""
+    shape = synth.DecodeShape(N=6, Lc=30000, H=64, G=4, d=128, dI=128, B=128, k=32)
+    _decode_check(shape, np.array([30000, 4095, 4096, 4097, 129, 22222]), seed=13)
 
 
 def test_decode_full_size_subset():
