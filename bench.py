@@ -159,6 +159,33 @@ def cpu_baseline_prefill(x, shape, target_s=15.0):
                       f"its blocks), {total_s:.1f} s wall"}
 
 
+def cpu_baseline_sparse_attn(x, ids, shape, target_s=15.0):
+    """The oracle's main branch on a random sample of query rows, given the same ids."""
+    import oracle
+    lib = oracle.load()
+    host = {n: x[n].cpu() for n in ("q", "k", "v")}
+    ids_h = ids.cpu().numpy()
+    scale = 1.0 / math.sqrt(shape.d)
+    n, seed = 64, 1
+    total_rows, total_s = 0, 0.0
+    while total_s < target_s:
+        rows = _sample_rows(shape.L, n, seed)
+        t0 = time.perf_counter()
+        oracle.attend(host["q"], host["k"], host["v"], ids_h[rows], B_BLOCK, scale, rows=rows,
+                      lib=lib)
+        dt = time.perf_counter() - t0
+        total_rows += len(rows)
+        total_s += dt
+        seed += 1
+        if dt < target_s / 8:
+            n *= 2
+    return {"value": total_rows / total_s, "unit": "tokens/s",
+            "cores": oracle.num_threads(lib), "kind": "oracle",
+            "sample": f"{total_rows} query rows drawn uniformly from the L={shape.L} workload "
+                      f"(each row: attention of all heads over its listed blocks), "
+                      f"{total_s:.1f} s wall"}
+
+
 def cpu_baseline_decode(x, shape, target_s=15.0):
     """The decode oracle on batches of whole sequences (E4M3 index-key variant when
     the workload's index cache is FP8)."""
@@ -360,6 +387,15 @@ def main():
         def step():
             msa.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], kslots=s.k, out=out,
                         ids_out=ids, workspace=ws, return_ids=True)
+    elif wl.kind == "sparse_attn":     # main branch alone on constructed skewed ids
+        x = synth.prefill_inputs(s, seed=args.seed, plant="none", device=dev)
+        ids = synth.skewed_ids(s.L, s.G, s.k, hot=wl.hot_blocks, seed=args.seed, device=dev)
+        out = torch.empty_like(x["q"])
+        ws = msa._workspace(msa.workspace_size("sparse_attn", L=s.L, H=s.H, G=s.G, d=s.d,
+                                               k=s.k), dev)
+
+        def step():
+            msa.sparse_attn(x["q"], x["k"], x["v"], ids, out=out, workspace=ws)
     elif wl.kind == "prefill_varlen":
         parts = [synth.prefill_inputs(s, seed=args.seed + b, plant=wl.plant, n_plant=wl.n_plant,
                                       c=wl.c, device=dev) for b in range(wl.batch)]
@@ -477,7 +513,7 @@ def main():
               "ms_per_step": ms_per_step, "ms_per_step_median": median_ms,
               "ms_per_step_min": step_ms[0], "scaling": "weak", "vs_baseline": None,
               "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, planted blocks)"}
-    if wl.kind in ("prefill", "prefill_varlen"):
+    if wl.kind in ("prefill", "prefill_varlen", "sparse_attn"):
         nseq = wl.batch
         idn = ids.cpu().numpy().reshape(nseq, s.L, s.G, s.k)
         work = None
@@ -495,6 +531,15 @@ def main():
                             "query_chunk": min(-(-s.L // 128) * 128, 131072)}
         if wl.kind == "prefill_varlen":
             result["config"].update({"sequences": nseq, "new_tokens_per_call": wl.chunk or s.L})
+        if wl.kind == "sparse_attn":   # no index branch in the step
+            result["data"] = "synthetic (seeded N(0,1) bf16 q/k/v, constructed skewed block ids)"
+            result["config"].update({"ids": "constructed: blocks %s + own block + %d random"
+                                            % (list(wl.hot_blocks), s.k - 1 - len(wl.hot_blocks))})
+            del result["config"]["planting"]
+            for key_ in ("k1_index_pool", "k2_select"):
+                work["flops"].pop(key_, None)
+                work["bytes"].pop(key_, None)
+            work["f_total"] = work["flops"]["k4_kv_outer"]
         result["step_mfma_frac"] = work["f_total"] / (ms_per_step / 1e3) / PEAK_BF16_FLOPS
         result["algorithmic_flops_per_step"] = work["f_total"]
         result["dense_gqa_flops_per_step"] = work["dense_gqa_flops"]
@@ -545,6 +590,8 @@ def main():
             # rows of the first sequence (every sequence has the same shape)
             x0 = {n: x[n][:s.L] for n in ("q", "k", "v", "iq", "ik")}
             result["cpu_baseline"] = cpu_baseline_prefill(x0, s, args.cpu_seconds)
+        elif wl.kind == "sparse_attn":
+            result["cpu_baseline"] = cpu_baseline_sparse_attn(x, ids, s, args.cpu_seconds)
         elif wl.kind in ("decode", "decode_fp8idx"):
             result["cpu_baseline"] = cpu_baseline_decode(x, s, args.cpu_seconds)
         else:

@@ -36,7 +36,7 @@ import torch
 
 _CHUNK_ELEMS = 1 << 26  # elements drawn per generator chunk (256 MiB of fp32)
 
-T_Q, T_K, T_V, T_IQ, T_IK, T_PLANT = 1, 2, 3, 4, 5, 6
+T_Q, T_K, T_V, T_IQ, T_IK, T_PLANT, T_IDS = 1, 2, 3, 4, 5, 6, 7
 HOT_MEAN = 8.0   # strength of the group mean direction in idx-Q for "hot" planting
 
 
@@ -66,8 +66,8 @@ class DecodeShape:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "prefill" | "prefill_varlen" | "decode" | "decode_paged" |
-                              # "decode_fp8idx" | "decode_paged_fp8idx"
+    kind: str                 # "prefill" | "prefill_varlen" | "sparse_attn" | "decode" |
+                              # "decode_paged" | "decode_fp8idx" | "decode_paged_fp8idx"
     shape: object
     plant: str = "lit"
     n_plant: int = 4
@@ -91,6 +91,11 @@ WORKLOADS = {
                                PrefillShape(L=32768, H=64, G=4, d=128, dI=128)),
     "prefill_L131072": Workload("prefill_L131072", "prefill",
                                 PrefillShape(L=131072, H=64, G=4, d=128, dI=128)),
+    # the main branch alone on constructed skewed ids: blocks 0-3 + own block + 11
+    # random distinct blocks per (query, group), so blocks 0-3 are hot KV tiles
+    "sparse_attn_L131072_skewed": Workload("sparse_attn_L131072_skewed", "sparse_attn",
+                                           PrefillShape(L=131072, H=64, G=4, d=128, dI=128),
+                                           plant="none", hot_blocks=(0, 1, 2, 3)),
     "decode_N64_L262144": Workload("decode_N64_L262144", "decode",
                                    DecodeShape(N=64, Lc=262144, H=64, G=4, d=128, dI=128)),
     "prefill_L1048576_hot": Workload("prefill_L1048576_hot", "prefill",
@@ -249,6 +254,42 @@ def decode_inputs(shape: DecodeShape, seed: int, plant: str = "lit", n_plant: in
     out["ik_cache"] = ik
     out["seq_len"] = seq_len
     out["planted"] = planted
+    return out
+
+
+def skewed_ids(L: int, G: int, k: int, B: int = 128, hot: tuple = (0, 1, 2, 3), seed: int = 0,
+               device="cpu") -> torch.Tensor:
+    """Constructed block ids [L, G, k] int32 that make blocks ``hot`` hot KV tiles.
+
+    Row (i, g) with b(i) = i // B >= k lists the hot blocks, the own block b(i) and
+    k - 1 - len(hot) further blocks drawn uniformly without replacement from
+    [len(hot), b(i)); a row with b(i) < k lists every block 0 .. b(i) and pads with
+    -1.  Ids ascending.  Drawn in row chunks from per-(seed, chunk) generators.
+    """
+    nb = (L + B - 1) // B
+    nh = len(hot)
+    if tuple(hot) != tuple(range(nh)) or k < nh + 2:
+        raise ValueError("hot blocks must be 0 .. n-1 with n + 2 <= k")
+    m = k - 1 - nh
+    out = torch.empty((L, G, k), dtype=torch.int32, device=device)
+    blk = torch.arange(nb, device=device)
+    slot = torch.arange(k, device=device)
+    rows_per = max(1, (1 << 24) // (G * nb))
+    for ci, r0 in enumerate(range(0, L, rows_per)):
+        r1 = min(L, r0 + rows_per)
+        gen = torch.Generator(device=device)
+        gen.manual_seed(_seed(seed, T_IDS, ci))
+        bi = torch.arange(r0, r1, device=device) // B
+        key = torch.rand((r1 - r0, G, nb), generator=gen, device=device)
+        cand = (blk[None, :] >= nh) & (blk[None, :] < bi[:, None])
+        key = torch.where(cand[:, None, :], key, torch.full_like(key, 2.0))
+        drawn = torch.topk(key, m, dim=2, largest=False).indices
+        fixed = torch.cat([blk[:nh].expand(r1 - r0, G, nh), bi[:, None, None].expand(r1 - r0, G, 1)],
+                          dim=2)
+        long_rows = torch.sort(torch.cat([fixed, drawn], dim=2), dim=2).values
+        short_rows = torch.where(slot[None, :] <= bi[:, None], slot[None, :],
+                                 torch.full_like(slot[None, :], -1))[:, None, :].expand(r1 - r0, G, k)
+        out[r0:r1] = torch.where((bi >= k)[:, None, None], long_rows, short_rows).to(torch.int32)
     return out
 
 

@@ -114,6 +114,39 @@ def test_sparse_attn_with_oracle_ids():
     assert mx < _parity.MAX_ABS and mean < _parity.MEAN_ABS
 
 
+def _sparse_attn_skewed_check(shape, hot, seed, rows):
+    msa = _msa()
+    _say(f"sparse_attn skewed ids L={shape.L} H={shape.H} G={shape.G} hot={hot} seed={seed}")
+    x = synth.prefill_inputs(shape, seed=seed, plant="none", device=DEV)
+    ids = synth.skewed_ids(shape.L, shape.G, shape.k, hot=hot, seed=seed, device=DEV)
+    out = msa.sparse_attn(x["q"], x["k"], x["v"], ids)
+    torch.cuda.synchronize()
+    rows_t = torch.from_numpy(rows).to(DEV)
+    _say(f"  oracle on {len(rows)} rows")
+    # the oracle takes the ids of the listed rows only
+    ref = oracle.attend(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), ids[rows_t].cpu().numpy(), 128,
+                        1.0 / math.sqrt(shape.d), rows=rows)
+    mx, mean = _parity.compare_out(out[rows_t].float().cpu().numpy(), ref)
+    _say(f"  -> max {mx:.3e} mean {mean:.3e}")
+    assert mx < _parity.MAX_ABS and mean < _parity.MEAN_ABS
+    return ids
+
+
+def test_sparse_attn_skewed_ids_8k():
+    """Main branch alone on constructed ids with blocks 0-3 in every row (their lists
+    split into many tiles), rows of every block checked."""
+    shape = synth.PrefillShape(L=8192, H=64, G=4, d=128, dI=128, B=128, k=16)
+    _sparse_attn_skewed_check(shape, (0, 1, 2, 3), 3, _sample_rows(shape.L, 1024, 3))
+
+
+def test_sparse_attn_skewed_ids_128k_bench_config():
+    """The benchmark's constructed-skew workload (L = 131072, one query chunk, blocks
+    0-3 hot: 1024 tiles per hot list and group) on sampled rows."""
+    wl = synth.WORKLOADS["sparse_attn_L131072_skewed"]
+    ids = _sparse_attn_skewed_check(wl.shape, wl.hot_blocks, 0, _sample_rows(wl.shape.L, 768, 4))
+    assert (ids[128 * 16:, :, :4].cpu() == torch.arange(4, dtype=torch.int32)).all()
+
+
 @pytest.mark.parametrize("L", [1, 127, 128, 129, 1000, 4097])
 def test_ragged_lengths(L):
     shape = synth.PrefillShape(L=L, H=8, G=2, d=64, dI=32, B=128, k=4)
