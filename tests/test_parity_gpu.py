@@ -195,8 +195,9 @@ def _sample_rows(L, n, seed):
 
 
 def test_prefill_32k_sampled():
+    """The 32K workload: the first two blocks, the last block and 2048 uniform rows."""
     shape = synth.WORKLOADS["prefill_L32768"].shape
-    _full_check(shape, seed=0, rows=_sample_rows(shape.L, 512, 0))
+    _full_check(shape, seed=0, rows=_sample_rows(shape.L, 2048, 0))
 
 
 def test_hot_blocks_16k_sampled():
@@ -221,7 +222,8 @@ def test_prefill_128k_sampled():
     out, ids = msa.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], kslots=shape.k,
                            return_ids=True)
     torch.cuda.synchronize()
-    rows = _sample_rows(shape.L, 192, 2)
+    # the first two blocks, the last block and 2048 uniform rows
+    rows = _sample_rows(shape.L, 2048, 2)
     _say(f"  oracle on {len(rows)} rows")
     st = _parity.prefill_rows_vs_oracle(x, rows, ids[rows].cpu().numpy(),
                                         out[rows].float().cpu().numpy(), 128, shape.k,
@@ -315,12 +317,12 @@ def test_decode_k32_ragged():
     _decode_check(shape, np.array([30000, 4095, 4096, 4097, 129, 22222]), seed=13)
 
 
-def test_decode_full_size_subset():
-    """64 sequences x 262144 cached tokens; oracle on 6 of them."""
+def test_decode_full_size_all_sequences():
+    """64 sequences x 262144 cached tokens; oracle on every sequence."""
     wl = synth.WORKLOADS["decode_N64_L262144"]
     shape = wl.shape
     seq_len = np.full(shape.N, shape.Lc)
-    _decode_check(shape, seq_len, seed=0, seqs=np.array([0, 1, 17, 31, 48, 63]), device=DEV)
+    _decode_check(shape, seq_len, seed=0, device=DEV)
 
 
 # ------------------------- varlen / prefix prefill ---------------------------
@@ -769,10 +771,10 @@ def test_fp8_decode_tiny_dims():
 
 
 def test_fp8_decode_full_size_subset():
-    """64 sequences x 262144 cached tokens with an E4M3 index-key cache; oracle on 4."""
+    """64 sequences x 262144 cached tokens with an E4M3 index-key cache; oracle on 16."""
     shape = synth.WORKLOADS["decode_N64_L262144"].shape
-    _fp8_decode_check(shape, np.full(shape.N, shape.Lc), seed=0, seqs=np.array([0, 21, 42, 63]),
-                      device=DEV)
+    seqs = np.arange(0, 64, 4) + 3 * (np.arange(16) % 2)     # 0, 7, 8, 15, ..., 63
+    _fp8_decode_check(shape, np.full(shape.N, shape.Lc), seed=0, seqs=seqs, device=DEV)
 
 
 def test_paged_fp8_decode():
@@ -962,8 +964,10 @@ def test_prefill_1m_hot_sampled():
     out, ids = msa.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], kslots=s.k,
                            return_ids=True)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([np.arange(0, 256, 37), np.arange(s.L - 128, s.L, 41),
-                                     np.random.default_rng(3).choice(s.L, 40, replace=False)]))
+    # the first two blocks, the hot blocks 0-3 (rows of their own queries), the last
+    # block and 2048 uniform rows
+    rows = np.unique(np.concatenate([np.arange(0, 512, 3), np.arange(s.L - 128, s.L),
+                                     np.random.default_rng(3).choice(s.L, 2048, replace=False)]))
     _say(f"  oracle on {len(rows)} rows")
     # host copies: only the sampled q rows are materialised
     host = {n: x[n].cpu() for n in ("k", "v", "iq", "ik")}
