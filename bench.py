@@ -10,9 +10,12 @@ over all sequences.
 Prints ONE JSON line with the throughput, the roofline position of the kernel
 that dominates the step (its per-launch duration measured in-process with HIP
 events recorded on the library's stream), and the CPU oracle timed on a bounded
-sample of the same workload as a reported baseline.
+sample of the same workload as a reported baseline.  With the default workload
+(prefill, L = 131072) the line also reports, under "also", the 1M-token prefill
+with hot blocks and the decode step over 64 x 262144 cached tokens, each timed in
+the same run with its own roofline and kernel breakdown.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-also]
 """
 from __future__ import annotations
 
@@ -26,6 +29,9 @@ import time
 import numpy as np
 
 METRIC = "MSA prefill tokens/s @128K & 1M (1 GPU, % MFMA peak); decode us/step @256K"
+DEFAULT_WORKLOAD = "prefill_L131072"
+# reported beside the default workload: (workload, timed steps, warm-up steps)
+ALSO_WORKLOADS = (("prefill_L1048576_hot", 3, 1), ("decode_N64_L262144", 10, 3))
 PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12      # MI355X HBM3E
 B_BLOCK = 128
@@ -342,35 +348,15 @@ def _load_traffic(kernel: str, workload: str):
         return None
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill_L131072")
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--dense-baseline", choices=["auto", "on", "off"], default="auto",
-                    help="time dense causal GQA attention (PyTorch SDPA, fused backends only) on "
-                         "the same q/k/v; auto = prefill workloads up to L = 131072")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
-                    help="only run a plain device-to-device copy of GIB GiB (4 times), the "
-                         "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
-    args = ap.parse_args()
-    if args.copy_calibration > 0:
-        copy_calibration(args.copy_calibration)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the library has no multi-GPU path); "
-              f"--gpus {args.gpus} is not supported", file=sys.stderr)
-        sys.exit(2)
-
+def run_workload(args, name, steps, warmup, cpu_baseline, dense):
+    """Warm up, time exactly `steps` steps of one workload, break them down per
+    kernel, and return the result record (roofline, optional CPU and dense
+    baselines)."""
     import torch
     import block_sparse_long_idx_amd as msa
     import synth
 
-    wl = synth.WORKLOADS[args.workload]
+    wl = synth.WORKLOADS[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] workload {wl.name}: generating inputs on {dev}", file=sys.stderr, flush=True)
@@ -477,39 +463,39 @@ def main():
                                  workspace=ws, return_ids=True)
 
     torch.cuda.synchronize()
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    print(f"[bench] warmup {warmup}", file=sys.stderr, flush=True)
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps --------------------------------------
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] timing {steps} steps", file=sys.stderr, flush=True)
     # one event between consecutive steps: the K-step total and each step's time
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     ev[0].record()
-    for i in range(args.steps):
+    for i in range(steps):
         step()
         ev[i + 1].record()
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
-    ms_per_step = ev[0].elapsed_time(ev[-1]) / args.steps
-    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    ms_per_step = ev[0].elapsed_time(ev[-1]) / steps
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     median_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else \
         0.5 * (step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
 
     # ---- per-kernel breakdown: the same K steps with stage events -----------
-    msa.timing_enable(64 * args.steps + 64)
-    for _ in range(args.steps):
+    msa.timing_enable(64 * steps + 64)
+    for _ in range(steps):
         step()
     per_kernel = msa.timing_collect()
     msa.timing_disable()
-    kernels = {name: {"launches_per_step": n / args.steps, "ms_per_step": tot / args.steps,
+    kernels = {name: {"launches_per_step": n / steps, "ms_per_step": tot / steps,
                       "avg_launch_ms": tot / n} for name, (n, tot) in per_kernel.items()}
     dominant = max(kernels, key=lambda k_: kernels[k_]["ms_per_step"])
 
-    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+    result = {"metric": METRIC, "n_gpus": 1, "steps": steps, "warmup": warmup,
               "ms_per_step": ms_per_step, "ms_per_step_median": median_ms,
               "ms_per_step_min": step_ms[0], "scaling": "weak", "vs_baseline": None,
               "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, planted blocks)"}
@@ -584,7 +570,7 @@ def main():
                          for k_, v in kernels.items()}
 
     # ---- CPU oracle baseline (rank 0, N=1) ------------------------------------
-    if not args.no_cpu_baseline:
+    if cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         if wl.kind in ("prefill", "prefill_varlen"):
             # rows of the first sequence (every sequence has the same shape)
@@ -597,12 +583,58 @@ def main():
         else:
             result["cpu_baseline"] = cpu_baseline_decode_paged(x, s, args.cpu_seconds)
         result["cpu_baseline"]["host"] = _host()
-    want_dense = args.dense_baseline == "on" or (
-        args.dense_baseline == "auto" and wl.kind == "prefill" and s.L <= 131072)
+    want_dense = dense == "on" or (dense == "auto" and wl.kind == "prefill" and s.L <= 131072)
     if want_dense:
         print("[bench] dense causal GQA baseline (SDPA)", file=sys.stderr, flush=True)
         result["dense_baseline"] = dense_gqa_baseline(x, s, ms_per_step)
     result["wall_s_timed_region"] = wall_s
+    return result
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-also", action="store_true",
+                    help="with the default workload, skip the 1M-token prefill and the decode "
+                         "step that the line otherwise also reports (under \"also\")")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dense-baseline", choices=["auto", "on", "off"], default="auto",
+                    help="time dense causal GQA attention (PyTorch SDPA, fused backends only) on "
+                         "the same q/k/v; auto = prefill workloads up to L = 131072")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="only run a plain device-to-device copy of GIB GiB (4 times), the "
+                         "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
+    args = ap.parse_args()
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    result = run_workload(args, args.workload, args.steps, args.warmup,
+                          cpu_baseline=not args.no_cpu_baseline, dense=args.dense_baseline)
+    # the other two workloads of the headline metric, measured in the same run
+    if args.workload == DEFAULT_WORKLOAD and not args.no_also:
+        import torch
+        also = {}
+        for name, steps, warmup in ALSO_WORKLOADS:
+            torch.cuda.empty_cache()
+            r = run_workload(args, name, steps, warmup, cpu_baseline=False, dense="off")
+            also[name] = {key: r[key] for key in ("value", "unit", "higher_is_better", "steps",
+                                                   "warmup", "ms_per_step", "ms_per_step_median",
+                                                   "ms_per_step_min", "config", "roofline",
+                                                   "kernels")}
+            for key in ("step_mfma_frac", "step_hbm_frac"):
+                if key in r:
+                    also[name][key] = r[key]
+        result["also"] = also
     print(json.dumps(result), flush=True)
 
 
