@@ -316,6 +316,39 @@ def copy_calibration(gib: float):
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 4}), flush=True)
 
 
+def gemm_reference(n=8192, reps=20):
+    """What a plain library bf16 GEMM (torch.matmul -> hipBLASLt) sustains on this GPU,
+    on N(0,1) operands and on constant ones: the practical matrix-core rate the
+    contraction kernels are compared with, and how much the operand values alone
+    move it (a power-limited clock)."""
+    import torch
+    res = {"shape": [n, n, n], "dtype": "bf16", "library": "torch.matmul (hipBLASLt)"}
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(0)
+    for name in ("random", "constant"):
+        if name == "random":
+            a = torch.randn((n, n), generator=g, device="cuda:0").to(torch.bfloat16)
+            b = torch.randn((n, n), generator=g, device="cuda:0").to(torch.bfloat16)
+        else:
+            a = torch.full((n, n), 1.0, device="cuda:0", dtype=torch.bfloat16)
+            b = torch.full((n, n), 1.0, device="cuda:0", dtype=torch.bfloat16)
+        c = torch.empty((n, n), device="cuda:0", dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name + "_tflops"] = 2.0 * n ** 3 / (ms / 1e3) / 1e12
+        del a, b, c
+    res["random_frac_of_peak"] = res["random_tflops"] * 1e12 / PEAK_BF16_FLOPS
+    return res
+
+
 def _load_traffic(kernel: str, workload: str):
     """HBM traffic per launch from a committed rocprofv3 counter summary, if one is
     recorded for this kernel and workload and the source files it names (those
@@ -600,6 +633,9 @@ def main():
     ap.add_argument("--no-also", action="store_true",
                     help="with the default workload, skip the 1M-token prefill and the decode "
                          "step that the line otherwise also reports (under \"also\")")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip timing a plain bf16 library GEMM (8192^3) on random and on "
+                         "constant operands, the practical matrix-core reference")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dense-baseline", choices=["auto", "on", "off"], default="auto",
@@ -635,6 +671,8 @@ def main():
                 if key in r:
                     also[name][key] = r[key]
         result["also"] = also
+    if not args.no_gemm_reference:
+        result["gemm_reference"] = gemm_reference()
     print(json.dumps(result), flush=True)
 
 
