@@ -212,6 +212,13 @@ def test_hot_blocks_16k_sampled():
     assert frac > 0.99
 
 
+def test_prefill_ragged_100003_sampled():
+    """A long sequence whose last block is partial (100003 = 781 * 128 + 35 tokens):
+    the first two blocks, the last block and 1024 uniform rows."""
+    shape = synth.PrefillShape(L=100003, H=64, G=4, d=128, dI=128, B=128, k=16)
+    _full_check(shape, seed=11, rows=_sample_rows(shape.L, 1024, 11))
+
+
 def test_determinism_128k():
     """The 128K workload twice: ids and outputs bitwise equal, although the order of
     entries inside the scheduler's lists follows LDS atomic timing."""
@@ -333,6 +340,16 @@ def test_decode_k32_ragged():
     """k = 32 slots (4096 keys per query) over ragged lengths."""
     shape = synth.DecodeShape(N=6, Lc=30000, H=64, G=4, d=128, dI=128, B=128, k=32)
     _decode_check(shape, np.array([30000, 4095, 4096, 4097, 129, 22222]), seed=13)
+
+
+def test_decode_full_size_ragged_lengths():
+    """The full-size cache (64 x 262144) with random lengths from 1 to 262144: short
+    sequences, partial own blocks, and the oracle on every sequence."""
+    shape = synth.WORKLOADS["decode_N64_L262144"].shape
+    rng = np.random.default_rng(21)
+    seq_len = rng.integers(1, shape.Lc + 1, shape.N)
+    seq_len[:4] = [1, 128, 129, shape.Lc]
+    _decode_check(shape, seq_len, seed=21, device=DEV)
 
 
 def test_decode_full_size_all_sequences():
