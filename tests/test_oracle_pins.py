@@ -341,6 +341,59 @@ def check_prefix_and_decode(lib):
         assert np.array_equal(outd[n], out[sl - 1])
 
 
+def check_decode_distinct_sequences(lib):
+    """Decode over caches that differ per sequence (three independently seeded
+    sequences, each cache padded to Lmax with unrelated values past its length)
+    equals each sequence's own prefill at its last token, bit for bit."""
+    B, k, H, G, d, dI = 16, 4, 4, 2, 16, 8
+    lens = [150, 77, 200]
+    Lmax = 200
+    scale = 1.0 / math.sqrt(d)
+    seqs = [_inputs(L, H, G, d, dI, B, k, 30 + n)[1] for n, L in enumerate(lens)]
+    pad = _inputs(Lmax, H, G, d, dI, B, k, 99)[1]
+    def cache(name):
+        out = []
+        for x, L in zip(seqs, lens):
+            out.append(torch.cat([x[name], pad[name][L:]]))
+        return torch.stack(out)
+    qd = torch.stack([x["q"][L - 1] for x, L in zip(seqs, lens)])
+    iqd = torch.stack([x["iq"][L - 1] for x, L in zip(seqs, lens)])
+    ids, gap, out = oracle.decode(qd, iqd, cache("k"), cache("v"), cache("ik"),
+                                  np.array(lens, np.int64), B, k, scale, lib=lib)
+    for n, (x, L) in enumerate(zip(seqs, lens)):
+        pid, pgap, pout = oracle.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], B, k, scale,
+                                         rows=np.array([L - 1]), lib=lib)
+        assert (ids[n] == pid[0]).all()
+        assert np.array_equal(out[n], pout[0])
+
+
+def check_gap_definition(lib):
+    """The near-tie gap of a row is |a - c| / max(|a|, |c|) for a = the score of the
+    last selected competitor and c = the best unselected one (0 when both are 0),
+    and +inf when every competitor is selected; constructed block scores."""
+    B, k, nb = 4, 4, 12
+    base = np.array([5, 9, 1, 7, 3, 8, 2, 6, 4, 0], np.float32)
+    S = np.full((3, 5, nb), -np.inf, np.float32)
+    S[0, 0, :10] = base                      # picks 9, 8, 7; next 6
+    S[0, 1, :10] = -base                     # picks 0, -1, -2; next -3
+    S[0, 2, :10] = [1, 1, 1, 1, 1, 0, 0, 0, 0, 0]   # ties: picks blocks 0-2; next 1
+    S[0, 3, :10] = [0.5, -0.5, 3, 2, -4, -5, -6, -7, -8, -9]   # picks 3, 2, .5; next -.5
+    S[0, 4, :10] = 0.0
+    S[1, :, :2] = [[1, 2]] * 5               # row with b(i) = 2: every competitor taken
+    S[2, :, :10] = base
+    rows = np.array([10 * B + 1, 2 * B + 3, 10 * B + 3])
+    ids, gap = oracle.select(S, rows, B, k, lib=lib)
+    assert ids[0, 0].tolist() == [1, 3, 5, 10]
+    assert ids[0, 1].tolist() == [2, 6, 9, 10]
+    assert ids[0, 2].tolist() == [0, 1, 2, 10]
+    assert ids[0, 3].tolist() == [0, 2, 3, 10]
+    expect = [1.0 / 7.0, 1.0 / 3.0, 0.0, 2.0, 0.0]
+    for g, e in enumerate(expect):
+        assert abs(float(gap[0, g]) - e) < 1e-6, (g, gap[0, g], e)
+    assert np.isinf(gap[1]).all() and (ids[1, :, :3] == [0, 1, 2]).all()
+    assert abs(float(gap[2, 0]) - 1.0 / 7.0) < 1e-6
+
+
 # --------------------------------------------------------------------------
 # 10. Paged decode ("MiniMax M3 的采用瓶颈…" §对建设者的影响: paged MSA decode) is
 #     decode on the cache that the block table spells out: pages laid out by an
@@ -495,8 +548,9 @@ def check_paged_fp8_decode(lib):
 
 PINS = [check_dense_equivalence, check_local_only, check_masked_attention, check_exp_free,
         check_constructed, check_tie_break, check_brute_force, check_invariants,
-        check_properties, check_prefix_and_decode, check_paged_decode, check_e4m3,
-        check_fp8_decode, check_paged_fp8_decode]
+        check_properties, check_prefix_and_decode, check_decode_distinct_sequences,
+        check_gap_definition, check_paged_decode, check_e4m3, check_fp8_decode,
+        check_paged_fp8_decode]
 
 
 @pytest.mark.parametrize("check", PINS, ids=[c.__name__ for c in PINS])
@@ -537,6 +591,14 @@ MUTANTS = {
                              "if (e == 0) v = ldexp((double)m / 8.0, -7);"),
     "fp8_token_scale_ignored": ("s *= (double)kscale[t];", "s *= 1.0;"),
     "fp8_scale_of_wrong_token": ("s *= (double)kscale[t];", "s *= (double)kscale[b * B];"),
+    "decode_key_cache_of_sequence_0": ("const uint16_t *k_n = kc + n * Lmax * G * d;",
+                                       "const uint16_t *k_n = kc;"),
+    "decode_index_cache_of_sequence_0": ("const uint16_t *ik_n = ikc + n * Lmax * dI;",
+                                         "const uint16_t *ik_n = ikc;"),
+    "decode_query_one_token_early": ("int64_t i = Ln - 1;", "int64_t i = Ln - 2;"),
+    "gap_from_first_pick": ("double a = last, c = S[nxt];", "double a = S[chosen[1]], c = S[nxt];"),
+    "gap_not_relative": ("*gap = (den == 0.0) ? 0.0f : (float)(fabs(a - c) / den);",
+                         "*gap = (float)fabs(a - c);"),
 }
 
 
