@@ -194,10 +194,12 @@ def _sample_rows(L, n, seed):
     return np.unique(np.concatenate([head, tail, mid]))
 
 
-def test_prefill_32k_sampled():
-    """The 32K workload: the first two blocks, the last block and 2048 uniform rows."""
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prefill_32k_sampled(seed):
+    """The 32K workload: the first two blocks, the last block and 2048 uniform rows
+    (512 for seeds other than 0)."""
     shape = synth.WORKLOADS["prefill_L32768"].shape
-    _full_check(shape, seed=0, rows=_sample_rows(shape.L, 2048, 0))
+    _full_check(shape, seed=seed, rows=_sample_rows(shape.L, 2048 if seed == 0 else 512, seed))
 
 
 def test_hot_blocks_16k_sampled():
@@ -237,18 +239,20 @@ def test_determinism_128k():
     assert torch.equal(runs[0][0].view(torch.int16), runs[1][0].view(torch.int16))
 
 
-def test_prefill_128k_sampled():
-    """The 128K workload in the launch configuration the benchmark times."""
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prefill_128k_sampled(seed):
+    """The 128K workload in the launch configuration the benchmark times (2048 uniform
+    rows for seed 0, 512 for the others, plus the first two and the last block)."""
     wl = synth.WORKLOADS["prefill_L131072"]
     shape = wl.shape
-    _say("prefill 128K: generate on GPU")
-    x = synth.prefill_inputs(shape, seed=0, plant=wl.plant, device=DEV)
+    _say(f"prefill 128K seed {seed}: generate on GPU")
+    x = synth.prefill_inputs(shape, seed=seed, plant=wl.plant, device=DEV)
     msa = _msa()
     out, ids = msa.prefill(x["q"], x["k"], x["v"], x["iq"], x["ik"], kslots=shape.k,
                            return_ids=True)
     torch.cuda.synchronize()
-    # the first two blocks, the last block and 2048 uniform rows
-    rows = _sample_rows(shape.L, 2048, 2)
+    # the first two blocks, the last block and uniform rows
+    rows = _sample_rows(shape.L, 2048 if seed == 0 else 512, 2 + seed)
     _say(f"  oracle on {len(rows)} rows")
     st = _parity.prefill_rows_vs_oracle(x, rows, ids[rows].cpu().numpy(),
                                         out[rows].float().cpu().numpy(), 128, shape.k,
