@@ -101,7 +101,9 @@ def decode_work(N, Lc, H, G, d, dI, k, B=B_BLOCK, paged=False, fp8idx=False):
     return {
         "bytes": {k1d: idx_bytes + N * G * nb * 4.0,
                   "k4d_split": kv_bytes + N * H * nsel * (d * 2 + 2 * d + 4),
-                  "k2_select": N * G * (nb * 4.0 + k * 4), "k5_combine": part / 2 + N * H * d * 2},
+                  "k2_select": N * G * (nb * 4.0 + k * 4), "k5_combine": part / 2 + N * H * d * 2,
+                  # the merged form: K/V and q in, the output out, partials stay in LDS
+                  "k4d_merge": kv_bytes + N * H * d * 2 * 2},
         "total_bytes": idx_bytes + kv_bytes + small + part,
         "flops": 2.0 * N * G * dI * nb * B + 4.0 * N * H * d * ((nsel - 1) * B + (p % B) + 1),
     }

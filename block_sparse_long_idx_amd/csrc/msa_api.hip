@@ -130,11 +130,11 @@ struct TimedLaunch {
     int name;
     hipEvent_t start, stop;
 };
-enum StageName { kK1, kK2, kK3, kK4, kK5, kK1d, kK4d, kKpc, kK1d8, kQuant, kNumStages };
+enum StageName { kK1, kK2, kK3, kK4, kK5, kK1d, kK4d, kKpc, kK1d8, kQuant, kK4dm, kNumStages };
 const char *const kStageNames[kNumStages] = {"k1_index_pool", "k2_select", "k3_schedule",
                                              "k4_kv_outer", "k5_combine", "k1d_index_pool",
                                              "k4d_split", "page_check", "k1d_index_pool_fp8",
-                                             "quantize_e4m3"};
+                                             "quantize_e4m3", "k4d_merge"};
 struct Timing {
     bool on = false;
     int cap = 0, used = 0;
@@ -174,6 +174,25 @@ int attn_chunk(const uint16_t *q, const uint16_t *kx, const uint16_t *vx, const 
                                       single, s));
     MSA_TIMED(kK5, launch_k5_combine(w.po, w.plse, ids_c, C, H, G, d, k, nbc, out + q0 * H * d,
                                      single, s));
+    return MSA_OK;
+}
+
+// Decode main branch over the selected slots: K4d + K5, or the one launch that
+// merges each (sequence, group)'s slots in LDS where their partials fit (same
+// output bits).  po / plse are the partials' workspace of the two-launch form.
+int decode_attend(const uint16_t *q, const uint16_t *kc, const uint16_t *vc, const int32_t *ids,
+                  const int32_t *len, const int32_t *table, int maxb, int N, int64_t Lmax, int H,
+                  int G, int d, int kslots, float scale, uint16_t *po, float *plse, uint16_t *out,
+                  hipStream_t s) {
+    if (k4d_merge_supported(d, H / G, kslots)) {
+        MSA_TIMED(kK4dm, launch_k4d_merge(q, kc, vc, ids, len, table, maxb, N, Lmax, H, G, d,
+                                          kslots, scale, out, s));
+        return MSA_OK;
+    }
+    MSA_TIMED(kK4d, launch_k4d_split(q, kc, vc, ids, len, table, maxb, N, Lmax, H, G, d, kslots,
+                                     scale, po, plse, s));
+    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out,
+                                     BatchMap{}, s));
     return MSA_OK;
 }
 
@@ -550,10 +569,8 @@ int msa_decode(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache
     MSA_TIMED(kK1d, launch_k1d_index_pool(idx_q, idx_k_cache, seq_len, nullptr, 0, S, N, Lmax, G,
                                           dI, nbp, s));
     MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, seq_len, Lmax, ids, s));
-    MSA_TIMED(kK4d, launch_k4d_split(q, k_cache, v_cache, ids, seq_len, nullptr, 0, N, Lmax, H, G,
-                                     d, kslots, scale, po, plse, s));
-    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, BatchMap{}, s));
-    return MSA_OK;
+    return decode_attend(q, k_cache, v_cache, ids, seq_len, nullptr, 0, N, Lmax, H, G, d,
+                         kslots, scale, po, plse, out, s);
 }
 
 // ----------------------------- paged decode -------------------------------
@@ -602,10 +619,8 @@ int msa_decode_paged(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k
     MSA_TIMED(kK1d, launch_k1d_index_pool(idx_q, idx_k_pages, eff_len, block_table, max_blocks, S,
                                           N, Lmax, G, dI, nbp, s));
     MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, eff_len, Lmax, ids, s));
-    MSA_TIMED(kK4d, launch_k4d_split(q, k_pages, v_pages, ids, eff_len, block_table, max_blocks, N,
-                                     Lmax, H, G, d, kslots, scale, po, plse, s));
-    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, BatchMap{}, s));
-    return MSA_OK;
+    return decode_attend(q, k_pages, v_pages, ids, eff_len, block_table, max_blocks, N, Lmax, H,
+                         G, d, kslots, scale, po, plse, out, s);
 }
 
 // ----------------------- FP8 (E4M3) index-key cache ------------------------
@@ -648,10 +663,8 @@ int msa_decode_fp8idx(const uint16_t *q, const uint16_t *idx_q, const uint16_t *
     MSA_TIMED(kK1d8, launch_k1d_index_pool_fp8(idx_q, idx_k_e4m3, idx_k_scale, seq_len, nullptr, 0,
                                                S, N, Lmax, G, dI, nbp, s));
     MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, seq_len, Lmax, ids, s));
-    MSA_TIMED(kK4d, launch_k4d_split(q, k_cache, v_cache, ids, seq_len, nullptr, 0, N, Lmax, H, G,
-                                     d, kslots, scale, po, plse, s));
-    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, BatchMap{}, s));
-    return MSA_OK;
+    return decode_attend(q, k_cache, v_cache, ids, seq_len, nullptr, 0, N, Lmax, H, G, d,
+                         kslots, scale, po, plse, out, s);
 }
 
 int msa_decode_paged_fp8idx(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_pages,
@@ -690,10 +703,8 @@ int msa_decode_paged_fp8idx(const uint16_t *q, const uint16_t *idx_q, const uint
     MSA_TIMED(kK1d8, launch_k1d_index_pool_fp8(idx_q, idx_k_pages_e4m3, idx_k_scale_pages, eff_len,
                                                block_table, max_blocks, S, N, Lmax, G, dI, nbp, s));
     MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, eff_len, Lmax, ids, s));
-    MSA_TIMED(kK4d, launch_k4d_split(q, k_pages, v_pages, ids, eff_len, block_table, max_blocks, N,
-                                     Lmax, H, G, d, kslots, scale, po, plse, s));
-    MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out, BatchMap{}, s));
-    return MSA_OK;
+    return decode_attend(q, k_pages, v_pages, ids, eff_len, block_table, max_blocks, N, Lmax, H,
+                         G, d, kslots, scale, po, plse, out, s);
 }
 
 // ------------------------------ timing ------------------------------------

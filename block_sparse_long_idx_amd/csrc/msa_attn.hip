@@ -496,6 +496,194 @@ hipError_t launch_k4d_split(const uint16_t *q, const uint16_t *kc, const uint16_
 }
 
 // ---------------------------------------------------------------------------
+// K4d with the combine inside: one work-group per (sequence, group) walks that
+// group's valid slots in slot order (K/V of the next slot staged while the current
+// one is attended, as in K4d; the q rows loaded once), keeps every slot's
+// normalised o (bf16) and log2-sum-exp in LDS, and finally merges them per
+// (head, 8 d values) with K5's arithmetic, in slot order: the output is bitwise
+// the one K4d + K5 give, without the partials' trip through memory and the second
+// launch.  Used when the slots' partials fit in LDS beside the staged block.
+// ---------------------------------------------------------------------------
+// LDS: the staged block (4 * kBlock * D bytes, 64 KB at d = 128) plus the partials,
+// at most 96 KB, so the whole stays within the CU's 160 KB.
+constexpr size_t kK4dmPartialBytes = 96 * 1024;
+template <int D, int R, int KMAX>
+constexpr bool k4dm_fits() {
+    return (size_t)KMAX * R * D * 2 + (size_t)KMAX * R * 4 <= kK4dmPartialBytes;
+}
+
+template <int D, int R, int KMAX>
+__global__ __launch_bounds__(256, 1) void k4d_merge(const uint16_t *__restrict__ q,
+                                                 const uint16_t *__restrict__ kc,
+                                                 const uint16_t *__restrict__ vc,
+                                                 const int32_t *__restrict__ ids,
+                                                 const int32_t *__restrict__ seq_len,
+                                                 const int32_t *__restrict__ table, int maxb,
+                                                 int64_t Lmax, int H, int G, int kslots,
+                                                 float scale_log2, uint16_t *__restrict__ out) {
+    static_assert(k4dm_fits<D, R, KMAX>(), "partials must fit in LDS");
+    __shared__ __attribute__((aligned(16))) char lds_k[kBlock * D * 2];
+    __shared__ __attribute__((aligned(16))) char lds_vt[D * kBlock * 2];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_po[KMAX][R][D];
+    __shared__ float lds_l[KMAX][R];
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int kv_row_bytes = G * D * 2;
+    const int64_t ng = blockIdx.x;
+    const int64_t n = ng / G;
+    const int g = (int)(ng % G);
+    const int32_t *idr = ids + ng * kslots;
+    auto next_valid = [&](int sl) {
+        for (; sl < kslots; ++sl)
+            if (idr[sl] >= 0) return sl;
+        return kslots;
+    };
+    // first K/V element of slot sl's block (contiguous cache or its page)
+    auto kv_src = [&](int sl, int &nrows) {
+        const int j = idr[sl];
+        const int64_t tok0 =
+            table ? (int64_t)table[n * maxb + j] * kBlock : n * Lmax + (int64_t)j * kBlock;
+        nrows = table ? kBlock : (int)min<int64_t>(kBlock, Lmax - (int64_t)j * kBlock);
+        return (tok0 * G + g) * D;
+    };
+    // Roles by wave as in K4d: waves 2-3 stage, wave 0 attends, wave 1 keeps the
+    // barrier count; every role walks the same valid slots and meets two barriers
+    // per slot.
+    const int first = next_valid(0);
+    if (wave >= 2) {
+        const int stid = tid - 2 * kWave;
+        KVStage<D, 2 * kWave> st;
+        int sl = first, nrows;
+        if (sl < kslots) {
+            int64_t off = kv_src(sl, nrows);
+            st.load(reinterpret_cast<const char *>(kc + off),
+                    reinterpret_cast<const char *>(vc + off), kv_row_bytes, nrows, stid);
+        }
+        while (sl < kslots) {
+            st.store(lds_k, lds_vt, stid);
+            __syncthreads();                       // (A) the slot's block is in LDS
+            const int nxt = next_valid(sl + 1);
+            if (nxt < kslots) {
+                const int64_t off = kv_src(nxt, nrows);
+                st.load(reinterpret_cast<const char *>(kc + off),
+                        reinterpret_cast<const char *>(vc + off), kv_row_bytes, nrows, stid);
+            }
+            __syncthreads();                       // (B) the slot's attention is done
+            sl = nxt;
+        }
+    } else if (wave == 0) {
+        // an inactive lane reads the group's first head row; its result is discarded
+        const int l32 = lane & 31, hf = lane >> 5;
+        const bool active = l32 < R;
+        bf16x8 qb[D / 16];
+        load_q<D>(qb, q + (n * H + (int64_t)g * R + (active ? l32 : 0)) * D, hf);
+        const int64_t p = (int64_t)seq_len[n] - 1;
+        for (int sl = first; sl < kslots; sl = next_valid(sl + 1)) {
+            __syncthreads();                       // (A)
+            const int j = idr[sl];
+            attend_pass<D>(lds_k, lds_vt, qb, active, p - (int64_t)j * kBlock, scale_log2, lane,
+                           [&](const u32x4 (&w)[D / 16], float lse) {
+                               if (!active) return;
+#pragma unroll
+                               for (int u = 0; u < D / 16; ++u)
+                                   *reinterpret_cast<u32x4 *>(
+                                       &lds_po[sl][l32][8 * (4 * (u >> 1) + 2 * (u & 1) + hf)]) = w[u];
+                               if (hf == 0) lds_l[sl][l32] = lse;
+                           });
+            __syncthreads();                       // (B)
+        }
+    } else {
+        for (int sl = first; sl < kslots; sl = next_valid(sl + 1)) {
+            __syncthreads();                       // (A)
+            __syncthreads();                       // (B)
+        }
+    }
+    __syncthreads();                               // every slot's partial is in LDS
+    // K5's merge, per (head, 8 d values), slots in order
+    constexpr int TPH = D / 8;
+    for (int t = tid; t < R * TPH; t += 256) {
+        const int h = t / TPH, sub = t % TPH;
+        u32x4 v[KMAX];
+        float l[KMAX];
+        bool ok[KMAX];
+#pragma unroll
+        for (int sl = 0; sl < KMAX; ++sl) {
+            ok[sl] = sl < kslots && idr[sl] >= 0;
+            l[sl] = ok[sl] ? lds_l[sl][h] : 0.0f;
+            v[sl] = ok[sl] ? *reinterpret_cast<const u32x4 *>(&lds_po[sl][h][sub * 8])
+                           : u32x4{0, 0, 0, 0};
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int sl = 0; sl < KMAX; ++sl)
+            if (ok[sl]) M = fmaxf(M, l[sl]);
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        float wsum = 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < KMAX; ++sl) {
+            if (!ok[sl]) continue;
+            const float wt = __builtin_amdgcn_exp2f(l[sl] - M);
+            wsum += wt;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += wt * bf16_to_f32(v[sl][e] & 0xFFFFu);
+                acc[2 * e + 1] += wt * bf16_to_f32(v[sl][e] >> 16);
+            }
+        }
+        const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+        u32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+        store16_stream(out + ((n * H) + (int64_t)g * R + h) * D + sub * 8, r);
+    }
+}
+
+template <int D, int R, int KMAX>
+static hipError_t k4dm_launch(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
+                              const int32_t *ids, const int32_t *seq_len, const int32_t *table,
+                              int maxb, int N, int64_t Lmax, int H, int G, int k, float sl2,
+                              uint16_t *out, hipStream_t s) {
+    if constexpr (k4dm_fits<D, R, KMAX>()) {
+        hipLaunchKernelGGL((k4d_merge<D, R, KMAX>), dim3((unsigned)((int64_t)N * G)), dim3(256),
+                           0, s, q, kc, vc, ids, seq_len, table, maxb, Lmax, H, G, k, sl2, out);
+        return hipGetLastError();
+    } else {
+        return hipErrorNotSupported;
+    }
+}
+
+template <int D, int R>
+static hipError_t k4dm_dispatch(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
+                                const int32_t *ids, const int32_t *seq_len, const int32_t *table,
+                                int maxb, int N, int64_t Lmax, int H, int G, int k, float sl2,
+                                uint16_t *out, hipStream_t s) {
+    if (k <= 4) return k4dm_launch<D, R, 4>(q, kc, vc, ids, seq_len, table, maxb, N, Lmax, H, G, k, sl2, out, s);
+    if (k <= 8) return k4dm_launch<D, R, 8>(q, kc, vc, ids, seq_len, table, maxb, N, Lmax, H, G, k, sl2, out, s);
+    if (k <= 16) return k4dm_launch<D, R, 16>(q, kc, vc, ids, seq_len, table, maxb, N, Lmax, H, G, k, sl2, out, s);
+    return hipErrorNotSupported;
+}
+
+hipError_t launch_k4d_merge(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
+                            const int32_t *ids, const int32_t *seq_len, const int32_t *table,
+                            int maxb, int N, int64_t Lmax, int H, int G, int d, int k, float scale,
+                            uint16_t *out, hipStream_t s) {
+    if (N <= 0) return hipSuccess;
+    const float sl2 = scale * kLog2e;
+    const int R = H / G;
+#define K4DM_CASE(dd, rr) \
+    if (d == dd && R == rr) return k4dm_dispatch<dd, rr>(q, kc, vc, ids, seq_len, table, maxb, N, Lmax, H, G, k, sl2, out, s);
+    K4DM_CASE(64, 1) K4DM_CASE(64, 2) K4DM_CASE(64, 4) K4DM_CASE(64, 8) K4DM_CASE(64, 16) K4DM_CASE(64, 32)
+    K4DM_CASE(128, 1) K4DM_CASE(128, 2) K4DM_CASE(128, 4) K4DM_CASE(128, 8) K4DM_CASE(128, 16) K4DM_CASE(128, 32)
+#undef K4DM_CASE
+    return hipErrorNotSupported;
+}
+
+bool k4d_merge_supported(int d, int R, int k) {
+    if (k < 1 || k > 16 || (d != 64 && d != 128)) return false;
+    const int km = k <= 4 ? 4 : (k <= 8 ? 8 : 16);
+    return (size_t)km * R * d * 2 + (size_t)km * R * 4 <= kK4dmPartialBytes;
+}
+
+// ---------------------------------------------------------------------------
 // K5: combine.  D/8 threads per (query, head), 8 d values per thread.  The partials
 // of all valid slots of a thread are requested at once; a slot is valid when
 // 0 <= id < nb_lim -- the rule K3 used to build the lists -- so stale workspace

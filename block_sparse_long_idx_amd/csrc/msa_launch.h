@@ -126,6 +126,15 @@ hipError_t launch_k4d_split(const uint16_t *q, const uint16_t *kc, const uint16_
                             int maxb, int N, int64_t Lmax, int H, int G, int d, int k, float scale,
                             uint16_t *po, float *plse, hipStream_t s);
 
+// K4d and K5 in one launch: one work-group per (sequence, group) attends its valid
+// slots in order and merges them in LDS; out [N, H, d] bitwise as K4d + K5.  Only
+// where k4d_merge_supported(d, H/G, k) (the partials of k slots fit in LDS).
+bool k4d_merge_supported(int d, int R, int k);
+hipError_t launch_k4d_merge(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
+                            const int32_t *ids, const int32_t *seq_len, const int32_t *table,
+                            int maxb, int N, int64_t Lmax, int H, int G, int d, int k, float scale,
+                            uint16_t *out, hipStream_t s);
+
 // Paged decode: eff_len[n] = seq_len[n] when 1 <= seq_len[n] <= maxb * 128 and
 // every page id the sequence needs is in [0, num_pages), else 0.
 hipError_t launch_page_check(const int32_t *table, int maxb, int64_t num_pages,

@@ -259,7 +259,9 @@ MSA_API int msa_quantize_idx_k_e4m3(const uint16_t *idx_k, int64_t rows, int dI,
  * is bracketed by a pair of hipEvents recorded on the caller's stream; stages are
  * named "k1_index_pool", "k2_select", "k3_schedule" (its four small kernels as
  * one), "k4_kv_outer", "k5_combine", "k1d_index_pool", "k4d_split", "page_check",
- * "k1d_index_pool_fp8", "quantize_e4m3".
+ * "k1d_index_pool_fp8", "quantize_e4m3", "k4d_merge" (decode's attention with the
+ * combine of its slots in the same launch, used where the slots' partials fit in
+ * LDS: k <= 16 and k * (H/G) * d * 2 bytes <= 96 KiB).
  *   msa_timing_enable(max_launches): start recording (events for up to
  *       max_launches stages are created up front; further stages are not timed).
  *   msa_timing_collect(out, max_entries, n_out): waits for the recorded events
