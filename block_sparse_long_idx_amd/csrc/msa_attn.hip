@@ -504,6 +504,38 @@ hipError_t launch_k4d_split(const uint16_t *q, const uint16_t *kc, const uint16_
 // the one K4d + K5 give, without the partials' trip through memory and the second
 // launch.  Used when the slots' partials fit in LDS beside the staged block.
 // ---------------------------------------------------------------------------
+// The combine's arithmetic for one (query, head) and 8 consecutive d values: slots
+// with ok[s] carry a normalised partial v[s] (8 bf16) and its log2-sum-exp l[s];
+//   out = sum_s 2^(l[s] - M) v[s] / sum_s 2^(l[s] - M),  M = max_s l[s],
+// summed in slot order, rounded once to bf16 (all zeros when no slot is valid).
+// Shared by K5 and K4d's merged form, so both give the same bits.
+template <int KMAX>
+__device__ __forceinline__ u32x4 lse_merge(const u32x4 (&v)[KMAX], const float (&l)[KMAX],
+                                           const bool (&ok)[KMAX]) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s)
+        if (ok[s]) M = fmaxf(M, l[s]);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float wsum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+        if (!ok[s]) continue;
+        const float w = __builtin_amdgcn_exp2f(l[s] - M);
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += w * bf16_to_f32(v[s][e] & 0xFFFFu);
+            acc[2 * e + 1] += w * bf16_to_f32(v[s][e] >> 16);
+        }
+    }
+    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    return r;
+}
+
 // LDS: the staged block (4 * kBlock * D bytes, 64 KB at d = 128) plus the partials,
 // at most 96 KB, so the whole stays within the CU's 160 KB.
 constexpr size_t kK4dmPartialBytes = 96 * 1024;
@@ -598,7 +630,7 @@ __global__ __launch_bounds__(256, 1) void k4d_merge(const uint16_t *__restrict__
         }
     }
     __syncthreads();                               // every slot's partial is in LDS
-    // K5's merge, per (head, 8 d values), slots in order
+    // the combine, per (head, 8 d values), slots in order
     constexpr int TPH = D / 8;
     for (int t = tid; t < R * TPH; t += 256) {
         const int h = t / TPH, sub = t % TPH;
@@ -612,28 +644,8 @@ __global__ __launch_bounds__(256, 1) void k4d_merge(const uint16_t *__restrict__
             v[sl] = ok[sl] ? *reinterpret_cast<const u32x4 *>(&lds_po[sl][h][sub * 8])
                            : u32x4{0, 0, 0, 0};
         }
-        float M = -INFINITY;
-#pragma unroll
-        for (int sl = 0; sl < KMAX; ++sl)
-            if (ok[sl]) M = fmaxf(M, l[sl]);
-        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        float wsum = 0.0f;
-#pragma unroll
-        for (int sl = 0; sl < KMAX; ++sl) {
-            if (!ok[sl]) continue;
-            const float wt = __builtin_amdgcn_exp2f(l[sl] - M);
-            wsum += wt;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[2 * e] += wt * bf16_to_f32(v[sl][e] & 0xFFFFu);
-                acc[2 * e + 1] += wt * bf16_to_f32(v[sl][e] >> 16);
-            }
-        }
-        const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-        u32x4 r;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-        store16_stream(out + ((n * H) + (int64_t)g * R + h) * D + sub * 8, r);
+        store16_stream(out + ((n * H) + (int64_t)g * R + h) * D + sub * 8,
+                       lse_merge<KMAX>(v, l, ok));
     }
 }
 
@@ -742,28 +754,7 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
             }
         }
     }
-    float M = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < KMAX; ++s)
-        if (ok[s]) M = fmaxf(M, l[s]);
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    float wsum = 0.0f;
-#pragma unroll
-    for (int s = 0; s < KMAX; ++s) {
-        if (!ok[s]) continue;
-        const float w = __builtin_amdgcn_exp2f(l[s] - M);
-        wsum += w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc[2 * e] += w * bf16_to_f32(v[s][e] & 0xFFFFu);
-            acc[2 * e + 1] += w * bf16_to_f32(v[s][e] >> 16);
-        }
-    }
-    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-    u32x4 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-    store16_stream(out + ih * D + sub * 8, r);
+    store16_stream(out + ih * D + sub * 8, lse_merge<KMAX>(v, l, ok));
 }
 
 template <int D>
