@@ -29,3 +29,57 @@ def test_decode_work_counts_the_index_stream():
     assert abs(w8["bytes"]["k1d_index_pool_fp8"] - 64 * 2047 * 128 * (128 + 4)
                - 64 * 4 * 2047 * 4) < 1
     assert w8["total_bytes"] < 0.6 * w["total_bytes"]
+
+
+def test_traffic_record_follows_its_sources(tmp_path, monkeypatch):
+    """A counter record counts only while the sources it names hash as recorded:
+    the committed records load, and a record whose hash no longer matches (a kernel
+    changed after its counters were taken) gives no traffic figure."""
+    import glob
+    import hashlib
+    import re
+    records = glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md"))
+    assert records
+    for path in records:
+        text = open(path).read()
+        kernel = re.search(r"- kernel: (\S+)", text).group(1)
+        workload = re.search(r"- workload: (\S+)", text).group(1)
+        files = re.search(r"- sources: (.*)", text).group(1).split()
+        h = hashlib.sha256()
+        for f in files:
+            h.update(open(os.path.join(ROOT, "block_sparse_long_idx_amd", "csrc", f), "rb").read())
+        current = re.search(r"- sources_sha256_16: (\w+)", text).group(1) == h.hexdigest()[:16]
+        val = bench._load_traffic(kernel, workload)
+        # a value exactly when the record matches the sources as they are now
+        assert (val is not None) == current, (kernel, workload)
+        if current:
+            assert val == float(re.search(r"- hbm_bytes_per_launch: (\d+)", text).group(1))
+    # a copy of the repository layout with one record whose hash is stale
+    import shutil
+    fake = tmp_path / "repo"
+    (fake / "profiles").mkdir(parents=True)
+    shutil.copytree(os.path.join(ROOT, "block_sparse_long_idx_amd", "csrc"),
+                    fake / "block_sparse_long_idx_amd" / "csrc")
+    src = open(os.path.join(ROOT, "profiles", "traffic_k4_kv_outer_prefill_L131072.md")).read()
+    stale = re.sub(r"sources_sha256_16: \w+", "sources_sha256_16: 0000000000000000", src)
+    (fake / "profiles" / "traffic_k4_kv_outer_prefill_L131072.md").write_text(stale)
+    shutil.copy(os.path.join(ROOT, "bench.py"), fake / "bench.py")
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_copy", fake / "bench.py")
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert mod._load_traffic("k4_kv_outer", "prefill_L131072") is None
+    assert mod._load_traffic("k4_kv_outer", "no_such_workload") is None
+
+
+def test_every_workload_kind_is_benchmarked():
+    import synth
+    kinds = {"prefill", "prefill_varlen", "sparse_attn", "decode", "decode_fp8idx",
+             "decode_paged", "decode_paged_fp8idx"}
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    for name, wl in synth.WORKLOADS.items():
+        assert wl.kind in kinds, name
+        assert f'"{wl.kind}"' in src, (name, wl.kind)
+    assert bench.DEFAULT_WORKLOAD in synth.WORKLOADS
+    for name, steps, warmup in bench.ALSO_WORKLOADS:
+        assert name in synth.WORKLOADS and steps >= 1 and warmup >= 0
