@@ -30,12 +30,27 @@ import numpy as np
 
 METRIC = "MSA prefill tokens/s @128K & 1M (1 GPU, % MFMA peak); decode us/step @256K"
 DEFAULT_WORKLOAD = "prefill_L131072"
-# reported beside the default workload: (workload, timed steps, warm-up steps)
-ALSO_WORKLOADS = (("prefill_L1048576_hot", 3, 1), ("decode_N64_L262144", 10, 3))
+# reported beside the default workload: (workload, timed steps, warm-up steps) -- the
+# other configurations of the metric (1M-token prefill with hot blocks, decode over
+# 64 x 262144 cached tokens), the L = 4096 and L = 32768 prefills, and decode over an
+# E4M3 index-key cache and over shuffled 128-token pages
+ALSO_WORKLOADS = (("prefill_L1048576_hot", 3, 1), ("decode_N64_L262144", 10, 3),
+                  ("tiny_prefill_L4096", 20, 5), ("prefill_L32768", 10, 3),
+                  ("decode_fp8idx_N64_L262144", 10, 3), ("decode_paged_N64_L262144", 10, 3))
 PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12      # MI355X HBM3E
 B_BLOCK = 128
 K4_QUERIES = 128             # (query, slot) entries per KV-outer work item
+
+# The roofline that bounds each kernel: the two contractions (index scores, sparse
+# attention) on the bf16 matrix cores, measured by their algorithmic FLOPs; every
+# other kernel on HBM bandwidth, measured by its algorithmic bytes.
+KERNEL_ROOF = {
+    "k1_index_pool": "mfma", "k4_kv_outer": "mfma",
+    "k2_select": "hbm", "k3_schedule": "hbm", "k5_combine": "hbm",
+    "k1d_index_pool": "hbm", "k1d_index_pool_fp8": "hbm", "k4d_merge": "hbm",
+    "k4d_split": "hbm", "page_check": "hbm", "quantize_e4m3": "hbm",
+}
 
 
 # --------------------------------------------------------------------------
@@ -55,7 +70,11 @@ def prefill_work(L, H, G, d, dI, k, B=B_BLOCK, list_counts=None):
     K1 scores every competitor key of every (query, group): 2*G*dI FLOP per
     (query, key) pair with key block < b(i).  K4 attends, per (query, group),
     the tokens of its selected blocks inside the causal window: 4*r*d FLOP per
-    attended (query, group, token) for the r heads of the group.
+    attended (query, group, token) for the r heads of the group.  Those two are
+    measured by FLOPs; the bytes they move are the design's (the block-score hand-off
+    from K1 to K2; K4's gathered q rows, partial rows and staged K/V blocks) and are
+    reported apart, under "design_bytes".  The HBM-bound kernels K2, K3 and K5 are
+    measured by their bytes.
     """
     r = H // G
     i = np.arange(L, dtype=np.int64)
@@ -70,16 +89,17 @@ def prefill_work(L, H, G, d, dI, k, B=B_BLOCK, list_counts=None):
     k2_bytes = 4.0 * G * float(np.sum(np.where(bi > k - 1, comp_rows, 0))) + 4.0 * L * G * k
     items = float(np.sum(np.ceil(np.asarray(list_counts) / K4_QUERIES))) \
         if list_counts is not None else entries / K4_QUERIES
-    k4_bytes = (entries * r * d * 2            # gathered q rows
-                + entries * r * (2 * d + 4)    # partial (o bf16, lse fp32) writes
-                + items * 2 * B * d * 2)       # K and V block staged per work item
     k5_bytes = entries * r * (2 * d + 4) + L * H * d * 2 + 4.0 * L * G * k
-    k1_bytes = (L * G * dI * 2 + 4.0 * G * float(np.sum(bi)))   # idx_q once + block scores out
     return {
         "flops": {"k1_index_pool": f_idx, "k4_kv_outer": f_attn},
-        "bytes": {"k1_index_pool": k1_bytes, "k2_select": k2_bytes,
-                  "k3_schedule": 12.0 * L * G * k, "k4_kv_outer": k4_bytes,
+        "bytes": {"k2_select": k2_bytes, "k3_schedule": 12.0 * L * G * k,
                   "k5_combine": k5_bytes},
+        "design_bytes": {
+            "k1_index_pool": {"idx_q_in": L * G * dI * 2.0,
+                              "block_scores_out": 4.0 * G * float(np.sum(bi))},
+            "k4_kv_outer": {"q_rows_gathered": entries * r * d * 2.0,
+                            "partial_rows_out": entries * r * (2 * d + 4.0),
+                            "kv_blocks_staged": items * 2 * B * d * 2.0}},
         "pairs": pairs, "attended_per_group": attended, "entries": entries,
         "f_total": f_idx + f_attn,
         "dense_gqa_flops": 4.0 * H * d * float(np.sum(i + 1)),
@@ -113,11 +133,31 @@ def _add_work(a, b):
     """Sum of two prefill_work records (work of a batch of sequences)."""
     out = {}
     for key, val in a.items():
-        if isinstance(val, dict):
-            out[key] = {k_: val[k_] + b[key][k_] for k_ in val}
-        else:
-            out[key] = val + b[key]
+        out[key] = _add_work(val, b[key]) if isinstance(val, dict) else val + b[key]
     return out
+
+
+def roofline(kernel: str, work: dict, n_launch: float, avg_launch_ms: float) -> dict:
+    """Roofline position of one kernel: its algorithmic work per launch (FLOPs for the
+    matrix-core kernels, bytes for the others, per KERNEL_ROOF) over its average launch
+    duration, against MI355X's published peak.  For a matrix-core kernel the bytes its
+    design moves are reported beside it (design_bytes_per_launch), never as its work."""
+    t = avg_launch_ms / 1e3
+    if KERNEL_ROOF[kernel] == "mfma":
+        f = work["flops"][kernel] / n_launch
+        roof = {"bound": "mfma", "achieved": f / t / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
+                "unit": "TFLOP/s", "flops_per_launch": f}
+        design = work.get("design_bytes", {}).get(kernel)
+        if design:
+            per = {name: v / n_launch for name, v in design.items()}
+            roof["design_bytes_per_launch"] = per
+            roof["design_bytes_GBps"] = sum(per.values()) / t / 1e9
+    else:
+        b = work["bytes"][kernel] / n_launch
+        roof = {"bound": "hbm", "achieved": b / t / 1e9, "peak": PEAK_HBM_BYTES / 1e9,
+                "unit": "GB/s", "bytes_per_launch": b}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    return roof
 
 
 # --------------------------------------------------------------------------
@@ -560,6 +600,7 @@ def run_workload(args, name, steps, warmup, cpu_baseline, dense):
             for key_ in ("k1_index_pool", "k2_select"):
                 work["flops"].pop(key_, None)
                 work["bytes"].pop(key_, None)
+                work["design_bytes"].pop(key_, None)
             work["f_total"] = work["flops"]["k4_kv_outer"]
         result["step_mfma_frac"] = work["f_total"] / (ms_per_step / 1e3) / PEAK_BF16_FLOPS
         result["algorithmic_flops_per_step"] = work["f_total"]
@@ -576,25 +617,7 @@ def run_workload(args, name, steps, warmup, cpu_baseline, dense):
     # ---- roofline of the dominant kernel -------------------------------------
     kd = kernels[dominant]
     n_launch = kd["launches_per_step"]
-    t_launch = kd["avg_launch_ms"] / 1e3
-    flops = work.get("flops", {})
-    if isinstance(flops, dict) and dominant in flops:
-        per_launch_flops = flops[dominant] / n_launch
-        per_launch_bytes = work["bytes"].get(dominant, 0.0) / n_launch
-        intensity = per_launch_flops / max(per_launch_bytes, 1.0)
-        if intensity >= PEAK_BF16_FLOPS / PEAK_HBM_BYTES or dominant == "k1_index_pool":
-            roof = {"bound": "mfma", "achieved": per_launch_flops / t_launch / 1e12,
-                    "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"}
-        else:
-            roof = {"bound": "hbm", "achieved": per_launch_bytes / t_launch / 1e9,
-                    "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s"}
-        roof["mfma_tflops"] = per_launch_flops / t_launch / 1e12
-        roof["mfma_frac"] = roof["mfma_tflops"] * 1e12 / PEAK_BF16_FLOPS
-    else:
-        per_launch_bytes = work["bytes"][dominant] / n_launch
-        roof = {"bound": "hbm", "achieved": per_launch_bytes / t_launch / 1e9,
-                "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof = roofline(dominant, work, n_launch, kd["avg_launch_ms"])
     roof["traffic"] = _load_traffic(dominant, wl.name)
     roof["kernel"] = dominant
     roof["launches_per_step"] = n_launch

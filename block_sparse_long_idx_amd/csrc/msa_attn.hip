@@ -386,14 +386,17 @@ __global__ __launch_bounds__(256, 2) void k4d_split(const uint16_t *__restrict__
         return n_items;
     };
     // item -> first K/V element of its block: contiguous cache [N, Lmax, G, D], or the
-    // block's page of a paged cache [pages, 128, G, D] (a page is always whole)
+    // block's page of a paged cache [pages, 128, G, D].  Only the sequence's cached
+    // rows are read: in the query's own block the rows at and past seq_len (not yet
+    // written, possibly non-finite) are staged as zeros, so that a masked key
+    // contributes exactly 0 to the P V product.
     auto kv_src = [&](int64_t it, int &nrows) {
         const int64_t n = it / ((int64_t)G * kslots);
         const int g = (int)((it / kslots) % G);
         const int j = ids[it];
         const int64_t tok0 =
             table ? (int64_t)table[n * maxb + j] * kBlock : n * Lmax + (int64_t)j * kBlock;
-        nrows = table ? kBlock : (int)min<int64_t>(kBlock, Lmax - (int64_t)j * kBlock);
+        nrows = (int)max<int64_t>(1, min<int64_t>(kBlock, (int64_t)seq_len[n] - (int64_t)j * kBlock));
         return (tok0 * G + g) * D;
     };
     // Roles by wave: waves 2-3 stage K/V (store the current item, then load the next
@@ -569,12 +572,13 @@ __global__ __launch_bounds__(256, 1) void k4d_merge(const uint16_t *__restrict__
             if (idr[sl] >= 0) return sl;
         return kslots;
     };
-    // first K/V element of slot sl's block (contiguous cache or its page)
+    // first K/V element of slot sl's block (contiguous cache or its page); rows at and
+    // past seq_len in the own block are staged as zeros (as in K4d)
     auto kv_src = [&](int sl, int &nrows) {
         const int j = idr[sl];
         const int64_t tok0 =
             table ? (int64_t)table[n * maxb + j] * kBlock : n * Lmax + (int64_t)j * kBlock;
-        nrows = table ? kBlock : (int)min<int64_t>(kBlock, Lmax - (int64_t)j * kBlock);
+        nrows = (int)max<int64_t>(1, min<int64_t>(kBlock, (int64_t)seq_len[n] - (int64_t)j * kBlock));
         return (tok0 * G + g) * D;
     };
     // Roles by wave as in K4d: waves 2-3 stage, wave 0 attends, wave 1 keeps the

@@ -104,6 +104,9 @@ MSA_API int msa_select_blocks(const uint16_t *idx_q, const uint16_t *idx_k, int6
  *                                   Rows violating this give unspecified values in
  *                                   their own output rows only.
  *   out       [L, H, d]  bf16 OUT
+ * Inputs must be finite.  The queries of one block attend that block's keys as one
+ * tile with the keys past each query masked to weight 0, so a non-finite V value at
+ * token t would also reach the outputs of the queries of t's block that precede t.
  * ------------------------------------------------------------------------- */
 MSA_API size_t msa_sparse_attn_workspace_size(int64_t L, int H, int G, int d, int B, int kslots);
 MSA_API int msa_sparse_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -167,7 +170,9 @@ MSA_API int msa_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint1
  *   idx_k_cache [N, Lmax, dI]     bf16
  *   seq_len     [N] int32 DEVICE  1 <= seq_len[n] <= Lmax.  A sequence outside that
  *                                 range gets ids all -1 and a zero output row;
- *                                 nothing outside its cache is read.
+ *                                 nothing outside its cache is read.  Rows at and
+ *                                 past seq_len[n] of its caches are never read (they
+ *                                 may hold anything, non-finite values included).
  *   out         [N, H, d]         bf16 OUT
  *   block_ids_out [N, G, k] int32 OUT, may be NULL
  * ------------------------------------------------------------------------- */
@@ -196,6 +201,7 @@ MSA_API int msa_decode(const uint16_t *q, const uint16_t *idx_q, const uint16_t 
  * A sequence whose length is out of range, or one of whose needed table entries
  * lies outside [0, num_pages), gets ids all -1 and a zero output row, and none of
  * its pages is read (the table is checked on the device before any page read).
+ * The rows of a sequence's last page at and past its length are never read.
  * Requires B == 128 and max_blocks * 128 <= INT32_MAX; other limits as msa_decode.
  * ------------------------------------------------------------------------- */
 MSA_API size_t msa_decode_paged_workspace_size(int N, int max_blocks, int H, int G, int d, int dI,

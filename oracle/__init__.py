@@ -48,12 +48,16 @@ def load(path: str | None = None):
                                   P, i64, P, P, P]
     lib.oracle_decode_attend.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, i32, f64, P, i64,
                                          P, P]
+    lib.oracle_decode_block_scores.argtypes = [P, P, P, i64, i32, i32, i32, P, i64, i64, P]
+    lib.oracle_decode_block_scores_fp8.argtypes = [P, P, P, P, i64, i32, i32, i32, P, i64, i64,
+                                                   P]
     lib.oracle_e4m3_table.argtypes = [P]
     lib.oracle_decode_fp8idx.argtypes = [P, P, P, P, P, P, P, i64, i32, i32, i32, i32, i32, i32,
                                          f64, P, i64, P, P, P]
     for f in (lib.oracle_block_scores, lib.oracle_select, lib.oracle_attend,
               lib.oracle_prefill_rows, lib.oracle_decode, lib.oracle_decode_attend,
-              lib.oracle_e4m3_table, lib.oracle_decode_fp8idx):
+              lib.oracle_e4m3_table, lib.oracle_decode_fp8idx, lib.oracle_decode_block_scores,
+              lib.oracle_decode_block_scores_fp8):
         f.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
@@ -184,6 +188,63 @@ def decode_attend(q, k_cache, v_cache, seq_len, ids, B, scale, seqs, lib=None):
                              ids.shape[2], float(scale), _ptr(seqs), len(seqs), _ptr(ids),
                              _ptr(out))
     return out
+
+
+def decode_block_scores(iq, ik_cache, seq_len, B, seqs, lib=None):
+    """Decode block scores S[nseqs, G, nbmax] (fp32) of the listed sequences: the
+    query at position seq_len[n]-1 against sequence n's own index keys; blocks past
+    the query's own block are -inf.  nbmax = ceil(max listed seq_len / B)."""
+    lib = lib or load()
+    iq, ikc = _u16(iq), _u16(ik_cache)
+    N, G, dI = iq.shape
+    Lmax = ikc.shape[1]
+    seq_len = np.ascontiguousarray(np.asarray(seq_len, dtype=np.int64))
+    seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+    nbmax = int((seq_len[seqs].max() + B - 1) // B) if len(seqs) else 1
+    S = np.empty((len(seqs), G, nbmax), np.float32)
+    lib.oracle_decode_block_scores(_ptr(iq), _ptr(ikc), _ptr(seq_len), Lmax, G, dI, B,
+                                   _ptr(seqs), len(seqs), nbmax, _ptr(S))
+    return S
+
+
+def decode_block_scores_fp8(iq, ik8, kscale, seq_len, B, seqs, lib=None):
+    """As decode_block_scores, over an E4M3 index-key cache with per-token scales."""
+    lib = lib or load()
+    iq = _u16(iq)
+    ik8 = np.ascontiguousarray(ik8.cpu().numpy() if hasattr(ik8, "cpu") else ik8, np.uint8)
+    ks = np.ascontiguousarray(kscale.cpu().numpy() if hasattr(kscale, "cpu") else kscale,
+                              np.float32)
+    N, G, dI = iq.shape
+    Lmax = ik8.shape[1]
+    seq_len = np.ascontiguousarray(np.asarray(seq_len, dtype=np.int64))
+    seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+    nbmax = int((seq_len[seqs].max() + B - 1) // B) if len(seqs) else 1
+    S = np.empty((len(seqs), G, nbmax), np.float32)
+    lib.oracle_decode_block_scores_fp8(_ptr(iq), _ptr(ik8), _ptr(ks), _ptr(seq_len), Lmax, G, dI,
+                                       B, _ptr(seqs), len(seqs), nbmax, _ptr(S))
+    return S
+
+
+def decode_paged_block_scores(iq, ik_pages, block_table, seq_len, B, seqs, lib=None):
+    """Decode block scores of the listed (valid) sequences of a paged cache: the
+    sequence's index-key pages gathered in logical order, then decode_block_scores."""
+    iq, ikp = _u16(iq), _u16(ik_pages)
+    table = np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table,
+                       dtype=np.int64)
+    lens = np.asarray(seq_len.cpu() if hasattr(seq_len, "cpu") else seq_len, dtype=np.int64)
+    dI = ikp.shape[2]
+    seqs = np.asarray(seqs, np.int64)
+    nbmax = int((lens[seqs].max() + B - 1) // B) if len(seqs) else 1
+    S = np.full((len(seqs), iq.shape[1], nbmax), -np.inf, np.float32)
+    for r, n in enumerate(seqs):
+        pages = _pages_of(table, lens, n, B, ikp.shape[0])
+        if pages is None:
+            raise ValueError(f"sequence {n} is not valid")
+        Lc = len(pages) * B
+        s1 = decode_block_scores(iq[n:n + 1], ikp[pages].reshape(1, Lc, dI), [int(lens[n])], B,
+                                 [0], lib=lib)
+        S[r, :, :s1.shape[2]] = s1[0]
+    return S
 
 
 def decode_paged(q, iq, k_pages, v_pages, ik_pages, block_table, seq_len, B, kslots, scale=None,

@@ -321,7 +321,9 @@ void oracle_decode(const uint16_t *q, const uint16_t *iq, const uint16_t *kc,
     }
 }
 
-/* Decode main branch only, for the listed sequences with the given ids[nseqs,G,k]. */
+/* Decode main branch only, for the listed sequences with the given ids[nseqs,G,k]:
+ * the query of sequence n is its last cached token (position seq_len[n]-1), attended
+ * over the listed blocks of that sequence's own K/V caches (step 4). */
 void oracle_decode_attend(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
                           const int64_t *seq_len, int64_t Lmax, int H, int G, int d, int B, int k,
                           double scale, const int64_t *seqs, int64_t nseqs, const int32_t *ids,
@@ -331,8 +333,34 @@ void oracle_decode_attend(const uint16_t *q, const uint16_t *kc, const uint16_t 
     for (int64_t r = 0; r < nseqs; ++r) {
         int64_t n = seqs[r];
         int64_t Ln = seq_len[n];
-        row_attend(q + n * H * d, kc + n * Lmax * G * d, vc + n * Lmax * G * d, ids + r * G * k,
-                   Ln - 1, Ln, H, G, d, B, k, scale, out + r * H * d);
+        int64_t qpos = Ln - 1;                           /* the last cached token */
+        const uint16_t *kseq = kc + n * Lmax * G * d;    /* sequence n's caches */
+        const uint16_t *vseq = vc + n * Lmax * G * d;
+        row_attend(q + n * H * d, kseq, vseq, ids + r * G * k, qpos, Ln, H, G, d, B, k, scale,
+                   out + r * H * d);
+    }
+}
+
+/* Decode block scores (steps 1 + 2) of the listed sequences: S[nseqs,G,nbmax] for
+ * the query at position seq_len[n]-1 against sequence n's own index-key cache;
+ * nbmax >= ceil(seq_len[n]/B) for every listed n, and blocks past the query's own
+ * block hold -INFINITY. */
+void oracle_decode_block_scores(const uint16_t *iq, const uint16_t *ikc, const int64_t *seq_len,
+                                int64_t Lmax, int G, int dI, int B, const int64_t *seqs,
+                                int64_t nseqs, int64_t nbmax, float *S)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nseqs; ++r) {
+        int64_t n = seqs[r];
+        int64_t Ln = seq_len[n];
+        int64_t nb = (Ln + B - 1) / B;
+        const uint16_t *iks = ikc + n * Lmax * dI;       /* sequence n's index keys */
+        float *tmp = (float *)malloc(sizeof(float) * (size_t)(G * nb));
+        row_block_scores(iq + n * G * dI, iks, Ln - 1, Ln, G, dI, B, tmp);
+        for (int g = 0; g < G; ++g)
+            for (int64_t b = 0; b < nbmax; ++b)
+                S[(r * G + g) * nbmax + b] = (b < nb) ? tmp[g * nb + b] : -INFINITY;
+        free(tmp);
     }
 }
 
@@ -364,6 +392,28 @@ void oracle_decode_fp8idx(const uint16_t *q, const uint16_t *iq, const uint16_t 
         row_attend(q + n * H * d, kc + n * Lmax * G * d, vc + n * Lmax * G * d, ids + r * G * k,
                    i, Ln, H, G, d, B, k, scale, out + r * H * d);
         free(S);
+    }
+}
+
+/* Decode block scores over an FP8 index-key cache (ik8[N,Lmax,dI] E4M3 bytes,
+ * kscale[N,Lmax]); layout and conventions as oracle_decode_block_scores. */
+void oracle_decode_block_scores_fp8(const uint16_t *iq, const uint8_t *ik8, const float *kscale,
+                                    const int64_t *seq_len, int64_t Lmax, int G, int dI, int B,
+                                    const int64_t *seqs, int64_t nseqs, int64_t nbmax, float *S)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nseqs; ++r) {
+        int64_t n = seqs[r];
+        int64_t Ln = seq_len[n];
+        int64_t nb = (Ln + B - 1) / B;
+        const uint8_t *ik8s = ik8 + n * Lmax * dI;       /* sequence n's E4M3 keys */
+        const float *kss = kscale + n * Lmax;            /* and their scales */
+        float *tmp = (float *)malloc(sizeof(float) * (size_t)(G * nb));
+        row_block_scores_fp8(iq + n * G * dI, ik8s, kss, Ln - 1, Ln, G, dI, B, tmp);
+        for (int g = 0; g < G; ++g)
+            for (int64_t b = 0; b < nbmax; ++b)
+                S[(r * G + g) * nbmax + b] = (b < nb) ? tmp[g * nb + b] : -INFINITY;
+        free(tmp);
     }
 }
 

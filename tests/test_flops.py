@@ -41,3 +41,34 @@ def test_decode_work():
     # idx-K stream of all competitor blocks dominates: ~4 GiB of the ~4.57 GB step
     assert 4.2e9 < w["bytes"]["k1d_index_pool"] < 4.4e9
     assert 4.4e9 < w["total_bytes"] < 4.7e9
+
+
+def test_kernel_roofs():
+    """Each kernel is placed on the roof its work has: the index-score and the
+    sparse-attention contractions on the bf16 matrix cores (2*G*dI FLOP per scored
+    (query, key) pair, 4*r*d FLOP per attended (query, group, token)); selection,
+    scheduling, combine and the decode stream on HBM bandwidth."""
+    assert bench.KERNEL_ROOF["k1_index_pool"] == "mfma"
+    assert bench.KERNEL_ROOF["k4_kv_outer"] == "mfma"
+    for k in ("k2_select", "k3_schedule", "k5_combine", "k1d_index_pool", "k1d_index_pool_fp8",
+              "k4d_merge", "k4d_split"):
+        assert bench.KERNEL_ROOF[k] == "hbm", k
+    L, H, G, d, dI, k = 131072, 64, 4, 128, 128, 16
+    w = bench.prefill_work(L, H, G, d, dI, k)
+    # K4 at 13.2 ms per launch: its FLOPs over the bf16 peak, whatever bytes it moves
+    r4 = bench.roofline("k4_kv_outer", w, 1, 13.2)
+    assert r4["bound"] == "mfma" and r4["unit"] == "TFLOP/s"
+    assert abs(r4["frac"] - w["flops"]["k4_kv_outer"] / 13.2e-3 / 2.5e15) < 1e-12
+    assert 0.25 < r4["frac"] < 0.26
+    # the gathered q rows and the partial round trip are the KV-outer design's bytes,
+    # reported beside the FLOPs and never as the kernel's work
+    assert set(r4["design_bytes_per_launch"]) == {"q_rows_gathered", "partial_rows_out",
+                                                  "kv_blocks_staged"}
+    assert "k4_kv_outer" not in w["bytes"] and "k1_index_pool" not in w["bytes"]
+    r1 = bench.roofline("k1_index_pool", w, 1, 6.85)
+    assert r1["bound"] == "mfma" and 0.50 < r1["frac"] < 0.52
+    r5 = bench.roofline("k5_combine", w, 1, 6.28)
+    assert r5["bound"] == "hbm" and r5["unit"] == "GB/s"
+    wd = bench.decode_work(64, 262144, 64, 4, 128, 128, 16)
+    rd = bench.roofline("k1d_index_pool", wd, 1, 0.7146)
+    assert rd["bound"] == "hbm" and 0.74 < rd["frac"] < 0.76

@@ -367,6 +367,130 @@ def check_decode_distinct_sequences(lib):
         assert np.array_equal(out[n], pout[0])
 
 
+def _distinct_decode_case():
+    """Three independently seeded sequences in caches padded to Lmax with unrelated
+    values past each length (the setting of check_decode_distinct_sequences)."""
+    B, k, H, G, d, dI = 16, 4, 4, 2, 16, 8
+    lens = [150, 77, 200]
+    Lmax = 200
+    seqs = [_inputs(L, H, G, d, dI, B, k, 30 + n)[1] for n, L in enumerate(lens)]
+    pad = _inputs(Lmax, H, G, d, dI, B, k, 99)[1]
+    cache = {name: torch.stack([torch.cat([x[name], pad[name][L:]]) for x, L in zip(seqs, lens)])
+             for name in ("k", "v", "ik")}
+    qd = torch.stack([x["q"][L - 1] for x, L in zip(seqs, lens)])
+    iqd = torch.stack([x["iq"][L - 1] for x, L in zip(seqs, lens)])
+    return B, k, d, lens, seqs, cache, qd, iqd
+
+
+def _random_valid_ids(rng, pos, G, k, B):
+    """Arbitrary valid selections (not from the index branch): the own block plus up
+    to k-1 distinct earlier blocks, ascending, -1 padded."""
+    ids = np.full((len(pos), G, k), -1, np.int32)
+    for r, i in enumerate(pos):
+        bi = int(i) // B
+        for g in range(G):
+            m = int(rng.integers(0, min(k - 1, bi) + 1))
+            ch = sorted(list(rng.choice(bi, size=m, replace=False)) + [bi]) if bi else [0]
+            ids[r, g, :len(ch)] = ch
+    return ids
+
+
+def check_decode_attend(lib):
+    """The decode main branch on given ids (what the parity tests attend on near-tie
+    rows) is the prefill main branch of each sequence's own data at its last token:
+    with the ids decode selected it reproduces decode bit for bit, and with arbitrary
+    valid ids it equals oracle.attend on that sequence's row L-1 (pinned to library
+    SDPA by check_masked_attention), for sequences listed in any order."""
+    B, k, d, lens, seqs, cache, qd, iqd = _distinct_decode_case()
+    scale = 1.0 / math.sqrt(d)
+    lens_a = np.array(lens, np.int64)
+    ids, gap, out = oracle.decode(qd, iqd, cache["k"], cache["v"], cache["ik"], lens_a, B, k,
+                                  scale, lib=lib)
+    att = oracle.decode_attend(qd, cache["k"], cache["v"], lens_a, ids, B, scale, [0, 1, 2],
+                               lib=lib)
+    assert np.array_equal(att, out)
+    rng = np.random.default_rng(5)
+    G = iqd.shape[1]
+    order = [2, 0, 1]
+    rids = _random_valid_ids(rng, lens_a[order] - 1, G, k, B)
+    att2 = oracle.decode_attend(qd, cache["k"], cache["v"], lens_a, rids, B, scale, order,
+                                lib=lib)
+    for r, n in enumerate(order):
+        x, L = seqs[n], lens[n]
+        ref = oracle.attend(x["q"], x["k"], x["v"], rids[r:r + 1], B, scale,
+                            rows=np.array([L - 1]), lib=lib)
+        assert np.array_equal(att2[r], ref[0]), (n, L)
+
+
+def check_decode_block_scores(lib):
+    """Decode block scores (what the parity tests' near-tie band check reads) are the
+    prefill block scores of each sequence's own data at its last token, -inf past the
+    own block; the selection on them is decode's.  Over an E4M3 cache with power-of-two
+    scales they equal the scores of the dequantised keys; over pages they equal the
+    contiguous cache's."""
+    B, k, d, lens, seqs, cache, qd, iqd = _distinct_decode_case()
+    lens_a = np.array(lens, np.int64)
+    order = [1, 2, 0]
+    S = oracle.decode_block_scores(iqd, cache["ik"], lens_a, B, order, lib=lib)
+    for r, n in enumerate(order):
+        x, L = seqs[n], lens[n]
+        ref = oracle.block_scores(x["iq"], x["ik"], B, rows=np.array([L - 1]), lib=lib)[0]
+        nb = ref.shape[1]
+        assert np.array_equal(S[r, :, :nb], ref), (n, L)
+        assert np.isneginf(S[r, :, nb:]).all()
+    ids, gap, _ = oracle.decode(qd, iqd, cache["k"], cache["v"], cache["ik"], lens_a, B, k,
+                                1.0, seqs=order, lib=lib)
+    sids, sgap = oracle.select(S, lens_a[order] - 1, B, k, lib=lib)
+    assert np.array_equal(sids, ids) and np.array_equal(sgap, gap)
+    # E4M3 cache with power-of-two scales == the dequantised bf16 keys
+    rng = np.random.default_rng(17)
+    mag = torch.tensor(np.exp2(rng.integers(-5, 6, (3, cache["ik"].shape[1], 1))),
+                       dtype=torch.float32)
+    ikx = (cache["ik"].float() * mag).to(torch.bfloat16)
+    codes, sc = oracle.quantize_e4m3_rows(ikx, lib)
+    table = oracle.e4m3_table(lib)
+    deq = _bf16(table[codes] * sc[..., None])
+    S8 = oracle.decode_block_scores_fp8(iqd, codes, sc, lens_a, B, order, lib=lib)
+    Sd = oracle.decode_block_scores(iqd, deq, lens_a, B, order, lib=lib)
+    assert np.array_equal(S8, Sd)
+    # pages laid out by an independent permutation == the contiguous cache
+    pg = synth.paginate({"ik_cache": cache["ik"]}, B, seed=8, extra_pages=3, names=("ik_cache",))
+    Sp = oracle.decode_paged_block_scores(iqd, pg["ik_pages"], pg["block_table"], lens_a, B,
+                                          order, lib=lib)
+    assert np.array_equal(Sp, S)
+
+
+def check_paged_attend(lib):
+    """The paged decode main branch on given ids is the paged decode's own when fed
+    its ids (shuffled pages, and pages shared between sequences), and the contiguous
+    decode main branch on the caches the table spells out for arbitrary valid ids."""
+    B, k = 16, 4
+    sh = synth.DecodeShape(N=4, Lc=150, H=4, G=2, d=16, dI=8, B=B, k=k)
+    seq_len = np.array([150, 40, 97, 64], np.int64)
+    x = synth.decode_inputs(sh, seed=22, seq_len=seq_len)
+    pg = synth.paginate(x, B, seed=22, extra_pages=4)
+    scale = 1.0 / math.sqrt(sh.d)
+    for share in (False, True):
+        table = pg["block_table"].clone()
+        if share:
+            table[2, :3] = table[0, :3]
+        ids, _, out, valid = oracle.decode_paged(x["q"], x["iq"], pg["k_pages"], pg["v_pages"],
+                                                 pg["ik_pages"], table, seq_len, B, k, scale,
+                                                 lib=lib)
+        assert valid.all()
+        att = oracle.decode_paged_attend(x["q"], pg["k_pages"], pg["v_pages"], table, seq_len,
+                                         ids, B, scale, np.arange(sh.N), lib=lib)
+        assert np.array_equal(att, out), share
+    rng = np.random.default_rng(9)
+    order = np.array([3, 1, 0])
+    rids = _random_valid_ids(rng, seq_len[order] - 1, sh.G, k, B)
+    att2 = oracle.decode_paged_attend(x["q"], pg["k_pages"], pg["v_pages"], pg["block_table"],
+                                      seq_len, rids, B, scale, order, lib=lib)
+    ref = oracle.decode_attend(x["q"], x["k_cache"], x["v_cache"], seq_len, rids, B, scale,
+                               order, lib=lib)
+    assert np.array_equal(att2, ref)
+
+
 def check_gap_definition(lib):
     """The near-tie gap of a row is |a - c| / max(|a|, |c|) for a = the score of the
     last selected competitor and c = the best unselected one (0 when both are 0),
@@ -550,7 +674,8 @@ PINS = [check_dense_equivalence, check_local_only, check_masked_attention, check
         check_constructed, check_tie_break, check_brute_force, check_invariants,
         check_properties, check_prefix_and_decode, check_decode_distinct_sequences,
         check_gap_definition, check_paged_decode, check_e4m3, check_fp8_decode,
-        check_paged_fp8_decode]
+        check_paged_fp8_decode, check_decode_attend, check_decode_block_scores,
+        check_paged_attend]
 
 
 @pytest.mark.parametrize("check", PINS, ids=[c.__name__ for c in PINS])
@@ -596,6 +721,18 @@ MUTANTS = {
     "decode_index_cache_of_sequence_0": ("const uint16_t *ik_n = ikc + n * Lmax * dI;",
                                          "const uint16_t *ik_n = ikc;"),
     "decode_query_one_token_early": ("int64_t i = Ln - 1;", "int64_t i = Ln - 2;"),
+    "decode_attend_query_one_token_early": ("int64_t qpos = Ln - 1;", "int64_t qpos = Ln - 2;"),
+    "decode_attend_caches_of_sequence_0": ("const uint16_t *kseq = kc + n * Lmax * G * d;",
+                                           "const uint16_t *kseq = kc;",
+                                           "const uint16_t *vseq = vc + n * Lmax * G * d;",
+                                           "const uint16_t *vseq = vc;"),
+    "decode_scores_cache_of_sequence_0": ("const uint16_t *iks = ikc + n * Lmax * dI;",
+                                          "const uint16_t *iks = ikc;"),
+    "decode_scores_fp8_cache_of_sequence_0": ("const uint8_t *ik8s = ik8 + n * Lmax * dI;",
+                                              "const uint8_t *ik8s = ik8;"),
+    "decode_scores_query_one_token_early": (
+        "row_block_scores(iq + n * G * dI, iks, Ln - 1, Ln, G, dI, B, tmp);",
+        "row_block_scores(iq + n * G * dI, iks, Ln - 2, Ln, G, dI, B, tmp);"),
     "gap_from_first_pick": ("double a = last, c = S[nxt];", "double a = S[chosen[1]], c = S[nxt];"),
     "gap_not_relative": ("*gap = (den == 0.0) ? 0.0f : (float)(fabs(a - c) / den);",
                          "*gap = (float)fabs(a - c);"),

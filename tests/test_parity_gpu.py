@@ -84,6 +84,8 @@ def test_select_blocks_tiny():
     _parity.check_selection_valid(ids, rows, TINY.k)
     tie, nmis = _parity.compare_ids(ids, oids, gap)
     assert nmis == 0
+    tr = np.nonzero(tie.any(axis=1))[0]
+    _parity.check_near_tie_band(ids[tr], oids[tr], S[tr], rows[tr])
 
 
 def test_sparse_attn_with_oracle_ids():
@@ -310,13 +312,20 @@ def _decode_check(shape, seq_len, seed, seqs=None, device="cpu"):
     _parity.check_selection_valid(ids[seqs], pos, shape.k)
     tie, nmis = _parity.compare_ids(ids[seqs], oids, gap)
     ref = oout.copy()
+    banded = 0
     if tie.any():
         tr = np.nonzero(tie.any(axis=1))[0]
+        lens_t = np.clip(seq_len, 1, shape.Lc)[seqs[tr]]
+        sel = torch.as_tensor(seqs[tr], device=x["iq"].device)
+        S = oracle.decode_block_scores(x["iq"][sel], x["ik_cache"][sel], lens_t, 128,
+                                       np.arange(len(tr)))
+        banded = _parity.check_near_tie_band(ids[seqs[tr]], oids[tr], S, lens_t - 1)
         ref[tr] = oracle.decode_attend(x["q"], x["k_cache"], x["v_cache"],
                                        np.clip(seq_len, 1, shape.Lc), ids[seqs[tr]], 128, scale,
                                        seqs[tr])
     mx, mean = _parity.compare_out(out[seqs], ref)
-    _say(f"  -> near_ties {int(tie.sum())} mismatches {nmis} max {mx:.3e} mean {mean:.3e}")
+    _say(f"  -> near_ties {int(tie.sum())} (band checked {banded}) mismatches {nmis} "
+         f"max {mx:.3e} mean {mean:.3e}")
     assert nmis == 0
     assert mx < _parity.MAX_ABS and mean < _parity.MEAN_ABS
     for n in np.nonzero(~valid)[0]:
@@ -583,6 +592,71 @@ def test_prefix_prefill_32k_matches_whole():
     assert torch.equal(out.view(torch.int16), o1[P:].view(torch.int16))
 
 
+_BF16_NAN = 0x7FC0
+
+
+def _poison_past_len(cache: torch.Tensor, seq_len) -> torch.Tensor:
+    """A copy of a per-sequence cache [N, Lmax, ...] whose rows at and past each
+    sequence's length hold bf16 NaN (rows a decode may not read)."""
+    c = cache.clone()
+    v = c.view(torch.int16)
+    for n, L in enumerate(seq_len):
+        v[n, int(L):] = _BF16_NAN
+    return c
+
+
+@pytest.mark.parametrize("k,Lc", [(8, 2000), (32, 5000)])
+def test_decode_ignores_rows_past_seq_len(k, Lc):
+    """Cache rows at and past seq_len are not part of the sequence (not yet written):
+    NaN there must change neither the ids nor a single output bit.  k = 8 runs the
+    attention with its combine in one launch, k = 32 the split form plus the combine."""
+    msa = _msa()
+    shape = synth.DecodeShape(N=6, Lc=Lc, H=16, G=4, d=128, dI=128, B=128, k=k)
+    seq_len = np.array([1, 130, Lc // 2 + 5, Lc - 1, Lc, 700])
+    _say(f"decode NaN past seq_len k={k} Lc={Lc} seq_len={list(seq_len)}")
+    x = synth.decode_inputs(shape, seed=12, seq_len=seq_len)
+    sl = torch.tensor(seq_len.astype(np.int32), device=DEV)
+    d = {n: x[n].to(DEV) for n in ("q", "iq", "k_cache", "v_cache", "ik_cache")}
+    o1, i1 = msa.decode(d["q"], d["iq"], d["k_cache"], d["v_cache"], d["ik_cache"], sl,
+                        kslots=k, return_ids=True)
+    bad = {n: _poison_past_len(d[n], seq_len) for n in ("k_cache", "v_cache", "ik_cache")}
+    o2, i2 = msa.decode(d["q"], d["iq"], bad["k_cache"], bad["v_cache"], bad["ik_cache"], sl,
+                        kslots=k, return_ids=True)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert not torch.isnan(o2.float()).any()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_paged_decode_ignores_rows_past_seq_len():
+    """Paged decode: the rows of a sequence's last page past its length hold NaN
+    (a page being filled); ids and outputs must be bitwise those of clean pages."""
+    msa = _msa()
+    shape = synth.DecodeShape(N=5, Lc=2000, H=16, G=4, d=128, dI=128, B=128, k=16)
+    seq_len = np.array([1, 129, 1000, 1999, 640])
+    _say(f"paged decode NaN past seq_len seq_len={list(seq_len)}")
+    x = synth.decode_inputs(shape, seed=13, seq_len=seq_len)
+    pg = synth.paginate({n: x[n] for n in ("k_cache", "v_cache", "ik_cache")}, 128, 13,
+                        extra_pages=2)
+    g = {n: t.to(DEV) for n, t in pg.items()}
+    q, iq = x["q"].to(DEV), x["iq"].to(DEV)
+    sl = torch.tensor(seq_len.astype(np.int32), device=DEV)
+    o1, i1 = msa.decode_paged(q, iq, g["k_pages"], g["v_pages"], g["ik_pages"], g["block_table"],
+                              sl, kslots=shape.k, return_ids=True)
+    bad = {n: g[n].clone() for n in ("k_pages", "v_pages", "ik_pages")}
+    for n, L in enumerate(seq_len):
+        b = (int(L) - 1) // 128
+        page = int(pg["block_table"][n, b])
+        for name in bad:
+            bad[name].view(torch.int16)[page, int(L) - 128 * b:] = _BF16_NAN
+    o2, i2 = msa.decode_paged(q, iq, bad["k_pages"], bad["v_pages"], bad["ik_pages"],
+                              g["block_table"], sl, kslots=shape.k, return_ids=True)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert not torch.isnan(o2.float()).any()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
 # ----------------------------- paged decode ---------------------------------
 def _compact_pages(pg, table, seqs, seq_len, B=128):
     """CPU copies of only the pages the listed sequences need, with their table
@@ -651,15 +725,20 @@ def _paged_check(shape, seq_len, seed, share=(), bad=(), seqs=None, device="cpu"
     _parity.check_selection_valid(ids[vs], seq_len[vs] - 1, shape.k)
     tie, nmis = _parity.compare_ids(ids[vs], oids[valid], gap[valid])
     ref = oout[valid].copy()
+    banded = 0
     if tie.any():
-        # near-tie sequences: attend the GPU's own selection
+        # near-tie sequences: the GPU's competitors lie inside the tie band, and the
+        # oracle attends the GPU's own selection
         tr = np.nonzero(tie.any(axis=1))[0]
+        S = oracle.decode_paged_block_scores(x["iq"][seqs], sub["ik_pages"], sub_table,
+                                             seq_len[seqs], 128, np.nonzero(valid)[0][tr])
+        banded = _parity.check_near_tie_band(ids[vs[tr]], oids[valid][tr], S, seq_len[vs[tr]] - 1)
         ref[tr] = oracle.decode_paged_attend(x["q"][seqs], sub["k_pages"], sub["v_pages"],
                                              sub_table, seq_len[seqs], ids[vs[tr]], 128, scale,
                                              np.nonzero(valid)[0][tr])
     mx, mean = _parity.compare_out(out[vs], ref)
-    _say(f"  -> valid {len(vs)}/{len(seqs)} near_ties {int(tie.sum())} mismatches {nmis} "
-         f"max {mx:.3e} mean {mean:.3e}")
+    _say(f"  -> valid {len(vs)}/{len(seqs)} near_ties {int(tie.sum())} (band checked {banded}) "
+         f"mismatches {nmis} max {mx:.3e} mean {mean:.3e}")
     assert nmis == 0
     assert mx < _parity.MAX_ABS and mean < _parity.MEAN_ABS
 
@@ -780,12 +859,18 @@ def _fp8_decode_check(shape, seq_len, seed, seqs=None, device="cpu", spread=Fals
     _parity.check_selection_valid(ids[seqs], pos, shape.k)
     tie, nmis = _parity.compare_ids(ids[seqs], oids, gap)
     ref = oout.copy()
+    banded = 0
     if tie.any():
         tr = np.nonzero(tie.any(axis=1))[0]
+        S = oracle.decode_block_scores_fp8(x["iq"][sub.to(x["q"].device)],
+                                           codes[sub.to(codes.device)].cpu(),
+                                           ksc[sub.to(ksc.device)].cpu(), lens, 128, tr)
+        banded = _parity.check_near_tie_band(ids[seqs[tr]], oids[tr], S, lens[tr] - 1)
         ref[tr] = oracle.decode_attend(x["q"][sub.to(x["q"].device)], kc, vc, lens, ids[seqs[tr]],
                                        128, scale, tr)
     mx, mean = _parity.compare_out(out[seqs], ref)
-    _say(f"  -> near_ties {int(tie.sum())} mismatches {nmis} max {mx:.3e} mean {mean:.3e}; "
+    _say(f"  -> near_ties {int(tie.sum())} (band checked {banded}) mismatches {nmis} "
+         f"max {mx:.3e} mean {mean:.3e}; "
          f"(seq, group) selections equal to the bf16 cache's: {same.mean():.4f}")
     assert nmis == 0
     assert mx < _parity.MAX_ABS and mean < _parity.MEAN_ABS
