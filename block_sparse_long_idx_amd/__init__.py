@@ -93,6 +93,9 @@ def load_library():
     lib.msa_decode.argtypes = [P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, i32, i32, f32, P,
                                P, P, sz, P]
     lib.msa_decode.restype = i32
+    lib.msa_decode_static.argtypes = [P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, i32, i32,
+                                      f32, P, P, P]
+    lib.msa_decode_static.restype = i32
     lib.msa_decode_paged_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
     lib.msa_decode_paged_workspace_size.restype = sz
     lib.msa_decode_paged.argtypes = [P, P, P, P, P, i64, P, i32, P, i32, i32, i32, i32, i32, i32,
@@ -283,6 +286,40 @@ def decode(q, idx_q, k_cache, v_cache, idx_k_cache, seq_len, kslots: int = 16, B
                         _ptr(ids_out), _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "msa_decode")
     return (out, ids_out) if return_ids else out
+
+
+def decode_static(q, idx_q, k_cache, v_cache, idx_k_cache, seq_len, kslots: int = 16,
+                  B: int = 128, scale=None, return_ids: bool = False, out=None, ids_out=None):
+    """msa_decode without a caller workspace (the library's per-GPU static array of
+    STATIC_SCRATCH_BYTES): same results as decode().  Pass out / ids_out to keep the
+    call free of allocations."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(idx_q, "idx_q", torch.bfloat16, 3, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _need(idx_k_cache, "idx_k_cache", torch.bfloat16, 3, dev)
+    _need(seq_len, "seq_len", torch.int32, 1, dev)
+    N, H, d = q.shape
+    G, dI = idx_q.shape[1], idx_q.shape[2]
+    Lmax = k_cache.shape[1]
+    if (k_cache.shape != (N, Lmax, G, d) or v_cache.shape != (N, Lmax, G, d)
+            or idx_k_cache.shape != (N, Lmax, dI) or seq_len.shape != (N,)):
+        raise MSAError("inconsistent shapes for decode inputs")
+    if out is None:
+        out = torch.empty_like(q)
+    if return_ids and ids_out is None:
+        ids_out = torch.empty((N, G, kslots), dtype=torch.int32, device=dev)
+    st = lib.msa_decode_static(_ptr(q), _ptr(idx_q), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(idx_k_cache), _ptr(seq_len), N, Lmax, H, G, d, dI, B, kslots,
+                               _scale(scale, d), _ptr(out), _ptr(ids_out), _stream(dev))
+    _check(st, "msa_decode_static")
+    return (out, ids_out) if return_ids else out
+
+
+# bytes of the per-GPU workspace array of decode_static (MSA_STATIC_SCRATCH_BYTES)
+STATIC_SCRATCH_BYTES = 64 << 20
 
 
 def decode_paged(q, idx_q, k_pages, v_pages, idx_k_pages, block_table, seq_len, kslots: int = 16,

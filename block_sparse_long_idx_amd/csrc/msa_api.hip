@@ -19,6 +19,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 
 #include "msa.h"
@@ -543,10 +544,13 @@ size_t msa_decode_workspace_size(int N, int64_t Lmax, int H, int G, int d, int d
     return c.used;
 }
 
-int msa_decode(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache,
-               const uint16_t *v_cache, const uint16_t *idx_k_cache, const int32_t *seq_len,
-               int N, int64_t Lmax, int H, int G, int d, int dI, int B, int kslots, float scale,
-               uint16_t *out, int32_t *block_ids_out, void *ws, size_t ws_bytes, void *stream) {
+namespace {
+// Argument checks of msa_decode (everything but the workspace); MSA_OK with N == 0
+// means there is nothing to do.
+int decode_args_status(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache,
+                       const uint16_t *v_cache, const uint16_t *idx_k_cache,
+                       const int32_t *seq_len, int N, int64_t Lmax, int H, int G, int d, int dI,
+                       int B, int kslots, const uint16_t *out) {
     if (N < 0 || Lmax < 0 || H <= 0 || G <= 0 || d <= 0 || dI <= 0 || B <= 0 || kslots < 1 ||
         H % G)
         return MSA_ERR_INVALID_ARG;
@@ -555,6 +559,17 @@ int msa_decode(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache
         return MSA_ERR_INVALID_ARG;
     if (B != kBlock || !d_ok(d) || !r_ok(H, G) || !index_ok(G, dI) || kslots > 32)
         return MSA_ERR_UNSUPPORTED;
+    return MSA_OK;
+}
+}  // namespace
+
+int msa_decode(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache,
+               const uint16_t *v_cache, const uint16_t *idx_k_cache, const int32_t *seq_len,
+               int N, int64_t Lmax, int H, int G, int d, int dI, int B, int kslots, float scale,
+               uint16_t *out, int32_t *block_ids_out, void *ws, size_t ws_bytes, void *stream) {
+    const int as = decode_args_status(q, idx_q, k_cache, v_cache, idx_k_cache, seq_len, N, Lmax,
+                                      H, G, d, dI, B, kslots, out);
+    if (as != MSA_OK || N == 0) return as;
     const int st = check_ws(ws, ws_bytes, msa_decode_workspace_size(N, Lmax, H, G, d, dI, B, kslots));
     if (st != MSA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -571,6 +586,60 @@ int msa_decode(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache
     MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, seq_len, Lmax, ids, s));
     return decode_attend(q, k_cache, v_cache, ids, seq_len, nullptr, 0, N, Lmax, H, G, d,
                          kslots, scale, po, plse, out, s);
+}
+
+// ------------------- decode without a caller workspace ---------------------
+// The workspace of msa_decode_static: a device array of the library, one copy per
+// GPU (each GPU the library runs on holds its MSA_STATIC_SCRATCH_BYTES until the
+// process ends).  Host code never passes `scratch` itself to a kernel (in host code
+// the name is only a stand-in for the symbol): it takes each device's address of
+// the array once, with hipGetSymbolAddress, and uses that address.
+static __device__ __align__(256) char scratch[MSA_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// This device's address of `scratch`, looked up on the first call on the device.
+// The stream must belong to the current device.
+int scratch_address(hipStream_t s, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MSA_ERR_HIP;
+    if (s) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(s, &sdev) != hipSuccess) return MSA_ERR_HIP;
+        if ((int)sdev != dev) return MSA_ERR_INVALID_ARG;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MSA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MSA_OK;
+}
+}  // namespace
+
+int msa_decode_static(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache,
+                      const uint16_t *v_cache, const uint16_t *idx_k_cache,
+                      const int32_t *seq_len, int N, int64_t Lmax, int H, int G, int d, int dI,
+                      int B, int kslots, float scale, uint16_t *out, int32_t *block_ids_out,
+                      void *stream) {
+    const int as = decode_args_status(q, idx_q, k_cache, v_cache, idx_k_cache, seq_len, N, Lmax,
+                                      H, G, d, dI, B, kslots, out);
+    if (as != MSA_OK || N == 0) return as;
+    // the shape's workspace must fit in the array (checked before any HIP call)
+    if (msa_decode_workspace_size(N, Lmax, H, G, d, dI, B, kslots) > MSA_STATIC_SCRATCH_BYTES)
+        return MSA_ERR_WORKSPACE_TOO_SMALL;
+    void *ws = nullptr;
+    const int st = scratch_address(static_cast<hipStream_t>(stream), &ws);
+    if (st != MSA_OK) return st;
+    // same kernels and launches as msa_decode; no part of the workspace needs to
+    // start at zero (every value read was written earlier in the same call)
+    return msa_decode(q, idx_q, k_cache, v_cache, idx_k_cache, seq_len, N, Lmax, H, G, d, dI, B,
+                      kslots, scale, out, block_ids_out, ws, MSA_STATIC_SCRATCH_BYTES, stream);
 }
 
 // ----------------------------- paged decode -------------------------------

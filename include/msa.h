@@ -183,6 +183,26 @@ MSA_API int msa_decode(const uint16_t *q, const uint16_t *idx_q, const uint16_t 
                uint16_t *out, int32_t *block_ids_out, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Decode without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The arguments, kernels and results (bitwise) of msa_decode, minus
+ * ws / ws_bytes: the workspace is a device array of the library,
+ * MSA_STATIC_SCRATCH_BYTES on each GPU the library runs on, held until the process
+ * ends.  A shape whose msa_decode_workspace_size() exceeds MSA_STATIC_SCRATCH_BYTES
+ * returns MSA_ERR_WORKSPACE_TOO_SMALL (checked before any HIP call); `stream` must
+ * belong to the current device (else MSA_ERR_INVALID_ARG).  Calls no allocating
+ * routine.  Every call on one GPU shares that GPU's array and leaves its contents
+ * there: calls that may overlap on one GPU (other streams, other host threads) race
+ * and must be ordered by the caller.
+ * ------------------------------------------------------------------------- */
+#define MSA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+MSA_API int msa_decode_static(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache,
+                              const uint16_t *v_cache, const uint16_t *idx_k_cache,
+                              const int32_t *seq_len, int N, int64_t Lmax, int H, int G, int d,
+                              int dI, int B, int kslots, float scale, uint16_t *out,
+                              int32_t *block_ids_out, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Paged decode [SERVE: paged MSA decode; M3-20x §二 (B = 128-token blocks)].
  * The same computation as msa_decode, with the caches held in fixed 128-token
  * pages so that every MSA block is exactly one page: logical token t of sequence

@@ -249,3 +249,19 @@ def test_paged_fp8_decode_arguments(lib):
     assert call(B=64) == UNSUPPORTED
     assert call(dI=48) == UNSUPPORTED
     assert call(nbytes=ctypes.c_size_t(64)) == WS_SMALL
+
+
+def test_decode_static_refuses_oversize_before_any_launch(lib):
+    """msa_decode_static (the decode for callers that cannot allocate) refuses a shape
+    whose workspace exceeds its per-GPU array, before any HIP call -- so this runs
+    without a GPU and never dereferences the (dummy) pointers."""
+    N, Lmax, H, G, d, dI, k = 64, 1 << 24, 64, 4, 128, 128, 16
+    assert lib.msa_decode_workspace_size(N, Lmax, H, G, d, dI, 128, k) > msa.STATIC_SCRATCH_BYTES
+    dummy = ctypes.c_void_p(256)
+    assert lib.msa_decode_static(dummy, dummy, dummy, dummy, dummy, dummy, N, Lmax, H, G, d, dI,
+                                 128, k, 0.0, dummy, None, None) == WS_SMALL
+    assert lib.msa_decode_static(None, dummy, dummy, dummy, dummy, dummy, 4, 1024, H, G, d, dI,
+                                 128, k, 0.0, dummy, None, None) == INVALID
+    src = open(HEADER).read()
+    assert "#define MSA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)" in src
+    assert msa.STATIC_SCRATCH_BYTES == 64 << 20
