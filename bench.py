@@ -613,6 +613,11 @@ def run_workload(args, name, steps, warmup, cpu_baseline, dense):
         result["config"] = {"workload": wl.name, "N": s.N, "Lc": s.Lc, "H": s.H, "G": s.G,
                             "d": s.d, "dI": s.dI, "B": s.B, "k": s.k}
         result["step_hbm_frac"] = work["total_bytes"] / (ms_per_step / 1e3) / PEAK_HBM_BYTES
+        # share of the planted (relevant) blocks that the selection found
+        idn = ids.cpu().numpy()
+        hits = [b in idn[n, g] for n, row in enumerate(x["planted"]) for g, blk in enumerate(row)
+                for b in blk]
+        result["planted_block_recall"] = float(np.mean(hits)) if hits else None
 
     # ---- roofline of the dominant kernel -------------------------------------
     kd = kernels[dominant]
@@ -692,7 +697,7 @@ def main():
                                                    "warmup", "ms_per_step", "ms_per_step_median",
                                                    "ms_per_step_min", "config", "roofline",
                                                    "kernels")}
-            for key in ("step_mfma_frac", "step_hbm_frac"):
+            for key in ("step_mfma_frac", "step_hbm_frac", "planted_block_recall"):
                 if key in r:
                     also[name][key] = r[key]
         result["also"] = also

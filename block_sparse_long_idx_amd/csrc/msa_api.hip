@@ -17,6 +17,7 @@
 #include <stdint.h>
 
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <algorithm>
 #include <mutex>
@@ -32,11 +33,16 @@ using namespace msa;
 constexpr int64_t kChunkQ = 131072;    // preferred queries per prefill chunk
 constexpr size_t kAlign = 256;
 
-// Workspace carving: with base == nullptr only the size is accumulated.
+// Workspace carving: with base == nullptr only the size is accumulated.  With a
+// buffer, `cap` is its size: every entry point checks fits() after carving and
+// before its first launch, so a planner that carved more than the buffer holds is
+// an error, never an out-of-bounds write.
 struct Carver {
     char *base;
+    size_t cap;
     size_t used = 0;
-    explicit Carver(void *b) : base(static_cast<char *>(b)) {}
+    explicit Carver(void *b, size_t capacity = SIZE_MAX)
+        : base(static_cast<char *>(b)), cap(capacity) {}
     template <typename T>
     T *take(int64_t count) {
         used = (used + kAlign - 1) / kAlign * kAlign;
@@ -44,7 +50,12 @@ struct Carver {
         used += (size_t)std::max<int64_t>(count, 0) * sizeof(T);
         return p;
     }
+    bool fits() const { return used <= cap; }
 };
+#define MSA_CHECK_CARVE(c)                                             \
+    do {                                                               \
+        if (!(c).fits()) return MSA_ERR_WORKSPACE_TOO_SMALL;           \
+    } while (0)
 
 struct AttnWs {
     SchedBuffers sb;
@@ -143,10 +154,30 @@ struct Timing {
 };
 Timing g_timing;
 
+// Debug aid: with MSA_DEBUG_SYNC=1 in the environment every stage is followed by a
+// synchronisation of its stream, so an asynchronous fault is reported (on stderr,
+// as MSA_ERR_HIP) by the call and stage that caused it.  Not for use under graph
+// capture, where synchronising is not allowed.  Read at every stage, so a process
+// may switch it on and off.
+bool debug_sync() {
+    const char *e = getenv("MSA_DEBUG_SYNC");
+    return e && e[0] == '1';
+}
+
+hipError_t after_stage(int stage, hipStream_t s, hipError_t e) {
+    if (e != hipSuccess || !debug_sync()) return e;
+    const hipError_t w = hipStreamSynchronize(s);
+    const hipError_t l = hipGetLastError();
+    const hipError_t r = w != hipSuccess ? w : l;
+    if (r != hipSuccess)
+        fprintf(stderr, "[msa] stage %s failed: %s\n", kStageNames[stage], hipGetErrorString(r));
+    return r;
+}
+
 // Runs `launch` (returning hipError_t), bracketed by events when timing is on.
 template <typename F>
 hipError_t timed(int stage, hipStream_t s, F &&launch) {
-    if (!g_timing.on || g_timing.used >= g_timing.cap) return launch();
+    if (!g_timing.on || g_timing.used >= g_timing.cap) return after_stage(stage, s, launch());
     TimedLaunch &t = g_timing.rec[g_timing.used];
     if (hipEventRecord(t.start, s) != hipSuccess) return hipErrorUnknown;
     const hipError_t e = launch();
@@ -154,7 +185,7 @@ hipError_t timed(int stage, hipStream_t s, F &&launch) {
     if (hipEventRecord(t.stop, s) != hipSuccess) return hipErrorUnknown;
     t.name = stage;
     ++g_timing.used;
-    return hipSuccess;
+    return after_stage(stage, s, hipSuccess);
 }
 
 #define MSA_TRY(expr)                                   \
@@ -229,9 +260,10 @@ int msa_select_blocks(const uint16_t *idx_q, const uint16_t *idx_k, int64_t L, i
     const int64_t C = fit_chunk(L, ws_bytes, [&](int64_t c) { return select_bytes(c, L, G); });
     if (C == 0) return MSA_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    Carver c(ws);
+    Carver c(ws, ws_bytes);
     const int nbp = nb_padded(L);
     float *S = c.take<float>(C * G * nbp);
+    MSA_CHECK_CARVE(c);
     for (int64_t q0 = 0; q0 < L; q0 += C) {
         const int64_t qend = std::min(L, q0 + C);
         MSA_TIMED(kK1, launch_k1_index_pool(idx_q, idx_k, S, L, q0, qend, G, dI, nbp, s));
@@ -263,8 +295,9 @@ int msa_sparse_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     if (C == 0) return MSA_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     scale = default_scale(scale, d);
-    Carver c(ws);
+    Carver c(ws, ws_bytes);
     const AttnWs w = carve_attn(c, C, H, G, d, kslots, (int)nblocks(L));
+    MSA_CHECK_CARVE(c);
     for (int64_t q0 = 0; q0 < L; q0 += C) {
         const int64_t qend = std::min(L, q0 + C);
         const int rc = attn_chunk(q, k, v, block_ids + q0 * G * kslots, L, q0, qend, H, G, d, kslots,
@@ -298,10 +331,11 @@ int prefill_range(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
                                 [&](int64_t c) { return prefill_bytes(c, L, H, G, d, kslots); });
     if (C == 0) return MSA_ERR_WORKSPACE_TOO_SMALL;
     const int nbp = nb_padded(L);
-    Carver c(ws);
+    Carver c(ws, ws_bytes);
     float *S = c.take<float>(C * G * nbp);
     int32_t *ids_ws = c.take<int32_t>(C * G * kslots);
     const AttnWs w = carve_attn(c, C, H, G, d, kslots, (int)nblocks(L));
+    MSA_CHECK_CARVE(c);
     for (int64_t q0 = P; q0 < L; q0 += C) {
         const int64_t qend = std::min(L, q0 + C);
         int32_t *ids_c = ids ? ids + q0 * G * kslots : ids_ws;
@@ -388,7 +422,8 @@ int plan_batches(const int64_t *cu_q, const int64_t *cu_kv, int nseq, int H, int
 int run_batch(const BatchPlan &b, const uint16_t *q, const uint16_t *k, const uint16_t *v,
               const uint16_t *idx_q, const uint16_t *idx_k, const int64_t *cu_q,
               const int64_t *cu_kv, int H, int G, int d, int dI, int kslots, float scale,
-              uint16_t *out, int32_t *block_ids_out, void *ws, hipStream_t s) {
+              uint16_t *out, int32_t *block_ids_out, void *ws, size_t ws_bytes,
+              hipStream_t s) {
     BatchTable t;
     t.n = b.n;
     t.rows = (int)b.rows;
@@ -412,7 +447,7 @@ int run_batch(const BatchPlan &b, const uint16_t *q, const uint16_t *k, const ui
     t.k1_off[b.n] = (int)k1wg;
     const int64_t rows = b.rows;
     const int nbp = b.nbp;
-    Carver c(ws);
+    Carver c(ws, ws_bytes);
     float *S = c.take<float>(rows * G * nbp);
     int32_t *ids_ws = c.take<int32_t>(rows * G * kslots);
     int32_t *row_len = c.take<int32_t>(rows);
@@ -422,6 +457,7 @@ int run_batch(const BatchPlan &b, const uint16_t *q, const uint16_t *k, const ui
     int32_t *blk_rows = c.take<int32_t>(b.blocks);
     BatchTable *dtab = c.take<BatchTable>(1);
     const AttnWs w = carve_attn(c, rows, H, G, d, kslots, (int)b.blocks);
+    MSA_CHECK_CARVE(c);
     int32_t *ids = block_ids_out ? block_ids_out + q_base * G * kslots : ids_ws;
     BatchMap bm;
     bm.row_len = row_len;
@@ -509,7 +545,7 @@ int msa_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         [&](const BatchPlan &b) {
                             if (b.n == 1) return one_sequence(b.members[0]);
                             return run_batch(b, q, k, v, idx_q, idx_k, cu_q, cu_kv, H, G, d, dI,
-                                             kslots, scale, out, block_ids_out, ws, s);
+                                             kslots, scale, out, block_ids_out, ws, ws_bytes, s);
                         });
 }
 
@@ -575,11 +611,12 @@ int msa_decode(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache
     hipStream_t s = static_cast<hipStream_t>(stream);
     scale = default_scale(scale, d);
     const int nbp = nb_padded(Lmax);
-    Carver c(ws);
+    Carver c(ws, ws_bytes);
     float *S = c.take<float>((int64_t)N * G * nbp);
     int32_t *ids_ws = c.take<int32_t>((int64_t)N * G * kslots);
     uint16_t *po = c.take<uint16_t>((int64_t)N * H * kslots * d);
     float *plse = c.take<float>((int64_t)N * H * kslots);
+    MSA_CHECK_CARVE(c);
     int32_t *ids = block_ids_out ? block_ids_out : ids_ws;
     MSA_TIMED(kK1d, launch_k1d_index_pool(idx_q, idx_k_cache, seq_len, nullptr, 0, S, N, Lmax, G,
                                           dI, nbp, s));
@@ -676,12 +713,13 @@ int msa_decode_paged(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k
     scale = default_scale(scale, d);
     const int64_t Lmax = (int64_t)max_blocks * B;
     const int nbp = nb_padded(Lmax);
-    Carver c(ws);
+    Carver c(ws, ws_bytes);
     float *S = c.take<float>((int64_t)N * G * nbp);
     int32_t *ids_ws = c.take<int32_t>((int64_t)N * G * kslots);
     uint16_t *po = c.take<uint16_t>((int64_t)N * H * kslots * d);
     float *plse = c.take<float>((int64_t)N * H * kslots);
     int32_t *eff_len = c.take<int32_t>(N);
+    MSA_CHECK_CARVE(c);
     int32_t *ids = block_ids_out ? block_ids_out : ids_ws;
     // every later stage sees only lengths whose pages were checked
     MSA_TIMED(kKpc, launch_page_check(block_table, max_blocks, num_pages, seq_len, N, eff_len, s));
@@ -723,11 +761,12 @@ int msa_decode_fp8idx(const uint16_t *q, const uint16_t *idx_q, const uint16_t *
     hipStream_t s = static_cast<hipStream_t>(stream);
     scale = default_scale(scale, d);
     const int nbp = nb_padded(Lmax);
-    Carver c(ws);
+    Carver c(ws, ws_bytes);
     float *S = c.take<float>((int64_t)N * G * nbp);
     int32_t *ids_ws = c.take<int32_t>((int64_t)N * G * kslots);
     uint16_t *po = c.take<uint16_t>((int64_t)N * H * kslots * d);
     float *plse = c.take<float>((int64_t)N * H * kslots);
+    MSA_CHECK_CARVE(c);
     int32_t *ids = block_ids_out ? block_ids_out : ids_ws;
     MSA_TIMED(kK1d8, launch_k1d_index_pool_fp8(idx_q, idx_k_e4m3, idx_k_scale, seq_len, nullptr, 0,
                                                S, N, Lmax, G, dI, nbp, s));
@@ -760,12 +799,13 @@ int msa_decode_paged_fp8idx(const uint16_t *q, const uint16_t *idx_q, const uint
     scale = default_scale(scale, d);
     const int64_t Lmax = (int64_t)max_blocks * B;
     const int nbp = nb_padded(Lmax);
-    Carver c(ws);
+    Carver c(ws, ws_bytes);
     float *S = c.take<float>((int64_t)N * G * nbp);
     int32_t *ids_ws = c.take<int32_t>((int64_t)N * G * kslots);
     uint16_t *po = c.take<uint16_t>((int64_t)N * H * kslots * d);
     float *plse = c.take<float>((int64_t)N * H * kslots);
     int32_t *eff_len = c.take<int32_t>(N);
+    MSA_CHECK_CARVE(c);
     int32_t *ids = block_ids_out ? block_ids_out : ids_ws;
     // every later stage sees only lengths whose pages were checked
     MSA_TIMED(kKpc, launch_page_check(block_table, max_blocks, num_pages, seq_len, N, eff_len, s));

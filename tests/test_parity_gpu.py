@@ -901,6 +901,89 @@ def test_fp8_decode_full_size_subset():
     _fp8_decode_check(shape, np.full(shape.N, shape.Lc), seed=0, seqs=seqs, device=DEV)
 
 
+def _e4m3_score_band(iq, ik, codes, ksc, seq_len, B=128):
+    """Per (sequence, group) of a decode batch, over the competitor blocks: the bf16
+    block scores S (fp32 products of the bf16 values) and, per block, D = max over
+    its tokens of |s8_t - s_t|, where s8_t is the token's score on the dequantised
+    E4M3 key (scale * e4m3(byte), exact in bf16) and s_t the bf16 one.  A block
+    maximum moves at most as far as its farthest token, so the E4M3 block score lies
+    in [S - D, S + D].  Also the coarse per-(sequence, group) bound
+    E = max_t sum_c |iq_c| |ik[t, c] - scale[t] e4m3(byte[t, c])|.  Torch on the
+    inputs' device."""
+    N, G = iq.shape[0], iq.shape[1]
+    E = torch.zeros((N, G), dtype=torch.float64)
+    S, D = [], []
+    for n in range(N):
+        nb = (int(seq_len[n]) - 1) // B
+        T = nb * B
+        if nb == 0:
+            S.append(None)
+            D.append(None)
+            continue
+        a = ik[n, :T].float()
+        deq = codes[n, :T].view(torch.float8_e4m3fn).float() * ksc[n, :T, None]
+        qa = iq[n].float()                                        # [G, dI]
+        E[n] = ((a - deq).abs() @ qa.abs().T).amax(dim=0).double().cpu()
+        s16 = a @ qa.T                                            # [T, G]
+        s8 = deq @ qa.T
+        S.append(s16.view(nb, B, G).amax(dim=1).T.double().cpu())            # [G, nb]
+        D.append((s8 - s16).abs().view(nb, B, G).amax(dim=1).T.double().cpu())
+    return E, S, D
+
+
+def test_fp8_decode_band_vs_bf16_full_size():
+    """The E4M3 index-key cache moves each block score by at most D (per block, from
+    the bytes), so the E4M3 decode may select differently from the bf16 decode only
+    among blocks whose score intervals [S - D, S + D] reach the boundary: with L15 the
+    15th largest S - D and U16 the 16th largest S + D of a (sequence, group), every
+    block with S - D > U16 must be selected and none with S + D < L15 may be.
+    64 sequences x 262144 tokens; also reports the coarse bound E, how many blocks
+    per row lie in the band, and the planted-block recall of both paths."""
+    msa = _msa()
+    shape = synth.WORKLOADS["decode_N64_L262144"].shape
+    _say("fp8 band vs bf16, decode 64 x 262144")
+    x = synth.decode_inputs(shape, seed=0, device=DEV)
+    codes, ksc = _refs.e4m3_rows_torch(x["ik_cache"])
+    sl = torch.tensor(np.asarray(x["seq_len"], np.int32), device=DEV)
+    o8, i8 = msa.decode_fp8idx(x["q"], x["iq"], x["k_cache"], x["v_cache"], codes, ksc, sl,
+                               kslots=shape.k, return_ids=True)
+    ob, ib = msa.decode(x["q"], x["iq"], x["k_cache"], x["v_cache"], x["ik_cache"], sl,
+                        kslots=shape.k, return_ids=True)
+    torch.cuda.synchronize()
+    E, S, D = _e4m3_score_band(x["iq"], x["ik_cache"], codes, ksc, x["seq_len"])
+    i8n, ibn = i8.cpu().numpy(), ib.cpu().numpy()
+    m = shape.k - 1
+    agree = 0
+    band_sizes, band_picks = [], []
+    for n in range(shape.N):
+        nb = (int(x["seq_len"][n]) - 1) // 128
+        for g in range(shape.G):
+            agree += np.array_equal(i8n[n, g], ibn[n, g])
+            sc, dv = S[n][g].numpy(), D[n][g].numpy()
+            lo, hi = sc - dv, sc + dv
+            L15 = np.sort(lo)[-m]
+            U16 = np.sort(hi)[-(m + 1)]
+            margin = 1e-4 * max(abs(L15), abs(U16)) + 1e-4      # fp32 accumulation
+            pick = np.array([b for b in i8n[n, g] if 0 <= b < nb])
+            must = np.nonzero(lo > U16 + margin)[0]
+            never = hi < L15 - margin
+            assert set(must.tolist()) <= set(pick.tolist()), (n, g, sorted(must), sorted(pick))
+            assert not never[pick].any(), (n, g, pick[never[pick]])
+            band = ~never & ~(lo > U16 + margin)
+            band_sizes.append(int(band.sum()))
+            band_picks.append(int(band[pick].sum()))
+    rows = shape.N * shape.G
+    rec = {name: np.mean([b in ids[n, g] for n in range(shape.N) for g in range(shape.G)
+                          for b in x["planted"][n][g]])
+           for name, ids in (("bf16", ibn), ("e4m3", i8n))}
+    _say(f"  -> coarse bound E median {float(E.median()):.3f}, per-block D median "
+         f"{float(np.median([d_.median().item() for d_ in D if d_ is not None])):.3f}; blocks in "
+         f"the band per row: median {int(np.median(band_sizes))} (of ~2047), of which picked "
+         f"{np.mean(band_picks):.1f}; identical selections {agree}/{rows}; planted-block recall "
+         f"bf16 {rec['bf16']:.4f} e4m3 {rec['e4m3']:.4f}")
+    assert rec["e4m3"] >= rec["bf16"] - 0.02
+
+
 def test_paged_fp8_decode():
     """Paged decode over E4M3 index-key pages: the oracle on a ragged batch (with a
     bad page id and a too-long sequence), and bitwise equality with the contiguous
