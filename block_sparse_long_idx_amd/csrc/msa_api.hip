@@ -77,7 +77,7 @@ AttnWs carve_attn(Carver &c, int64_t C, int H, int G, int d, int k, int nb) {
     w.sb.tcnt = c.take<int>(k3_tile_groups(max_items) * kK3Buckets);
     w.sb.list = c.take<uint32_t>(C * G * k);
     w.po = c.take<uint16_t>(C * H * k * d);
-    w.plse = c.take<float>(C * H * k);
+    w.plse = c.take<float>(2 * C * H * k);   // (maximum, sum) per partial row
     return w;
 }
 
@@ -205,7 +205,7 @@ int attn_chunk(const uint16_t *q, const uint16_t *kx, const uint16_t *vx, const 
     MSA_TIMED(kK4, launch_k4_kv_outer(q, kx, vx, w.sb, nbc, L, q0, C, H, G, d, k, scale, w.po, w.plse,
                                       single, s));
     MSA_TIMED(kK5, launch_k5_combine(w.po, w.plse, ids_c, C, H, G, d, k, nbc, out + q0 * H * d,
-                                     single, s));
+                                     single, true, s));
     return MSA_OK;
 }
 
@@ -224,7 +224,7 @@ int decode_attend(const uint16_t *q, const uint16_t *kc, const uint16_t *vc, con
     MSA_TIMED(kK4d, launch_k4d_split(q, kc, vc, ids, len, table, maxb, N, Lmax, H, G, d, kslots,
                                      scale, po, plse, s));
     MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out,
-                                     BatchMap{}, s));
+                                     BatchMap{}, false, s));
     return MSA_OK;
 }
 
@@ -473,7 +473,7 @@ int run_batch(const BatchPlan &b, const uint16_t *q, const uint16_t *k, const ui
     MSA_TIMED(kK4, launch_k4_kv_outer(q + q_base * H * d, k, v, w.sb, (int)b.blocks, 0, 0, rows, H,
                                       G, d, kslots, scale, w.po, w.plse, bm, s));
     MSA_TIMED(kK5, launch_k5_combine(w.po, w.plse, ids, rows, H, G, d, kslots, 0,
-                                     out + q_base * H * d, bm, s));
+                                     out + q_base * H * d, bm, true, s));
     return MSA_OK;
 }
 

@@ -46,10 +46,13 @@ __device__ __forceinline__ void load_q(bf16x8 (&qb)[D / 16], const uint16_t *qro
 //   qb     : the column's q row as the B operand (see load_q)
 //   rel    : the column's token position minus the staged block's first position;
 //            0 <= rel < 128 marks the query's own block, whose keys past it are masked
-//   emit   : receives the column's normalised partial as bf16 16-byte chunks --
-//            w[u] holds chunk 4(u/2) + 2(u%2) + hf of the row (elements 8c .. 8c+7) --
-//            and its log2-sum-exp, and writes them
-template <int D, typename Emit>
+//   emit   : receives the column's partial as bf16 16-byte chunks -- w[u] holds
+//            chunk 4(u/2) + 2(u%2) + hf of the row (elements 8c .. 8c+7) -- and writes
+//            it.  NORM: o normalised by its row sum, plus the log2-sum-exp of the
+//            scaled scores (emit(w, lse, sum)); !NORM: o NOT normalised, plus the row
+//            maximum m (scaled, log2 units) and the row sum l of 2^(s - m)
+//            (emit(w, m, l)) -- the combine divides, which saves the multiplies here
+template <int D, bool NORM, typename Emit>
 __device__ __forceinline__ void attend_pass(const char *lds_k, const char *lds_vt,
                                             const bf16x8 (&qb)[D / 16], bool active, int64_t rel,
                                             float scale_log2, int lane, Emit emit) {
@@ -127,10 +130,10 @@ __device__ __forceinline__ void attend_pass(const char *lds_k, const char *lds_v
         }
         __builtin_amdgcn_sched_barrier(0);
     }
-    // normalise, pack to bf16, and swap half-rows between the lane halves
+    // normalise (NORM), pack to bf16, and swap half-rows between the lane halves
     // (v_permlane32_swap) so each lane holds 8 consecutive d values (16 bytes):
     // before, lane half hf holds d = 16q + 4hf + {0..3} and 16q + 8 + 4hf + {0..3}
-    const float inv = 1.0f / sum;
+    const float inv = NORM ? 1.0f / sum : 1.0f;
     u32x4 w[D / 16];
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
@@ -138,17 +141,26 @@ __device__ __forceinline__ void attend_pass(const char *lds_k, const char *lds_v
         for (int q2 = 0; q2 < 2; ++q2) {
             const f32x16 &acc = o[md];
             const int r0 = 8 * q2;          // registers of ip = 2q2 (r0..r0+3) and 2q2+1
-            uint32_t a0 = pack_bf16x2(acc[r0 + 0] * inv, acc[r0 + 1] * inv);
-            uint32_t a1 = pack_bf16x2(acc[r0 + 2] * inv, acc[r0 + 3] * inv);
-            uint32_t b0 = pack_bf16x2(acc[r0 + 4] * inv, acc[r0 + 5] * inv);
-            uint32_t b1 = pack_bf16x2(acc[r0 + 6] * inv, acc[r0 + 7] * inv);
+            uint32_t a0, a1, b0, b1;
+            if constexpr (NORM) {
+                a0 = pack_bf16x2(acc[r0 + 0] * inv, acc[r0 + 1] * inv);
+                a1 = pack_bf16x2(acc[r0 + 2] * inv, acc[r0 + 3] * inv);
+                b0 = pack_bf16x2(acc[r0 + 4] * inv, acc[r0 + 5] * inv);
+                b1 = pack_bf16x2(acc[r0 + 6] * inv, acc[r0 + 7] * inv);
+            } else {
+                a0 = pack_bf16x2(acc[r0 + 0], acc[r0 + 1]);
+                a1 = pack_bf16x2(acc[r0 + 2], acc[r0 + 3]);
+                b0 = pack_bf16x2(acc[r0 + 4], acc[r0 + 5]);
+                b1 = pack_bf16x2(acc[r0 + 6], acc[r0 + 7]);
+            }
             const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
             const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
             // lower half now holds d = 32md + 16q2 + 0..7, upper half 32md + 16q2 + 8..15
             w[2 * md + q2] = u32x4{s0[0], s1[0], s0[1], s1[1]};
         }
     }
-    emit(w, mx * scale_log2 + __log2f(sum));
+    if constexpr (NORM) emit(w, mx * scale_log2 + __log2f(sum), sum);
+    else emit(w, mx * scale_log2, sum);
 }
 
 // Writes the 32 partial rows of a pass (row = MFMA column, 2D bytes) through the
@@ -205,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     const uint16_t *__restrict__ vx, const int *__restrict__ offs, const int *__restrict__ toff,
     const int *__restrict__ total, const int *__restrict__ items, const int *__restrict__ order,
     const uint32_t *__restrict__ list, int nb, int64_t L, int64_t q0, int H, int G, int kslots,
-    float scale_log2, uint16_t *__restrict__ po, float *__restrict__ plse, const BatchMap bm) {
+    float scale_log2, uint16_t *__restrict__ po, f32x2 *__restrict__ pml, const BatchMap bm) {
     __shared__ __attribute__((aligned(16))) char lds_k[kBlock * D * 2];
     __shared__ __attribute__((aligned(16))) char lds_vt[D * kBlock * 2];
     static_assert(kK4Queries <= 256, "one entry per thread is staged");
@@ -300,12 +312,12 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
         const uint32_t my_row =
             act ? ((uint32_t)il * (uint32_t)H + (uint32_t)hh) * (uint32_t)kslots + (uint32_t)s
                 : ~0u;
-        attend_pass<D>(lds_k, lds_vt, qr, act, BATCH ? (int64_t)in.rel : q0 + il - blk0,
-                       scale_log2, lane, [&](const u32x4 (&w)[D / 16], float lse) {
+        attend_pass<D, false>(lds_k, lds_vt, qr, act, BATCH ? (int64_t)in.rel : q0 + il - blk0,
+                       scale_log2, lane, [&](const u32x4 (&w)[D / 16], float m, float l) {
 #pragma unroll
                            for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(nqr[ks]));
                            asm volatile("" ::"v"(nin.entry), "v"(nin.rel));
-                           if (act && hf == 0) plse[lrow] = lse;
+                           if (act && hf == 0) pml[lrow] = f32x2{m, l};
                            // row = column: query col / R of the pass, head col % R
                            store_rows_staged<D>(lds_stg[wave], w, lane, [&](int col) -> uint16_t * {
                                const uint32_t row = (uint32_t)__shfl((int)my_row, col, kWave);
@@ -331,14 +343,15 @@ static hipError_t k4_dispatch(const uint16_t *q, const uint16_t *kx, const uint1
                               const BatchMap &bm, hipStream_t s) {
     const int64_t grid = round_up(k4_max_items(C, G, k, nb), 8 * kK4Run);
     if (grid == 0) return hipSuccess;
+    f32x2 *pml = reinterpret_cast<f32x2 *>(plse);
     if (bm.row_kvpos)
         hipLaunchKernelGGL((k4_kv_outer<D, R, true>), dim3((unsigned)grid), dim3(256), 0, s, q, kx,
                            vx, sb.offs, sb.toff, sb.total, sb.items, sb.order, sb.list, nb, L, q0, H, G, k,
-                           scale_log2, po, plse, bm);
+                           scale_log2, po, pml, bm);
     else
         hipLaunchKernelGGL((k4_kv_outer<D, R, false>), dim3((unsigned)grid), dim3(256), 0, s, q, kx,
                            vx, sb.offs, sb.toff, sb.total, sb.items, sb.order, sb.list, nb, L, q0, H, G, k,
-                           scale_log2, po, plse, bm);
+                           scale_log2, po, pml, bm);
     return hipGetLastError();
 }
 
@@ -449,8 +462,8 @@ __global__ __launch_bounds__(256, 2) void k4d_split(const uint16_t *__restrict__
             const int64_t hh = (int64_t)g * R + (active ? l32 : 0);
             const int64_t prow = (n * H + hh) * kslots + s;
             const int64_t lrow = ((n * G + g) * kslots + s) * R + (active ? l32 : 0);
-            attend_pass<D>(lds_k, lds_vt, qb, active, p - (int64_t)j * kBlock, scale_log2, lane,
-                           [&](const u32x4 (&w)[D / 16], float lse) {
+            attend_pass<D, true>(lds_k, lds_vt, qb, active, p - (int64_t)j * kBlock, scale_log2, lane,
+                           [&](const u32x4 (&w)[D / 16], float lse, float) {
                                if (!active) return;
 #pragma unroll
                                for (int u = 0; u < D / 16; ++u)
@@ -526,6 +539,37 @@ __device__ __forceinline__ u32x4 lse_merge(const u32x4 (&v)[KMAX], const float (
         if (!ok[s]) continue;
         const float w = __builtin_amdgcn_exp2f(l[s] - M);
         wsum += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += w * bf16_to_f32(v[s][e] & 0xFFFFu);
+            acc[2 * e + 1] += w * bf16_to_f32(v[s][e] >> 16);
+        }
+    }
+    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    return r;
+}
+
+// The same merge for partials that carry their o unnormalised, with the row maximum
+// m[s] (log2 units) and row sum l[s] of 2^(score - m[s]):
+//   out = sum_s 2^(m[s] - M) v[s] / sum_s 2^(m[s] - M) l[s],  M = max_s m[s],
+// summed in slot order, rounded once to bf16 (all zeros when no slot is valid).
+template <int KMAX>
+__device__ __forceinline__ u32x4 ml_merge(const u32x4 (&v)[KMAX], const f32x2 (&ml)[KMAX],
+                                          const bool (&ok)[KMAX]) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s)
+        if (ok[s]) M = fmaxf(M, ml[s][0]);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float wsum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+        if (!ok[s]) continue;
+        const float w = __builtin_amdgcn_exp2f(ml[s][0] - M);
+        wsum += w * ml[s][1];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             acc[2 * e] += w * bf16_to_f32(v[s][e] & 0xFFFFu);
@@ -616,8 +660,8 @@ __global__ __launch_bounds__(256, 1) void k4d_merge(const uint16_t *__restrict__
         for (int sl = first; sl < kslots; sl = next_valid(sl + 1)) {
             __syncthreads();                       // (A)
             const int j = idr[sl];
-            attend_pass<D>(lds_k, lds_vt, qb, active, p - (int64_t)j * kBlock, scale_log2, lane,
-                           [&](const u32x4 (&w)[D / 16], float lse) {
+            attend_pass<D, true>(lds_k, lds_vt, qb, active, p - (int64_t)j * kBlock, scale_log2, lane,
+                           [&](const u32x4 (&w)[D / 16], float lse, float) {
                                if (!active) return;
 #pragma unroll
                                for (int u = 0; u < D / 16; ++u)
@@ -706,7 +750,7 @@ bool k4d_merge_supported(int d, int R, int k) {
 // contents never enter the result, and padding slots (rows with fewer than k
 // selectable blocks) cost no memory traffic.
 // ---------------------------------------------------------------------------
-template <int D, int KMAX>
+template <int D, int KMAX, bool UNNORM>
 __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ po,
                                                   const float *__restrict__ plse,
                                                   const int32_t *__restrict__ ids, int64_t nq,
@@ -724,10 +768,14 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
     const int32_t *idr = ids + (i * G + g) * kslots;
     // batch: ids are local to the row's sequence and valid up to its own block
     if (bm.row_len) nb_lim = (bm.row_len[i] - 1) / kBlock + 1;
-    const float *lr = plse + (i * G + g) * kslots * R + (h - g * R);   // slot s at lr[s * R]
+    // slot s at lr[s * R] (normalised partials: log2-sum-exp) or mlr[s * R]
+    // (unnormalised: row maximum and row sum)
+    const float *lr = plse + (i * G + g) * kslots * R + (h - g * R);
+    const f32x2 *mlr = reinterpret_cast<const f32x2 *>(plse) + (i * G + g) * kslots * R + (h - g * R);
     const uint16_t *pr = po + ih * kslots * D + sub * 8;
     u32x4 v[KMAX];
     float l[KMAX];
+    f32x2 ml[KMAX];
     bool ok[KMAX];
     if (kslots == KMAX) {
         // full rows: ids as 16-byte vectors (rows are 16-byte aligned)
@@ -742,7 +790,8 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
         }
 #pragma unroll
         for (int s = 0; s < KMAX; ++s) {
-            l[s] = ok[s] ? lr[s * R] : 0.0f;
+            if constexpr (UNNORM) ml[s] = ok[s] ? mlr[s * R] : f32x2{0.0f, 0.0f};
+            else l[s] = ok[s] ? lr[s * R] : 0.0f;
             v[s] = ok[s] ? load16_stream(pr + s * D) : u32x4{0, 0, 0, 0};
         }
     } else {
@@ -751,39 +800,45 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
             if (s < kslots) {
                 const int id = idr[s];
                 ok[s] = id >= 0 && id < nb_lim;
-                l[s] = ok[s] ? lr[s * R] : 0.0f;
+                if constexpr (UNNORM) ml[s] = ok[s] ? mlr[s * R] : f32x2{0.0f, 0.0f};
+                else l[s] = ok[s] ? lr[s * R] : 0.0f;
                 v[s] = ok[s] ? load16_stream(pr + s * D) : u32x4{0, 0, 0, 0};
             } else {
                 ok[s] = false;
             }
         }
     }
-    store16_stream(out + ih * D + sub * 8, lse_merge<KMAX>(v, l, ok));
+    if constexpr (UNNORM) store16_stream(out + ih * D + sub * 8, ml_merge<KMAX>(v, ml, ok));
+    else store16_stream(out + ih * D + sub * 8, lse_merge<KMAX>(v, l, ok));
 }
 
-template <int D>
+template <int D, bool UNNORM>
 static hipError_t k5_dispatch(const uint16_t *po, const float *plse, const int32_t *ids,
                               int64_t nq, int H, int G, int k, int nb_lim, uint16_t *out,
                               const BatchMap &bm, hipStream_t s) {
     constexpr int PPW = 256 / (D / 8);
     const dim3 grid((unsigned)((nq * H + PPW - 1) / PPW));
     if (k <= 4)
-        hipLaunchKernelGGL((k5_combine<D, 4>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
+        hipLaunchKernelGGL((k5_combine<D, 4, UNNORM>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
     else if (k <= 8)
-        hipLaunchKernelGGL((k5_combine<D, 8>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
+        hipLaunchKernelGGL((k5_combine<D, 8, UNNORM>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
     else if (k <= 16)
-        hipLaunchKernelGGL((k5_combine<D, 16>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
+        hipLaunchKernelGGL((k5_combine<D, 16, UNNORM>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
     else
-        hipLaunchKernelGGL((k5_combine<D, 32>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
+        hipLaunchKernelGGL((k5_combine<D, 32, UNNORM>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
     return hipGetLastError();
 }
 
 hipError_t launch_k5_combine(const uint16_t *po, const float *plse, const int32_t *ids, int64_t nq,
                              int H, int G, int d, int k, int nb_lim, uint16_t *out,
-                             const BatchMap &bm, hipStream_t s) {
+                             const BatchMap &bm, bool unnorm, hipStream_t s) {
     if (nq <= 0) return hipSuccess;
-    if (d == 64) return k5_dispatch<64>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, s);
-    if (d == 128) return k5_dispatch<128>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, s);
+    if (d == 64)
+        return unnorm ? k5_dispatch<64, true>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, s)
+                      : k5_dispatch<64, false>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, s);
+    if (d == 128)
+        return unnorm ? k5_dispatch<128, true>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, s)
+                      : k5_dispatch<128, false>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, s);
     return hipErrorInvalidValue;
 }
 

@@ -111,9 +111,11 @@ int k3_num_groups(int64_t C);
 int64_t k3_tile_groups(int64_t max_items);
 
 // K4: KV-outer attention over the scheduled lists -> partials per (query, head,
-// slot): po [(i*H + h)*k + slot][d] bf16 (normalised o), plse [((i*G + g)*k + slot)*R
-// + h % R] fp32 (log2-sum-exp of the scaled scores).  With a batch map, q holds the
-// batch's rows (q0 = 0) and the lists are per global block.
+// slot): po [(i*H + h)*k + slot][d] bf16 (o NOT normalised), and at pml = plse viewed
+// as float pairs, [((i*G + g)*k + slot)*R + h % R] = (row maximum of the scaled
+// scores in log2 units, row sum of 2^(score - maximum)); plse holds 2*C*H*k floats.
+// With a batch map, q holds the batch's rows (q0 = 0) and the lists are per global
+// block.
 hipError_t launch_k4_kv_outer(const uint16_t *q, const uint16_t *kx, const uint16_t *vx,
                               const SchedBuffers &sb, int nb, int64_t L, int64_t q0, int64_t C,
                               int H, int G, int d, int k, float scale, uint16_t *po, float *plse,
@@ -142,10 +144,12 @@ hipError_t launch_page_check(const int32_t *table, int maxb, int64_t num_pages,
 
 // K5: two-phase combine of the partials of `nq` queries into out[nq, H, d].
 // ids [nq, G, k]: a slot is merged when 0 <= id < nb_lim, or with a batch map when
-// 0 <= id <= b(row) -- the rule K3 scheduled by.
+// 0 <= id <= b(row) -- the rule K3 scheduled by.  unnorm: the partials are K4's
+// (unnormalised o with (maximum, sum) pairs); else K4d's (normalised o with their
+// log2-sum-exp, plse [((i*G + g)*k + slot)*R + h % R]).
 hipError_t launch_k5_combine(const uint16_t *po, const float *plse, const int32_t *ids, int64_t nq,
                              int H, int G, int d, int k, int nb_lim, uint16_t *out,
-                             const BatchMap &bm, hipStream_t s);
+                             const BatchMap &bm, bool unnorm, hipStream_t s);
 
 // Fill n ints with a value (used instead of hipMemsetAsync so calls stay capturable).
 hipError_t launch_fill_i32(int *p, int64_t n, int value, hipStream_t s);
