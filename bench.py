@@ -46,7 +46,7 @@ K4_QUERIES = 128             # (query, slot) entries per KV-outer work item
 # attention) on the bf16 matrix cores, measured by their algorithmic FLOPs; every
 # other kernel on HBM bandwidth, measured by its algorithmic bytes.
 KERNEL_ROOF = {
-    "k1_index_pool": "mfma", "k4_kv_outer": "mfma",
+    "k1_index_pool": "mfma", "k12_index_select": "mfma", "k4_kv_outer": "mfma",
     "k2_select": "hbm", "k3_schedule": "hbm", "k5_combine": "hbm",
     "k1d_index_pool": "hbm", "k1d_index_pool_fp8": "hbm", "k4d_merge": "hbm",
     "k4d_split": "hbm", "page_check": "hbm", "quantize_e4m3": "hbm",
@@ -64,7 +64,21 @@ def paper_flop_ratio(H: int, G: int, d: int, dI: int, L: int, kB: int) -> float:
     return dense / msa
 
 
-def prefill_work(L, H, G, d, dI, k, B=B_BLOCK, list_counts=None):
+def fused_index_rows(L, k, chunk=131072, B=B_BLOCK):
+    """Query rows whose index branch the fused kernel (k12_index_select) serves: those
+    of query chunks whose shortest row has at least as many competitor blocks as the
+    chunk has query blocks (the library's rule; chunks of `chunk` queries from 0)."""
+    fused = np.zeros(L, bool)
+    if k - 1 > 16:
+        return fused
+    for q0 in range(0, L, chunk):
+        qend = min(L, q0 + chunk)
+        if q0 // B >= -(-(qend - q0) // B):
+            fused[q0:qend] = True
+    return fused
+
+
+def prefill_work(L, H, G, d, dI, k, B=B_BLOCK, list_counts=None, chunk=131072):
     """Algorithmic FLOPs and bytes of each prefill kernel over one whole step.
 
     K1 scores every competitor key of every (query, group): 2*G*dI FLOP per
@@ -84,19 +98,25 @@ def prefill_work(L, H, G, d, dI, k, B=B_BLOCK, list_counts=None):
     attended = float(np.sum((nsel - 1) * B + (i - bi * B + 1)))       # per group
     entries = float(np.sum(nsel)) * G                                 # (query, group, slot)
     f_idx = 2.0 * G * dI * pairs
+    fused = fused_index_rows(L, k, chunk, B)
+    f_k12 = 2.0 * G * dI * float(np.sum((bi * B)[fused]))
     f_attn = 4.0 * r * d * G * attended
-    comp_rows = np.maximum(bi - 0, 0)
-    k2_bytes = 4.0 * G * float(np.sum(np.where(bi > k - 1, comp_rows, 0))) + 4.0 * L * G * k
     items = float(np.sum(np.ceil(np.asarray(list_counts) / K4_QUERIES))) \
         if list_counts is not None else entries / K4_QUERIES
     k5_bytes = entries * r * (2 * d + 4) + L * H * d * 2 + 4.0 * L * G * k
+    unf = ~fused
+    k2_bytes = (4.0 * G * float(np.sum(np.where((bi > k - 1) & unf, bi, 0)))
+                + 4.0 * float(np.sum(unf)) * G * k)
     return {
-        "flops": {"k1_index_pool": f_idx, "k4_kv_outer": f_attn},
+        "flops": {"k1_index_pool": f_idx - f_k12, "k12_index_select": f_k12,
+                  "k4_kv_outer": f_attn},
         "bytes": {"k2_select": k2_bytes, "k3_schedule": 12.0 * L * G * k,
                   "k5_combine": k5_bytes},
         "design_bytes": {
-            "k1_index_pool": {"idx_q_in": L * G * dI * 2.0,
-                              "block_scores_out": 4.0 * G * float(np.sum(bi))},
+            "k1_index_pool": {"idx_q_in": float(np.sum(unf)) * G * dI * 2.0,
+                              "block_scores_out": 4.0 * G * float(np.sum(bi[unf]))},
+            "k12_index_select": {"idx_q_in": float(np.sum(fused)) * G * dI * 2.0,
+                                 "ids_out": 4.0 * float(np.sum(fused)) * G * k},
             "k4_kv_outer": {"q_rows_gathered": entries * r * d * 2.0,
                             "partial_rows_out": entries * r * (2 * d + 4.0),
                             "kv_blocks_staged": items * 2 * B * d * 2.0}},
@@ -597,7 +617,7 @@ def run_workload(args, name, steps, warmup, cpu_baseline, dense):
             result["config"].update({"ids": "constructed: blocks %s + own block + %d random"
                                             % (list(wl.hot_blocks), s.k - 1 - len(wl.hot_blocks))})
             del result["config"]["planting"]
-            for key_ in ("k1_index_pool", "k2_select"):
+            for key_ in ("k1_index_pool", "k12_index_select", "k2_select"):
                 work["flops"].pop(key_, None)
                 work["bytes"].pop(key_, None)
                 work["design_bytes"].pop(key_, None)

@@ -85,9 +85,35 @@ int64_t chunk_of(int64_t L) { return std::min<int64_t>(round_up(std::max<int64_t
 int64_t nblocks(int64_t L) { return (L + kBlock - 1) / kBlock; }
 int nb_padded(int64_t L) { return (int)round_up(std::max<int64_t>(nblocks(L), 1), 8); }
 
-size_t select_bytes(int64_t C, int64_t L, int G) {
+// Index branch of a query chunk [q0, qend): the fused kernel K12 (no block scores in
+// memory) when it serves the shape and the chunk's rows are long and alike -- its
+// shortest row has at least as many competitor blocks as the chunk has query
+// blocks, so that its work-groups (one per 64 queries, over all their key blocks)
+// run for similar times and sweep the key tiles together, reusing them from L2.
+// Otherwise K1 (32-block key chunks, L2-friendly for the triangle of short rows)
+// and K2.
+bool use_k12(int64_t q0, int64_t qend, int G, int dI, int k) {
+    return k12_supported(G, dI, k) && q0 / kBlock >= (qend - q0 + kBlock - 1) / kBlock;
+}
+// Workspace: K12's candidate lists and the block scores of the chunks K1 + K2 serve
+// (with K12 available those chunks end before 2C, which bounds their row length).
+struct IndexWs {
+    float *S = nullptr;        // K1 + K2
+    uint64_t *cand = nullptr;  // K12
+};
+IndexWs carve_index(Carver &c, int64_t C, int64_t L, int G, int dI, int k) {
+    IndexWs w;
+    if (k12_supported(G, dI, k)) {
+        w.cand = c.take<uint64_t>(k12_cand_entries(C, G));
+        w.S = c.take<float>(C * G * nb_padded(std::min(L, 2 * C)));
+    } else {
+        w.S = c.take<float>(C * G * nb_padded(L));
+    }
+    return w;
+}
+size_t select_bytes(int64_t C, int64_t L, int G, int dI, int k) {
     Carver c(nullptr);
-    c.take<float>(C * G * nb_padded(L));
+    carve_index(c, C, L, G, dI, k);
     return c.used;
 }
 size_t attn_bytes(int64_t C, int64_t L, int H, int G, int d, int k) {
@@ -95,9 +121,9 @@ size_t attn_bytes(int64_t C, int64_t L, int H, int G, int d, int k) {
     carve_attn(c, C, H, G, d, k, (int)nblocks(L));
     return c.used;
 }
-size_t prefill_bytes(int64_t C, int64_t L, int H, int G, int d, int k) {
+size_t prefill_bytes(int64_t C, int64_t L, int H, int G, int d, int dI, int k) {
     Carver c(nullptr);
-    c.take<float>(C * G * nb_padded(L));
+    carve_index(c, C, L, G, dI, k);
     c.take<int32_t>(C * G * k);
     carve_attn(c, C, H, G, d, k, (int)nblocks(L));
     return c.used;
@@ -142,11 +168,11 @@ struct TimedLaunch {
     int name;
     hipEvent_t start, stop;
 };
-enum StageName { kK1, kK2, kK3, kK4, kK5, kK1d, kK4d, kKpc, kK1d8, kQuant, kK4dm, kNumStages };
+enum StageName { kK1, kK2, kK3, kK4, kK5, kK1d, kK4d, kKpc, kK1d8, kQuant, kK4dm, kK12, kNumStages };
 const char *const kStageNames[kNumStages] = {"k1_index_pool", "k2_select", "k3_schedule",
                                              "k4_kv_outer", "k5_combine", "k1d_index_pool",
                                              "k4d_split", "page_check", "k1d_index_pool_fp8",
-                                             "quantize_e4m3", "k4d_merge"};
+                                             "quantize_e4m3", "k4d_merge", "k12_index_select"};
 struct Timing {
     bool on = false;
     int cap = 0, used = 0;
@@ -193,6 +219,20 @@ hipError_t timed(int stage, hipStream_t s, F &&launch) {
         if ((expr) != hipSuccess) return MSA_ERR_HIP;   \
     } while (0)
 #define MSA_TIMED(stage, expr) MSA_TRY(timed(stage, s, [&]() { return (expr); }))
+
+// Index branch of queries [q0, qend): ids [(i-q0)*G + g][k] at ids_c.
+int index_chunk(const IndexWs &w, const uint16_t *idx_q, const uint16_t *idx_k, int64_t L,
+                int64_t q0, int64_t qend, int G, int dI, int k, int32_t *ids_c, hipStream_t s) {
+    if (use_k12(q0, qend, G, dI, k)) {
+        MSA_TIMED(kK12, launch_k12_index_select(idx_q, idx_k, ids_c, w.cand, q0, qend, G, dI, k, s));
+        return MSA_OK;
+    }
+    // block-score rows of the chunk's own length (the carve holds them)
+    const int nbp = k12_supported(G, dI, k) ? nb_padded(qend) : nb_padded(L);
+    MSA_TIMED(kK1, launch_k1_index_pool(idx_q, idx_k, w.S, L, q0, qend, G, dI, nbp, s));
+    MSA_TIMED(kK2, launch_k2_select(w.S, nbp, (qend - q0) * G, G, k, q0, nullptr, 0, ids_c, s));
+    return MSA_OK;
+}
 
 // Shared by prefill and sparse_attn: K3 + K4 + K5 for queries [q0, qend).
 int attn_chunk(const uint16_t *q, const uint16_t *kx, const uint16_t *vx, const int32_t *ids_c,
@@ -245,9 +285,9 @@ const char *msa_status_string(int status) {
 
 // ------------------------------- select -----------------------------------
 size_t msa_select_blocks_workspace_size(int64_t L, int G, int dI, int B, int k) {
-    (void)dI; (void)B; (void)k;
+    (void)B;
     if (L <= 0 || G <= 0) return 0;
-    return select_bytes(chunk_of(L), L, G);
+    return select_bytes(chunk_of(L), L, G, dI, k);
 }
 
 int msa_select_blocks(const uint16_t *idx_q, const uint16_t *idx_k, int64_t L, int G, int dI,
@@ -257,18 +297,17 @@ int msa_select_blocks(const uint16_t *idx_q, const uint16_t *idx_k, int64_t L, i
     if (!idx_q || !idx_k || !block_ids) return MSA_ERR_INVALID_ARG;
     if (B != kBlock || !index_ok(G, dI) || k > 32) return MSA_ERR_UNSUPPORTED;
     if (check_ptr(ws) != MSA_OK) return MSA_ERR_WORKSPACE_TOO_SMALL;
-    const int64_t C = fit_chunk(L, ws_bytes, [&](int64_t c) { return select_bytes(c, L, G); });
+    const int64_t C =
+        fit_chunk(L, ws_bytes, [&](int64_t c) { return select_bytes(c, L, G, dI, k); });
     if (C == 0) return MSA_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     Carver c(ws, ws_bytes);
-    const int nbp = nb_padded(L);
-    float *S = c.take<float>(C * G * nbp);
+    const IndexWs iw = carve_index(c, C, L, G, dI, k);
     MSA_CHECK_CARVE(c);
     for (int64_t q0 = 0; q0 < L; q0 += C) {
         const int64_t qend = std::min(L, q0 + C);
-        MSA_TIMED(kK1, launch_k1_index_pool(idx_q, idx_k, S, L, q0, qend, G, dI, nbp, s));
-        MSA_TIMED(kK2, launch_k2_select(S, nbp, (qend - q0) * G, G, k, q0, nullptr, 0,
-                                        block_ids + q0 * G * k, s));
+        const int rc = index_chunk(iw, idx_q, idx_k, L, q0, qend, G, dI, k, block_ids + q0 * G * k, s);
+        if (rc != MSA_OK) return rc;
     }
     return MSA_OK;
 }
@@ -311,7 +350,7 @@ int msa_sparse_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 size_t msa_prefill_workspace_size(int64_t L, int H, int G, int d, int dI, int B, int k) {
     (void)dI; (void)B;
     if (L <= 0 || G <= 0 || H <= 0 || d <= 0 || k <= 0) return 0;
-    return prefill_bytes(chunk_of(L), L, H, G, d, k);
+    return prefill_bytes(chunk_of(L), L, H, G, d, dI, k);
 }
 
 }  // extern "C"
@@ -327,21 +366,20 @@ int prefill_range(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
                   const uint16_t *idx_k, int64_t L, int64_t P, int H, int G, int d, int dI,
                   int kslots, float scale, uint16_t *out, int32_t *ids, void *ws, size_t ws_bytes,
                   hipStream_t s) {
-    const int64_t C = fit_chunk(L, ws_bytes,
-                                [&](int64_t c) { return prefill_bytes(c, L, H, G, d, kslots); });
+    const int64_t C = fit_chunk(
+        L, ws_bytes, [&](int64_t c) { return prefill_bytes(c, L, H, G, d, dI, kslots); });
     if (C == 0) return MSA_ERR_WORKSPACE_TOO_SMALL;
-    const int nbp = nb_padded(L);
     Carver c(ws, ws_bytes);
-    float *S = c.take<float>(C * G * nbp);
+    const IndexWs iw = carve_index(c, C, L, G, dI, kslots);
     int32_t *ids_ws = c.take<int32_t>(C * G * kslots);
     const AttnWs w = carve_attn(c, C, H, G, d, kslots, (int)nblocks(L));
     MSA_CHECK_CARVE(c);
     for (int64_t q0 = P; q0 < L; q0 += C) {
         const int64_t qend = std::min(L, q0 + C);
         int32_t *ids_c = ids ? ids + q0 * G * kslots : ids_ws;
-        MSA_TIMED(kK1, launch_k1_index_pool(idx_q, idx_k, S, L, q0, qend, G, dI, nbp, s));
-        MSA_TIMED(kK2, launch_k2_select(S, nbp, (qend - q0) * G, G, kslots, q0, nullptr, 0, ids_c, s));
-        const int rc = attn_chunk(q, k, v, ids_c, L, q0, qend, H, G, d, kslots, scale, out, w, s);
+        int rc = index_chunk(iw, idx_q, idx_k, L, q0, qend, G, dI, kslots, ids_c, s);
+        if (rc != MSA_OK) return rc;
+        rc = attn_chunk(q, k, v, ids_c, L, q0, qend, H, G, d, kslots, scale, out, w, s);
         if (rc != MSA_OK) return rc;
     }
     return MSA_OK;
@@ -493,7 +531,7 @@ int msa_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
         L > kMaxPrefillLen)
         return MSA_ERR_UNSUPPORTED;
     if (check_ptr(ws) != MSA_OK) return MSA_ERR_WORKSPACE_TOO_SMALL;
-    if (fit_chunk(L, ws_bytes, [&](int64_t c) { return prefill_bytes(c, L, H, G, d, kslots); }) == 0)
+    if (fit_chunk(L, ws_bytes, [&](int64_t c) { return prefill_bytes(c, L, H, G, d, dI, kslots); }) == 0)
         return MSA_ERR_WORKSPACE_TOO_SMALL;
     return prefill_range(q, k, v, idx_q, idx_k, L, 0, H, G, d, dI, kslots, default_scale(scale, d),
                          out, block_ids_out, ws, ws_bytes, static_cast<hipStream_t>(stream));
@@ -524,7 +562,7 @@ int msa_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     if (check_ptr(ws) != MSA_OK) return MSA_ERR_WORKSPACE_TOO_SMALL;
     // every sequence must fit at least one 128-query chunk (the longest needs most)
     if (fit_chunk(max_L, ws_bytes,
-                  [&](int64_t c) { return prefill_bytes(c, max_L, H, G, d, kslots); }) == 0)
+                  [&](int64_t c) { return prefill_bytes(c, max_L, H, G, d, dI, kslots); }) == 0)
         return MSA_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     scale = default_scale(scale, d);
@@ -557,7 +595,7 @@ size_t msa_prefill_varlen_workspace_size(const int64_t *cu_q, const int64_t *cu_
     for (int sq = 0; sq < nseq; ++sq) {
         const int64_t C = cu_q[sq + 1] - cu_q[sq], L = cu_kv[sq + 1] - cu_kv[sq];
         if (C <= 0 || L < C) continue;
-        need = std::max(need, prefill_bytes(chunk_of(L), L, H, G, d, k));
+        need = std::max(need, prefill_bytes(chunk_of(L), L, H, G, d, dI, k));
     }
     // the batches formed when the workspace is not the limit
     plan_batches(cu_q, cu_kv, nseq, H, G, d, k, SIZE_MAX, cu_kv[nseq] < (int64_t)INT32_MAX - kBlock,

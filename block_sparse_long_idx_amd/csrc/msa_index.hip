@@ -239,6 +239,220 @@ static hipError_t k1_dispatch_batch(const uint16_t *iq, const uint16_t *ik, floa
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// K12: index scores, block max-pool and the exp-free selection in one kernel
+// ("MiniMax M3 算力省 20 倍", §二 Index Branch: max-pooled block scores, top-k per
+// group, the own block always kept; §四 Kernel: selection on raw scores, no exp).
+// The block scores never leave the chip: a work-group owns 256 stacked index rows
+// (64 queries x G groups of one query block) and sweeps ALL their competitor key
+// blocks 0 .. b(i)-1 (K1 splits that range into 32-block items), scoring each
+// staged 128-key tile with K1's MFMA tiling.  Every row keeps, in registers, the
+// score tau of its current (k-1)-th best block and the length of a short candidate
+// list in memory (CAP entries of (score, block) per row, in the workspace): a block
+// enters the list only when its score is above tau -- so a block scoring the same
+// as the current (k-1)-th best, which has a smaller id, never displaces it -- and
+// whenever some row's list is full the wave cuts every row's list to its k-1 best
+// (rank = number of entries with a larger score, or an equal score and a smaller
+// block id) and raises tau.  Blocks arrive in increasing id order, so the final
+// cut is exactly the selection of K2.  After the sweep each row emits its own block
+// plus the kept competitors, ascending, padded with -1.
+// Work-groups run longest first (query block descending) and go to the XCDs in
+// turn, so the work-groups that share an XCD sweep nearby key ranges together and
+// reuse the staged key tiles from its L2.
+// ---------------------------------------------------------------------------
+constexpr int kK12Cap = 32;   // candidate list entries per row
+constexpr int kK12Keep = 16;  // most competitors kept per row (k - 1), half the list
+
+// Cuts one row's list (cnt entries at c) to its `keep` best entries, stored in rank
+// order; tau becomes the keep-th best score once cnt >= keep.
+__device__ __forceinline__ void k12_cut(uint2 *c, int &cnt, float &tau, int keep) {
+    float sc[kK12Cap];
+    int id[kK12Cap];
+#pragma unroll
+    for (int e = 0; e < kK12Cap; ++e) {
+        const uint2 v = e < cnt ? c[e] : uint2{__float_as_uint(-INFINITY), 0x7FFFFFFFu};
+        sc[e] = __uint_as_float(v.x);
+        id[e] = (int)v.y;
+    }
+    float t = -INFINITY;
+#pragma unroll
+    for (int a = 0; a < kK12Cap; ++a) {
+        int rank = 0;
+#pragma unroll
+        for (int b = 0; b < kK12Cap; ++b)
+            rank += (sc[b] > sc[a]) || (sc[b] == sc[a] && id[b] < id[a]);
+        if (rank < keep && a < cnt) c[rank] = uint2{__float_as_uint(sc[a]), (uint32_t)id[a]};
+        if (rank == keep - 1 && a < cnt) t = sc[a];
+    }
+    if (cnt >= keep) tau = t;
+    cnt = min(cnt, keep);
+}
+
+template <int G, int DI>
+__global__ __launch_bounds__(256, 2) void k12_index_select(
+    const uint16_t *__restrict__ iq, const uint16_t *__restrict__ ik, int32_t *__restrict__ ids,
+    uint2 *__restrict__ cand, int64_t q0, int64_t qend, int qb0, int qb1, int k) {
+    constexpr int NT = K1Tiling<G>::NT;
+    constexpr int NTHR = K1Tiling<G>::THREADS;
+    constexpr int P = K1Tiling<G>::P;
+    constexpr int CPR = DI / 8;
+    constexpr int KS = DI / 16;
+    constexpr int TILE = kBlock * DI * 2;
+    __shared__ __attribute__((aligned(16))) char lds_k[2][TILE];
+
+    const int qb = qb1 - 1 - (int)(blockIdx.x / P);     // longest first
+    const int part = (int)(blockIdx.x % P);
+    if (qb < qb0) return;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int hf = lane >> 5, l32 = lane & 31;
+
+    bf16x8 bq[NT][KS];
+    const int64_t row0 = ((int64_t)qb * kBlock + part * K1Tiling<G>::QT) * G;
+    const int64_t row_end = qend * G;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int64_t row = row0 + wave * 32 * NT + nt * 32 + l32;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            bq[nt][ks] = as_bf16x8(row < row_end ? load16(iq + row * DI + (2 * ks + hf) * 8)
+                                                 : u32x4{0, 0, 0, 0});
+    }
+    // The row this lane keeps the selection of: with two N-tiles lane half hf owns
+    // row nt = hf; with one both halves hold the same row and half 0 owns it.
+    const int my_nt = NT == 2 ? hf : 0;
+    const int64_t my_row = row0 + wave * 32 * NT + my_nt * 32 + l32;
+    const bool owner = (NT == 2 || hf == 0) && my_row < row_end;
+    uint2 *my_cand = cand + (owner ? (my_row - q0 * G) * kK12Cap : 0);
+    const int keep = k - 1;
+    float tau = -INFINITY;
+    int cnt = 0;
+
+    if (qb > 0 && keep > 0) {
+        const char *ikb = reinterpret_cast<const char *>(ik);
+        const int64_t blk_bytes = (int64_t)kBlock * DI * 2;
+        stage_rows_direct<CPR, NTHR>(lds_k[0], ikb, DI * 2, tid);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // A row's candidate from block j is written to its list at the start of block
+        // j + 1, ahead of that block's tile copy: the wait for the copy at the end of
+        // an iteration then does not also wait on a store just issued.  pend holds its
+        // score (-inf: none; scores are finite).
+        float pend = -INFINITY;
+        for (int j = 0; j < qb; ++j) {
+            const int buf = j & 1;
+            const bool more = j + 1 < qb;
+            if (owner && pend > -INFINITY)
+                my_cand[cnt - 1] = uint2{__float_as_uint(pend), (uint32_t)(j - 1)};
+            pend = -INFINITY;
+            // the per-block scoring of K1 (same operands, same MFMA order)
+            float mx[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) mx[nt] = -INFINITY;
+            const char *kt = lds_k[buf];
+            bf16x8 a_cur[KS], a_nxt[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                a_cur[ks] = as_bf16x8(load16(kt + swz<CPR>(l32, 2 * ks + hf)));
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                if (mt < 3) {
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        a_nxt[ks] = as_bf16x8(load16(kt + swz<CPR>((mt + 1) * 32 + l32, 2 * ks + hf)));
+                }
+                if (mt == 2 && more)
+                    stage_rows_direct<CPR, NTHR>(lds_k[buf ^ 1], ikb + (j + 1) * blk_bytes, DI * 2, tid);
+                __builtin_amdgcn_sched_barrier(0);
+                f32x16 acc[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma32(a_cur[ks], bq[nt][ks], acc[nt]);
+                }
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    float m = acc[nt][0];
+#pragma unroll
+                    for (int r = 1; r < 16; ++r) m = __builtin_fmaxf(m, acc[nt][r]);
+                    mx[nt] = __builtin_fmaxf(mx[nt], m);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) a_cur[ks] = a_nxt[ks];
+            }
+            float mine = -INFINITY;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const float m = fmaxf(mx[nt], xor_shfl(mx[nt], 32));
+                if (nt == my_nt) mine = m;
+            }
+            if (owner && mine > tau) {
+                pend = mine;
+                ++cnt;
+            }
+            // a full list, or the last block: cut (the last cut leaves the selection)
+            if (__ballot(cnt == kK12Cap) || j == qb - 1) {
+                if (owner && pend > -INFINITY)
+                    my_cand[cnt - 1] = uint2{__float_as_uint(pend), (uint32_t)j};
+                pend = -INFINITY;
+                if (owner) k12_cut(my_cand, cnt, tau, keep);
+            }
+            __builtin_amdgcn_s_waitcnt(0);   // the next tile has landed in LDS
+            __syncthreads();
+        }
+    }
+    if (!owner) return;
+    // the own block and the kept competitors (at most kK12Keep), ascending
+    int sel[kK12Keep];
+#pragma unroll
+    for (int e = 0; e < kK12Keep; ++e) sel[e] = e < cnt ? (int)my_cand[e].y : 0x7FFFFFFF;
+    int32_t *out = ids + (my_row - q0 * G) * k;
+#pragma unroll
+    for (int a = 0; a < kK12Keep; ++a) {
+        int rank = 0;
+#pragma unroll
+        for (int b = 0; b < kK12Keep; ++b) rank += sel[b] < sel[a];
+        if (a < cnt) out[rank] = sel[a];
+    }
+    out[cnt] = qb;                               // every competitor id is below qb
+    for (int sl = cnt + 1; sl < k; ++sl) out[sl] = -1;
+}
+
+template <int G, int DI>
+static hipError_t k12_dispatch(const uint16_t *iq, const uint16_t *ik, int32_t *ids, uint2 *cand,
+                               int64_t q0, int64_t qend, int k, hipStream_t s) {
+    const int qb0 = (int)(q0 / kBlock);
+    const int qb1 = (int)((qend + kBlock - 1) / kBlock);
+    const int64_t grid = (int64_t)(qb1 - qb0) * K1Tiling<G>::P;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL((k12_index_select<G, DI>), dim3((unsigned)grid), dim3(K1Tiling<G>::THREADS),
+                       0, s, iq, ik, ids, cand, q0, qend, qb0, qb1, k);
+    return hipGetLastError();
+}
+
+bool k12_supported(int G, int dI, int k) {
+    return k >= 1 && k - 1 <= kK12Keep && (G == 1 || G == 2 || G == 4 || G == 8) &&
+           (dI == 32 || dI == 64 || dI == 128) && G * dI <= 512;
+}
+
+int64_t k12_cand_entries(int64_t C, int G) { return C * G * kK12Cap; }
+
+hipError_t launch_k12_index_select(const uint16_t *iq, const uint16_t *ik, int32_t *ids,
+                                   void *cand, int64_t q0, int64_t qend, int G, int dI, int k,
+                                   hipStream_t s) {
+    uint2 *c = static_cast<uint2 *>(cand);
+#define K12_CASE(g, di) \
+    if (G == g && dI == di) return k12_dispatch<g, di>(iq, ik, ids, c, q0, qend, k, s);
+    K12_CASE(1, 32) K12_CASE(1, 64) K12_CASE(1, 128)
+    K12_CASE(2, 32) K12_CASE(2, 64) K12_CASE(2, 128)
+    K12_CASE(4, 32) K12_CASE(4, 64) K12_CASE(4, 128)
+    K12_CASE(8, 32) K12_CASE(8, 64)
+#undef K12_CASE
+    return hipErrorInvalidValue;
+}
+
 int64_t k1_num_workgroups(int64_t q0, int64_t qend, int G) {
     const int qb0 = (int)(q0 / kBlock), qb1 = (int)((qend + kBlock - 1) / kBlock);
     const int64_t n = k1_num_items(qb0, qb1);

@@ -32,6 +32,15 @@ hipError_t launch_k1_index_pool(const uint16_t *iq, const uint16_t *ik, float *S
                                 int64_t q0, int64_t qend, int G, int dI, int nbp,
                                 hipStream_t s);
 
+// K12: K1 and K2 in one kernel -- ids [(i-q0)*G + g][k] of queries [q0, qend) (q0 a
+// multiple of 128) without block scores in memory; cand holds k12_cand_entries(C, G)
+// 8-byte candidate entries for a chunk of C queries.  Only where k12_supported.
+bool k12_supported(int G, int dI, int k);
+int64_t k12_cand_entries(int64_t C, int G);
+hipError_t launch_k12_index_select(const uint16_t *iq, const uint16_t *ik, int32_t *ids,
+                                   void *cand, int64_t q0, int64_t qend, int G, int dI, int k,
+                                   hipStream_t s);
+
 // K1d: decode block scores S[n*G + g][b] for blocks b < b(seq_len[n]-1).
 // table == nullptr: contiguous cache ikc [N, Lmax, dI]; otherwise a paged cache
 // [pages, 128, dI] with block b of sequence n in page table[n * maxb + b].

@@ -287,7 +287,11 @@ MSA_API int msa_quantize_idx_k_e4m3(const uint16_t *idx_k, int64_t rows, int dI,
  * one), "k4_kv_outer", "k5_combine", "k1d_index_pool", "k4d_split", "page_check",
  * "k1d_index_pool_fp8", "quantize_e4m3", "k4d_merge" (decode's attention with the
  * combine of its slots in the same launch, used where the slots' partials fit in
- * LDS: k <= 16 and k * (H/G) * d * 2 bytes <= 96 KiB).
+ * LDS: k <= 16 and k * (H/G) * d * 2 bytes <= 96 KiB), "k12_index_select" (index
+ * scores, max-pool and selection in one launch, with no block scores in memory:
+ * msa_select_blocks and msa_prefill use it for the query chunks whose shortest row
+ * has at least as many competitor blocks as the chunk has query blocks, k <= 17;
+ * the other chunks run k1_index_pool + k2_select; the ids are the same).
  *   msa_timing_enable(max_launches): start recording (events for up to
  *       max_launches stages are created up front; further stages are not timed).
  *   msa_timing_collect(out, max_entries, n_out): waits for the recorded events

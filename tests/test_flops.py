@@ -32,8 +32,15 @@ def test_prefill_work_matches_closed_forms():
     assert abs(dense - 4 * H * d * L * (L + 1) / 2) < 1
     # at 1M the index branch dominates MSA's algorithmic FLOPs (~89%)
     w1 = bench.prefill_work(1 << 20, H, G, d, dI, k)
-    frac = w1["flops"]["k1_index_pool"] / w1["f_total"]
+    frac = (w1["flops"]["k1_index_pool"] + w1["flops"]["k12_index_select"]) / w1["f_total"]
     assert 0.88 < frac < 0.90
+    # the fused index kernel serves the query chunks whose rows are long: at 1M (chunks
+    # of 131072 queries) chunks 1..7; at 128K (one chunk from query 0) none
+    fused = bench.fused_index_rows(1 << 20, k)
+    assert not fused[:131072].any() and fused[131072:].all()
+    assert not bench.fused_index_rows(131072, k).any()
+    assert not bench.fused_index_rows(1 << 20, 18).any()      # k - 1 > 16: K1 + K2 only
+    assert w["flops"]["k12_index_select"] == 0.0
 
 
 def test_decode_work():

@@ -1065,6 +1065,44 @@ def test_chunked_workspace_invariance():
                     workspace=msa._workspace(4096, DEV))
 
 
+@pytest.mark.parametrize("L,H,G,d,dI,k", [(20000, 16, 4, 128, 128, 16), (9000, 8, 2, 64, 32, 4),
+                                           (12000, 16, 8, 64, 64, 17), (6000, 4, 1, 64, 128, 2)])
+def test_fused_selection_matches_two_kernel_path(L, H, G, d, dI, k):
+    """The fused index kernel (scores, max-pool and selection in one launch, used for
+    query chunks whose rows are long) gives bitwise the ids -- and so the outputs --
+    of K1 + K2: a workspace for 1024-query chunks makes every chunk from query 1024
+    on use it, against one whole-sequence chunk served by K1 + K2; and the oracle on
+    sampled rows of the chunked call."""
+    msa = _msa()
+    shape = synth.PrefillShape(L=L, H=H, G=G, d=d, dI=dI, B=128, k=k)
+    _say(f"fused selection L={L} H={H} G={G} d={d} dI={dI} k={k}")
+    x = synth.prefill_inputs(shape, seed=9)
+    dv = {n: t.to(DEV) for n, t in x.items() if isinstance(t, torch.Tensor)}
+    o1, i1 = msa.prefill(dv["q"], dv["k"], dv["v"], dv["iq"], dv["ik"], kslots=k, return_ids=True)
+    need = msa.workspace_size("prefill", L=1024, H=H, G=G, d=d, dI=dI, k=k)
+    # the chunk size the library picks is the largest that fits: size for 1024 queries of L
+    lo, hi = need, msa.workspace_size("prefill", L=L, H=H, G=G, d=d, dI=dI, k=k)
+    ws = None
+    for frac in (64, 32, 16, 8, 4):
+        cand = max(lo, hi // frac)
+        ws = msa._workspace(cand, DEV)
+        try:
+            o2, i2 = msa.prefill(dv["q"], dv["k"], dv["v"], dv["iq"], dv["ik"], kslots=k,
+                                 return_ids=True, workspace=ws)
+            break
+        except msa.MSAError:
+            continue
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    rows = np.unique(np.concatenate([np.arange(L - 200, L), np.random.default_rng(1).choice(L, 300, replace=False)]))
+    st = _parity.prefill_rows_vs_oracle(x, rows, i2.cpu().numpy()[rows], o2.float().cpu().numpy()[rows],
+                                        128, k, 1.0 / math.sqrt(d))
+    _say(f"  -> {st}")
+    assert st["id_mismatches"] == 0
+    assert st["max_abs"] < _parity.MAX_ABS and st["mean_abs"] < _parity.MEAN_ABS
+
+
 def _select_vs_oracle(iq, ik, k, rows):
     """select_blocks on the GPU and the oracle's selection for the same rows."""
     msa = _msa()
