@@ -1103,6 +1103,43 @@ def test_fused_selection_matches_two_kernel_path(L, H, G, d, dI, k):
     assert st["max_abs"] < _parity.MAX_ABS and st["mean_abs"] < _parity.MEAN_ABS
 
 
+def test_skewed_ids_masks_and_chunking():
+    """Constructed skewed ids (blocks 0-3 in nearly every row, so K4's lists of those
+    blocks span many tiles) where about 5% of the rows drop block 2, some rows of
+    group 1 lack all of blocks 0-3, and L is not a multiple of 128 (a short last
+    query block).  Checked against the oracle on sampled rows, and bitwise against a
+    run split into ~2048-query chunks."""
+    msa = _msa()
+    L, H, G, d, k = 24526, 16, 4, 128, 16
+    shape = synth.PrefillShape(L=L, H=H, G=G, d=d, dI=128, B=128, k=k)
+    _say(f"skewed ids, masks and chunking L={L} H={H} G={G}")
+    x = synth.prefill_inputs(shape, seed=11, plant="none")
+    ids = synth.skewed_ids(L, G, k, hot=(0, 1, 2, 3), seed=11).numpy()
+    r = np.arange(L)
+    drop = (r % 19 == 0) & (r // 128 >= k)
+    sub = ids[drop]
+    sub[sub == 2] = -1
+    ids[drop] = sub
+    none_rows = (r % 97 == 5) & (r // 128 >= k)          # group 1: no hot block at all
+    g1 = ids[none_rows, 1]
+    g1[np.isin(g1, [0, 1, 2, 3])] = -1
+    ids[none_rows, 1] = g1
+    dv = {n: x[n].to(DEV) for n in ("q", "k", "v")}
+    idt = torch.from_numpy(ids).to(DEV)
+    o1 = msa.sparse_attn(dv["q"], dv["k"], dv["v"], idt)
+    full = msa.workspace_size("sparse_attn", L=L, H=H, G=G, d=d, k=k)
+    o2 = msa.sparse_attn(dv["q"], dv["k"], dv["v"], idt, workspace=msa._workspace(full // 10, DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    rows = np.unique(np.concatenate([np.nonzero(drop)[0][::7], np.nonzero(none_rows)[0],
+                                     np.arange(L - 60, L),
+                                     np.random.default_rng(2).choice(L, 700, replace=False)]))
+    ref = oracle.attend(x["q"], x["k"], x["v"], ids[rows], 128, 1.0 / math.sqrt(d), rows=rows)
+    mx, mean = _parity.compare_out(o1.float().cpu().numpy()[rows], ref)
+    _say(f"  -> oracle on {len(rows)} rows: max {mx:.3e} mean {mean:.3e}")
+    assert mx < _parity.MAX_ABS and mean < _parity.MEAN_ABS
+
+
 def _select_vs_oracle(iq, ik, k, rows):
     """select_blocks on the GPU and the oracle's selection for the same rows."""
     msa = _msa()
