@@ -64,16 +64,22 @@ def paper_flop_ratio(H: int, G: int, d: int, dI: int, L: int, kB: int) -> float:
     return dense / msa
 
 
-def fused_index_rows(L, k, chunk=131072, B=B_BLOCK):
+K12_MIN_WORKGROUPS = 1024          # the library's floor for a fused launch
+K12_QUERY_BLOCK_PARTS = {1: 1, 2: 2, 4: 2, 8: 4}   # K12 work-groups per query block
+
+
+def fused_index_rows(L, k, chunk=131072, B=B_BLOCK, G=4):
     """Query rows whose index branch the fused kernel (k12_index_select) serves: those
     of query chunks whose shortest row has at least as many competitor blocks as the
-    chunk has query blocks (the library's rule; chunks of `chunk` queries from 0)."""
+    chunk has query blocks and that give the kernel at least 1024 work-groups (the
+    library's rule; chunks of `chunk` queries from 0)."""
     fused = np.zeros(L, bool)
     if k - 1 > 16:
         return fused
     for q0 in range(0, L, chunk):
         qend = min(L, q0 + chunk)
-        if q0 // B >= -(-(qend - q0) // B):
+        nqb = -(-(qend - q0) // B)
+        if q0 // B >= nqb and nqb * K12_QUERY_BLOCK_PARTS[G] >= K12_MIN_WORKGROUPS:
             fused[q0:qend] = True
     return fused
 
@@ -98,7 +104,7 @@ def prefill_work(L, H, G, d, dI, k, B=B_BLOCK, list_counts=None, chunk=131072):
     attended = float(np.sum((nsel - 1) * B + (i - bi * B + 1)))       # per group
     entries = float(np.sum(nsel)) * G                                 # (query, group, slot)
     f_idx = 2.0 * G * dI * pairs
-    fused = fused_index_rows(L, k, chunk, B)
+    fused = fused_index_rows(L, k, chunk, B, G)
     f_k12 = 2.0 * G * dI * float(np.sum((bi * B)[fused]))
     f_attn = 4.0 * r * d * G * attended
     items = float(np.sum(np.ceil(np.asarray(list_counts) / K4_QUERIES))) \

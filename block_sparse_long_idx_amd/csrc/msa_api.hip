@@ -86,14 +86,23 @@ int64_t nblocks(int64_t L) { return (L + kBlock - 1) / kBlock; }
 int nb_padded(int64_t L) { return (int)round_up(std::max<int64_t>(nblocks(L), 1), 8); }
 
 // Index branch of a query chunk [q0, qend): the fused kernel K12 (no block scores in
-// memory) when it serves the shape and the chunk's rows are long and alike -- its
+// memory) when it serves the shape, the chunk's rows are long and alike -- its
 // shortest row has at least as many competitor blocks as the chunk has query
 // blocks, so that its work-groups (one per 64 queries, over all their key blocks)
-// run for similar times and sweep the key tiles together, reusing them from L2.
-// Otherwise K1 (32-block key chunks, L2-friendly for the triangle of short rows)
-// and K2.
+// run for similar times and sweep the key tiles together, reusing them from L2 --
+// and the chunk has enough queries for K12's work-groups to fill the part.
+// Otherwise K1 (32-block key chunks, L2-friendly for the triangle of short rows,
+// and many short items) and K2.
+// MSA_FUSED_INDEX in the environment overrides the rule (read at every chunk): "0"
+// never uses K12, "1" uses it for every chunk whose rows are long, however few
+// work-groups it gets (tests use it to run K12 on small shapes).  The ids are the
+// same either way.
 bool use_k12(int64_t q0, int64_t qend, int G, int dI, int k) {
-    return k12_supported(G, dI, k) && q0 / kBlock >= (qend - q0 + kBlock - 1) / kBlock;
+    const char *e = getenv("MSA_FUSED_INDEX");
+    const int mode = (e && e[0] == '0') ? 0 : (e && e[0] == '1') ? 1 : -1;
+    if (mode == 0 || !k12_supported(G, dI, k)) return false;
+    if (q0 / kBlock < (qend - q0 + kBlock - 1) / kBlock) return false;
+    return mode == 1 || k12_num_workgroups(qend - q0, G) >= kK12MinWorkgroups;
 }
 // Workspace: K12's candidate lists and the block scores of the chunks K1 + K2 serve
 // (with K12 available those chunks end before 2C, which bounds their row length).

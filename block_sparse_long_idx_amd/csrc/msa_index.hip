@@ -439,6 +439,16 @@ bool k12_supported(int G, int dI, int k) {
 
 int64_t k12_cand_entries(int64_t C, int G) { return C * G * kK12Cap; }
 
+int64_t k12_num_workgroups(int64_t C, int G) {
+    const int64_t nqb = (C + kBlock - 1) / kBlock;
+    switch (G) {
+    case 1: return nqb * K1Tiling<1>::P;
+    case 2: return nqb * K1Tiling<2>::P;
+    case 4: return nqb * K1Tiling<4>::P;
+    default: return nqb * K1Tiling<8>::P;
+    }
+}
+
 hipError_t launch_k12_index_select(const uint16_t *iq, const uint16_t *ik, int32_t *ids,
                                    void *cand, int64_t q0, int64_t qend, int G, int dI, int k,
                                    hipStream_t s) {

@@ -37,6 +37,11 @@ hipError_t launch_k1_index_pool(const uint16_t *iq, const uint16_t *ik, float *S
 // 8-byte candidate entries for a chunk of C queries.  Only where k12_supported.
 bool k12_supported(int G, int dI, int k);
 int64_t k12_cand_entries(int64_t C, int G);
+// K12 work-groups of a chunk of C queries (one per 64 queries at G = 4, each over
+// all key blocks of its rows), and the fewest worth a K12 launch: four per CU, so
+// that the long-lived work-groups fill the part.
+int64_t k12_num_workgroups(int64_t C, int G);
+constexpr int64_t kK12MinWorkgroups = 1024;
 hipError_t launch_k12_index_select(const uint16_t *iq, const uint16_t *ik, int32_t *ids,
                                    void *cand, int64_t q0, int64_t qend, int G, int dI, int k,
                                    hipStream_t s);

@@ -40,6 +40,12 @@ def test_prefill_work_matches_closed_forms():
     assert not fused[:131072].any() and fused[131072:].all()
     assert not bench.fused_index_rows(131072, k).any()
     assert not bench.fused_index_rows(1 << 20, 18).any()      # k - 1 > 16: K1 + K2 only
+    # too few work-groups to fill the part: 16384-query chunks (256 at G = 4) stay on
+    # K1 + K2, 65536-query chunks (1024) are fused
+    assert not bench.fused_index_rows(131072, k, chunk=16384).any()
+    f64 = bench.fused_index_rows(262144, k, chunk=65536)
+    assert not f64[:65536].any() and f64[65536:].all()
+    assert not bench.fused_index_rows(262144, k, chunk=65536, G=1).any()   # 512 at G = 1
     assert w["flops"]["k12_index_select"] == 0.0
 
 

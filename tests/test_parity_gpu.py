@@ -4,6 +4,7 @@ CPU oracle on the same seeded inputs.  Block ids bit-exact outside near-ties
 from __future__ import annotations
 
 import math
+import os
 import sys
 
 import numpy as np
@@ -1071,9 +1072,22 @@ def test_fused_selection_matches_two_kernel_path(L, H, G, d, dI, k):
     """The fused index kernel (scores, max-pool and selection in one launch, used for
     query chunks whose rows are long) gives bitwise the ids -- and so the outputs --
     of K1 + K2: a workspace for 1024-query chunks makes every chunk from query 1024
-    on use it, against one whole-sequence chunk served by K1 + K2; and the oracle on
-    sampled rows of the chunked call."""
+    on use it (MSA_FUSED_INDEX=1 lifts the floor on its work-group count that these
+    small chunks miss), against one whole-sequence chunk served by K1 + K2; and the
+    oracle on sampled rows of the chunked call."""
     msa = _msa()
+    old_env = os.environ.get("MSA_FUSED_INDEX")
+    os.environ["MSA_FUSED_INDEX"] = "1"
+    try:
+        _fused_vs_two_kernel(msa, L, H, G, d, dI, k)
+    finally:
+        if old_env is None:
+            os.environ.pop("MSA_FUSED_INDEX", None)
+        else:
+            os.environ["MSA_FUSED_INDEX"] = old_env
+
+
+def _fused_vs_two_kernel(msa, L, H, G, d, dI, k):
     shape = synth.PrefillShape(L=L, H=H, G=G, d=d, dI=dI, B=128, k=k)
     _say(f"fused selection L={L} H={H} G={G} d={d} dI={dI} k={k}")
     x = synth.prefill_inputs(shape, seed=9)
