@@ -93,31 +93,33 @@ int nb_padded(int64_t L) { return (int)round_up(std::max<int64_t>(nblocks(L), 1)
 // and the chunk has enough queries for K12's work-groups to fill the part.
 // Otherwise K1 (32-block key chunks, L2-friendly for the triangle of short rows,
 // and many short items) and K2.
-// MSA_FUSED_INDEX in the environment overrides the rule (read at every chunk): "0"
-// never uses K12, "1" uses it for every chunk whose rows are long, however few
-// work-groups it gets (tests use it to run K12 on small shapes).  The ids are the
-// same either way.
+// MSA_FUSED_INDEX=1 in the environment (read at every chunk) uses K12 for every
+// chunk whose rows are long, however few work-groups it gets (tests use it to run
+// K12 on small shapes).  The ids are the same either way.
 bool use_k12(int64_t q0, int64_t qend, int G, int dI, int k) {
-    const char *e = getenv("MSA_FUSED_INDEX");
-    const int mode = (e && e[0] == '0') ? 0 : (e && e[0] == '1') ? 1 : -1;
-    if (mode == 0 || !k12_supported(G, dI, k)) return false;
+    if (!k12_supported(G, dI, k)) return false;
     if (q0 / kBlock < (qend - q0 + kBlock - 1) / kBlock) return false;
-    return mode == 1 || k12_num_workgroups(qend - q0, G) >= kK12MinWorkgroups;
+    const char *e = getenv("MSA_FUSED_INDEX");
+    return (e && e[0] == '1') || k12_num_workgroups(qend - q0, G) >= kK12MinWorkgroups;
 }
-// Workspace: K12's candidate lists and the block scores of the chunks K1 + K2 serve
-// (with K12 available those chunks end before 2C, which bounds their row length).
+// Workspace: K12's candidate lists and the block scores of the chunks K1 + K2
+// serve.  Where K12 takes the chunks whose rows are long (chunks of C queries give
+// it enough work-groups), K1 serves only chunks that end before 2C, which bounds
+// their rows; otherwise the rows must hold every key block of the sequence.
 struct IndexWs {
     float *S = nullptr;        // K1 + K2
+    int64_t s_floats = 0;      // its capacity
     uint64_t *cand = nullptr;  // K12
 };
 IndexWs carve_index(Carver &c, int64_t C, int64_t L, int G, int dI, int k) {
     IndexWs w;
+    int64_t nb = nb_padded(L);
     if (k12_supported(G, dI, k)) {
         w.cand = c.take<uint64_t>(k12_cand_entries(C, G));
-        w.S = c.take<float>(C * G * nb_padded(std::min(L, 2 * C)));
-    } else {
-        w.S = c.take<float>(C * G * nb_padded(L));
+        if (k12_num_workgroups(C, G) >= kK12MinWorkgroups) nb = nb_padded(std::min(L, 2 * C));
     }
+    w.s_floats = C * G * nb;
+    w.S = c.take<float>(w.s_floats);
     return w;
 }
 size_t select_bytes(int64_t C, int64_t L, int G, int dI, int k) {
@@ -232,12 +234,15 @@ hipError_t timed(int stage, hipStream_t s, F &&launch) {
 // Index branch of queries [q0, qend): ids [(i-q0)*G + g][k] at ids_c.
 int index_chunk(const IndexWs &w, const uint16_t *idx_q, const uint16_t *idx_k, int64_t L,
                 int64_t q0, int64_t qend, int G, int dI, int k, int32_t *ids_c, hipStream_t s) {
-    if (use_k12(q0, qend, G, dI, k)) {
+    // block-score rows of the chunk's own length; K1 + K2 only where the carve holds
+    // them (otherwise K12, which needs no block scores and gives the same ids)
+    const int nbp = k12_supported(G, dI, k) ? nb_padded(qend) : nb_padded(L);
+    const bool k1_fits = (qend - q0) * G * (int64_t)nbp <= w.s_floats;
+    if (use_k12(q0, qend, G, dI, k) || (!k1_fits && k12_supported(G, dI, k))) {
         MSA_TIMED(kK12, launch_k12_index_select(idx_q, idx_k, ids_c, w.cand, q0, qend, G, dI, k, s));
         return MSA_OK;
     }
-    // block-score rows of the chunk's own length (the carve holds them)
-    const int nbp = k12_supported(G, dI, k) ? nb_padded(qend) : nb_padded(L);
+    if (!k1_fits) return MSA_ERR_WORKSPACE_TOO_SMALL;   // unreachable: the carve holds nb_padded(L)
     MSA_TIMED(kK1, launch_k1_index_pool(idx_q, idx_k, w.S, L, q0, qend, G, dI, nbp, s));
     MSA_TIMED(kK2, launch_k2_select(w.S, nbp, (qend - q0) * G, G, k, q0, nullptr, 0, ids_c, s));
     return MSA_OK;

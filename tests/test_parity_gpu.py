@@ -1117,6 +1117,33 @@ def _fused_vs_two_kernel(msa, L, H, G, d, dI, k):
     assert st["max_abs"] < _parity.MAX_ABS and st["mean_abs"] < _parity.MEAN_ABS
 
 
+@pytest.mark.parametrize("frac", [10, 40])
+def test_small_chunks_long_rows_on_k1(frac):
+    """A workspace for a tenth (a fortieth) of the sequence gives query chunks too
+    small for the fused index kernel, so chunks far from the start -- rows much
+    longer than twice the chunk -- are scored by K1 + K2: the block scores must hold
+    every key block.  Ids and outputs bitwise those of one whole-sequence chunk,
+    for msa_prefill and msa_select_blocks."""
+    msa = _msa()
+    shape = synth.PrefillShape(L=40000, H=16, G=4, d=128, dI=128, B=128, k=16)
+    _say(f"small chunks, long rows on K1: L={shape.L} workspace 1/{frac}")
+    x = synth.prefill_inputs(shape, seed=12)
+    dv = {n: t.to(DEV) for n, t in x.items() if isinstance(t, torch.Tensor)}
+    o1, i1 = msa.prefill(dv["q"], dv["k"], dv["v"], dv["iq"], dv["ik"], kslots=shape.k,
+                         return_ids=True)
+    full = msa.workspace_size("prefill", L=shape.L, H=shape.H, G=shape.G, d=shape.d,
+                              dI=shape.dI, k=shape.k)
+    o2, i2 = msa.prefill(dv["q"], dv["k"], dv["v"], dv["iq"], dv["ik"], kslots=shape.k,
+                         return_ids=True, workspace=msa._workspace(full // frac, DEV))
+    sel_full = msa.workspace_size("select", L=shape.L, G=shape.G, dI=shape.dI, k=shape.k)
+    i3 = msa.select_blocks(dv["iq"], dv["ik"], k=shape.k,
+                           workspace=msa._workspace(sel_full // frac, DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert torch.equal(i1, i3)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
 def test_skewed_ids_masks_and_chunking():
     """Constructed skewed ids (blocks 0-3 in nearly every row, so K4's lists of those
     blocks span many tiles) where about 5% of the rows drop block 2, some rows of
