@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     const int run = blockIdx.x / 8;
     const int x = ((run / kK4Run) * 8 + (int)(blockIdx.x % 8)) * kK4Run + run % kK4Run;
     if (x >= tot) return;
-    const int u = order[x];                                  // the work item (tile)
+    const int u = order ? order[x] : x;                      // the work item (tile)
     if ((unsigned)u >= (unsigned)tot) return;                // (order is a permutation)
     const int li = items[u];                                 // list of this tile
     const int g = li / nb, j = li % nb;
@@ -344,13 +344,15 @@ static hipError_t k4_dispatch(const uint16_t *q, const uint16_t *kx, const uint1
     const int64_t grid = round_up(k4_max_items(C, G, k, nb), 8 * kK4Run);
     if (grid == 0) return hipSuccess;
     f32x2 *pml = reinterpret_cast<f32x2 *>(plse);
+    // small chunks have no run order (K3 skips the sort): items in list order
+    const int *order = C <= kK3NoOrderQueries ? nullptr : sb.order;
     if (bm.row_kvpos)
         hipLaunchKernelGGL((k4_kv_outer<D, R, true>), dim3((unsigned)grid), dim3(256), 0, s, q, kx,
-                           vx, sb.offs, sb.toff, sb.total, sb.items, sb.order, sb.list, nb, L, q0, H, G, k,
+                           vx, sb.offs, sb.toff, sb.total, sb.items, order, sb.list, nb, L, q0, H, G, k,
                            scale_log2, po, pml, bm);
     else
         hipLaunchKernelGGL((k4_kv_outer<D, R, false>), dim3((unsigned)grid), dim3(256), 0, s, q, kx,
-                           vx, sb.offs, sb.toff, sb.total, sb.items, sb.order, sb.list, nb, L, q0, H, G, k,
+                           vx, sb.offs, sb.toff, sb.total, sb.items, order, sb.list, nb, L, q0, H, G, k,
                            scale_log2, po, pml, bm);
     return hipGetLastError();
 }

@@ -16,6 +16,9 @@ constexpr int kK4Queries = 128;
 constexpr int kK4Run = 16;
 // Queries whose entries one K3 work-group sorts.
 constexpr int kK3Queries = 2048;
+// Chunks of at most this many queries skip K4's run-order sort (their q rows are
+// few; three launches saved): K4 then runs the items in list order.
+constexpr int64_t kK3NoOrderQueries = 4096;
 // K4 work items that one work-group of K3's tile-ordering passes handles, and the
 // most (group, query window) buckets those passes sort the items into.
 constexpr int kK3Tiles = 4096;

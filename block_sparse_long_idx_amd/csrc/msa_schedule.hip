@@ -364,7 +364,7 @@ hipError_t launch_k3_schedule(const int32_t *ids, int64_t C, int G, int k, int n
     const int nw = (int)((C + (1ll << sh) - 1) >> sh);
     const int nbk = G * nw;
     const int64_t nTW = k3_tile_groups(k4_max_items(C, G, k, nb));
-    if (nTW == 0) return hipSuccess;
+    if (nTW == 0 || C <= kK3NoOrderQueries) return hipSuccess;
     hipLaunchKernelGGL(k3_tile_count, dim3((unsigned)nTW), dim3(256), 0, s, sb.offs, sb.toff,
                        sb.total, sb.items, sb.list, nb, sh, nw, nbk, sb.tcnt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
