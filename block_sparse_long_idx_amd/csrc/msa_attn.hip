@@ -163,6 +163,94 @@ __device__ __forceinline__ void attend_pass(const char *lds_k, const char *lds_v
     else emit(w, mx * scale_log2, sum);
 }
 
+// Decode's attention core on v_mfma_f32_16x16x32_bf16: one query's R <= 16 heads are
+// the 16 columns, so half the arithmetic of the 32-column core above is not spent on
+// empty columns.  Lane l: head n = l % 16, quarter qt = l / 16.  K is staged with
+// k_lds_row<true> (KVStage<..., true>): M-tile mt, register r of quarter qt holds key
+// 32 (mt / 2) + 8 qt + 4 (mt % 2) + r, so M-tiles 2t and 2t + 1 give a lane exactly the
+// P^T operand of keys 32t + 8qt .. 32t + 8qt + 7; V^T is read in key order.
+//   qb    : the head's q row as the B operand: step ks holds d = 32ks + 8qt .. + 7
+//   rel   : the query's position minus the block's first; keys past it are masked
+//   emit  : emit(w, lse, sum) with o normalised by its row sum, w[md] the four bf16
+//           values at d = 16md + 4qt .. + 3 of head n, lse the log2-sum-exp of the
+//           scaled scores
+template <int D>
+__device__ __forceinline__ void load_q16(bf16x8 (&qb)[D / 32], const uint16_t *qrow, int qt) {
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) qb[ks] = as_bf16x8(load16(qrow + (4 * ks + qt) * 8));
+}
+
+template <int D, typename Emit>
+__device__ __forceinline__ void attend16_pass(const char *lds_k, const char *lds_vt,
+                                              const bf16x8 (&qb)[D / 32], bool active, int64_t rel,
+                                              float scale_log2, int lane, Emit emit) {
+    constexpr int CPR = D / 8;
+    const int m = lane & 15, qt = lane >> 4;
+    f32x4 sc[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+        sc[mt] = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const bf16x8 a = as_bf16x8(load16(lds_k + swz<CPR>(16 * mt + m, 4 * ks + qt)));
+            sc[mt] = mfma16(a, qb[ks], sc[mt]);
+        }
+    }
+    // causal mask inside the query's own block
+    const bool local = active && rel < kBlock;
+    if (__ballot(local)) {
+        const int lim = local ? (int)rel : kBlock;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (32 * (mt >> 1) + 8 * qt + 4 * (mt & 1) + r > lim) sc[mt][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[mt][r]);
+    mx = fmaxf(mx, xor_shfl(mx, 16));
+    mx = fmaxf(mx, xor_shfl(mx, 32));
+    const float nmx = -mx * scale_log2;
+    float sum = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sc[mt][r], scale_log2, nmx));
+            sc[mt][r] = p;
+            sum += p;
+        }
+    }
+    sum += xor_shfl(sum, 16);
+    sum += xor_shfl(sum, 32);
+    bf16x8 pb[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+        u32x4 w;
+        w[0] = pack_bf16x2(sc[2 * kt][0], sc[2 * kt][1]);
+        w[1] = pack_bf16x2(sc[2 * kt][2], sc[2 * kt][3]);
+        w[2] = pack_bf16x2(sc[2 * kt + 1][0], sc[2 * kt + 1][1]);
+        w[3] = pack_bf16x2(sc[2 * kt + 1][2], sc[2 * kt + 1][3]);
+        pb[kt] = as_bf16x8(w);
+    }
+    const float inv = 1.0f / sum;
+    u32x2 w[D / 16];
+#pragma unroll
+    for (int md = 0; md < D / 16; ++md) {
+        f32x4 o = f32x4{};
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            const bf16x8 a = as_bf16x8(load16(lds_vt + swz_vt(16 * md + m, 4 * kt + qt)));
+            o = mfma16(a, pb[kt], o);
+        }
+        w[md] = u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+    }
+    emit(w, mx * scale_log2 + __log2f(sum), sum);
+}
+
 // Writes the 32 partial rows of a pass (row = MFMA column, 2D bytes) through the
 // wave's LDS staging buffer, 8 rows per round, so that every global store writes
 // whole rows (CR = D/8 lanes x 16 bytes per row) rather than 32-byte pieces of 32
@@ -423,7 +511,7 @@ __global__ __launch_bounds__(256, 2) void k4d_split(const uint16_t *__restrict__
     if (first >= n_items) return;
     if (wave >= 2) {
         const int stid = tid - 2 * kWave;
-        KVStage<D, 2 * kWave> st;
+        KVStage<D, 2 * kWave, (R <= 16)> st;   // K rows as the attention core reads them
         int64_t item = first;
         int nrows;
         int64_t off = kv_src(item, nrows);
@@ -439,6 +527,42 @@ __global__ __launch_bounds__(256, 2) void k4d_split(const uint16_t *__restrict__
                         reinterpret_cast<const char *>(vc + off), kv_row_bytes, nrows, stid);
             }
             __syncthreads();                       // (B) the item's attention is done
+            item = nxt;
+        }
+    } else if (wave == 0 && R <= 16) {
+        // 16-column core: head n = lane % 16 in every lane quarter; the q rows of an
+        // item are requested before barrier (B) of the previous one.  An inactive
+        // lane reads the group's first head row and its result is discarded.
+        const int n16 = lane & 15, qt = lane >> 4;
+        const bool active = n16 < R;
+        auto q_row = [&](int64_t it) {
+            const int64_t n = it / ((int64_t)G * kslots);
+            const int g = (int)((it / kslots) % G);
+            return q + (n * H + (int64_t)g * R + (active ? n16 : 0)) * D;
+        };
+        bf16x8 qb[D / 32];
+        load_q16<D>(qb, q_row(first), qt);
+        for (int64_t item = first; item < n_items;) {
+            __syncthreads();                       // (A)
+            const int64_t n = item / ((int64_t)G * kslots);
+            const int g = (int)((item / kslots) % G);
+            const int s = (int)(item % kslots);
+            const int j = ids[item];
+            const int64_t p = (int64_t)seq_len[n] - 1;
+            const int64_t hh = (int64_t)g * R + (active ? n16 : 0);
+            const int64_t prow = (n * H + hh) * kslots + s;
+            const int64_t lrow = ((n * G + g) * kslots + s) * R + (active ? n16 : 0);
+            attend16_pass<D>(lds_k, lds_vt, qb, active, p - (int64_t)j * kBlock, scale_log2, lane,
+                             [&](const u32x2 (&w)[D / 16], float lse, float) {
+                                 if (!active) return;
+#pragma unroll
+                                 for (int md = 0; md < D / 16; ++md)
+                                     store8(po + prow * D + 16 * md + 4 * qt, w[md]);
+                                 if (qt == 0) plse[lrow] = lse;
+                             });
+            const int64_t nxt = next_valid(item + gridDim.x);
+            if (nxt < n_items) load_q16<D>(qb, q_row(nxt), qt);
+            __syncthreads();                       // (B)
             item = nxt;
         }
     } else if (wave == 0) {
@@ -633,7 +757,7 @@ __global__ __launch_bounds__(256, 1) void k4d_merge(const uint16_t *__restrict__
     const int first = next_valid(0);
     if (wave >= 2) {
         const int stid = tid - 2 * kWave;
-        KVStage<D, 2 * kWave> st;
+        KVStage<D, 2 * kWave, (R <= 16)> st;   // K rows as the attention core reads them
         int sl = first, nrows;
         if (sl < kslots) {
             int64_t off = kv_src(sl, nrows);
@@ -651,6 +775,27 @@ __global__ __launch_bounds__(256, 1) void k4d_merge(const uint16_t *__restrict__
             }
             __syncthreads();                       // (B) the slot's attention is done
             sl = nxt;
+        }
+    } else if (wave == 0 && R <= 16) {
+        // 16-column core (head n = lane % 16 in every lane quarter); an inactive lane
+        // reads the group's first head row and its result is discarded
+        const int n16 = lane & 15, qt = lane >> 4;
+        const bool active = n16 < R;
+        bf16x8 qb[D / 32];
+        load_q16<D>(qb, q + (n * H + (int64_t)g * R + (active ? n16 : 0)) * D, qt);
+        const int64_t p = (int64_t)seq_len[n] - 1;
+        for (int sl = first; sl < kslots; sl = next_valid(sl + 1)) {
+            __syncthreads();                       // (A)
+            const int j = idr[sl];
+            attend16_pass<D>(lds_k, lds_vt, qb, active, p - (int64_t)j * kBlock, scale_log2, lane,
+                             [&](const u32x2 (&w)[D / 16], float lse, float) {
+                                 if (!active) return;
+#pragma unroll
+                                 for (int md = 0; md < D / 16; ++md)
+                                     store8(&lds_po[sl][n16][16 * md + 4 * qt], w[md]);
+                                 if (qt == 0) lds_l[sl][n16] = lse;
+                             });
+            __syncthreads();                       // (B)
         }
     } else if (wave == 0) {
         // an inactive lane reads the group's first head row; its result is discarded

@@ -129,7 +129,19 @@ __device__ __forceinline__ int swz_vt(int d, int chunk) {
 // so a block costs one memory round trip; store() writes LDS.  Between the two the
 // caller may do other work (the loads stay in flight).  NTHR threads (tid in
 // [0, NTHR)) take part.
-template <int D, int NTHR = 256>
+// LDS row of key `row` in a staged K tile.  32x32 attention (P16 false): bits 2
+// and 3 swapped, so that a lane's S^T accumulators, read 8 at a time, are the P^T
+// operand for 8 consecutive keys.  16x16 attention (P16 true): with
+// key = 32a + 8b + 4c + r (r < 4, c < 2, b < 4) the row is 32a + 16c + 4b + r, so
+// that M-tile 2t + c, register r of lane quarter b holds key 32t + 8b + 4c + r and
+// a lane's two M-tiles of step t give it the keys 32t + 8b .. 32t + 8b + 7.
+template <bool P16>
+__device__ __forceinline__ int k_lds_row(int row) {
+    if constexpr (P16) return (row & 0x63) | (((row >> 3) & 3) << 2) | (((row >> 2) & 1) << 4);
+    else return (row & ~12) | ((row & 4) << 1) | ((row & 8) >> 1);
+}
+
+template <int D, int NTHR = 256, bool P16 = false>
 struct KVStage {
     static constexpr int CPR = D / 8;
     static constexpr int kRowsPerIter = NTHR / CPR;
@@ -165,8 +177,7 @@ struct KVStage {
 #pragma unroll
         for (int it = 0; it < kKIters; ++it) {
             const int row = tid / CPR + it * kRowsPerIter;
-            const int lrow = (row & ~12) | ((row & 4) << 1) | ((row & 8) >> 1);
-            store16(lds_k + swz<CPR>(lrow, c), row <= last ? kr[it] : zero);
+            store16(lds_k + swz<CPR>(k_lds_row<P16>(row), c), row <= last ? kr[it] : zero);
         }
 #pragma unroll
         for (int it = 0; it < kVIters; ++it) {
