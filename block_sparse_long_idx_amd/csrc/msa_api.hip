@@ -83,6 +83,21 @@ AttnWs carve_attn(Carver &c, int64_t C, int H, int G, int d, int k, int nb) {
 
 int64_t chunk_of(int64_t L) { return std::min<int64_t>(round_up(std::max<int64_t>(L, 1), kBlock), kChunkQ); }
 int64_t nblocks(int64_t L) { return (L + kBlock - 1) / kBlock; }
+
+// Valid selection slots over queries at positions [p0, p1): a query in block j has
+// min(k, j + 1) candidate blocks (its own and the earlier ones), the rest are -1.
+int64_t valid_slots(int64_t p0, int64_t p1, int k) {
+    int64_t n = 0;
+    for (int64_t j = p0 / kBlock; j * kBlock < p1; ++j) {
+        const int64_t a = std::max(p0, j * kBlock), b = std::min(p1, (j + 1) * kBlock);
+        n += (b - a) * std::min<int64_t>(k, j + 1);
+    }
+    return n;
+}
+
+// Rows that hold fewer valid slots than empty ones on the whole take K5's grid-stride
+// form (its one round trip per row beats the extra registers it needs).
+bool sparse_rows(int64_t valid, int64_t rows, int k) { return 2 * valid < rows * k; }
 int nb_padded(int64_t L) { return (int)round_up(std::max<int64_t>(nblocks(L), 1), 8); }
 
 // Index branch of a query chunk [q0, qend): the fused kernel K12 (no block scores in
@@ -259,7 +274,7 @@ int attn_chunk(const uint16_t *q, const uint16_t *kx, const uint16_t *vx, const 
     MSA_TIMED(kK4, launch_k4_kv_outer(q, kx, vx, w.sb, nbc, L, q0, C, H, G, d, k, scale, w.po, w.plse,
                                       single, s));
     MSA_TIMED(kK5, launch_k5_combine(w.po, w.plse, ids_c, C, H, G, d, k, nbc, out + q0 * H * d,
-                                     single, true, s));
+                                     single, true, sparse_rows(valid_slots(q0, qend, k), C, k), s));
     return MSA_OK;
 }
 
@@ -278,7 +293,7 @@ int decode_attend(const uint16_t *q, const uint16_t *kc, const uint16_t *vc, con
     MSA_TIMED(kK4d, launch_k4d_split(q, kc, vc, ids, len, table, maxb, N, Lmax, H, G, d, kslots,
                                      scale, po, plse, s));
     MSA_TIMED(kK5, launch_k5_combine(po, plse, ids, N, H, G, d, kslots, 0x7FFFFFFF, out,
-                                     BatchMap{}, false, s));
+                                     BatchMap{}, false, false, s));
     return MSA_OK;
 }
 
@@ -481,7 +496,7 @@ int run_batch(const BatchPlan &b, const uint16_t *q, const uint16_t *k, const ui
     t.rows = (int)b.rows;
     t.blocks = (int)b.blocks;
     const int64_t q_base = cu_q[b.members[0]];
-    int64_t maxL = 0, blk = 0, k1wg = 0;
+    int64_t maxL = 0, blk = 0, k1wg = 0, valid = 0;
     for (int m = 0; m < b.n; ++m) {
         const int sq = b.members[m];
         const int64_t L = cu_kv[sq + 1] - cu_kv[sq], C = cu_q[sq + 1] - cu_q[sq];
@@ -492,6 +507,7 @@ int run_batch(const BatchPlan &b, const uint16_t *q, const uint16_t *k, const ui
         t.kv_len[m] = (int)L;
         blk += nblocks(L);
         k1wg += k1_num_workgroups(L - C, L, G);
+        valid += valid_slots(L - C, L, kslots);
         maxL = std::max(maxL, L);
     }
     t.q_off[b.n] = t.rows;
@@ -525,7 +541,8 @@ int run_batch(const BatchPlan &b, const uint16_t *q, const uint16_t *k, const ui
     MSA_TIMED(kK4, launch_k4_kv_outer(q + q_base * H * d, k, v, w.sb, (int)b.blocks, 0, 0, rows, H,
                                       G, d, kslots, scale, w.po, w.plse, bm, s));
     MSA_TIMED(kK5, launch_k5_combine(w.po, w.plse, ids, rows, H, G, d, kslots, 0,
-                                     out + q_base * H * d, bm, true, s));
+                                     out + q_base * H * d, bm, true,
+                                     sparse_rows(valid, rows, kslots), s));
     return MSA_OK;
 }
 

@@ -959,33 +959,120 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
     else store16_stream(out + ih * D + sub * 8, lse_merge<KMAX>(v, l, ok));
 }
 
+template <int D, int KMAX, bool UNNORM>
+__global__ __launch_bounds__(256) void k5_combine_strided(const uint16_t *__restrict__ po,
+                                                  const float *__restrict__ plse,
+                                                  const int32_t *__restrict__ ids, int64_t nq,
+                                                  int H, int G, int kslots, int nb_lim,
+                                                  uint16_t *__restrict__ out, const BatchMap bm) {
+    constexpr int TPH = D / 8;
+    constexpr int PPW = 256 / TPH;
+    const int64_t n_items = nq * H;
+    const int64_t stride = (int64_t)gridDim.x * PPW;
+    const int sub = threadIdx.x % TPH;
+    const int R = H / G;
+    // Rows with few valid slots (a batch of short sequences) leave k5_combine bound by
+    // two memory round trips per item: ids, then the partials they select.  Here each
+    // thread walks its items with a grid stride, one item ahead: the next item's ids
+    // row (and in a batch its length) are requested with the current item's
+    // partials.  Same merge, bitwise the same output; for full rows the extra
+    // registers (three waves per SIMD instead of four) cost more than it saves.
+    struct Sel {
+        int id[KMAX];
+        int lim;
+    };
+    auto fetch = [&](int64_t it, Sel &x) {
+        const int64_t i = (it < n_items ? it : 0) / H;
+        const int g = (int)((it < n_items ? it : 0) % H) / R;
+        const int32_t *idr = ids + (i * G + g) * kslots;
+        if (kslots == KMAX) {
+            // full rows: ids as 16-byte vectors (rows are 16-byte aligned)
+#pragma unroll
+            for (int s4 = 0; s4 < KMAX / 4; ++s4) {
+                const u32x4 iv = load16(idr + 4 * s4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x.id[4 * s4 + e] = (int)iv[e];
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < KMAX; ++s) x.id[s] = s < kslots ? idr[s] : -1;
+        }
+        // batch: ids are local to the row's sequence and valid up to its own block
+        x.lim = bm.row_len ? (bm.row_len[i] - 1) / kBlock + 1 : nb_lim;
+    };
+    auto step = [&](int64_t ih, const Sel &cur, Sel &nxt) {
+        const int64_t i = ih / H;
+        const int h = (int)(ih % H);
+        const int g = h / R;
+        // slot s at lr[s * R] (normalised partials: log2-sum-exp) or mlr[s * R]
+        // (unnormalised: row maximum and row sum)
+        const float *lr = plse + (i * G + g) * kslots * R + (h - g * R);
+        const f32x2 *mlr = reinterpret_cast<const f32x2 *>(plse) + (i * G + g) * kslots * R + (h - g * R);
+        const uint16_t *pr = po + ih * kslots * D + sub * 8;
+        u32x4 v[KMAX];
+        float l[KMAX];
+        f32x2 ml[KMAX];
+        bool ok[KMAX];
+#pragma unroll
+        for (int s = 0; s < KMAX; ++s) {
+            ok[s] = cur.id[s] >= 0 && cur.id[s] < cur.lim;
+            if constexpr (UNNORM) ml[s] = ok[s] ? mlr[s * R] : f32x2{0.0f, 0.0f};
+            else l[s] = ok[s] ? lr[s * R] : 0.0f;
+            v[s] = ok[s] ? load16_stream(pr + s * D) : u32x4{0, 0, 0, 0};
+        }
+        fetch(ih + stride, nxt);
+        if constexpr (UNNORM) store16_stream(out + ih * D + sub * 8, ml_merge<KMAX>(v, ml, ok));
+        else store16_stream(out + ih * D + sub * 8, lse_merge<KMAX>(v, l, ok));
+    };
+    int64_t ih = (int64_t)blockIdx.x * PPW + threadIdx.x / TPH;
+    Sel sa, sb;
+    fetch(ih, sa);
+    for (; ih < n_items; ih += 2 * stride) {
+        step(ih, sa, sb);
+        if (ih + stride < n_items) step(ih + stride, sb, sa);
+    }
+}
+
+template <int D, int KMAX, bool UNNORM>
+static void k5_launch(const uint16_t *po, const float *plse, const int32_t *ids, int64_t nq,
+                      int H, int G, int k, int nb_lim, uint16_t *out, const BatchMap &bm,
+                      bool sparse_rows, hipStream_t s) {
+    constexpr int PPW = 256 / (D / 8);
+    const int64_t need = (nq * H + PPW - 1) / PPW;
+    if (sparse_rows) {
+        // enough work-groups to fill the part several times over; each thread then
+        // walks its items with a stride
+        constexpr int64_t kMaxGrid = 4096;
+        hipLaunchKernelGGL((k5_combine_strided<D, KMAX, UNNORM>),
+                           dim3((unsigned)(need < kMaxGrid ? need : kMaxGrid)), dim3(256), 0, s,
+                           po, plse, ids, nq, H, G, k, nb_lim, out, bm);
+    } else {
+        hipLaunchKernelGGL((k5_combine<D, KMAX, UNNORM>), dim3((unsigned)need), dim3(256), 0, s,
+                           po, plse, ids, nq, H, G, k, nb_lim, out, bm);
+    }
+}
+
 template <int D, bool UNNORM>
 static hipError_t k5_dispatch(const uint16_t *po, const float *plse, const int32_t *ids,
                               int64_t nq, int H, int G, int k, int nb_lim, uint16_t *out,
-                              const BatchMap &bm, hipStream_t s) {
-    constexpr int PPW = 256 / (D / 8);
-    const dim3 grid((unsigned)((nq * H + PPW - 1) / PPW));
-    if (k <= 4)
-        hipLaunchKernelGGL((k5_combine<D, 4, UNNORM>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
-    else if (k <= 8)
-        hipLaunchKernelGGL((k5_combine<D, 8, UNNORM>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
-    else if (k <= 16)
-        hipLaunchKernelGGL((k5_combine<D, 16, UNNORM>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
-    else
-        hipLaunchKernelGGL((k5_combine<D, 32, UNNORM>), grid, dim3(256), 0, s, po, plse, ids, nq, H, G, k, nb_lim, out, bm);
+                              const BatchMap &bm, bool sparse_rows, hipStream_t s) {
+    if (k <= 4) k5_launch<D, 4, UNNORM>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, sparse_rows, s);
+    else if (k <= 8) k5_launch<D, 8, UNNORM>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, sparse_rows, s);
+    else if (k <= 16) k5_launch<D, 16, UNNORM>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, sparse_rows, s);
+    else k5_launch<D, 32, UNNORM>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, sparse_rows, s);
     return hipGetLastError();
 }
 
 hipError_t launch_k5_combine(const uint16_t *po, const float *plse, const int32_t *ids, int64_t nq,
                              int H, int G, int d, int k, int nb_lim, uint16_t *out,
-                             const BatchMap &bm, bool unnorm, hipStream_t s) {
+                             const BatchMap &bm, bool unnorm, bool sparse_rows, hipStream_t s) {
     if (nq <= 0) return hipSuccess;
     if (d == 64)
-        return unnorm ? k5_dispatch<64, true>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, s)
-                      : k5_dispatch<64, false>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, s);
+        return unnorm ? k5_dispatch<64, true>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, sparse_rows, s)
+                      : k5_dispatch<64, false>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, sparse_rows, s);
     if (d == 128)
-        return unnorm ? k5_dispatch<128, true>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, s)
-                      : k5_dispatch<128, false>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, s);
+        return unnorm ? k5_dispatch<128, true>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, sparse_rows, s)
+                      : k5_dispatch<128, false>(po, plse, ids, nq, H, G, k, nb_lim, out, bm, sparse_rows, s);
     return hipErrorInvalidValue;
 }
 

@@ -164,9 +164,11 @@ hipError_t launch_page_check(const int32_t *table, int maxb, int64_t num_pages,
 // 0 <= id <= b(row) -- the rule K3 scheduled by.  unnorm: the partials are K4's
 // (unnormalised o with (maximum, sum) pairs); else K4d's (normalised o with their
 // log2-sum-exp, plse [((i*G + g)*k + slot)*R + h % R]).
+// sparse_rows: most rows hold few valid slots (a batch of short sequences); then a
+// grid-stride form that requests the next item's ids with the current partials runs.
 hipError_t launch_k5_combine(const uint16_t *po, const float *plse, const int32_t *ids, int64_t nq,
                              int H, int G, int d, int k, int nb_lim, uint16_t *out,
-                             const BatchMap &bm, bool unnorm, hipStream_t s);
+                             const BatchMap &bm, bool unnorm, bool sparse_rows, hipStream_t s);
 
 // Fill n ints with a value (used instead of hipMemsetAsync so calls stay capturable).
 hipError_t launch_fill_i32(int *p, int64_t n, int value, hipStream_t s);
