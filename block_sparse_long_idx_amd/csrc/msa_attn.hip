@@ -251,51 +251,6 @@ __device__ __forceinline__ void attend16_pass(const char *lds_k, const char *lds
     emit(w, mx * scale_log2 + __log2f(sum), sum);
 }
 
-// Writes the 32 partial rows of a pass (row = MFMA column, 2D bytes) through the
-// wave's LDS staging buffer, 8 rows per round, so that every global store writes
-// whole rows (CR = D/8 lanes x 16 bytes per row) rather than 32-byte pieces of 32
-// rows: scattered 32-byte writes cost HBM write bandwidth.  w is attend_pass's
-// chunk layout; row_dst(row) is the destination of a row, nullptr if inactive.
-// The row pitch is padded by 32 bytes so the staging writes are bank-conflict free.
-template <int D>
-constexpr int kStageBytes = 8 * (2 * D + 32);
-
-template <int D, typename RowDst>
-__device__ __forceinline__ void store_rows_staged(char *stg, const u32x4 (&w)[D / 16], int lane,
-                                                  RowDst row_dst) {
-    constexpr int CR = D / 8;
-    constexpr int PITCH = 2 * D + 32;
-    constexpr int NR = 8 * CR / kWave;    // chunks a lane moves per round
-    const int l32 = lane & 31, hf = lane >> 5;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        if ((l32 >> 3) == r) {
-#pragma unroll
-            for (int u = 0; u < D / 16; ++u) {
-                const int c = 4 * (u >> 1) + 2 * (u & 1) + hf;
-                *reinterpret_cast<u32x4 *>(stg + (l32 & 7) * PITCH + 16 * c) = w[u];
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        u32x4 v[NR];
-#pragma unroll
-        for (int x = 0; x < NR; ++x) {
-            const int idx = x * kWave + lane;
-            v[x] = *reinterpret_cast<const u32x4 *>(stg + (idx / CR) * PITCH + 16 * (idx % CR));
-        }
-        // every lane has read this round's rows before the next round overwrites them
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-        for (int x = 0; x < NR; ++x) {
-            const int idx = x * kWave + lane;
-            uint16_t *dst = row_dst(8 * r + idx / CR);
-            if (dst) store16_stream(dst + 8 * (idx % CR), v[x]);
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // K4: KV-outer sparse attention over the scheduled lists.
 // ---------------------------------------------------------------------------
@@ -310,8 +265,6 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
     __shared__ __attribute__((aligned(16))) char lds_vt[D * kBlock * 2];
     static_assert(kK4Queries <= 256, "one entry per thread is staged");
     __shared__ uint32_t lds_e[kK4Queries];                   // the item's (query, slot) entries
-    // whole-row partial stores go through a per-wave LDS staging buffer
-    __shared__ __attribute__((aligned(16))) char lds_stg[4][kStageBytes<D>];
     // XCD-aware order: work-group b runs on XCD b % 8.  Runs of kK4Run consecutive
     // items of the run order (one group, middle entries in one query window) go to
     // the XCDs in turn, so at any time all XCDs gather the q rows of one narrow range
@@ -394,23 +347,24 @@ __global__ __launch_bounds__(256, 2) void k4_kv_outer(
         const int s = in.entry & 31;
         const int64_t lrow = ((il * G + g) * kslots + s) * R + h;
         const bool act = in.act;
-        // partial row of this lane's column (32 bits: every row index fits, see the
-        // launcher), or ~0 for an inactive column; the staged stores fetch each
-        // row's index from the lane that owns its column
-        const uint32_t my_row =
-            act ? ((uint32_t)il * (uint32_t)H + (uint32_t)hh) * (uint32_t)kslots + (uint32_t)s
-                : ~0u;
         attend_pass<D, false>(lds_k, lds_vt, qr, act, BATCH ? (int64_t)in.rel : q0 + il - blk0,
                        scale_log2, lane, [&](const u32x4 (&w)[D / 16], float m, float l) {
 #pragma unroll
                            for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(nqr[ks]));
                            asm volatile("" ::"v"(nin.entry), "v"(nin.rel));
                            if (act && hf == 0) pml[lrow] = f32x2{m, l};
-                           // row = column: query col / R of the pass, head col % R
-                           store_rows_staged<D>(lds_stg[wave], w, lane, [&](int col) -> uint16_t * {
-                               const uint32_t row = (uint32_t)__shfl((int)my_row, col, kWave);
-                               return row == ~0u ? nullptr : po + (size_t)row * D;
-                           });
+                           // The partials of one (query, group, slot) are a block of R
+                           // heads x D/8 chunks of 16 bytes, chunk-major: chunk c of
+                           // head h at (c * R + h) * 16 bytes.  The lane holds chunks
+                           // 2u + hf of its column's head, so the columns of one query
+                           // write 2 * R * 16 contiguous bytes per store instruction --
+                           // whole lines, with no staging through LDS.
+                           if (act) {
+                               uint16_t *dst = po + (size_t)(lrow - h) * D + h * 8;
+#pragma unroll
+                               for (int u = 0; u < D / 16; ++u)
+                                   store16_stream(dst + (2 * u + hf) * (R * 8), w[u]);
+                           }
                        });
     };
     for (int p = 0; p < npass; ++p) {
@@ -451,10 +405,6 @@ hipError_t launch_k4_kv_outer(const uint16_t *q, const uint16_t *kx, const uint1
                               const BatchMap &bm, hipStream_t s) {
     const float sl2 = scale * kLog2e;
     const int R = H / G;
-    // partial rows are indexed with 32 bits inside the kernel (~0 marks none); the
-    // entry points keep C <= 131072 rows per launch, H <= 256 and k <= 32, so
-    // C * H * k < 2^30 -- this check only guards the assumption
-    if (C * H * (int64_t)k >= (int64_t)UINT32_MAX) return hipErrorInvalidValue;
 #define K4_CASE(dd, rr) \
     if (d == dd && R == rr) return k4_dispatch<dd, rr>(q, kx, vx, sb, nb, L, q0, C, H, G, k, sl2, po, plse, bm, s);
     K4_CASE(64, 1) K4_CASE(64, 2) K4_CASE(64, 4) K4_CASE(64, 8) K4_CASE(64, 16) K4_CASE(64, 32)
@@ -891,35 +841,80 @@ bool k4d_merge_supported(int d, int R, int k) {
 }
 
 // ---------------------------------------------------------------------------
-// K5: combine.  D/8 threads per (query, head), 8 d values per thread.  The partials
-// of all valid slots of a thread are requested at once; a slot is valid when
+// K5: combine.  One thread per (query, head, 8 d values).  The partials of all
+// valid slots of a thread are requested at once; a slot is valid when
 // 0 <= id < nb_lim -- the rule K3 used to build the lists -- so stale workspace
 // contents never enter the result, and padding slots (rows with fewer than k
 // selectable blocks) cost no memory traffic.
+//
+// Two partial layouts:
+//   UNNORM (prefill, K4): o unnormalised with (maximum, sum) pairs; the partials of a
+//     (query, group, slot) are one block of R heads x D/8 chunks, chunk-major
+//     (chunk c of head h at (c * R + h) * 16 bytes).  Thread T takes block row
+//     bq = T / (R * D/8) (= query * G + group), chunk c = (T % (R * D/8)) / R and head
+//     h = T % R, so a wave reads whole runs of a block.
+//   !UNNORM (decode's split form): o normalised with its log2-sum-exp; one row of D
+//     per (query, head, slot).  Thread T takes item T / (D/8) = query * H + head,
+//     chunk T % (D/8).
 // ---------------------------------------------------------------------------
+struct K5Map {
+    int64_t bq;        // query * G + group
+    int hl;            // head within the group
+    int c;             // 16-byte chunk of the d values
+};
+
+template <int D, bool UNNORM>
+__device__ __forceinline__ K5Map k5_map(int64_t T, int R) {
+    constexpr int TPH = D / 8;
+    K5Map m;
+    if constexpr (UNNORM) {
+        const int64_t n = (int64_t)R * TPH;
+        m.bq = T / n;
+        const int w = (int)(T - m.bq * n);
+        m.c = w / R;
+        m.hl = w - m.c * R;
+    } else {
+        const int64_t ih = T / TPH;
+        m.c = (int)(T - ih * TPH);
+        m.bq = ih / R;
+        m.hl = (int)(ih - m.bq * R);
+    }
+    return m;
+}
+
+// Where thread m's chunk of slot 0 lives, and the distance between slots.
+template <int D, bool UNNORM>
+__device__ __forceinline__ const uint16_t *k5_partial(const uint16_t *po, const K5Map &m, int R,
+                                                      int kslots, int64_t &slot_stride) {
+    if constexpr (UNNORM) {
+        slot_stride = (int64_t)R * D;
+        return po + m.bq * kslots * R * D + m.c * (R * 8) + m.hl * 8;
+    } else {
+        slot_stride = D;
+        return po + (m.bq * R + m.hl) * kslots * D + m.c * 8;
+    }
+}
+
 template <int D, int KMAX, bool UNNORM>
 __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ po,
                                                   const float *__restrict__ plse,
                                                   const int32_t *__restrict__ ids, int64_t nq,
                                                   int H, int G, int kslots, int nb_lim,
                                                   uint16_t *__restrict__ out, const BatchMap bm) {
-    constexpr int TPH = D / 8;
-    constexpr int PPW = 256 / TPH;
-    const int64_t ih = (int64_t)blockIdx.x * PPW + threadIdx.x / TPH;
-    if (ih >= nq * H) return;
-    const int sub = threadIdx.x % TPH;
-    const int64_t i = ih / H;
-    const int h = (int)(ih % H);
-    const int g = h / (H / G);
     const int R = H / G;
-    const int32_t *idr = ids + (i * G + g) * kslots;
+    const int64_t T = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (T >= nq * H * (D / 8)) return;
+    const K5Map mp = k5_map<D, UNNORM>(T, R);
+    const int64_t i = mp.bq / G;
+    const int32_t *idr = ids + mp.bq * kslots;
     // batch: ids are local to the row's sequence and valid up to its own block
     if (bm.row_len) nb_lim = (bm.row_len[i] - 1) / kBlock + 1;
     // slot s at lr[s * R] (normalised partials: log2-sum-exp) or mlr[s * R]
     // (unnormalised: row maximum and row sum)
-    const float *lr = plse + (i * G + g) * kslots * R + (h - g * R);
-    const f32x2 *mlr = reinterpret_cast<const f32x2 *>(plse) + (i * G + g) * kslots * R + (h - g * R);
-    const uint16_t *pr = po + ih * kslots * D + sub * 8;
+    const float *lr = plse + mp.bq * kslots * R + mp.hl;
+    const f32x2 *mlr = reinterpret_cast<const f32x2 *>(plse) + mp.bq * kslots * R + mp.hl;
+    int64_t ss;
+    const uint16_t *pr = k5_partial<D, UNNORM>(po, mp, R, kslots, ss);
     u32x4 v[KMAX];
     float l[KMAX];
     f32x2 ml[KMAX];
@@ -939,7 +934,7 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
         for (int s = 0; s < KMAX; ++s) {
             if constexpr (UNNORM) ml[s] = ok[s] ? mlr[s * R] : f32x2{0.0f, 0.0f};
             else l[s] = ok[s] ? lr[s * R] : 0.0f;
-            v[s] = ok[s] ? load16_stream(pr + s * D) : u32x4{0, 0, 0, 0};
+            v[s] = ok[s] ? load16_stream(pr + s * ss) : u32x4{0, 0, 0, 0};
         }
     } else {
 #pragma unroll
@@ -949,14 +944,15 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
                 ok[s] = id >= 0 && id < nb_lim;
                 if constexpr (UNNORM) ml[s] = ok[s] ? mlr[s * R] : f32x2{0.0f, 0.0f};
                 else l[s] = ok[s] ? lr[s * R] : 0.0f;
-                v[s] = ok[s] ? load16_stream(pr + s * D) : u32x4{0, 0, 0, 0};
+                v[s] = ok[s] ? load16_stream(pr + s * ss) : u32x4{0, 0, 0, 0};
             } else {
                 ok[s] = false;
             }
         }
     }
-    if constexpr (UNNORM) store16_stream(out + ih * D + sub * 8, ml_merge<KMAX>(v, ml, ok));
-    else store16_stream(out + ih * D + sub * 8, lse_merge<KMAX>(v, l, ok));
+    uint16_t *dst = out + (mp.bq * R + mp.hl) * D + mp.c * 8;
+    if constexpr (UNNORM) store16_stream(dst, ml_merge<KMAX>(v, ml, ok));
+    else store16_stream(dst, lse_merge<KMAX>(v, l, ok));
 }
 
 template <int D, int KMAX, bool UNNORM>
@@ -965,26 +961,22 @@ __global__ __launch_bounds__(256) void k5_combine_strided(const uint16_t *__rest
                                                   const int32_t *__restrict__ ids, int64_t nq,
                                                   int H, int G, int kslots, int nb_lim,
                                                   uint16_t *__restrict__ out, const BatchMap bm) {
-    constexpr int TPH = D / 8;
-    constexpr int PPW = 256 / TPH;
-    const int64_t n_items = nq * H;
-    const int64_t stride = (int64_t)gridDim.x * PPW;
-    const int sub = threadIdx.x % TPH;
+    const int64_t n_thr = nq * H * (D / 8);
+    const int64_t stride = (int64_t)gridDim.x * 256;
     const int R = H / G;
     // Rows with few valid slots (a batch of short sequences) leave k5_combine bound by
-    // two memory round trips per item: ids, then the partials they select.  Here each
-    // thread walks its items with a grid stride, one item ahead: the next item's ids
-    // row (and in a batch its length) are requested with the current item's
+    // two memory round trips per thread: ids, then the partials they select.  Here
+    // each thread walks its shares with a grid stride, one ahead: the next share's ids
+    // row (and in a batch its length) are requested with the current share's
     // partials.  Same merge, bitwise the same output; for full rows the extra
     // registers (three waves per SIMD instead of four) cost more than it saves.
     struct Sel {
         int id[KMAX];
         int lim;
     };
-    auto fetch = [&](int64_t it, Sel &x) {
-        const int64_t i = (it < n_items ? it : 0) / H;
-        const int g = (int)((it < n_items ? it : 0) % H) / R;
-        const int32_t *idr = ids + (i * G + g) * kslots;
+    auto fetch = [&](int64_t T, Sel &x) {
+        const K5Map mp = k5_map<D, UNNORM>(T < n_thr ? T : 0, R);
+        const int32_t *idr = ids + mp.bq * kslots;
         if (kslots == KMAX) {
             // full rows: ids as 16-byte vectors (rows are 16-byte aligned)
 #pragma unroll
@@ -998,17 +990,16 @@ __global__ __launch_bounds__(256) void k5_combine_strided(const uint16_t *__rest
             for (int s = 0; s < KMAX; ++s) x.id[s] = s < kslots ? idr[s] : -1;
         }
         // batch: ids are local to the row's sequence and valid up to its own block
-        x.lim = bm.row_len ? (bm.row_len[i] - 1) / kBlock + 1 : nb_lim;
+        x.lim = bm.row_len ? (bm.row_len[mp.bq / G] - 1) / kBlock + 1 : nb_lim;
     };
-    auto step = [&](int64_t ih, const Sel &cur, Sel &nxt) {
-        const int64_t i = ih / H;
-        const int h = (int)(ih % H);
-        const int g = h / R;
+    auto step = [&](int64_t T, const Sel &cur, Sel &nxt) {
+        const K5Map mp = k5_map<D, UNNORM>(T, R);
         // slot s at lr[s * R] (normalised partials: log2-sum-exp) or mlr[s * R]
         // (unnormalised: row maximum and row sum)
-        const float *lr = plse + (i * G + g) * kslots * R + (h - g * R);
-        const f32x2 *mlr = reinterpret_cast<const f32x2 *>(plse) + (i * G + g) * kslots * R + (h - g * R);
-        const uint16_t *pr = po + ih * kslots * D + sub * 8;
+        const float *lr = plse + mp.bq * kslots * R + mp.hl;
+        const f32x2 *mlr = reinterpret_cast<const f32x2 *>(plse) + mp.bq * kslots * R + mp.hl;
+        int64_t ss;
+        const uint16_t *pr = k5_partial<D, UNNORM>(po, mp, R, kslots, ss);
         u32x4 v[KMAX];
         float l[KMAX];
         f32x2 ml[KMAX];
@@ -1018,18 +1009,19 @@ __global__ __launch_bounds__(256) void k5_combine_strided(const uint16_t *__rest
             ok[s] = cur.id[s] >= 0 && cur.id[s] < cur.lim;
             if constexpr (UNNORM) ml[s] = ok[s] ? mlr[s * R] : f32x2{0.0f, 0.0f};
             else l[s] = ok[s] ? lr[s * R] : 0.0f;
-            v[s] = ok[s] ? load16_stream(pr + s * D) : u32x4{0, 0, 0, 0};
+            v[s] = ok[s] ? load16_stream(pr + s * ss) : u32x4{0, 0, 0, 0};
         }
-        fetch(ih + stride, nxt);
-        if constexpr (UNNORM) store16_stream(out + ih * D + sub * 8, ml_merge<KMAX>(v, ml, ok));
-        else store16_stream(out + ih * D + sub * 8, lse_merge<KMAX>(v, l, ok));
+        fetch(T + stride, nxt);
+        uint16_t *dst = out + (mp.bq * R + mp.hl) * D + mp.c * 8;
+        if constexpr (UNNORM) store16_stream(dst, ml_merge<KMAX>(v, ml, ok));
+        else store16_stream(dst, lse_merge<KMAX>(v, l, ok));
     };
-    int64_t ih = (int64_t)blockIdx.x * PPW + threadIdx.x / TPH;
+    int64_t T = (int64_t)blockIdx.x * 256 + threadIdx.x;
     Sel sa, sb;
-    fetch(ih, sa);
-    for (; ih < n_items; ih += 2 * stride) {
-        step(ih, sa, sb);
-        if (ih + stride < n_items) step(ih + stride, sb, sa);
+    fetch(T, sa);
+    for (; T < n_thr; T += 2 * stride) {
+        step(T, sa, sb);
+        if (T + stride < n_thr) step(T + stride, sb, sa);
     }
 }
 
@@ -1037,8 +1029,7 @@ template <int D, int KMAX, bool UNNORM>
 static void k5_launch(const uint16_t *po, const float *plse, const int32_t *ids, int64_t nq,
                       int H, int G, int k, int nb_lim, uint16_t *out, const BatchMap &bm,
                       bool sparse_rows, hipStream_t s) {
-    constexpr int PPW = 256 / (D / 8);
-    const int64_t need = (nq * H + PPW - 1) / PPW;
+    const int64_t need = (nq * H * (D / 8) + 255) / 256;
     if (sparse_rows) {
         // enough work-groups to fill the part several times over; each thread then
         // walks its items with a stride
