@@ -895,16 +895,12 @@ __device__ __forceinline__ const uint16_t *k5_partial(const uint16_t *po, const 
     }
 }
 
+// The merge of thread T's share (valid and in range), from its partials.
 template <int D, int KMAX, bool UNNORM>
-__global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ po,
-                                                  const float *__restrict__ plse,
-                                                  const int32_t *__restrict__ ids, int64_t nq,
-                                                  int H, int G, int kslots, int nb_lim,
-                                                  uint16_t *__restrict__ out, const BatchMap bm) {
-    const int R = H / G;
-    const int64_t T = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (T >= nq * H * (D / 8)) return;
-    const K5Map mp = k5_map<D, UNNORM>(T, R);
+__device__ __forceinline__ u32x4 k5_share(const uint16_t *__restrict__ po,
+                                          const float *__restrict__ plse,
+                                          const int32_t *__restrict__ ids, const K5Map &mp, int R,
+                                          int G, int kslots, int nb_lim, const BatchMap &bm) {
     const int64_t i = mp.bq / G;
     const int32_t *idr = ids + mp.bq * kslots;
     // batch: ids are local to the row's sequence and valid up to its own block
@@ -950,9 +946,39 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
             }
         }
     }
-    uint16_t *dst = out + (mp.bq * R + mp.hl) * D + mp.c * 8;
-    if constexpr (UNNORM) store16_stream(dst, ml_merge<KMAX>(v, ml, ok));
-    else store16_stream(dst, lse_merge<KMAX>(v, l, ok));
+    if constexpr (UNNORM) return ml_merge<KMAX>(v, ml, ok);
+    else return lse_merge<KMAX>(v, l, ok);
+}
+
+template <int D, int KMAX, bool UNNORM>
+__global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ po,
+                                                  const float *__restrict__ plse,
+                                                  const int32_t *__restrict__ ids, int64_t nq,
+                                                  int H, int G, int kslots, int nb_lim,
+                                                  uint16_t *__restrict__ out, const BatchMap bm) {
+    const int R = H / G;
+    const int64_t T = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t n_thr = nq * H * (D / 8);
+    const bool live = T < n_thr;
+    K5Map mp{0, 0, 0};
+    u32x4 r = {0, 0, 0, 0};
+    if (live) {
+        mp = k5_map<D, UNNORM>(T, R);
+        r = k5_share<D, KMAX, UNNORM>(po, plse, ids, mp, R, G, kslots, nb_lim, bm);
+    }
+    const int64_t o_idx = (mp.bq * R + mp.hl) * (D / 8) + mp.c;   // output chunk
+    // Chunk-major blocks that fit a work-group whole (R * D/8 <= 256, a divisor of
+    // 256) give it the output chunks [256 b, 256 b + 256) -- the same set as its
+    // threads' T, since whole blocks are live or not -- in another order: the
+    // results are exchanged through LDS so that the stores write them contiguously.
+    if (UNNORM && R * (D / 8) <= 256) {
+        __shared__ u32x4 lds_out[256];
+        if (live) lds_out[o_idx - (int64_t)blockIdx.x * 256] = r;
+        __syncthreads();
+        if (live) store16_stream(out + T * 8, lds_out[threadIdx.x]);
+    } else if (live) {
+        store16_stream(out + o_idx * 8, r);
+    }
 }
 
 template <int D, int KMAX, bool UNNORM>
