@@ -972,10 +972,13 @@ __global__ __launch_bounds__(256) void k5_combine(const uint16_t *__restrict__ p
     // threads' T, since whole blocks are live or not -- in another order: the
     // results are exchanged through LDS so that the stores write them contiguously.
     if (UNNORM && R * (D / 8) <= 256) {
-        __shared__ u32x4 lds_out[256];
-        if (live) lds_out[o_idx - (int64_t)blockIdx.x * 256] = r;
+        // one 16-byte pad per 16 entries: the writes (16 heads of one chunk, 256 B
+        // apart) then fall in distinct banks
+        __shared__ u32x4 lds_out[256 + 16];
+        const int e = (int)(o_idx - (int64_t)blockIdx.x * 256);
+        if (live) lds_out[e + (e >> 4)] = r;
         __syncthreads();
-        if (live) store16_stream(out + T * 8, lds_out[threadIdx.x]);
+        if (live) store16_stream(out + T * 8, lds_out[threadIdx.x + (threadIdx.x >> 4)]);
     } else if (live) {
         store16_stream(out + o_idx * 8, r);
     }
