@@ -10,13 +10,16 @@
 //     LDS (V transposed); every wave then takes 32 MFMA columns = 32/R queries x R
 //     heads of the group, gathers their q rows straight into MFMA registers,
 //     computes S^T = K Q^T, the block-local softmax (causal mask only in the query's
-//     own block), O^T = V^T P^T, and writes the normalised partial o (bf16) and its
-//     log2-sum-exp (fp32) to the entry's own (query, head, slot) location.
-// K4d (decode, split over slots): one work item per (sequence, group, slot); a
-//     work-group takes several items and loads the next one's K/V while it attends.
-// K5  (combine, both paths): per (query, head) the partials of its valid slots are
-//     merged with the log-sum-exp rule  out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M),
-//     M = max_s lse_s -- the merge that keeps the softmax exact.
+//     own block), O^T = V^T P^T, and writes the partial o unnormalised (bf16, one
+//     chunk-major block per (query, group, slot)) with its row maximum m and row sum
+//     l (fp32) to the entry's own location.
+// K4d (decode): one work-group per (sequence, group) attends its slots in order and
+//     merges them in LDS; the split form (one work item per (sequence, group, slot),
+//     normalised o with its log2-sum-exp) feeds K5 where the partials do not fit.
+// K5  (combine): per (query, head) the partials of its valid slots are merged with
+//     the log-sum-exp rule  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
+//     M = max_s m_s (for normalised partials l_s = 1 and m_s = lse_s) -- the merge
+//     that keeps the softmax exact.
 //
 // Contraction-index relabelling: the K rows fed as the A operand of S^T are
 // permuted (pi below) so that the S^T accumulators of a lane, read 8 at a time,
