@@ -128,9 +128,11 @@ int k3_num_groups(int64_t C);
 int64_t k3_tile_groups(int64_t max_items);
 
 // K4: KV-outer attention over the scheduled lists -> partials per (query, head,
-// slot): po [(i*H + h)*k + slot][d] bf16 (o NOT normalised), and at pml = plse viewed
-// as float pairs, [((i*G + g)*k + slot)*R + h % R] = (row maximum of the scaled
-// scores in log2 units, row sum of 2^(score - maximum)); plse holds 2*C*H*k floats.
+// slot): po holds one block of R*d bf16 per (query i, group g, slot), at
+// ((i*G + g)*k + slot)*R*d, chunk-major: the 8 values of chunk c (d = 8c .. 8c+7)
+// of head h % R at (c*R + h % R)*8 (o NOT normalised); at pml = plse viewed as
+// float pairs, [((i*G + g)*k + slot)*R + h % R] = (row maximum of the scaled scores
+// in log2 units, row sum of 2^(score - maximum)); plse holds 2*C*H*k floats.
 // With a batch map, q holds the batch's rows (q0 = 0) and the lists are per global
 // block.
 hipError_t launch_k4_kv_outer(const uint16_t *q, const uint16_t *kx, const uint16_t *vx,
@@ -138,7 +140,9 @@ hipError_t launch_k4_kv_outer(const uint16_t *q, const uint16_t *kx, const uint1
                               int H, int G, int d, int k, float scale, uint16_t *po, float *plse,
                               const BatchMap &bm, hipStream_t s);
 
-// K4d: decode split over slots -> partials per (sequence, head, slot).  Cache
+// K4d: decode split over slots -> partials per (sequence, head, slot): rows
+// po [(n*H + h)*k + slot][d] (o normalised) and plse [((n*G + g)*k + slot)*R + h % R]
+// (log2-sum-exp).  Cache
 // addressing as in K1d (kc, vc [N, Lmax, G, d] or pages [pages, 128, G, d]).
 hipError_t launch_k4d_split(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
                             const int32_t *ids, const int32_t *seq_len, const int32_t *table,
