@@ -23,6 +23,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -419,11 +420,26 @@ def gemm_reference(n=8192, reps=20):
     return res
 
 
+def sources_code_hash(paths) -> str:
+    """First 16 hex digits of the SHA-256 of the given source files' code: comments
+    removed and every run of whitespace made one space, so that a change to the
+    comments alone leaves a counter record valid and any change to the code does
+    not."""
+    import hashlib
+    h = hashlib.sha256()
+    for fp in paths:
+        text = open(fp, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
+
+
 def _load_traffic(kernel: str, workload: str):
     """HBM traffic per launch from a committed rocprofv3 counter summary, if one is
     recorded for this kernel and workload and the source files it names (those
     that decide the kernel's code, launch and work list) are unchanged."""
-    import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", f"traffic_{kernel}_{workload}.md")
     if not os.path.exists(path):
@@ -437,13 +453,10 @@ def _load_traffic(kernel: str, workload: str):
     if not files:
         return None
     src = os.path.join(here, "block_sparse_long_idx_amd", "csrc")
-    h = hashlib.sha256()
-    for f in files:
-        fp = os.path.join(src, f)
-        if not os.path.exists(fp):
-            return None
-        h.update(open(fp, "rb").read())
-    if rec.get("sources_sha256_16") != h.hexdigest()[:16]:
+    paths = [os.path.join(src, f) for f in files]
+    if not all(os.path.exists(fp) for fp in paths):
+        return None
+    if rec.get("sources_sha256_16") != sources_code_hash(paths):
         return None
     try:
         return float(rec["hbm_bytes_per_launch"])

@@ -47,7 +47,10 @@ def test_traffic_record_follows_its_sources(tmp_path, monkeypatch):
         files = re.search(r"- sources: (.*)", text).group(1).split()
         h = hashlib.sha256()
         for f in files:
-            h.update(open(os.path.join(ROOT, "block_sparse_long_idx_amd", "csrc", f), "rb").read())
+            code = open(os.path.join(ROOT, "block_sparse_long_idx_amd", "csrc", f)).read()
+            # the code alone: block and line comments out, whitespace runs as one space
+            code = re.sub(r"//[^\n]*", " ", re.sub(r"/\*.*?\*/", " ", code, flags=re.S))
+            h.update(" ".join(code.split()).encode() + b"\0")
         current = re.search(r"- sources_sha256_16: (\w+)", text).group(1) == h.hexdigest()[:16]
         val = bench._load_traffic(kernel, workload)
         # a value exactly when the record matches the sources as they are now
@@ -70,6 +73,17 @@ def test_traffic_record_follows_its_sources(tmp_path, monkeypatch):
     spec.loader.exec_module(mod)
     assert mod._load_traffic("k4_kv_outer", "prefill_L131072") is None
     assert mod._load_traffic("k4_kv_outer", "no_such_workload") is None
+    # the committed record in that copy: valid; still valid after a comment edit to a
+    # source it names; void after a change to that source's code
+    (fake / "profiles" / "traffic_k4_kv_outer_prefill_L131072.md").write_text(src)
+    assert mod._load_traffic("k4_kv_outer", "prefill_L131072") is not None
+    attn = fake / "block_sparse_long_idx_amd" / "csrc" / "msa_attn.hip"
+    code = attn.read_text()
+    attn.write_text("// a new comment line\n/* and a block\n   comment */\n" + code)
+    assert mod._load_traffic("k4_kv_outer", "prefill_L131072") is not None
+    attn.write_text(code.replace("kBlock", "kBlock ", 1).replace("return", "return  ", 1)
+                    .replace("namespace msa {", "namespace msa {\nconstexpr int kUnused = 1;", 1))
+    assert mod._load_traffic("k4_kv_outer", "prefill_L131072") is None
 
 
 def test_every_workload_kind_is_benchmarked():
