@@ -52,7 +52,8 @@ KERNEL_ROOF = {
     "k1_index_pool": "mfma", "k12_index_select": "mfma", "k4_kv_outer": "mfma",
     "k2_select": "hbm", "k3_schedule": "hbm", "k5_combine": "hbm",
     "k1d_index_pool": "hbm", "k1d_index_pool_fp8": "hbm", "k4d_merge": "hbm",
-    "k4d_split": "hbm", "page_check": "hbm", "quantize_e4m3": "hbm",
+    "k4d_split": "hbm", "k4d_online": "hbm", "k4d_parts": "hbm", "page_check": "hbm",
+    "quantize_e4m3": "hbm",
 }
 
 
@@ -146,13 +147,22 @@ def decode_work(N, Lc, H, G, d, dI, k, B=B_BLOCK, paged=False, fp8idx=False):
     if paged:                                          # block-table reads
         small += N * (nb + 1) * 4.0 * 2 + N * G * nsel * 4.0 * 2
     part = N * H * nsel * (2 * d + 4) * 2.0
+    # parts per (sequence, group) of the decode attention (the library's rule: one
+    # launch from 256 (sequence, group) pairs on, else parts for 512 work-groups);
+    # with parts, K5 merges P partials per head
+    P = 1 if N * G >= 256 else min(k, -(-512 // (N * G)))
     k1d = "k1d_index_pool_fp8" if fp8idx else "k1d_index_pool"
     return {
         "bytes": {k1d: idx_bytes + N * G * nb * 4.0,
                   "k4d_split": kv_bytes + N * H * nsel * (d * 2 + 2 * d + 4),
-                  "k2_select": N * G * (nb * 4.0 + k * 4), "k5_combine": part / 2 + N * H * d * 2,
-                  # the merged form: K/V and q in, the output out, partials stay in LDS
-                  "k4d_merge": kv_bytes + N * H * d * 2 * 2},
+                  "k2_select": N * G * (nb * 4.0 + k * 4),
+                  "k5_combine": (N * H * min(P, nsel) * (2 * d + 4) if P > 1 else part / 2)
+                  + N * H * d * 2,
+                  # the one-launch forms: K/V and q in, the output out, partials stay on chip
+                  "k4d_merge": kv_bytes + N * H * d * 2 * 2,
+                  "k4d_online": kv_bytes + N * H * d * 2 * 2,
+                  # in parts: K/V and q in, one normalised partial per (head, part) out
+                  "k4d_parts": kv_bytes + N * H * d * 2 + N * H * min(P, nsel) * (2 * d + 4)},
         "total_bytes": idx_bytes + kv_bytes + small + part,
         "flops": 2.0 * N * G * dI * nb * B + 4.0 * N * H * d * ((nsel - 1) * B + (p % B) + 1),
     }

@@ -32,6 +32,11 @@ using namespace msa;
 
 constexpr int64_t kChunkQ = 131072;    // preferred queries per prefill chunk
 constexpr size_t kAlign = 256;
+// decode attention: one work-group per (sequence, group) once a launch has that many
+// (one per CU of the 256-CU part); fewer pairs split their slots into parts, two
+// work-groups per CU
+constexpr int64_t kDecodeOneLaunchPairs = 256;
+constexpr int64_t kDecodePartWorkGroups = 512;
 
 // Workspace carving: with base == nullptr only the size is accumulated.  With a
 // buffer, `cap` is its size: every entry point checks fits() after carving and
@@ -194,11 +199,13 @@ struct TimedLaunch {
     int name;
     hipEvent_t start, stop;
 };
-enum StageName { kK1, kK2, kK3, kK4, kK5, kK1d, kK4d, kKpc, kK1d8, kQuant, kK4dm, kK12, kNumStages };
+enum StageName { kK1, kK2, kK3, kK4, kK5, kK1d, kK4d, kKpc, kK1d8, kQuant, kK4dm, kK12, kK4do,
+                 kK4dp, kNumStages };
 const char *const kStageNames[kNumStages] = {"k1_index_pool", "k2_select", "k3_schedule",
                                              "k4_kv_outer", "k5_combine", "k1d_index_pool",
                                              "k4d_split", "page_check", "k1d_index_pool_fp8",
-                                             "quantize_e4m3", "k4d_merge", "k12_index_select"};
+                                             "quantize_e4m3", "k4d_merge", "k12_index_select",
+                                             "k4d_online", "k4d_parts"};
 struct Timing {
     bool on = false;
     int cap = 0, used = 0;
@@ -278,13 +285,33 @@ int attn_chunk(const uint16_t *q, const uint16_t *kx, const uint16_t *vx, const 
     return MSA_OK;
 }
 
-// Decode main branch over the selected slots: K4d + K5, or the one launch that
-// merges each (sequence, group)'s slots in LDS where their partials fit (same
-// output bits).  po / plse are the partials' workspace of the two-launch form.
+// Decode main branch over the selected slots.  Up to 16 heads per group: one launch
+// with a running merge per (sequence, group) once there are 256 such pairs, else the
+// slots in parts (two work-groups per CU) merged by K5.  32 heads per group: the
+// launch that merges each (sequence, group)'s slots in LDS where their partials fit,
+// else K4d + K5 (same output bits).  po / plse hold the parts' or the slots' partials,
+// mark the parts' validity.
 int decode_attend(const uint16_t *q, const uint16_t *kc, const uint16_t *vc, const int32_t *ids,
                   const int32_t *len, const int32_t *table, int maxb, int N, int64_t Lmax, int H,
-                  int G, int d, int kslots, float scale, uint16_t *po, float *plse, uint16_t *out,
-                  hipStream_t s) {
+                  int G, int d, int kslots, float scale, uint16_t *po, float *plse, int32_t *mark,
+                  uint16_t *out, hipStream_t s) {
+    if (k4d_online_supported(d, H / G)) {
+        // parts per (sequence, group) for small batches: enough work-groups for two per CU
+        const int64_t ng = (int64_t)N * G;
+        const int P = ng >= kDecodeOneLaunchPairs
+                          ? 1
+                          : (int)std::min<int64_t>(kslots, (kDecodePartWorkGroups + ng - 1) / ng);
+        if (P > 1) {
+            MSA_TIMED(kK4dp, launch_k4d_parts(q, kc, vc, ids, len, table, maxb, N, Lmax, H, G, d,
+                                              kslots, P, scale, po, plse, mark, s));
+            MSA_TIMED(kK5, launch_k5_combine(po, plse, mark, N, H, G, d, P, 1, out, BatchMap{},
+                                             false, false, s));
+            return MSA_OK;
+        }
+        MSA_TIMED(kK4do, launch_k4d_online(q, kc, vc, ids, len, table, maxb, N, Lmax, H, G, d,
+                                           kslots, scale, out, s));
+        return MSA_OK;
+    }
     if (k4d_merge_supported(d, H / G, kslots)) {
         MSA_TIMED(kK4dm, launch_k4d_merge(q, kc, vc, ids, len, table, maxb, N, Lmax, H, G, d,
                                           kslots, scale, out, s));
@@ -646,6 +673,7 @@ size_t msa_decode_workspace_size(int N, int64_t Lmax, int H, int G, int d, int d
     c.take<int32_t>((int64_t)N * G * k);
     c.take<uint16_t>((int64_t)N * H * k * d);
     c.take<float>((int64_t)N * H * k);
+    c.take<int32_t>((int64_t)N * G * k);
     return c.used;
 }
 
@@ -685,13 +713,14 @@ int msa_decode(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_cache
     int32_t *ids_ws = c.take<int32_t>((int64_t)N * G * kslots);
     uint16_t *po = c.take<uint16_t>((int64_t)N * H * kslots * d);
     float *plse = c.take<float>((int64_t)N * H * kslots);
+    int32_t *mark = c.take<int32_t>((int64_t)N * G * kslots);
     MSA_CHECK_CARVE(c);
     int32_t *ids = block_ids_out ? block_ids_out : ids_ws;
     MSA_TIMED(kK1d, launch_k1d_index_pool(idx_q, idx_k_cache, seq_len, nullptr, 0, S, N, Lmax, G,
                                           dI, nbp, s));
     MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, seq_len, Lmax, ids, s));
     return decode_attend(q, k_cache, v_cache, ids, seq_len, nullptr, 0, N, Lmax, H, G, d,
-                         kslots, scale, po, plse, out, s);
+                         kslots, scale, po, plse, mark, out, s);
 }
 
 // ------------------- decode without a caller workspace ---------------------
@@ -787,6 +816,7 @@ int msa_decode_paged(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k
     int32_t *ids_ws = c.take<int32_t>((int64_t)N * G * kslots);
     uint16_t *po = c.take<uint16_t>((int64_t)N * H * kslots * d);
     float *plse = c.take<float>((int64_t)N * H * kslots);
+    int32_t *mark = c.take<int32_t>((int64_t)N * G * kslots);
     int32_t *eff_len = c.take<int32_t>(N);
     MSA_CHECK_CARVE(c);
     int32_t *ids = block_ids_out ? block_ids_out : ids_ws;
@@ -796,7 +826,7 @@ int msa_decode_paged(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k
                                           N, Lmax, G, dI, nbp, s));
     MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, eff_len, Lmax, ids, s));
     return decode_attend(q, k_pages, v_pages, ids, eff_len, block_table, max_blocks, N, Lmax, H,
-                         G, d, kslots, scale, po, plse, out, s);
+                         G, d, kslots, scale, po, plse, mark, out, s);
 }
 
 // ----------------------- FP8 (E4M3) index-key cache ------------------------
@@ -835,13 +865,14 @@ int msa_decode_fp8idx(const uint16_t *q, const uint16_t *idx_q, const uint16_t *
     int32_t *ids_ws = c.take<int32_t>((int64_t)N * G * kslots);
     uint16_t *po = c.take<uint16_t>((int64_t)N * H * kslots * d);
     float *plse = c.take<float>((int64_t)N * H * kslots);
+    int32_t *mark = c.take<int32_t>((int64_t)N * G * kslots);
     MSA_CHECK_CARVE(c);
     int32_t *ids = block_ids_out ? block_ids_out : ids_ws;
     MSA_TIMED(kK1d8, launch_k1d_index_pool_fp8(idx_q, idx_k_e4m3, idx_k_scale, seq_len, nullptr, 0,
                                                S, N, Lmax, G, dI, nbp, s));
     MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, seq_len, Lmax, ids, s));
     return decode_attend(q, k_cache, v_cache, ids, seq_len, nullptr, 0, N, Lmax, H, G, d,
-                         kslots, scale, po, plse, out, s);
+                         kslots, scale, po, plse, mark, out, s);
 }
 
 int msa_decode_paged_fp8idx(const uint16_t *q, const uint16_t *idx_q, const uint16_t *k_pages,
@@ -873,6 +904,7 @@ int msa_decode_paged_fp8idx(const uint16_t *q, const uint16_t *idx_q, const uint
     int32_t *ids_ws = c.take<int32_t>((int64_t)N * G * kslots);
     uint16_t *po = c.take<uint16_t>((int64_t)N * H * kslots * d);
     float *plse = c.take<float>((int64_t)N * H * kslots);
+    int32_t *mark = c.take<int32_t>((int64_t)N * G * kslots);
     int32_t *eff_len = c.take<int32_t>(N);
     MSA_CHECK_CARVE(c);
     int32_t *ids = block_ids_out ? block_ids_out : ids_ws;
@@ -882,7 +914,7 @@ int msa_decode_paged_fp8idx(const uint16_t *q, const uint16_t *idx_q, const uint
                                                block_table, max_blocks, S, N, Lmax, G, dI, nbp, s));
     MSA_TIMED(kK2, launch_k2_select(S, nbp, (int64_t)N * G, G, kslots, 0, eff_len, Lmax, ids, s));
     return decode_attend(q, k_pages, v_pages, ids, eff_len, block_table, max_blocks, N, Lmax, H,
-                         G, d, kslots, scale, po, plse, out, s);
+                         G, d, kslots, scale, po, plse, mark, out, s);
 }
 
 // ------------------------------ timing ------------------------------------

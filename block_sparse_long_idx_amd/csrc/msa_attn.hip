@@ -13,9 +13,13 @@
 //     own block), O^T = V^T P^T, and writes the partial o unnormalised (bf16, one
 //     chunk-major block per (query, group, slot)) with its row maximum m and row sum
 //     l (fp32) to the entry's own location.
-// K4d (decode): one work-group per (sequence, group) attends its slots in order and
-//     merges them in LDS; the split form (one work item per (sequence, group, slot),
-//     normalised o with its log2-sum-exp) feeds K5 where the partials do not fit.
+// K4d (decode), up to 16 heads per group: one work-group per (sequence, group)
+//     attends its slots in order (two K/V buffers, the next slots' K/V in flight) and
+//     folds each into a running log-sum-exp merge in registers (k4d_online); small
+//     batches split each (sequence, group)'s slots into parts, one work-group each,
+//     whose normalised outputs K5 merges (k4d_parts).  32 heads per group: the
+//     slots' partials merged in LDS (k4d_merge), or where they do not fit the split
+//     form (one work item per (sequence, group, slot)) feeding K5.
 // K5  (combine): per (query, head) the partials of its valid slots are merged with
 //     the log-sum-exp rule  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
 //     M = max_s m_s (for normalised partials l_s = 1 and m_s = lse_s) -- the merge
@@ -174,19 +178,20 @@ __device__ __forceinline__ void attend_pass(const char *lds_k, const char *lds_v
 // P^T operand of keys 32t + 8qt .. 32t + 8qt + 7; V^T is read in key order.
 //   qb    : the head's q row as the B operand: step ks holds d = 32ks + 8qt .. + 7
 //   rel   : the query's position minus the block's first; keys past it are masked
-//   emit  : emit(w, lse, sum) with o normalised by its row sum, w[md] the four bf16
-//           values at d = 16md + 4qt .. + 3 of head n, lse the log2-sum-exp of the
-//           scaled scores
+// attend16_core leaves o unnormalised in fp32: o[md] holds d = 16md + 4qt .. + 3 of
+// head n, with the row maximum ms of the scaled scores (log2 units) and the row sum
+// of 2^(score - ms).
 template <int D>
 __device__ __forceinline__ void load_q16(bf16x8 (&qb)[D / 32], const uint16_t *qrow, int qt) {
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) qb[ks] = as_bf16x8(load16(qrow + (4 * ks + qt) * 8));
 }
 
-template <int D, typename Emit>
-__device__ __forceinline__ void attend16_pass(const char *lds_k, const char *lds_vt,
+template <int D>
+__device__ __forceinline__ void attend16_core(const char *lds_k, const char *lds_vt,
                                               const bf16x8 (&qb)[D / 32], bool active, int64_t rel,
-                                              float scale_log2, int lane, Emit emit) {
+                                              float scale_log2, int lane, f32x4 (&o)[D / 16],
+                                              float &ms, float &sum) {
     constexpr int CPR = D / 8;
     const int m = lane & 15, qt = lane >> 4;
     f32x4 sc[8];
@@ -217,7 +222,7 @@ __device__ __forceinline__ void attend16_pass(const char *lds_k, const char *lds
     mx = fmaxf(mx, xor_shfl(mx, 16));
     mx = fmaxf(mx, xor_shfl(mx, 32));
     const float nmx = -mx * scale_log2;
-    float sum = 0.0f;
+    sum = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
@@ -239,19 +244,16 @@ __device__ __forceinline__ void attend16_pass(const char *lds_k, const char *lds
         w[3] = pack_bf16x2(sc[2 * kt + 1][2], sc[2 * kt + 1][3]);
         pb[kt] = as_bf16x8(w);
     }
-    const float inv = 1.0f / sum;
-    u32x2 w[D / 16];
 #pragma unroll
     for (int md = 0; md < D / 16; ++md) {
-        f32x4 o = f32x4{};
+        o[md] = f32x4{};
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             const bf16x8 a = as_bf16x8(load16(lds_vt + swz_vt(16 * md + m, 4 * kt + qt)));
-            o = mfma16(a, pb[kt], o);
+            o[md] = mfma16(a, pb[kt], o[md]);
         }
-        w[md] = u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
     }
-    emit(w, mx * scale_log2 + __log2f(sum), sum);
+    ms = mx * scale_log2;
 }
 
 // ---------------------------------------------------------------------------
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(256, 2) void k4d_split(const uint16_t *__restrict__
     if (first >= n_items) return;
     if (wave >= 2) {
         const int stid = tid - 2 * kWave;
-        KVStage<D, 2 * kWave, (R <= 16)> st;   // K rows as the attention core reads them
+        KVStage<D, 2 * kWave> st;
         int64_t item = first;
         int nrows;
         int64_t off = kv_src(item, nrows);
@@ -480,42 +482,6 @@ __global__ __launch_bounds__(256, 2) void k4d_split(const uint16_t *__restrict__
                         reinterpret_cast<const char *>(vc + off), kv_row_bytes, nrows, stid);
             }
             __syncthreads();                       // (B) the item's attention is done
-            item = nxt;
-        }
-    } else if (wave == 0 && R <= 16) {
-        // 16-column core: head n = lane % 16 in every lane quarter; the q rows of an
-        // item are requested before barrier (B) of the previous one.  An inactive
-        // lane reads the group's first head row and its result is discarded.
-        const int n16 = lane & 15, qt = lane >> 4;
-        const bool active = n16 < R;
-        auto q_row = [&](int64_t it) {
-            const int64_t n = it / ((int64_t)G * kslots);
-            const int g = (int)((it / kslots) % G);
-            return q + (n * H + (int64_t)g * R + (active ? n16 : 0)) * D;
-        };
-        bf16x8 qb[D / 32];
-        load_q16<D>(qb, q_row(first), qt);
-        for (int64_t item = first; item < n_items;) {
-            __syncthreads();                       // (A)
-            const int64_t n = item / ((int64_t)G * kslots);
-            const int g = (int)((item / kslots) % G);
-            const int s = (int)(item % kslots);
-            const int j = ids[item];
-            const int64_t p = (int64_t)seq_len[n] - 1;
-            const int64_t hh = (int64_t)g * R + (active ? n16 : 0);
-            const int64_t prow = (n * H + hh) * kslots + s;
-            const int64_t lrow = ((n * G + g) * kslots + s) * R + (active ? n16 : 0);
-            attend16_pass<D>(lds_k, lds_vt, qb, active, p - (int64_t)j * kBlock, scale_log2, lane,
-                             [&](const u32x2 (&w)[D / 16], float lse, float) {
-                                 if (!active) return;
-#pragma unroll
-                                 for (int md = 0; md < D / 16; ++md)
-                                     store8(po + prow * D + 16 * md + 4 * qt, w[md]);
-                                 if (qt == 0) plse[lrow] = lse;
-                             });
-            const int64_t nxt = next_valid(item + gridDim.x);
-            if (nxt < n_items) load_q16<D>(qb, q_row(nxt), qt);
-            __syncthreads();                       // (B)
             item = nxt;
         }
     } else if (wave == 0) {
@@ -584,8 +550,7 @@ hipError_t launch_k4d_split(const uint16_t *q, const uint16_t *kc, const uint16_
     const int R = H / G;
 #define K4D_CASE(dd, rr) \
     if (d == dd && R == rr) return k4d_dispatch<dd, rr>(q, kc, vc, ids, seq_len, table, maxb, N, Lmax, H, G, k, sl2, po, plse, s);
-    K4D_CASE(64, 1) K4D_CASE(64, 2) K4D_CASE(64, 4) K4D_CASE(64, 8) K4D_CASE(64, 16) K4D_CASE(64, 32)
-    K4D_CASE(128, 1) K4D_CASE(128, 2) K4D_CASE(128, 4) K4D_CASE(128, 8) K4D_CASE(128, 16) K4D_CASE(128, 32)
+    K4D_CASE(64, 32) K4D_CASE(128, 32)
 #undef K4D_CASE
     return hipErrorInvalidValue;
 }
@@ -710,7 +675,7 @@ __global__ __launch_bounds__(256, 1) void k4d_merge(const uint16_t *__restrict__
     const int first = next_valid(0);
     if (wave >= 2) {
         const int stid = tid - 2 * kWave;
-        KVStage<D, 2 * kWave, (R <= 16)> st;   // K rows as the attention core reads them
+        KVStage<D, 2 * kWave> st;
         int sl = first, nrows;
         if (sl < kslots) {
             int64_t off = kv_src(sl, nrows);
@@ -728,27 +693,6 @@ __global__ __launch_bounds__(256, 1) void k4d_merge(const uint16_t *__restrict__
             }
             __syncthreads();                       // (B) the slot's attention is done
             sl = nxt;
-        }
-    } else if (wave == 0 && R <= 16) {
-        // 16-column core (head n = lane % 16 in every lane quarter); an inactive lane
-        // reads the group's first head row and its result is discarded
-        const int n16 = lane & 15, qt = lane >> 4;
-        const bool active = n16 < R;
-        bf16x8 qb[D / 32];
-        load_q16<D>(qb, q + (n * H + (int64_t)g * R + (active ? n16 : 0)) * D, qt);
-        const int64_t p = (int64_t)seq_len[n] - 1;
-        for (int sl = first; sl < kslots; sl = next_valid(sl + 1)) {
-            __syncthreads();                       // (A)
-            const int j = idr[sl];
-            attend16_pass<D>(lds_k, lds_vt, qb, active, p - (int64_t)j * kBlock, scale_log2, lane,
-                             [&](const u32x2 (&w)[D / 16], float lse, float) {
-                                 if (!active) return;
-#pragma unroll
-                                 for (int md = 0; md < D / 16; ++md)
-                                     store8(&lds_po[sl][n16][16 * md + 4 * qt], w[md]);
-                                 if (qt == 0) lds_l[sl][n16] = lse;
-                             });
-            __syncthreads();                       // (B)
         }
     } else if (wave == 0) {
         // an inactive lane reads the group's first head row; its result is discarded
@@ -831,8 +775,7 @@ hipError_t launch_k4d_merge(const uint16_t *q, const uint16_t *kc, const uint16_
     const int R = H / G;
 #define K4DM_CASE(dd, rr) \
     if (d == dd && R == rr) return k4dm_dispatch<dd, rr>(q, kc, vc, ids, seq_len, table, maxb, N, Lmax, H, G, k, sl2, out, s);
-    K4DM_CASE(64, 1) K4DM_CASE(64, 2) K4DM_CASE(64, 4) K4DM_CASE(64, 8) K4DM_CASE(64, 16) K4DM_CASE(64, 32)
-    K4DM_CASE(128, 1) K4DM_CASE(128, 2) K4DM_CASE(128, 4) K4DM_CASE(128, 8) K4DM_CASE(128, 16) K4DM_CASE(128, 32)
+    K4DM_CASE(64, 32) K4DM_CASE(128, 32)
 #undef K4DM_CASE
     return hipErrorNotSupported;
 }
@@ -842,6 +785,280 @@ bool k4d_merge_supported(int d, int R, int k) {
     const int km = k <= 4 ? 4 : (k <= 8 ? 8 : 16);
     return (size_t)km * R * d * 2 + (size_t)km * R * 4 <= kK4dmPartialBytes;
 }
+
+// ---------------------------------------------------------------------------
+// K4d with an online merge, one launch (R <= 16): one work-group per (sequence,
+// group) walks the group's valid slots in slot order with two K/V buffers in LDS.
+// Waves 2-3 stage: each holds two slots' K/V in registers, so that while slot t + 1
+// is stored into the free buffer, slot t + 2 is already in flight, and slot t + 3 is
+// requested as soon as slot t + 1's registers are free.  Wave 0 attends slot t with
+// the 16-column core and keeps a running merge in registers: per head the largest
+// scaled score M seen so far, the sum l of 2^(score - M), and o (fp32,
+// unnormalised).  Each slot's (o_s, m_s, l_s) is folded in with a = 2^(M - M'),
+// b = 2^(m_s - M'), M' = max(M, m_s):  o <- a o + b o_s,  l <- a l + b l_s -- the
+// log-sum-exp merge of the combine, one slot at a time and without rounding a slot's
+// o to bf16.  out = o / l (zeros when no slot is valid).  No partials leave the
+// work-group, so any k fits.  Wave 1 only keeps the barrier count.
+//
+// Barrier t closes step t: before it the stagers have stored the t-th valid slot
+// into buffer t & 1 and wave 0 has finished slot t - 1 (held in the other buffer,
+// which the stagers overwrite only after barrier t).  Every wave meets one barrier
+// per valid slot.
+// ---------------------------------------------------------------------------
+template <int D, int R>
+__global__ __launch_bounds__(256, 1) void k4d_online(const uint16_t *__restrict__ q,
+                                                  const uint16_t *__restrict__ kc,
+                                                  const uint16_t *__restrict__ vc,
+                                                  const int32_t *__restrict__ ids,
+                                                  const int32_t *__restrict__ seq_len,
+                                                  const int32_t *__restrict__ table, int maxb,
+                                                  int64_t Lmax, int H, int G, int kslots,
+                                                  float scale_log2, uint16_t *__restrict__ out) {
+    static_assert(R <= 16, "the 16-column core holds one query's heads");
+    __shared__ __attribute__((aligned(16))) char lds_k[2][kBlock * D * 2];
+    __shared__ __attribute__((aligned(16))) char lds_vt[2][D * kBlock * 2];
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int kv_row_bytes = G * D * 2;
+    const int64_t ng = blockIdx.x;
+    const int64_t n = ng / G;
+    const int g = (int)(ng % G);
+    const int32_t *idr = ids + ng * kslots;
+    auto next_valid = [&](int sl) {
+        for (; sl < kslots; ++sl)
+            if (idr[sl] >= 0) return sl;
+        return kslots;
+    };
+    const int first = next_valid(0);
+    if (wave >= 2) {
+        const int stid = tid - 2 * kWave;
+        using Stage = KVStage<D, 2 * kWave, true>;   // K rows as the 16-column core reads them
+        // request slot sl's block (contiguous cache or its page); rows at and past
+        // seq_len in the own block are staged as zeros (as in K4d)
+        auto request = [&](Stage &x, int sl) {
+            const int j = idr[sl];
+            const int64_t tok0 =
+                table ? (int64_t)table[n * maxb + j] * kBlock : n * Lmax + (int64_t)j * kBlock;
+            const int nrows = (int)max<int64_t>(
+                1, min<int64_t>(kBlock, (int64_t)seq_len[n] - (int64_t)j * kBlock));
+            const int64_t off = (tok0 * G + g) * D;
+            x.load(reinterpret_cast<const char *>(kc + off), reinterpret_cast<const char *>(vc + off),
+                   kv_row_bytes, nrows, stid);
+        };
+        Stage sa_regs, sb_regs;
+        int sa = first;
+        int sb = sa < kslots ? next_valid(sa + 1) : kslots;
+        if (sa < kslots) request(sa_regs, sa);
+        if (sb < kslots) request(sb_regs, sb);
+        int t = 0;
+        while (sa < kslots) {
+            sa_regs.store(lds_k[t & 1], lds_vt[t & 1], stid);
+            const int na = sb < kslots ? next_valid(sb + 1) : kslots;
+            if (na < kslots) request(sa_regs, na);
+            __syncthreads();                       // barrier t
+            ++t;
+            if (sb >= kslots) break;
+            sb_regs.store(lds_k[t & 1], lds_vt[t & 1], stid);
+            const int nb = na < kslots ? next_valid(na + 1) : kslots;
+            if (nb < kslots) request(sb_regs, nb);
+            __syncthreads();                       // barrier t
+            ++t;
+            sa = na;
+            sb = nb;
+        }
+    } else if (wave == 0) {
+        // head n16 = lane % 16 in every lane quarter; an inactive lane reads the
+        // group's first head row and its result is discarded
+        const int n16 = lane & 15, qt = lane >> 4;
+        const bool active = n16 < R;
+        bf16x8 qb[D / 32];
+        load_q16<D>(qb, q + (n * H + (int64_t)g * R + (active ? n16 : 0)) * D, qt);
+        const int64_t p = (int64_t)seq_len[n] - 1;
+        f32x4 acc[D / 16];
+#pragma unroll
+        for (int md = 0; md < D / 16; ++md) acc[md] = f32x4{};
+        float M = -INFINITY, l = 0.0f;
+        for (int sl = first, t = 0; sl < kslots; sl = next_valid(sl + 1), ++t) {
+            __syncthreads();                       // barrier t
+            f32x4 o[D / 16];
+            float ms, ls;
+            attend16_core<D>(lds_k[t & 1], lds_vt[t & 1], qb, active,
+                             p - (int64_t)idr[sl] * kBlock, scale_log2, lane, o, ms, ls);
+            const float Mn = fmaxf(M, ms);
+            const float a = __builtin_amdgcn_exp2f(M - Mn), b = __builtin_amdgcn_exp2f(ms - Mn);
+            l = fmaf(l, a, ls * b);
+#pragma unroll
+            for (int md = 0; md < D / 16; ++md)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[md][e] = fmaf(acc[md][e], a, o[md][e] * b);
+            M = Mn;
+        }
+        if (active) {
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+            uint16_t *dst = out + (n * H + (int64_t)g * R + n16) * D + 4 * qt;
+#pragma unroll
+            for (int md = 0; md < D / 16; ++md)
+                store8(dst + 16 * md, u32x2{pack_bf16x2(acc[md][0] * inv, acc[md][1] * inv),
+                                            pack_bf16x2(acc[md][2] * inv, acc[md][3] * inv)});
+        }
+    } else {
+        for (int sl = first; sl < kslots; sl = next_valid(sl + 1)) __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K4d in parts: the valid slots of a (sequence, group) are split into P parts of
+// consecutive slots, one work-group each (64 KB of LDS: two work-groups per CU), so
+// that twice as many slots are in flight per CU as with one work-group per (sequence,
+// group).  Within a part: waves 2-3 stage the next slot's K/V in registers while
+// wave 0 attends the current one with the 16-column core and folds it into a running
+// merge (as in k4d_online); the part then writes its o normalised (bf16) with its
+// log2-sum-exp, po [((n*H + h)*P + part)*D] and plse [((n*G + g)*P + part)*R + h%R],
+// and marks the part valid (mark = 0) or empty (-1).  K5 merges the parts.
+// ---------------------------------------------------------------------------
+template <int D, int R>
+__global__ __launch_bounds__(256, 2) void k4d_parts(const uint16_t *__restrict__ q,
+                                                 const uint16_t *__restrict__ kc,
+                                                 const uint16_t *__restrict__ vc,
+                                                 const int32_t *__restrict__ ids,
+                                                 const int32_t *__restrict__ seq_len,
+                                                 const int32_t *__restrict__ table, int maxb,
+                                                 int64_t Lmax, int H, int G, int kslots, int P,
+                                                 float scale_log2, uint16_t *__restrict__ po,
+                                                 float *__restrict__ plse, int32_t *__restrict__ mark) {
+    static_assert(R <= 16, "the 16-column core holds one query's heads");
+    __shared__ __attribute__((aligned(16))) char lds_k[kBlock * D * 2];
+    __shared__ __attribute__((aligned(16))) char lds_vt[D * kBlock * 2];
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int kv_row_bytes = G * D * 2;
+    const int64_t ngp = blockIdx.x;
+    const int part = (int)(ngp % P);
+    const int64_t ng = ngp / P;
+    const int64_t n = ng / G;
+    const int g = (int)(ng % G);
+    const int32_t *idr = ids + ng * kslots;
+    const int per = (kslots + P - 1) / P;
+    const int s_end = min(kslots, (part + 1) * per);
+    auto next_valid = [&](int sl) {
+        for (; sl < s_end; ++sl)
+            if (idr[sl] >= 0) return sl;
+        return s_end;
+    };
+    const int first = next_valid(part * per);
+    if (wave >= 2) {
+        const int stid = tid - 2 * kWave;
+        using Stage = KVStage<D, 2 * kWave, true>;   // K rows as the 16-column core reads them
+        // request slot sl's block (contiguous cache or its page); rows at and past
+        // seq_len in the own block are staged as zeros (as in K4d)
+        auto request = [&](Stage &x, int sl) {
+            const int j = idr[sl];
+            const int64_t tok0 =
+                table ? (int64_t)table[n * maxb + j] * kBlock : n * Lmax + (int64_t)j * kBlock;
+            const int nrows = (int)max<int64_t>(
+                1, min<int64_t>(kBlock, (int64_t)seq_len[n] - (int64_t)j * kBlock));
+            const int64_t off = (tok0 * G + g) * D;
+            x.load(reinterpret_cast<const char *>(kc + off), reinterpret_cast<const char *>(vc + off),
+                   kv_row_bytes, nrows, stid);
+        };
+        Stage st;
+        int sl = first;
+        if (sl < s_end) request(st, sl);
+        while (sl < s_end) {
+            st.store(lds_k, lds_vt, stid);
+            __syncthreads();                       // (A) the slot is in LDS
+            const int nxt = next_valid(sl + 1);
+            if (nxt < s_end) request(st, nxt);
+            __syncthreads();                       // (B) the slot's attention is done
+            sl = nxt;
+        }
+    } else if (wave == 0) {
+        // head n16 = lane % 16 in every lane quarter; an inactive lane reads the
+        // group's first head row and its result is discarded
+        const int n16 = lane & 15, qt = lane >> 4;
+        const bool active = n16 < R;
+        bf16x8 qb[D / 32];
+        load_q16<D>(qb, q + (n * H + (int64_t)g * R + (active ? n16 : 0)) * D, qt);
+        const int64_t p = (int64_t)seq_len[n] - 1;
+        f32x4 acc[D / 16];
+#pragma unroll
+        for (int md = 0; md < D / 16; ++md) acc[md] = f32x4{};
+        float M = -INFINITY, l = 0.0f;
+        for (int sl = first; sl < s_end; sl = next_valid(sl + 1)) {
+            __syncthreads();                       // (A)
+            f32x4 o[D / 16];
+            float ms, ls;
+            attend16_core<D>(lds_k, lds_vt, qb, active, p - (int64_t)idr[sl] * kBlock,
+                             scale_log2, lane, o, ms, ls);
+            const float Mn = fmaxf(M, ms);
+            const float a = __builtin_amdgcn_exp2f(M - Mn), b = __builtin_amdgcn_exp2f(ms - Mn);
+            l = fmaf(l, a, ls * b);
+#pragma unroll
+            for (int md = 0; md < D / 16; ++md)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[md][e] = fmaf(acc[md][e], a, o[md][e] * b);
+            M = Mn;
+            __syncthreads();                       // (B)
+        }
+        if (lane == 0) mark[ngp] = first < s_end ? 0 : -1;
+        if (first < s_end && active) {
+            const int64_t h = (int64_t)g * R + n16;
+            const float inv = 1.0f / l;
+            uint16_t *dst = po + ((n * H + h) * P + part) * D + 4 * qt;
+#pragma unroll
+            for (int md = 0; md < D / 16; ++md)
+                store8(dst + 16 * md, u32x2{pack_bf16x2(acc[md][0] * inv, acc[md][1] * inv),
+                                            pack_bf16x2(acc[md][2] * inv, acc[md][3] * inv)});
+            if (qt == 0) plse[(ng * P + part) * R + n16] = M + __log2f(l);
+        }
+    } else {
+        for (int sl = first; sl < s_end; sl = next_valid(sl + 1)) {
+            __syncthreads();                       // (A)
+            __syncthreads();                       // (B)
+        }
+    }
+}
+
+hipError_t launch_k4d_parts(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
+                            const int32_t *ids, const int32_t *seq_len, const int32_t *table,
+                            int maxb, int N, int64_t Lmax, int H, int G, int d, int k, int P,
+                            float scale, uint16_t *po, float *plse, int32_t *mark,
+                            hipStream_t s) {
+    if (N <= 0) return hipSuccess;
+    const float sl2 = scale * kLog2e;
+    const int R = H / G;
+    const dim3 grid((unsigned)((int64_t)N * G * P));
+#define K4DP_CASE(dd, rr)                                                                         \
+    if (d == dd && R == rr) {                                                                    \
+        hipLaunchKernelGGL((k4d_parts<dd, rr>), grid, dim3(256), 0, s, q, kc, vc, ids, seq_len,   \
+                           table, maxb, Lmax, H, G, k, P, sl2, po, plse, mark);                  \
+        return hipGetLastError();                                                                \
+    }
+    K4DP_CASE(64, 1) K4DP_CASE(64, 2) K4DP_CASE(64, 4) K4DP_CASE(64, 8) K4DP_CASE(64, 16)
+    K4DP_CASE(128, 1) K4DP_CASE(128, 2) K4DP_CASE(128, 4) K4DP_CASE(128, 8) K4DP_CASE(128, 16)
+#undef K4DP_CASE
+    return hipErrorNotSupported;
+}
+
+hipError_t launch_k4d_online(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
+                             const int32_t *ids, const int32_t *seq_len, const int32_t *table,
+                             int maxb, int N, int64_t Lmax, int H, int G, int d, int k, float scale,
+                             uint16_t *out, hipStream_t s) {
+    if (N <= 0) return hipSuccess;
+    const float sl2 = scale * kLog2e;
+    const int R = H / G;
+    const dim3 grid((unsigned)((int64_t)N * G));
+#define K4DO_CASE(dd, rr)                                                                         \
+    if (d == dd && R == rr) {                                                                    \
+        hipLaunchKernelGGL((k4d_online<dd, rr>), grid, dim3(256), 0, s, q, kc, vc, ids, seq_len,  \
+                           table, maxb, Lmax, H, G, k, sl2, out);                                \
+        return hipGetLastError();                                                                \
+    }
+    K4DO_CASE(64, 1) K4DO_CASE(64, 2) K4DO_CASE(64, 4) K4DO_CASE(64, 8) K4DO_CASE(64, 16)
+    K4DO_CASE(128, 1) K4DO_CASE(128, 2) K4DO_CASE(128, 4) K4DO_CASE(128, 8) K4DO_CASE(128, 16)
+#undef K4DO_CASE
+    return hipErrorNotSupported;
+}
+
+bool k4d_online_supported(int d, int R) { return (d == 64 || d == 128) && R >= 1 && R <= 16; }
 
 // ---------------------------------------------------------------------------
 // K5: combine.  One thread per (query, head, 8 d values).  The partials of all

@@ -140,7 +140,7 @@ hipError_t launch_k4_kv_outer(const uint16_t *q, const uint16_t *kx, const uint1
                               int H, int G, int d, int k, float scale, uint16_t *po, float *plse,
                               const BatchMap &bm, hipStream_t s);
 
-// K4d: decode split over slots -> partials per (sequence, head, slot): rows
+// K4d for R = H/G = 32: decode split over slots -> partials per (sequence, head, slot): rows
 // po [(n*H + h)*k + slot][d] (o normalised) and plse [((n*G + g)*k + slot)*R + h % R]
 // (log2-sum-exp).  Cache
 // addressing as in K1d (kc, vc [N, Lmax, G, d] or pages [pages, 128, G, d]).
@@ -149,14 +149,34 @@ hipError_t launch_k4d_split(const uint16_t *q, const uint16_t *kc, const uint16_
                             int maxb, int N, int64_t Lmax, int H, int G, int d, int k, float scale,
                             uint16_t *po, float *plse, hipStream_t s);
 
-// K4d and K5 in one launch: one work-group per (sequence, group) attends its valid
-// slots in order and merges them in LDS; out [N, H, d] bitwise as K4d + K5.  Only
-// where k4d_merge_supported(d, H/G, k) (the partials of k slots fit in LDS).
+// K4d and K5 in one launch for R = 32: one work-group per (sequence, group) attends
+// its valid slots in order and merges them in LDS; out [N, H, d] bitwise as K4d + K5.
+// Only where k4d_merge_supported(d, H/G, k) (the partials of k slots fit in LDS).
 bool k4d_merge_supported(int d, int R, int k);
 hipError_t launch_k4d_merge(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
                             const int32_t *ids, const int32_t *seq_len, const int32_t *table,
                             int maxb, int N, int64_t Lmax, int H, int G, int d, int k, float scale,
                             uint16_t *out, hipStream_t s);
+
+// K4d with an online merge, one launch: one work-group per (sequence, group) attends
+// its valid slots in order (two K/V buffers in LDS) and folds each slot into a running
+// log-sum-exp merge held in registers; out [N, H, d].  Any k; R = H/G <= 16
+// (k4d_online_supported).
+bool k4d_online_supported(int d, int R);
+hipError_t launch_k4d_online(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
+                             const int32_t *ids, const int32_t *seq_len, const int32_t *table,
+                             int maxb, int N, int64_t Lmax, int H, int G, int d, int k, float scale,
+                             uint16_t *out, hipStream_t s);
+
+// K4d in P parts of consecutive slots, one work-group each (two per CU): part
+// outputs normalised in po [((n*H + h)*P + part)*d], log2-sum-exp in
+// plse [((n*G + g)*P + part)*R + h % R], mark [(n*G + g)*P + part] = 0 (valid) or -1
+// (no valid slot).  K5 with k = P, nb_lim = 1 and ids = mark merges them.  R <= 16.
+hipError_t launch_k4d_parts(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
+                            const int32_t *ids, const int32_t *seq_len, const int32_t *table,
+                            int maxb, int N, int64_t Lmax, int H, int G, int d, int k, int P,
+                            float scale, uint16_t *po, float *plse, int32_t *mark,
+                            hipStream_t s);
 
 // Paged decode: eff_len[n] = seq_len[n] when 1 <= seq_len[n] <= maxb * 128 and
 // every page id the sequence needs is in [0, num_pages), else 0.

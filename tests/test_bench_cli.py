@@ -73,9 +73,16 @@ def test_traffic_record_follows_its_sources(tmp_path, monkeypatch):
     spec.loader.exec_module(mod)
     assert mod._load_traffic("k4_kv_outer", "prefill_L131072") is None
     assert mod._load_traffic("k4_kv_outer", "no_such_workload") is None
-    # the committed record in that copy: valid; still valid after a comment edit to a
-    # source it names; void after a change to that source's code
-    (fake / "profiles" / "traffic_k4_kv_outer_prefill_L131072.md").write_text(src)
+    # the record stamped with the copy's own sources: valid; still valid after a
+    # comment edit to a source it names; void after a change to that source's code
+    files = re.search(r"- sources: (.*)", src).group(1).split()
+    h = hashlib.sha256()
+    for f in files:
+        code = open(fake / "block_sparse_long_idx_amd" / "csrc" / f).read()
+        code = re.sub(r"//[^\n]*", " ", re.sub(r"/\*.*?\*/", " ", code, flags=re.S))
+        h.update(" ".join(code.split()).encode() + b"\0")
+    fresh = re.sub(r"sources_sha256_16: \w+", "sources_sha256_16: " + h.hexdigest()[:16], src)
+    (fake / "profiles" / "traffic_k4_kv_outer_prefill_L131072.md").write_text(fresh)
     assert mod._load_traffic("k4_kv_outer", "prefill_L131072") is not None
     attn = fake / "block_sparse_long_idx_amd" / "csrc" / "msa_attn.hip"
     code = attn.read_text()

@@ -64,7 +64,7 @@ def test_kernel_roofs():
     assert bench.KERNEL_ROOF["k1_index_pool"] == "mfma"
     assert bench.KERNEL_ROOF["k4_kv_outer"] == "mfma"
     for k in ("k2_select", "k3_schedule", "k5_combine", "k1d_index_pool", "k1d_index_pool_fp8",
-              "k4d_merge", "k4d_split"):
+              "k4d_merge", "k4d_split", "k4d_online", "k4d_parts"):
         assert bench.KERNEL_ROOF[k] == "hbm", k
     L, H, G, d, dI, k = 131072, 64, 4, 128, 128, 16
     w = bench.prefill_work(L, H, G, d, dI, k)

@@ -344,8 +344,26 @@ def test_decode_tiny_dims():
     _decode_check(shape, np.array([4096, 3000, 129, 640, 1]), seed=1)
 
 
-@pytest.mark.parametrize("H,G,d,dI,k", [(64, 8, 64, 64, 8), (16, 1, 128, 128, 16)])
+@pytest.mark.parametrize("N,G,k", [(128, 4, 16), (160, 4, 32), (9, 2, 1)])
+def test_decode_one_launch_attention(N, G, k):
+    """Decode attention in one launch (one work-group per (sequence, group), running
+    merge in registers): the form used once a launch has at least 512 (sequence,
+    group) pairs, or with k = 1; smaller batches split each pair's slots into parts
+    merged by the combine.  Ragged lengths, some past the cache, some of one token."""
+    shape = synth.DecodeShape(N=N, Lc=3000, H=4 * G, G=G, d=128, dI=128, B=128, k=k)
+    rng = np.random.default_rng(N)
+    seq_len = rng.integers(1, shape.Lc + 1, N)
+    seq_len[:4] = [1, 129, shape.Lc, shape.Lc + 7][:min(4, N)]
+    _decode_check(shape, seq_len, seed=N)
+
+
+@pytest.mark.parametrize("H,G,d,dI,k", [(64, 8, 64, 64, 8), (16, 1, 128, 128, 16),
+                                         (32, 1, 128, 128, 4), (64, 2, 128, 128, 16),
+                                         (32, 1, 64, 32, 8)])
 def test_decode_other_groupings(H, G, d, dI, k):
+    """Other head groupings; 32 heads per group run the 32-column decode forms (slots
+    merged in LDS where they fit: k = 4 at d = 128, k = 8 at d = 64; else the split
+    form and the combine: k = 16 at d = 128)."""
     shape = synth.DecodeShape(N=6, Lc=20000, H=H, G=G, d=d, dI=dI, B=128, k=k)
     _decode_check(shape, np.array([20000, 17000, 129, 2048, 1, 9999]), seed=12)
 
