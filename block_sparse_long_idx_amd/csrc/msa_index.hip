@@ -506,7 +506,7 @@ hipError_t launch_k1_index_pool(const uint16_t *iq, const uint16_t *ik, float *S
 // table == nullptr: ikc is [N, Lmax, DI]; otherwise ikc is [pages, 128, DI] and
 // table[n * maxb + b] names the page of block b (checked by the caller).
 // ---------------------------------------------------------------------------
-template <int G, int DI>
+template <int G, int DI, bool PAGED>
 __global__ __launch_bounds__(256) void k1d_index_pool(const uint16_t *__restrict__ iq,
                                                       const uint16_t *__restrict__ ikc,
                                                       const int32_t *__restrict__ seq_len,
@@ -515,7 +515,9 @@ __global__ __launch_bounds__(256) void k1d_index_pool(const uint16_t *__restrict
                                                       int nbp) {
     constexpr int KS = DI / 32;
     const int n = blockIdx.y;
-    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    // the wave index as a wave-uniform value, so that the block and its page-table
+    // entry are read with scalar loads
+    const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int b = blockIdx.x * 4 + wave;
     const int sl = seq_len[n];
     if (sl < 1 || sl > Lmax) return;
@@ -537,6 +539,10 @@ __global__ __launch_bounds__(256) void k1d_index_pool(const uint16_t *__restrict
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             a[mt][ks] = load16(base + (mt * 16 + l16) * DI + 32 * ks + 8 * qt);
+    // paged: every key load of the page issued before the first MFMA (the page id's
+    // read comes first, so the whole page's bytes are requested at once); contiguous
+    // blocks keep the compiler's interleaving, which measures the same or better
+    if constexpr (PAGED) __builtin_amdgcn_sched_barrier(0);
     float m = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
@@ -557,8 +563,12 @@ static hipError_t k1d_dispatch(const uint16_t *iq, const uint16_t *ikc, const in
     const int64_t nbmax = (Lmax - 1) / kBlock;   // competitors of the longest sequence
     if (nbmax <= 0 || N <= 0) return hipSuccess;
     dim3 grid((unsigned)((nbmax + 3) / 4), (unsigned)N);
-    hipLaunchKernelGGL((k1d_index_pool<G, DI>), grid, dim3(256), 0, s, iq, ikc, seq_len, table,
-                       maxb, S, Lmax, nbp);
+    if (table)
+        hipLaunchKernelGGL((k1d_index_pool<G, DI, true>), grid, dim3(256), 0, s, iq, ikc, seq_len,
+                           table, maxb, S, Lmax, nbp);
+    else
+        hipLaunchKernelGGL((k1d_index_pool<G, DI, false>), grid, dim3(256), 0, s, iq, ikc, seq_len,
+                           table, maxb, S, Lmax, nbp);
     return hipGetLastError();
 }
 
@@ -603,7 +613,8 @@ __global__ __launch_bounds__(256) void k1d_index_pool_fp8(const uint16_t *__rest
         return table ? (int64_t)table[n * maxb + b] * kBlock : n * Lmax + (int64_t)b * kBlock;
     };
     const int n = blockIdx.y;
-    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    // wave-uniform, so that the blocks' page-table entries are read with scalar loads
+    const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int b0 = (blockIdx.x * 4 + wave) * BPW;   // this wave's first block
     const int sl = seq_len[n];
     if (sl < 1 || sl > Lmax) return;
