@@ -162,7 +162,8 @@ MSA_API int msa_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint1
  * sequences; sequence n holds seq_len[n] cached tokens and its query is the LAST
  * cached token, position p = seq_len[n] - 1 (the new token is already inserted).
  * The query scores every block of its own cache, selects as in the index branch,
- * and attends over the selected blocks (split over the k slots, then combined).
+ * and attends over the selected blocks (exact softmax over their tokens, the slots
+ * merged by the log-sum-exp rule).
  *   q           [N, H, d]         bf16   query of each sequence
  *   idx_q       [N, G, dI]        bf16
  *   k_cache     [N, Lmax, G, d]   bf16   contiguous per-sequence caches
@@ -285,9 +286,13 @@ MSA_API int msa_quantize_idx_k_e4m3(const uint16_t *idx_k, int64_t rows, int dI,
  * is bracketed by a pair of hipEvents recorded on the caller's stream; stages are
  * named "k1_index_pool", "k2_select", "k3_schedule" (its four small kernels as
  * one), "k4_kv_outer", "k5_combine", "k1d_index_pool", "k4d_split", "page_check",
- * "k1d_index_pool_fp8", "quantize_e4m3", "k4d_merge" (decode's attention with the
- * combine of its slots in the same launch, used where the slots' partials fit in
- * LDS: k <= 16 and k * (H/G) * d * 2 bytes <= 96 KiB), "k12_index_select" (index
+ * "k1d_index_pool_fp8", "quantize_e4m3", "k4d_online" (decode's attention for up to
+ * 16 heads per group: one launch, each slot folded into a running log-sum-exp merge,
+ * used from 256 (sequence, group) pairs on), "k4d_parts" (the same for fewer pairs:
+ * each pair's slots in parts, then "k5_combine" merges the parts), "k4d_merge"
+ * (32 heads per group: the slots' combine in the same launch where their partials
+ * fit in LDS: k <= 16 and k * (H/G) * d * 2 bytes <= 96 KiB; else "k4d_split" and
+ * "k5_combine"), "k12_index_select" (index
  * scores, max-pool and selection in one launch, with no block scores in memory:
  * msa_select_blocks and msa_prefill use it for the query chunks whose shortest row
  * has at least as many competitor blocks as the chunk has query blocks, k <= 17;
