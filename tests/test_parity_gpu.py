@@ -624,15 +624,18 @@ def _poison_past_len(cache: torch.Tensor, seq_len) -> torch.Tensor:
     return c
 
 
-@pytest.mark.parametrize("k,Lc", [(8, 2000), (32, 5000)])
-def test_decode_ignores_rows_past_seq_len(k, Lc):
+@pytest.mark.parametrize("N,k,Lc", [(6, 8, 2000), (6, 32, 5000), (64, 16, 1500)])
+def test_decode_ignores_rows_past_seq_len(N, k, Lc):
     """Cache rows at and past seq_len are not part of the sequence (not yet written):
-    NaN there must change neither the ids nor a single output bit.  k = 8 runs the
-    attention with its combine in one launch, k = 32 the split form plus the combine."""
+    NaN there must change neither the ids nor a single output bit.  Six sequences run
+    the attention in parts merged by the combine; 64 sequences x 4 groups run it in
+    one launch with the running merge."""
     msa = _msa()
-    shape = synth.DecodeShape(N=6, Lc=Lc, H=16, G=4, d=128, dI=128, B=128, k=k)
+    shape = synth.DecodeShape(N=N, Lc=Lc, H=16, G=4, d=128, dI=128, B=128, k=k)
     seq_len = np.array([1, 130, Lc // 2 + 5, Lc - 1, Lc, 700])
-    _say(f"decode NaN past seq_len k={k} Lc={Lc} seq_len={list(seq_len)}")
+    if N > 6:
+        seq_len = np.concatenate([seq_len, np.random.default_rng(N).integers(1, Lc + 1, N - 6)])
+    _say(f"decode NaN past seq_len N={N} k={k} Lc={Lc} seq_len[:8]={list(seq_len[:8])}")
     x = synth.decode_inputs(shape, seed=12, seq_len=seq_len)
     sl = torch.tensor(seq_len.astype(np.int32), device=DEV)
     d = {n: x[n].to(DEV) for n in ("q", "iq", "k_cache", "v_cache", "ik_cache")}
