@@ -384,12 +384,14 @@ def test_decode_full_size_ragged_lengths():
     _decode_check(shape, seq_len, seed=21, device=DEV)
 
 
-def test_decode_full_size_all_sequences():
-    """64 sequences x 262144 cached tokens; oracle on every sequence."""
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_decode_full_size_all_sequences(seed):
+    """64 sequences x 262144 cached tokens (the one-launch attention with its running
+    merge); oracle on every sequence, three seeds."""
     wl = synth.WORKLOADS["decode_N64_L262144"]
     shape = wl.shape
     seq_len = np.full(shape.N, shape.Lc)
-    _decode_check(shape, seq_len, seed=0, device=DEV)
+    _decode_check(shape, seq_len, seed=seed, device=DEV)
 
 
 # ------------------------- varlen / prefix prefill ---------------------------
