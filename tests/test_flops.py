@@ -11,6 +11,37 @@ import numpy as np
 import bench
 
 
+def _page_figures():
+    """tests/golden/page_figures.txt: name -> value (figures the pages print)."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "page_figures.txt")
+    out = {}
+    for line in open(path, encoding="utf-8"):
+        if line.strip() and not line.startswith("#"):
+            name, value, _src = (f.strip() for f in line.split("|", 2))
+            out[name] = float(value)
+    return out
+
+
+def test_page_figures_reproduced():
+    """The accounting and the workload shapes against the figures the pages print
+    (tests/golden/page_figures.txt): the FLOP ratio at their context length and head
+    counts, to the printed precision; k blocks of B tokens = the per-query key budget;
+    the large workloads use the research model's heads, blocks and k."""
+    import synth
+    f = _page_figures()
+    H, G = int(f["query_heads"]), int(f["kv_heads"])
+    kB = int(f["selected_blocks"] * f["block_tokens"])
+    assert kB == f["max_keys_per_query"]
+    r = bench.paper_flop_ratio(H=H, G=G, d=128, dI=128, L=int(f["context_tokens"]), kB=kB)
+    assert round(r, 1) == f["attention_flop_ratio_vs_gqa"]
+    for name in ("prefill_L32768", "prefill_L131072", "prefill_L1048576_hot",
+                 "decode_N64_L262144"):
+        s = synth.WORKLOADS[name].shape
+        assert (s.H, s.G, s.B, s.k) == (H, G, int(f["block_tokens"]), int(f["selected_blocks"]))
+    assert synth.WORKLOADS["prefill_L1048576_hot"].shape.L == int(f["context_tokens"])
+
+
 def test_paper_ratio_28_4():
     r = bench.paper_flop_ratio(H=64, G=4, d=128, dI=128, L=1 << 20, kB=2048)
     assert round(r, 1) == 28.4
