@@ -53,7 +53,7 @@ KERNEL_ROOF = {
     "k2_select": "hbm", "k3_schedule": "hbm", "k5_combine": "hbm",
     "k1d_index_pool": "hbm", "k1d_index_pool_fp8": "hbm", "k4d_merge": "hbm",
     "k4d_split": "hbm", "k4d_online": "hbm", "k4d_parts": "hbm", "page_check": "hbm",
-    "quantize_e4m3": "hbm",
+    "quantize_e4m3": "hbm", "kd_dense": "mfma",
 }
 
 
@@ -88,7 +88,7 @@ def fused_index_rows(L, k, chunk=131072, B=B_BLOCK, G=4):
     return fused
 
 
-def prefill_work(L, H, G, d, dI, k, B=B_BLOCK, list_counts=None, chunk=131072):
+def prefill_work(L, H, G, d, dI, k, B=B_BLOCK, list_counts=None, chunk=131072, dense_main=True):
     """Algorithmic FLOPs and bytes of each prefill kernel over one whole step.
 
     K1 scores every competitor key of every (query, group): 2*G*dI FLOP per
@@ -99,6 +99,12 @@ def prefill_work(L, H, G, d, dI, k, B=B_BLOCK, list_counts=None, chunk=131072):
     from K1 to K2; K4's gathered q rows, partial rows and staged K/V blocks) and are
     reported apart, under "design_bytes".  The HBM-bound kernels K2, K3 and K5 are
     measured by their bytes.
+
+    A sequence of at most k blocks selects every causal block of every query
+    whatever the scores, so the library runs its main branch as dense causal
+    attention (kd_dense) without the index branch: its work is the attention's
+    4*r*d FLOP per (query, group, causal key), and no index FLOPs.  The call on
+    given ids (dense_main=False) always runs the KV-outer kernels.
     """
     r = H // G
     i = np.arange(L, dtype=np.int64)
@@ -106,6 +112,20 @@ def prefill_work(L, H, G, d, dI, k, B=B_BLOCK, list_counts=None, chunk=131072):
     nsel = np.minimum(k, bi + 1)
     pairs = float(np.sum(bi * B))                                     # scored (query, key)
     attended = float(np.sum((nsel - 1) * B + (i - bi * B + 1)))       # per group
+    dense_gqa = 4.0 * H * d * float(np.sum(i + 1))
+    if dense_main and L <= k * B:
+        tile = 4 * (32 // r)                      # queries per kd_dense work-group
+        tiles = -(-L // tile)
+        staged = sum(((t * tile) // B + 1) for t in range(tiles)) * G * 2 * B * d * 2.0
+        return {
+            "flops": {"kd_dense": dense_gqa},
+            "bytes": {},
+            "design_bytes": {"kd_dense": {"q_in": L * H * d * 2.0, "out": L * H * d * 2.0,
+                                          "ids_out": 4.0 * L * G * k,
+                                          "kv_blocks_staged": staged}},
+            "pairs": 0.0, "attended_per_group": attended, "entries": float(np.sum(nsel)) * G,
+            "f_total": dense_gqa, "dense_gqa_flops": dense_gqa,
+        }
     entries = float(np.sum(nsel)) * G                                 # (query, group, slot)
     f_idx = 2.0 * G * dI * pairs
     fused = fused_index_rows(L, k, chunk, B, G)
@@ -132,7 +152,7 @@ def prefill_work(L, H, G, d, dI, k, B=B_BLOCK, list_counts=None, chunk=131072):
                             "kv_blocks_staged": items * 2 * B * d * 2.0}},
         "pairs": pairs, "attended_per_group": attended, "entries": entries,
         "f_total": f_idx + f_attn,
-        "dense_gqa_flops": 4.0 * H * d * float(np.sum(i + 1)),
+        "dense_gqa_flops": dense_gqa,
     }
 
 
@@ -634,7 +654,8 @@ def run_workload(args, name, steps, warmup, cpu_baseline, dense):
             g_idx = np.broadcast_to(np.arange(s.G)[None, :, None], idn[b].shape)
             counts = np.bincount((g_idx[valid] * ((s.L + 127) // 128) + idn[b][valid]).ravel(),
                                  minlength=s.G * ((s.L + 127) // 128))
-            w_b = prefill_work(s.L, s.H, s.G, s.d, s.dI, s.k, list_counts=counts)
+            w_b = prefill_work(s.L, s.H, s.G, s.d, s.dI, s.k, list_counts=counts,
+                               dense_main=wl.kind != "sparse_attn")
             work = w_b if work is None else _add_work(work, w_b)
         result.update({"value": nseq * s.L / (ms_per_step / 1e3), "unit": "tokens/s",
                        "higher_is_better": True})

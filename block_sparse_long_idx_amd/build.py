@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
-SOURCES = ["msa_index.hip", "msa_select.hip", "msa_schedule.hip", "msa_attn.hip", "msa_api.hip"]
+SOURCES = ["msa_index.hip", "msa_select.hip", "msa_schedule.hip", "msa_attn.hip", "msa_dense.hip",
+           "msa_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

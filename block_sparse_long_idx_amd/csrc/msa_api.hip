@@ -200,12 +200,12 @@ struct TimedLaunch {
     hipEvent_t start, stop;
 };
 enum StageName { kK1, kK2, kK3, kK4, kK5, kK1d, kK4d, kKpc, kK1d8, kQuant, kK4dm, kK12, kK4do,
-                 kK4dp, kNumStages };
+                 kK4dp, kKd, kNumStages };
 const char *const kStageNames[kNumStages] = {"k1_index_pool", "k2_select", "k3_schedule",
                                              "k4_kv_outer", "k5_combine", "k1d_index_pool",
                                              "k4d_split", "page_check", "k1d_index_pool_fp8",
                                              "quantize_e4m3", "k4d_merge", "k12_index_select",
-                                             "k4d_online", "k4d_parts"};
+                                             "k4d_online", "k4d_parts", "kd_dense"};
 struct Timing {
     bool on = false;
     int cap = 0, used = 0;
@@ -413,6 +413,70 @@ size_t msa_prefill_workspace_size(int64_t L, int H, int G, int d, int dI, int B,
 
 namespace {
 
+// A sequence of at most k blocks keeps every causal block for every query (its own
+// block and all earlier ones are at most k): its main branch is dense causal
+// attention, run by kd_dense with no index branch, lists or partials.
+bool dense_sequence(int64_t L, int kslots) { return L <= (int64_t)kslots * kBlock; }
+
+// Packs dense sequences into launches of kd_dense: add() one sequence at a time (its
+// new queries at row q_row0 of q / out / ids, its tokens at row kv_row0 of k / v,
+// L tokens of which the first P are a cached prefix), then finish().  Row offsets
+// inside one launch are relative to its first member's rows and fit 32 bits.
+struct DenseLauncher {
+    const uint16_t *q, *k, *v;
+    uint16_t *out;
+    int32_t *ids;
+    int H, G, d, kslots;
+    float scale;
+    hipStream_t s;
+    DenseTable t;
+    int64_t q_base = 0, kv_base = 0;
+    int tiles = 0;
+    int status = MSA_OK;
+
+    void flush() {
+        if (t.n == 0) return;
+        t.tile_off[t.n] = tiles;
+        const hipError_t e = timed(kKd, s, [&]() {
+            return launch_kd_dense(q + q_base * H * d, k + kv_base * G * d, v + kv_base * G * d,
+                                   out + q_base * H * d, ids ? ids + q_base * G * kslots : nullptr,
+                                   t, H, G, d, kslots, scale, s);
+        });
+        if (e != hipSuccess && status == MSA_OK) status = MSA_ERR_HIP;
+        t.n = 0;
+        tiles = 0;
+    }
+    void add(int64_t q_row0, int64_t kv_row0, int64_t L, int64_t P) {
+        const int tq = dense_tile_queries(H, G);
+        const int64_t nt = (L - P + tq - 1) / tq;
+        for (int pass = 0; pass < 2; ++pass) {
+            if (t.n == 0) {
+                q_base = q_row0;
+                kv_base = kv_row0;
+            }
+            const int64_t dq = q_row0 - q_base, dk = kv_row0 - kv_base;
+            const bool fits = t.n < kBatchMaxSeq && dq >= 0 && dk >= 0 &&
+                              dq + (L - P) <= INT32_MAX && dk + L <= INT32_MAX &&
+                              ((int64_t)tiles + nt) * G <= INT32_MAX;
+            if (fits) {
+                t.tile_off[t.n] = tiles;
+                t.q_row0[t.n] = (int)dq;
+                t.kv_row0[t.n] = (int)dk;
+                t.len[t.n] = (int)L;
+                t.prefix[t.n] = (int)P;
+                ++t.n;
+                tiles += (int)nt;
+                return;
+            }
+            flush();   // a full launch: the sequence opens the next one
+        }
+    }
+    int finish() {
+        flush();
+        return status;
+    }
+};
+
 // Queries [P, L) of one causal sequence of L tokens (P a multiple of the chunk
 // granularity): K1..K5 per query chunk.  q, idx_q, out and ids are addressed by
 // absolute position (row i of the sequence at q + i*H*d); only rows >= P are
@@ -469,7 +533,9 @@ size_t batch_bytes(int64_t rows, int64_t blocks, int nbp, int H, int G, int d, i
 }
 
 // Greedy batching, in sequence order: a sequence with at most kBatchMaxNew new
-// tokens joins the open batch while the batch stays within kBatchMaxSeq sequences,
+// tokens joins the open batch while the batch stays within kBatchMaxSeq sequences
+// and follows the batch's last rows (a sequence of at most k blocks, which runs the
+// dense main branch instead, ends the open batch),
 // kChunkQ rows, kBatchMaxBlocks blocks and `ws_limit` bytes; a longer sequence
 // runs alone (measured: alone, the q rows of one long sequence stay in the
 // last-level cache across the attention's 16 re-reads of each row, which beats
@@ -491,6 +557,16 @@ int plan_batches(const int64_t *cu_q, const int64_t *cu_kv, int nseq, int H, int
     for (int sq = 0; sq < nseq; ++sq) {
         const int64_t C = cu_q[sq + 1] - cu_q[sq], L = cu_kv[sq + 1] - cu_kv[sq];
         if (C == 0) continue;
+        if (dense_sequence(L, k)) {
+            // dense sequences run apart (kd_dense); a batch's rows are contiguous, so
+            // the open batch ends before this sequence's rows
+            if (b.n > 0) {
+                const int rc = run(b);
+                if (rc != MSA_OK) return rc;
+                b = BatchPlan{};
+            }
+            continue;
+        }
         const bool batchable = allow_batch && C <= kBatchMaxNew;
         if (b.n > 0) {
             const int64_t rows = b.rows + C, blocks = b.blocks + nblocks(L);
@@ -591,6 +667,12 @@ int msa_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
     if (check_ptr(ws) != MSA_OK) return MSA_ERR_WORKSPACE_TOO_SMALL;
     if (fit_chunk(L, ws_bytes, [&](int64_t c) { return prefill_bytes(c, L, H, G, d, dI, kslots); }) == 0)
         return MSA_ERR_WORKSPACE_TOO_SMALL;
+    if (dense_sequence(L, kslots)) {
+        DenseLauncher dl{q, k, v, out, block_ids_out, H, G, d, kslots, default_scale(scale, d),
+                         static_cast<hipStream_t>(stream)};
+        dl.add(0, 0, L, 0);
+        return dl.finish();
+    }
     return prefill_range(q, k, v, idx_q, idx_k, L, 0, H, G, d, dI, kslots, default_scale(scale, d),
                          out, block_ids_out, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
@@ -637,6 +719,15 @@ int msa_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                              idx_k + cu_kv[sq] * dI, L, P, H, G, d, dI, kslots, scale,
                              rows_back(out, back, (int64_t)H * d), ids, ws, ws_bytes, s);
     };
+    {
+        DenseLauncher dl{q, k, v, out, block_ids_out, H, G, d, kslots, scale, s};
+        for (int sq = 0; sq < nseq; ++sq) {
+            const int64_t C = cu_q[sq + 1] - cu_q[sq], L = cu_kv[sq + 1] - cu_kv[sq];
+            if (C > 0 && dense_sequence(L, kslots)) dl.add(cu_q[sq], cu_kv[sq], L, L - C);
+        }
+        const int rc = dl.finish();
+        if (rc != MSA_OK) return rc;
+    }
     return plan_batches(cu_q, cu_kv, nseq, H, G, d, kslots, ws_bytes, allow_batch,
                         [&](const BatchPlan &b) {
                             if (b.n == 1) return one_sequence(b.members[0]);

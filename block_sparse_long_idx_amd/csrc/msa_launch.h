@@ -96,6 +96,25 @@ struct BatchTable {
     int kv_off[kBatchMaxSeq];        // absolute first K/V token of each sequence
     int kv_len[kBatchMaxSeq];        // its tokens, cached prefix + new
 };
+// Dense main branch of sequences of at most k blocks (their selection is every
+// causal block): up to kBatchMaxSeq sequences per launch.  Member m's new queries are
+// positions prefix[m] .. len[m]-1 of its sequence (prefix a multiple of 128), at rows
+// q_row0[m] .. of q / out / ids; its keys are rows kv_row0[m] .. + len[m]-1 of k / v.
+// tile_off: prefix sum of the work-groups' query tiles (dense_tile_queries queries
+// each) over the members.
+struct DenseTable {
+    int n = 0;
+    int tile_off[kBatchMaxSeq + 1];
+    int q_row0[kBatchMaxSeq];
+    int kv_row0[kBatchMaxSeq];
+    int len[kBatchMaxSeq];
+    int prefix[kBatchMaxSeq];
+};
+int dense_tile_queries(int H, int G);
+// out [rows, H, d] and, when ids is not null, ids [rows, G, k] (0 .. b(i), then -1).
+hipError_t launch_kd_dense(const uint16_t *q, const uint16_t *kx, const uint16_t *vx,
+                           uint16_t *out, int32_t *ids, const DenseTable &t, int H, int G, int d,
+                           int k, float scale, hipStream_t s);
 hipError_t launch_batch_setup(const BatchTable &t, BatchTable *dtab, int32_t *row_len,
                               int32_t *row_kvpos, int32_t *row_blk0, int32_t *blk_tok0,
                               int32_t *blk_rows, hipStream_t s);

@@ -116,6 +116,13 @@ MSA_API int msa_sparse_attn(const uint16_t *q, const uint16_t *k, const uint16_t
 /* ---------------------------------------------------------------------------
  * Whole prefill: msa_select_blocks followed by msa_sparse_attn on the same rows.
  * block_ids_out [L, G, k] may be NULL (the ids then live only in the workspace).
+ * A sequence of at most kslots blocks (L <= kslots * B) keeps every causal block of
+ * every row whatever the scores [M3-20x §二 Index Branch, §三 item 4], so its
+ * selection is blocks 0 .. b(i) (ascending, then -1) and its main branch is dense
+ * causal GQA attention: such a call runs one kernel ("kd_dense") that attends each
+ * query over its causal blocks with an online softmax and writes those ids; the
+ * index inputs are not read.  The outputs equal the general path's up to fp32
+ * rounding order (the ids are the same).
  * ------------------------------------------------------------------------- */
 MSA_API size_t msa_prefill_workspace_size(int64_t L, int H, int G, int d, int dI, int B, int k);
 MSA_API int msa_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *idx_q,
@@ -143,6 +150,8 @@ MSA_API int msa_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  * as far as the workspace holds them), every kernel of the path launched once per
  * batch.  Longer sequences,
  * and any that no batch can take, run alone in query chunks like msa_prefill.
+ * Sequences of at most kslots blocks run apart, all in one "kd_dense" launch (see
+ * msa_prefill), and end the open batch.
  * The results do not depend on the batching.
  * Workspace: msa_prefill_varlen_workspace_size gives the size at which every
  * batch is formed; the minimum is one 128-query chunk of
@@ -286,7 +295,8 @@ MSA_API int msa_quantize_idx_k_e4m3(const uint16_t *idx_k, int64_t rows, int dI,
  * is bracketed by a pair of hipEvents recorded on the caller's stream; stages are
  * named "k1_index_pool", "k2_select", "k3_schedule" (its four small kernels as
  * one), "k4_kv_outer", "k5_combine", "k1d_index_pool", "k4d_split", "page_check",
- * "k1d_index_pool_fp8", "quantize_e4m3", "k4d_online" (decode's attention for up to
+ * "k1d_index_pool_fp8", "quantize_e4m3", "kd_dense" (the main branch of sequences
+ * of at most kslots blocks, as dense causal attention), "k4d_online" (decode's attention for up to
  * 16 heads per group: one launch, each slot folded into a running log-sum-exp merge,
  * used from 256 (sequence, group) pairs on), "k4d_parts" (the same for fewer pairs:
  * each pair's slots in parts, then "k5_combine" merges the parts), "k4d_merge"

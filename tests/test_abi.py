@@ -217,16 +217,21 @@ def test_varlen_workspace_size(lib):
         aq, akv = (I64 * len(cu_q))(*cu_q), (I64 * len(cu_kv))(*cu_kv)
         return lib.msa_prefill_varlen_workspace_size(aq, akv, len(cu_q) - 1, H, G, d, dI, 128, k)
 
-    def single(L):
-        return lib.msa_prefill_workspace_size(L, 16, 4, 128, 128, 128, 8)
+    def single(L, k=8):
+        return lib.msa_prefill_workspace_size(L, 16, 4, 128, 128, 128, k)
 
     assert lib.msa_prefill_varlen_workspace_size(None, None, 0, 16, 4, 128, 128, 128, 8) == 0
     assert ws([0, 5000], [0, 5000]) == single(5000)
-    cu = [512 * i for i in range(65)]              # 64 sequences of 512 tokens, one batch
-    assert ws(cu, cu) > single(512)
-    assert ws(cu, cu) >= 64 * 512 * 16 * 8 * 128 * 2   # the partials of every row
-    cu2 = [512 * i for i in range(201)]            # 200 sequences: batches of 128 and 72
-    assert ws(cu2, cu2) == ws(cu2[:129], cu2[:129])
+    # sequences of more than k blocks (640 tokens, k = 4) are batched
+    cu = [640 * i for i in range(65)]              # 64 sequences, one batch
+    assert ws(cu, cu, k=4) > single(640, k=4)
+    assert ws(cu, cu, k=4) >= 64 * 640 * 16 * 4 * 128 * 2   # the partials of every row
+    cu2 = [640 * i for i in range(201)]            # 200 sequences: batches of 128 and 72
+    assert ws(cu2, cu2, k=4) == ws(cu2[:129], cu2[:129], k=4)
+    # sequences of at most k blocks run the dense main branch, which needs no batch
+    # workspace: only the single-sequence size remains
+    cu3 = [512 * i for i in range(65)]
+    assert ws(cu3, cu3) == single(512)
     # a sequence with nothing new adds nothing
     assert ws([0, 0, 300], [0, 4096, 4396]) == ws([0, 300], [0, 300])
     # more than 8192 new tokens: that sequence runs alone, with its own workspace size

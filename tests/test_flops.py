@@ -80,6 +80,28 @@ def test_prefill_work_matches_closed_forms():
     assert w["flops"]["k12_index_select"] == 0.0
 
 
+def test_prefill_work_dense_sequences():
+    """A sequence of at most k blocks keeps all its causal blocks in every row: its
+    work is dense causal GQA attention (one kernel, no index branch)."""
+    H, G, d, dI, k = 64, 4, 128, 128, 16
+    for L in (512, 700, 2048):
+        w = bench.prefill_work(L, H, G, d, dI, k)
+        assert set(w["flops"]) == {"kd_dense"} and w["bytes"] == {}
+        assert w["flops"]["kd_dense"] == 4 * H * d * L * (L + 1) / 2 == w["f_total"]
+        assert w["pairs"] == 0.0
+        # the sparse path attends exactly the same tokens
+        assert w["attended_per_group"] == L * (L + 1) / 2
+    w = bench.prefill_work(2049, H, G, d, dI, k)          # k + 1 blocks: the sparse path
+    assert "kd_dense" not in w["flops"] and w["flops"]["k4_kv_outer"] > 0
+    w = bench.prefill_work(512, H, G, d, dI, k, dense_main=False)   # given ids
+    assert "kd_dense" not in w["flops"]
+    assert bench.KERNEL_ROOF["kd_dense"] == "mfma"
+    # staged K/V: a work-group holds 8 queries at r = 16; 64 tiles per 512 queries,
+    # tile t stages blocks 0 .. 8t // 128
+    staged = bench.prefill_work(512, H, G, d, dI, k)["design_bytes"]["kd_dense"]["kv_blocks_staged"]
+    assert staged == 16 * (1 + 2 + 3 + 4) * G * 2 * 128 * d * 2
+
+
 def test_decode_work():
     w = bench.decode_work(64, 262144, 64, 4, 128, 128, 16)
     # idx-K stream of all competitor blocks dominates: ~4 GiB of the ~4.57 GB step
