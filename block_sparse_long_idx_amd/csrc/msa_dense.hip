@@ -22,18 +22,96 @@
 
 namespace msa {
 
+// Staging of one key block for the whole work-group (256 threads), K straight into
+// LDS and V transposed through registers.  Keys past `last` (the partial last block
+// of a sequence) re-read key `last`: they lie past every query of the sequence, so
+// their scores are masked and their probabilities are exactly 0, and the rows read
+// are the sequence's own (finite) rows.
+//
+// K: LDS row p holds key k_lds_row<false>(p) (bits 2 and 3 swapped, an involution)
+// in the swz<D/8> layout, as K4 reads it; one wave instruction fills 1 KB, lane l
+// the bytes [16 l, 16 l + 16), fetching the global chunk that the swizzle puts there.
+template <int D>
+__device__ __forceinline__ void stage_k_direct(char *lds_k, const char *src, int stride_bytes,
+                                               int last, int tid) {
+    constexpr int CPR = D / 8;
+    constexpr int kSegs = kBlock * CPR * 16 / 1024;
+    constexpr int kMask = (CPR < 16 ? CPR : 16) - 1;
+    const int lane = tid % kWave, wave = tid / kWave;
+#pragma unroll
+    for (int it = 0; it < kSegs / 4; ++it) {
+        const int seg = it * 4 + wave;
+        const int pos = seg * 1024 + lane * 16;
+        const int prow = pos / (CPR * 16);
+        const int chunk = ((pos / 16) % CPR) ^ (prow & kMask);
+        const int key = min(k_lds_row<false>(prow), last);
+        __builtin_amdgcn_global_load_lds(src + (uint32_t)(key * stride_bytes + chunk * 16),
+                                         (lds_ptr_t)(lds_k + seg * 1024), 16, 0, 0);
+    }
+}
+
+// V^T in the swz_vt layout: thread (c, kq) loads chunk c (d = 8c .. 8c + 7) of keys
+// 4kq .. 4kq + 3 and writes, for each of its 8 d, those 4 keys as one 8-byte word
+// (halves picked with byte permutes).
+template <int D>
+struct VStageT {
+    static constexpr int CPR = D / 8;
+    static constexpr int kQuadsPerIter = 256 / CPR;
+    static constexpr int kIters = (kBlock / 4) / kQuadsPerIter;
+    u32x4 vr[kIters][4];
+
+    __device__ __forceinline__ void load(const char *src, int stride_bytes, int last, int tid) {
+        const int c = tid % CPR;
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int kq = tid / CPR + it * kQuadsPerIter;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                vr[it][kk] = load16(src + (uint32_t)(min(4 * kq + kk, last) * stride_bytes + c * 16));
+        }
+    }
+
+    __device__ __forceinline__ void store(char *lds_vt, int tid) const {
+        const int c = tid % CPR;
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int key0 = 4 * (tid / CPR + it * kQuadsPerIter);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int w = e >> 1;
+                // low halves (even e) or high halves (odd e) of two words, as one word
+                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                const uint32_t lo = __builtin_amdgcn_perm(vr[it][1][w], vr[it][0][w], sel);
+                const uint32_t hi = __builtin_amdgcn_perm(vr[it][3][w], vr[it][2][w], sel);
+                store8(lds_vt + swz_vt(8 * c + e, key0 >> 3) + ((key0 >> 2) & 1) * 8,
+                       u32x2{lo, hi});
+            }
+        }
+    }
+};
+
+// Running-maximum slack (log2 units): a block moves the maximum only when some
+// column of the wave exceeds it by more than this, so most blocks skip the rescale
+// of o; probabilities then stay below 2^8, far inside fp32 and bf16 range, and
+// out = o / l is unchanged (o and l share the same reference maximum).
+constexpr float kMaxSlack = 8.0f;
+
 // One key block for a wave's 32 columns: the core of K4's attention pass (same
 // operand layouts and relabelled contraction index), with the block's softmax taken
 // against the running maximum instead of the block's own.
-//   rel : the column's query position minus the block's first token; keys past it
-//         are masked (only in the query's own block, rel < 128)
+//   nmt  : M-tiles (32 keys each) computed, 1..4, wave-uniform; the others lie past
+//          every query of the wave and get probability 0 with no MFMA work
+//   mask : the queries' own block: keys past the column's query are masked
+//   rel  : the column's query position minus the block's first token
+//   rmin : the smallest rel of the wave (wave-uniform)
+//   first: the sequence's first block (o, l still zero; no rescale)
 //   o, M, l : the running fp32 output (unnormalised), maximum (scaled, log2 units)
 //             and sum of the column
 template <int D>
 __device__ __forceinline__ void dense_block(const char *lds_k, const char *lds_vt,
-                                            const bf16x8 (&qb)[D / 16], bool active, int rel,
-                                            float scale_log2, int lane, f32x16 (&o)[D / 32],
-                                            float &M, float &l) {
+                                            const bf16x8 (&qb)[D / 16], int rel, int rmin, int nmt,
+                                            bool mask, bool first, float scale_log2, int lane,
+                                            f32x16 (&o)[D / 32], float &M, float &l) {
     constexpr int KS = D / 16;
     constexpr int CPR = D / 8;
     constexpr int MD = D / 32;
@@ -42,44 +120,52 @@ __device__ __forceinline__ void dense_block(const char *lds_k, const char *lds_v
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         sc[mt] = f32x16{};
+        if (mt < nmt) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 a = as_bf16x8(load16(lds_k + swz<CPR>(mt * 32 + l32, 2 * ks + hf)));
-            sc[mt] = mfma32(a, qb[ks], sc[mt]);
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = as_bf16x8(load16(lds_k + swz<CPR>(mt * 32 + l32, 2 * ks + hf)));
+                sc[mt] = mfma32(a, qb[ks], sc[mt]);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
-    // register r of M-tile mt holds key 32mt + 16(ip/2) + 8hf + 4(ip%2) + jj
-    const bool local = active && rel < kBlock;
-    if (__ballot(local)) {
-        const int lim = local ? rel - 8 * hf : kBlock;
+    if (mask) {
+        // register r of M-tile mt holds key 32mt + 16(ip/2) + 8hf + 4(ip%2) + jj
+        const int lim = rel - 8 * hf;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt) {
+            if (mt >= nmt || 32 * mt + 31 <= rmin) continue;   // skipped, or all visible
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int ip = r >> 2, jj = r & 3;
                 const int key = 32 * mt + 16 * (ip >> 1) + 4 * (ip & 1) + jj;   // minus 8hf
                 if (key > lim) sc[mt][r] = -INFINITY;
             }
+        }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
+        if (mt < nmt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[mt][r]);
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[mt][r]);
     mx = fmaxf(mx, xor_shfl(mx, 32));
     // key 0 of every block up to the query's own is visible, so mx is finite
-    const float Mn = fmaxf(M, mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(M - Mn);   // 0 on the first block
+    const float ms = mx * scale_log2;
+    const bool grow = first || __ballot(ms > M + kMaxSlack) != 0;
+    const float Mn = grow ? fmaxf(M, ms) : M;
+    const float alpha = __builtin_amdgcn_exp2f(M - Mn);   // 1 when M stays; 0 on the first block
+    // skipped M-tiles keep their zero scores as probabilities 0
     float sum = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
+        if (mt < nmt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sc[mt][r], scale_log2, -Mn));
-            sc[mt][r] = p;
-            sum += p;
-        }
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(sc[mt][r], scale_log2, -Mn));
+                sc[mt][r] = p;
+                sum += p;
+            }
     sum += xor_shfl(sum, 32);
     l = fmaf(l, alpha, sum);
     M = Mn;
@@ -96,12 +182,16 @@ __device__ __forceinline__ void dense_block(const char *lds_k, const char *lds_v
     }
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
+        if (grow && !first) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[md][e] *= alpha;
+            for (int e = 0; e < 16; ++e) o[md][e] *= alpha;
+        }
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt) {
-            const bf16x8 a = as_bf16x8(load16(lds_vt + swz_vt(md * 32 + l32, 2 * kt + hf)));
-            o[md] = mfma32(a, pb[kt], o[md]);
+            if (kt < 2 * nmt) {
+                const bf16x8 a = as_bf16x8(load16(lds_vt + swz_vt(md * 32 + l32, 2 * kt + hf)));
+                o[md] = mfma32(a, pb[kt], o[md]);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -130,10 +220,12 @@ __global__ __launch_bounds__(256, 2) void kd_dense(const uint16_t *__restrict__ 
     const int P = t.prefix[m], L = t.len[m];
     const int i0 = P + (tile - t.tile_off[m]) * TILE;   // first query of the tile
     const int b = i0 / kBlock;                          // the tile's own block
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int hf = lane >> 5, l32 = lane & 31;
     const int a = l32 / R, h = l32 % R;
-    const int i = i0 + wave * QPW + a;                   // this column's query
+    const int qw = i0 + wave * QPW;                      // the wave's first query
+    const int i = qw + a;                                // this column's query
     const bool act = i < L;
     // rows of the column's query in q / out / ids; an inactive column reads the
     // tile's first query row and its result is discarded
@@ -149,24 +241,29 @@ __global__ __launch_bounds__(256, 2) void kd_dense(const uint16_t *__restrict__ 
     float M = -INFINITY, l = 0.0f;
     const int kv_row_bytes = G * D * 2;
     const int64_t kv0 = (int64_t)t.kv_row0[m];
-    for (int kb = 0; kb <= b; ++kb) {
+    for (int kb = 0;; ++kb) {
         if (kb > 0) __syncthreads();                     // the previous block is read
         {
-            // rows past the sequence's end (its last block) are staged as zeros;
-            // they lie past every query of the sequence and are masked
-            const int nrows = min(kBlock, L - kb * kBlock);
+            const int last = min(kBlock, L - kb * kBlock) - 1;
             const int64_t off = ((kv0 + (int64_t)kb * kBlock) * G + g) * D;
             // the staging addresses are recomputed per block (an opaque copy of the
             // thread index), not held across the loop beside the running output
             int stid = tid;
             asm volatile("" : "+v"(stid));
-            KVStage<D> st;
-            st.load(reinterpret_cast<const char *>(kx + off), reinterpret_cast<const char *>(vx + off),
-                    kv_row_bytes, nrows, stid);
-            st.store(lds_k, lds_vt, stid);
+            stage_k_direct<D>(lds_k, reinterpret_cast<const char *>(kx + off), kv_row_bytes, last,
+                              stid);
+            VStageT<D> vs;
+            vs.load(reinterpret_cast<const char *>(vx + off), kv_row_bytes, last, stid);
+            vs.store(lds_vt, stid);
+            __builtin_amdgcn_s_waitcnt(0);               // the direct K loads have landed
         }
         __syncthreads();
-        dense_block<D>(lds_k, lds_vt, qb, act, i - kb * kBlock, scale_log2, lane, o, M, l);
+        const bool own = kb == b;
+        const int rmin = qw - kb * kBlock;
+        const int nmt = own ? (rmin + QPW - 1) / 32 + 1 : 4;
+        dense_block<D>(lds_k, lds_vt, qb, i - kb * kBlock, rmin, nmt, own, kb == 0, scale_log2, lane,
+                       o, M, l);
+        if (own) break;
     }
     // ids of the column's query: every block 0 .. b, ascending, then -1
     if (ids && act && hf == 0)

@@ -495,10 +495,12 @@ def _short_batch(n, seed, max_len=700):
 
 
 def test_prefill_varlen_many_short_sequences():
-    """150 sequences of 1 to 700 tokens, a third of them continuing a cached prefix:
-    two batches (128 and 22 sequences) of one launch set each.  Every sequence's rows
-    equal its own whole-sequence prefill bitwise; sampled rows match the oracle."""
-    kw = dict(H=16, G=4, d=128, dI=128, k=8)
+    """150 sequences of 1 to 700 tokens, a third of them continuing a cached prefix,
+    at k = 4: those of at most 512 tokens go to the dense kernel (one launch), the
+    others run in batches of one launch set each (ended by the dense ones between
+    them).  Every sequence's rows equal its own whole-sequence prefill bitwise;
+    sampled rows match the oracle."""
+    kw = dict(H=16, G=4, d=128, dI=128, k=4)
     lens, prefixes = _short_batch(150, seed=61)
     _say(f"varlen 150 short sequences, {sum(lens)} tokens, {sum(L - P for L, P in zip(lens, prefixes))} new")
     shapes, xs, cu_q, cu_kv, c = _packed_case(lens, prefixes, kw, seed=600)
@@ -546,11 +548,12 @@ def test_prefill_varlen_batching_is_invisible():
 
 
 def test_prefill_varlen_long_and_short_mixed():
-    """Short sequences around one with more than 8192 new tokens: batches {300, 500},
-    the long one alone, then {100, 200, 1}.  Every sequence's rows equal its own
-    whole-sequence prefill bitwise."""
+    """Short sequences around one with more than 8192 new tokens: batches {1300, 1500},
+    the long one alone, then {1100, 1200}, and the one-token sequence (at most k
+    blocks) on the dense kernel.  Every sequence's rows equal its own whole-sequence
+    prefill bitwise."""
     kw = dict(H=16, G=4, d=128, dI=128, k=8)
-    lens, prefixes = [300, 500, 9000, 100, 200, 1], [0, 384, 256, 0, 128, 0]
+    lens, prefixes = [1300, 1500, 9000, 1100, 1200, 1], [0, 384, 256, 0, 128, 0]
     shapes, xs, cu_q, cu_kv, c = _packed_case(lens, prefixes, kw, seed=900)
     _say(f"varlen mixed lens={lens} prefixes={prefixes}")
     out, ids = _varlen(c, cu_q, cu_kv, kw["k"])
@@ -563,8 +566,9 @@ def test_prefill_varlen_long_and_short_mixed():
 
 def test_prefill_varlen_256x512_bench_config():
     """The benchmark's packed-prompt workload in its launch configuration: 256 prompts
-    of 512 tokens (H = 64, G = 4, d = dI = 128, k = 16), two batches of 128, the
-    workspace sized by msa_prefill_varlen_workspace_size.  Sampled prompts equal
+    of 512 tokens (H = 64, G = 4, d = dI = 128, k = 16), at most k blocks each, so two
+    dense-kernel launches of 128, the workspace sized by
+    msa_prefill_varlen_workspace_size.  Sampled prompts equal
     their own prefill bitwise; sampled rows match the oracle."""
     msa = _msa()
     wl = synth.WORKLOADS["prefill_varlen_256x512"]
@@ -593,6 +597,52 @@ def test_prefill_varlen_256x512_bench_config():
             _say(f"  prompt {b} -> {st}")
             assert st["id_mismatches"] == 0
             assert st["max_abs"] < _parity.MAX_ABS and st["mean_abs"] < _parity.MEAN_ABS
+
+
+@pytest.mark.parametrize("H,G,d,k,L", [
+    (64, 4, 128, 16, 2048),   # exactly k blocks, 16 heads per group
+    (8, 8, 64, 4, 385),       # one head per group; last block of one token
+    (16, 8, 128, 8, 1000),    # 2 heads per group
+    (32, 8, 64, 2, 256),      # 4 heads per group, two whole blocks
+    (64, 8, 128, 3, 300),     # 8 heads per group
+    (32, 1, 128, 2, 129),     # 32 heads per group
+    (16, 4, 64, 1, 77),       # k = 1, one partial block
+    (8, 2, 64, 6, 1),         # one token
+])
+def test_dense_sequences(H, G, d, k, L):
+    """Sequences of at most k blocks (every row keeps all its causal blocks): the
+    dense kernel against the oracle on every row, for each head-per-group width and
+    both head dims; and against the general path (msa_select_blocks, then
+    msa_sparse_attn on its ids): the same ids, outputs within rounding."""
+    msa = _msa()
+    shape = synth.PrefillShape(L=L, H=H, G=G, d=d, dI=64, B=128, k=k)
+    st, out, ids = _full_check(shape, seed=L + H)
+    x = synth.prefill_inputs(shape, seed=L + H)
+    dev = {n: t_.to(DEV) for n, t_ in x.items() if isinstance(t_, torch.Tensor)}
+    ids2 = msa.select_blocks(dev["iq"], dev["ik"], k=k)
+    out2 = msa.sparse_attn(dev["q"], dev["k"], dev["v"], ids2)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2)
+    diff = (out.float() - out2.float()).abs()
+    _say(f"  vs general path: max {diff.max().item():.3g}")
+    assert diff.max().item() < _parity.MAX_ABS
+
+
+def test_dense_sequences_packed_launches():
+    """150 dense sequences (k = 16, 1 to 2048 tokens, a third continuing a cached
+    prefix) in one msa_prefill_varlen call: two dense launches (128 + 22 members),
+    every sequence's rows bitwise equal to its own whole-sequence prefill."""
+    kw = dict(H=16, G=4, d=128, dI=64, k=16)
+    lens, prefixes = _short_batch(150, seed=71, max_len=2048)
+    shapes, xs, cu_q, cu_kv, c = _packed_case(lens, prefixes, kw, seed=1700)
+    _say(f"dense packed: {len(lens)} sequences, {sum(lens)} tokens")
+    out, ids = _varlen(c, cu_q, cu_kv, kw["k"])
+    for i, (sh, x, P) in enumerate(zip(shapes, xs, prefixes)):
+        sl = slice(int(cu_q[i]), int(cu_q[i + 1]))
+        o1, i1 = _prefill_gpu(x, sh.k)
+        assert torch.equal(ids[sl], i1[P:]), f"sequence {i} (L={sh.L}, P={P}): ids"
+        assert torch.equal(out[sl].view(torch.int16), o1[P:].view(torch.int16)), \
+            f"sequence {i} (L={sh.L}, P={P}): out"
 
 
 def test_prefix_prefill_32k_matches_whole():
