@@ -33,13 +33,15 @@ METRIC = "MSA prefill tokens/s @128K & 1M (1 GPU, % MFMA peak); decode us/step @
 DEFAULT_WORKLOAD = "prefill_L131072"
 # reported beside the default workload: (workload, timed steps, warm-up steps) -- the
 # other configurations of the metric (1M-token prefill with hot blocks, decode over
-# 64 x 262144 cached tokens), the L = 4096 and L = 32768 prefills, and decode over an
-# E4M3 index-key cache and over shuffled 128-token pages
+# 64 x 262144 cached tokens), the L = 4096 and L = 32768 prefills, decode over an
+# E4M3 index-key cache and over shuffled 128-token pages, and a packed prefill of 256
+# prompts of 512 tokens (sequences of at most k blocks: the dense main branch)
 # (sub-millisecond steps are timed over more steps, so that one slow step -- a host
 # hiccup between launches -- moves the mean little)
 ALSO_WORKLOADS = (("prefill_L1048576_hot", 3, 1), ("decode_N64_L262144", 50, 5),
                   ("tiny_prefill_L4096", 50, 5), ("prefill_L32768", 10, 3),
-                  ("decode_fp8idx_N64_L262144", 50, 5), ("decode_paged_N64_L262144", 50, 5))
+                  ("decode_fp8idx_N64_L262144", 50, 5), ("decode_paged_N64_L262144", 50, 5),
+                  ("prefill_varlen_256x512", 20, 5))
 PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12      # MI355X HBM3E
 B_BLOCK = 128
