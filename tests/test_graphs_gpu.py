@@ -131,9 +131,10 @@ def test_prefill_graph():
 
 
 def test_batched_varlen_graph():
-    """A batch of 20 short prompts (one launch set) captured once."""
+    """A batch of 20 short prompts captured once, at k = 2: those of at most 256
+    tokens go to one dense-kernel launch, the runs of longer ones to K1..K5 batches."""
     import block_sparse_long_idx_amd as msa
-    kw = dict(H=16, G=4, d=128, dI=128, k=8)
+    kw = dict(H=16, G=4, d=128, dI=128, k=2)
     lens = [1, 127, 128, 129, 300, 511, 640, 700, 50, 200, 333, 64, 600, 256, 257, 90, 10, 400,
             512, 128]
     parts = [synth.prefill_inputs(synth.PrefillShape(L=L, B=128, **kw), seed=300 + i)
