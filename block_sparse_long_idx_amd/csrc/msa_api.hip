@@ -74,7 +74,7 @@ AttnWs carve_attn(Carver &c, int64_t C, int H, int G, int d, int k, int nb) {
     w.sb.counts = c.take<int>(lists);
     w.sb.offs = c.take<int>(lists + 1);
     w.sb.toff = c.take<int>(lists + 1);
-    w.sb.wcnt = c.take<int>((int64_t)k3_num_groups(C) * lists);
+    w.sb.wcnt = c.take<int>((int64_t)k3_num_groups(C, G) * lists);
     w.sb.total = c.take<int>(1);
     const int64_t max_items = k4_max_items(C, G, k, nb);
     w.sb.items = c.take<int>(max_items);

@@ -14,8 +14,12 @@ constexpr int kK1KeyChunk = 32;
 constexpr int kK4Queries = 128;
 // Consecutive K4 work items that one XCD takes before the next XCD's turn.
 constexpr int kK4Run = 16;
-// Queries whose entries one K3 work-group sorts.
+// Queries whose entries one K3 work-group sorts (count and scatter passes); small
+// chunks use fewer, halving from kK3Queries while the passes would have fewer than
+// kK3TargetGroups work-groups, down to kK3MinQueries.
 constexpr int kK3Queries = 2048;
+constexpr int kK3MinQueries = 64;
+constexpr int kK3TargetGroups = 256;
 // Chunks of at most this many queries skip K4's run-order sort (their q rows are
 // few; three launches saved): K4 then runs the items in list order.
 constexpr int64_t kK3NoOrderQueries = 4096;
@@ -133,7 +137,7 @@ struct SchedBuffers {
     int *counts;     // [nlists]
     int *offs;       // [nlists + 1]
     int *toff;       // [nlists + 1] prefix sum of ceil(count / kK4Queries)
-    int *wcnt;       // [G * k3_num_groups(C) * nb] per-work-group counts / prefixes
+    int *wcnt;       // [G * k3_num_groups(C, G) * nb] per-work-group counts / prefixes
     int *total;      // [1] number of K4 work items
     int *items;      // [k4_max_items] list index of every K4 work item
     int *order;      // [k4_max_items] K4's run order: work items by (group, first query)
@@ -143,7 +147,8 @@ struct SchedBuffers {
 hipError_t launch_k3_schedule(const int32_t *ids, int64_t C, int G, int k, int nb,
                               const SchedBuffers &sb, const BatchMap &bm, hipStream_t s);
 int64_t k4_max_items(int64_t C, int G, int k, int nb);
-int k3_num_groups(int64_t C);
+int k3_queries_per_group(int64_t C, int G);
+int k3_num_groups(int64_t C, int G);
 int64_t k3_tile_groups(int64_t max_items);
 
 // K4: KV-outer attention over the scheduled lists -> partials per (query, head,

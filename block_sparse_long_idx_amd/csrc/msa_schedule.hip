@@ -5,7 +5,9 @@
 // "MiniMax M3 的采用瓶颈…" §对建设者的影响: KV-block-major layout).
 //
 // A counting sort with no global atomics.  Work-group (w, g) owns the entries of
-// group g for kK3Queries consecutive queries of the chunk:
+// group g for qpw consecutive queries of the chunk (kK3Queries, halved for small
+// chunks until the count and scatter passes have about kK3TargetGroups work-groups,
+// down to kK3MinQueries):
 //   count    per-work-group histogram over the group's blocks, in LDS
 //   colscan  per list: exclusive prefix of the work-group counts, list total
 //   scan     offs = exclusive prefix of the list totals; toff = exclusive prefix of
@@ -130,8 +132,8 @@ hipError_t launch_batch_setup(const BatchTable &t, BatchTable *dtab, int32_t *ro
     return hipGetLastError();
 }
 
-// Entries of one work-group: queries [w*kK3Queries, (w+1)*kK3Queries) of the chunk,
-// group g, all k slots; entry e -> query w*kK3Queries + e / k, slot e % k.  Returns
+// Entries of one work-group: queries [w*qpw, (w+1)*qpw) of the chunk, group g, all
+// k slots; entry e -> query w*qpw + e / k, slot e % k.  Returns
 // the entry's list block, or -1 for an id that is not scheduled: outside [0, nb),
 // or in a batch outside [0, b(row)] (then the list block is the global one).
 __device__ __forceinline__ int entry_block(const int32_t *ids, int64_t C, int G, int k, int nb,
@@ -148,14 +150,14 @@ __device__ __forceinline__ int entry_block(const int32_t *ids, int64_t C, int G,
 // Count pass: per-work-group histogram in LDS, written (zeros included) to
 // wcnt[(g * nW + w) * nb + b].  No global atomics.
 __global__ __launch_bounds__(256) void k3_count(const int32_t *__restrict__ ids, int64_t C, int G,
-                                                int k, int nb, const BatchMap bm,
+                                                int k, int nb, int qpw, const BatchMap bm,
                                                 int *__restrict__ wcnt) {
     extern __shared__ int lds_cnt[];
     const int w = blockIdx.x, g = blockIdx.y, nW = gridDim.x;
     for (int b = threadIdx.x; b < nb; b += 256) lds_cnt[b] = 0;
     __syncthreads();
-    const int64_t i0 = (int64_t)w * kK3Queries;
-    for (int e = threadIdx.x; e < kK3Queries * k; e += 256) {
+    const int64_t i0 = (int64_t)w * qpw;
+    for (int e = threadIdx.x; e < qpw * k; e += 256) {
         const int id = entry_block(ids, C, G, k, nb, bm, g, i0 + e / k, e % k);
         if (id >= 0) atomicAdd(&lds_cnt[id], 1);
     }
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(256) void k3_colscan(int *__restrict__ wcnt, int G,
 // Scatter pass: each work-group places its entries at
 // offs[list] + (entries of earlier work-groups) + (rank inside this work-group).
 __global__ __launch_bounds__(256) void k3_scatter(const int32_t *__restrict__ ids, int64_t C, int G,
-                                                  int k, int nb, const BatchMap bm,
+                                                  int k, int nb, int qpw, const BatchMap bm,
                                                   const int *__restrict__ offs,
                                                   const int *__restrict__ wcnt,
                                                   uint32_t *__restrict__ list) {
@@ -198,8 +200,8 @@ __global__ __launch_bounds__(256) void k3_scatter(const int32_t *__restrict__ id
         rank[b] = 0;
     }
     __syncthreads();
-    const int64_t i0 = (int64_t)w * kK3Queries;
-    for (int e = threadIdx.x; e < kK3Queries * k; e += 256) {
+    const int64_t i0 = (int64_t)w * qpw;
+    for (int e = threadIdx.x; e < qpw * k; e += 256) {
         const int64_t i = i0 + e / k;
         const int s = e % k;
         const int id = entry_block(ids, C, G, k, nb, bm, g, i, s);
@@ -336,15 +338,25 @@ int64_t k4_max_items(int64_t C, int G, int k, int nb) {
     return (entries + kK4Queries - 1) / kK4Queries + (lists < entries ? lists : entries);
 }
 
-int k3_num_groups(int64_t C) { return (int)((C + kK3Queries - 1) / kK3Queries); }
+int k3_queries_per_group(int64_t C, int G) {
+    int qpw = kK3Queries;
+    while (qpw > kK3MinQueries && ((C + qpw - 1) / qpw) * G < kK3TargetGroups) qpw >>= 1;
+    return qpw;
+}
+
+int k3_num_groups(int64_t C, int G) {
+    const int qpw = k3_queries_per_group(C, G);
+    return (int)((C + qpw - 1) / qpw);
+}
 
 hipError_t launch_k3_schedule(const int32_t *ids, int64_t C, int G, int k, int nb,
                               const SchedBuffers &sb, const BatchMap &bm, hipStream_t s) {
     const int nlists = G * nb;
-    const int nW = k3_num_groups(C);
+    const int qpw = k3_queries_per_group(C, G);
+    const int nW = k3_num_groups(C, G);
     hipError_t e;
     const dim3 grid((unsigned)nW, (unsigned)G);
-    hipLaunchKernelGGL(k3_count, grid, dim3(256), nb * sizeof(int), s, ids, C, G, k, nb, bm,
+    hipLaunchKernelGGL(k3_count, grid, dim3(256), nb * sizeof(int), s, ids, C, G, k, nb, qpw, bm,
                        sb.wcnt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k3_colscan, dim3((unsigned)((nlists + 255) / 256)), dim3(256), 0, s,
@@ -353,8 +365,8 @@ hipError_t launch_k3_schedule(const int32_t *ids, int64_t C, int G, int k, int n
     hipLaunchKernelGGL(k3_scan, dim3(1), dim3(1024), 0, s, sb.counts, nlists, sb.offs, sb.toff,
                        sb.total, sb.items);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k3_scatter, grid, dim3(256), 2 * nb * sizeof(int), s, ids, C, G, k, nb, bm,
-                       sb.offs, sb.wcnt, sb.list);
+    hipLaunchKernelGGL(k3_scatter, grid, dim3(256), 2 * nb * sizeof(int), s, ids, C, G, k, nb, qpw,
+                       bm, sb.offs, sb.wcnt, sb.list);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     // K4's run order: query windows of 2^sh rows, the smallest (at least 512) for
