@@ -27,13 +27,15 @@ namespace msa {
 
 constexpr int kK1Flush = 8;   // key blocks buffered in LDS between flushes
 
-// Work items are ordered key-chunk-major: for key chunk c, query blocks
-// qb in [max(qb0, 32c+1), qb1) -- each split into P parts of 128/P queries --
-// score key blocks [32c, min(32c+32, qb)).
-__device__ __forceinline__ bool k1_item(int64_t item, int qb0, int qb1, int P, int &qb, int &part,
-                                        int &c) {
+// Work items are ordered key-chunk-major: for key chunk c of kc blocks, query
+// blocks qb in [max(qb0, kc*c+1), qb1) -- each split into P parts of 128/P queries
+// -- score key blocks [kc*c, min(kc*c+kc, qb)).  Every (query, key block) score is
+// written by exactly one item whatever kc: kc = kK1KeyChunk, or fewer for a small
+// query range so that the launch has enough work-groups (k1_key_chunk).
+__device__ __forceinline__ bool k1_item(int64_t item, int qb0, int qb1, int P, int kc, int &qb,
+                                        int &part, int &c) {
     for (c = 0;; ++c) {
-        const int lo = max(qb0, c * kK1KeyChunk + 1);
+        const int lo = max(qb0, c * kc + 1);
         if (lo >= qb1) return false;
         const int64_t n = (int64_t)(qb1 - lo) * P;
         if (item < n) {
@@ -45,10 +47,10 @@ __device__ __forceinline__ bool k1_item(int64_t item, int qb0, int qb1, int P, i
     }
 }
 
-int64_t k1_num_items(int qb0, int qb1) {
+int64_t k1_num_items(int qb0, int qb1, int kc) {
     int64_t total = 0;
     for (int c = 0;; ++c) {
-        const int lo = qb0 > c * kK1KeyChunk + 1 ? qb0 : c * kK1KeyChunk + 1;
+        const int lo = qb0 > c * kc + 1 ? qb0 : c * kc + 1;
         if (lo >= qb1) break;
         total += qb1 - lo;
     }
@@ -74,7 +76,7 @@ template <int G> struct K1Tiling {
 template <int G, int DI, bool BATCH>
 __global__ __launch_bounds__(256, 2) void k1_index_pool(
     const uint16_t *__restrict__ iq, const uint16_t *__restrict__ ik, float *__restrict__ S,
-    int64_t q0, int64_t qend, int nbp, int qb0, int qb1, int64_t n_items,
+    int64_t q0, int64_t qend, int nbp, int qb0, int qb1, int64_t n_items, int kc,
     const BatchTable *__restrict__ tab) {
     constexpr int NT = K1Tiling<G>::NT;
     constexpr int NTHR = K1Tiling<G>::THREADS;
@@ -113,9 +115,9 @@ __global__ __launch_bounds__(256, 2) void k1_index_pool(
         if (item >= n_items * P) return;
     }
     int qb, part, c;
-    if (!k1_item(item, qb0, qb1, P, qb, part, c)) return;
-    const int j0 = c * kK1KeyChunk;
-    const int j1 = min(j0 + kK1KeyChunk, qb);
+    if (!k1_item(item, qb0, qb1, P, kc, qb, part, c)) return;
+    const int j0 = c * kc;
+    const int j1 = min(j0 + kc, qb);
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int hf = lane >> 5, l32 = lane & 31;
@@ -220,11 +222,17 @@ static hipError_t k1_dispatch(const uint16_t *iq, const uint16_t *ik, float *S, 
                               int64_t qend, int nbp, hipStream_t s) {
     const int qb0 = (int)(q0 / kBlock);
     const int qb1 = (int)((qend + kBlock - 1) / kBlock);
-    const int64_t n = k1_num_items(qb0, qb1);
+    // key chunk: halved from kK1KeyChunk while the launch would have fewer than two
+    // work-groups per CU (a short query range otherwise leaves most CUs idle and
+    // serialises each work-group's key blocks), down to kK1MinKeyChunk
+    int kc = kK1KeyChunk;
+    while (kc > kK1MinKeyChunk && k1_num_items(qb0, qb1, kc) * K1Tiling<G>::P < kK1MinWorkGroups)
+        kc /= 2;
+    const int64_t n = k1_num_items(qb0, qb1, kc);
     if (n == 0) return hipSuccess;
     const int64_t grid = round_up(n * K1Tiling<G>::P, 8);
     hipLaunchKernelGGL((k1_index_pool<G, DI, false>), dim3((unsigned)grid), dim3(K1Tiling<G>::THREADS),
-                       0, s, iq, ik, S, q0, qend, nbp, qb0, qb1, n, nullptr);
+                       0, s, iq, ik, S, q0, qend, nbp, qb0, qb1, n, kc, nullptr);
     return hipGetLastError();
 }
 
@@ -235,7 +243,7 @@ static hipError_t k1_dispatch_batch(const uint16_t *iq, const uint16_t *ik, floa
     const int64_t grid = round_up(t.k1_off[t.n], 8);
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((k1_index_pool<G, DI, true>), dim3((unsigned)grid), dim3(K1Tiling<G>::THREADS),
-                       0, s, iq, ik, S, 0, 0, nbp, 0, 0, 0, dtab);
+                       0, s, iq, ik, S, 0, 0, nbp, 0, 0, 0, kK1KeyChunk, dtab);
     return hipGetLastError();
 }
 

@@ -10,6 +10,10 @@ constexpr int kBlock = 128;   // tokens per MSA block (B)
 
 // Key blocks scored by one K1 work-group item, and blocks buffered before a flush.
 constexpr int kK1KeyChunk = 32;
+// A single-range K1 launch with fewer than kK1MinWorkGroups work-groups halves its
+// key chunk, down to kK1MinKeyChunk blocks.
+constexpr int kK1MinKeyChunk = 8;
+constexpr int kK1MinWorkGroups = 512;
 // Queries per K4 work item (one staged K/V block serves up to this many queries).
 constexpr int kK4Queries = 128;
 // Consecutive K4 work items that one XCD takes before the next XCD's turn.
@@ -31,8 +35,8 @@ constexpr int kK3Buckets = 2048;
 // Round n up to a multiple of m.
 inline int64_t round_up(int64_t n, int64_t m) { return (n + m - 1) / m * m; }
 
-// Number of K1 work items for the query blocks [qb0, qb1).
-int64_t k1_num_items(int qb0, int qb1);
+// Number of K1 work items for the query blocks [qb0, qb1), key chunks of kc blocks.
+int64_t k1_num_items(int qb0, int qb1, int kc = kK1KeyChunk);
 
 // K1: block scores S[(i-q0)*G + g][b] for queries i in [q0, qend), blocks b < b(i).
 hipError_t launch_k1_index_pool(const uint16_t *iq, const uint16_t *ik, float *S, int64_t L,
