@@ -173,12 +173,20 @@ __global__ __launch_bounds__(256) void k3_colscan(int *__restrict__ wcnt, int G,
     const int64_t l = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (l >= (int64_t)G * nb) return;
     const int g = (int)(l / nb), b = (int)(l % nb);
+    int *col = wcnt + (int64_t)g * nW * nb + b;   // work-group w's count at col[w * nb]
+    // the counts are read 16 at a time before any prefix is written, so that a
+    // batch's loads are in flight together rather than one round trip per count
+    constexpr int kBatch = 16;
     int run = 0;
-    for (int w = 0; w < nW; ++w) {
-        int *p = wcnt + ((int64_t)g * nW + w) * nb + b;
-        const int c = *p;
-        *p = run;
-        run += c;
+    for (int w0 = 0; w0 < nW; w0 += kBatch) {
+        int c[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) c[j] = w0 + j < nW ? col[(int64_t)(w0 + j) * nb] : 0;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (w0 + j < nW) col[(int64_t)(w0 + j) * nb] = run;
+            run += c[j];
+        }
     }
     counts[l] = run;
 }
